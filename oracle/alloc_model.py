@@ -1,0 +1,127 @@
+"""Fixed-block free-list allocator with refcounted shared blocks (reference model).
+
+"Paged Attention and KV Cache Fragmentation" (inferenceengineering.co),
+section "How PagedAttention maps an OS concept onto GPU memory": every block
+has the same size, so a freed block always fits any later need; blocks are
+taken only as a sequence actually grows and returned the moment it finishes;
+requests that share a prefix (or beam-search branches) point at the same
+physical blocks.  "KV Cache Fragmentation" field guide (defragging.ai),
+section "Why it matters": sharing makes forks cheap.
+
+Readings where the pages are silent (the product allocator reproduces them
+bit for bit):
+  * the free list is a LIFO stack; with initial order o, the first pops return
+    o[0], o[1], ... ;
+  * append of n tokens needs ceil((len+n)/bs) - ceil(len/bs) new blocks, popped
+    in logical order; it is all-or-nothing;
+  * a sequence whose last, partly filled block is shared (refcount > 1) cannot
+    grow in place (the shared block would be written for every sharer);
+  * fork: the child gets the parent's block list and length, each block's
+    refcount goes up by one;
+  * free: logical blocks are visited last to first, refcount goes down, a block
+    reaching zero is pushed, so the next pops return the freed sequence's blocks
+    in their original logical order.
+"""
+from __future__ import annotations
+
+from enum import IntEnum
+
+
+class Status(IntEnum):
+    OK = 0
+    INVALID_ARG = -1
+    UNSUPPORTED = -2
+    OUT_OF_BLOCKS = -3
+    UNKNOWN_SEQ = -4
+    SHARED_BLOCK = -5
+
+
+def _ceil_div(a, b):
+    return -(-a // b)
+
+
+class AllocModel:
+    def __init__(self, NB: int, bs: int, initial_free_order=None):
+        if NB <= 0 or bs <= 0:
+            raise ValueError("NB and bs must be positive")
+        order = list(range(NB)) if initial_free_order is None else [int(x) for x in initial_free_order]
+        if sorted(order) != list(range(NB)):
+            raise ValueError("initial_free_order must be a permutation of 0..NB-1")
+        self.NB, self.bs = NB, bs
+        self.stack = order[::-1]  # top of stack = end of list = order[0]
+        self.rc = [0] * NB
+        self.blocks = {}
+        self.lens = {}
+
+    def num_free(self) -> int:
+        return len(self.stack)
+
+    def seq_add(self, seq) -> int:
+        if seq in self.blocks:
+            return Status.INVALID_ARG
+        self.blocks[seq] = []
+        self.lens[seq] = 0
+        return Status.OK
+
+    def append_slots(self, seq, n):
+        if seq not in self.blocks:
+            return Status.UNKNOWN_SEQ, None
+        if n < 0:
+            return Status.INVALID_ARG, None
+        blocks, L, bs = self.blocks[seq], self.lens[seq], self.bs
+        if n > 0 and L % bs != 0 and self.rc[blocks[-1]] > 1:
+            return Status.SHARED_BLOCK, None
+        need = _ceil_div(L + n, bs) - _ceil_div(L, bs)
+        if need > len(self.stack):
+            return Status.OUT_OF_BLOCKS, None
+        for _ in range(need):
+            blk = self.stack.pop()
+            self.rc[blk] = 1
+            blocks.append(blk)
+        slots = [blocks[p // bs] * bs + p % bs for p in range(L, L + n)]
+        self.lens[seq] = L + n
+        return Status.OK, slots
+
+    def fork(self, parent, child) -> int:
+        if parent not in self.blocks:
+            return Status.UNKNOWN_SEQ
+        if child in self.blocks:
+            return Status.INVALID_ARG
+        self.blocks[child] = list(self.blocks[parent])
+        self.lens[child] = self.lens[parent]
+        for blk in self.blocks[child]:
+            self.rc[blk] += 1
+        return Status.OK
+
+    def free(self, seq) -> int:
+        if seq not in self.blocks:
+            return Status.UNKNOWN_SEQ
+        for blk in reversed(self.blocks[seq]):
+            self.rc[blk] -= 1
+            if self.rc[blk] == 0:
+                self.stack.append(blk)
+        del self.blocks[seq]
+        del self.lens[seq]
+        return Status.OK
+
+    def seq_len(self, seq):
+        if seq not in self.blocks:
+            return Status.UNKNOWN_SEQ, None
+        return Status.OK, self.lens[seq]
+
+    def block_tables(self, seqs, max_blocks):
+        import numpy as np
+        table = np.full((len(seqs), max_blocks), -1, np.int32)
+        lens = np.zeros(len(seqs), np.int32)
+        for i, s in enumerate(seqs):
+            if s not in self.blocks:
+                return Status.UNKNOWN_SEQ, None, None
+            blocks = self.blocks[s]
+            if len(blocks) > max_blocks:
+                return Status.INVALID_ARG, None, None
+            table[i, :len(blocks)] = blocks
+            lens[i] = self.lens[s]
+        return Status.OK, table, lens
+
+    def refcount(self, blk) -> int:
+        return self.rc[blk]
