@@ -1,0 +1,297 @@
+#!/usr/bin/env python3
+"""Paged-KV decode benchmark on one MI355X.
+
+A step is one pass of the whole hot path over one batch: kv_append of this step's token
+for every sequence, then paged decode attention of every sequence's query over its paged
+KV (context-split partition kernel + split merge).  The default workload is a
+Llama-3.1-70B-shaped layer: 32 sequences at 8192 tokens (16 of them share one refcounted
+2048-token prefix), H_q 64, H_kv 8, head dim 128, bf16 KV, 16-token blocks scattered by
+the allocator.  Inputs are synthetic and resident in HBM before the timed region.
+
+Prints one JSON line.  `value` = algorithmic bytes of the step / step time in GB/s
+(KV counted once per distinct physical block).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "paged decode attention KV GB/s (% of HBM peak) and sequences/s per layer"
+HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E
+KERNEL_SOURCE = os.path.join(ROOT, "paged_kv_cache_223_amd", "csrc", "paged_decode.hip")
+COUNTERS = os.path.join(ROOT, "profiles", "decode_counters.json")
+
+WORKLOADS = {
+    "llama70b": ("llama70b_bf16", {}),
+    "llama8b": ("llama8b_bf16", {}),
+    "long128k": ("long128k_bf16", {}),
+    "fp8_bs8": ("mixed_fp8", {"bs": 8}),
+    "fp8_bs16": ("mixed_fp8", {"bs": 16}),
+    "fp8_bs32": ("mixed_fp8", {"bs": 32}),
+}
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=200)
+    p.add_argument("--warmup", type=int, default=20)
+    p.add_argument("--workload", default="llama70b", choices=sorted(WORKLOADS))
+    p.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the oracle baseline sample")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--identity-tables", action="store_true",
+                   help="lay every sequence out contiguously (identity block order) instead of scattered")
+    return p.parse_args()
+
+
+# ----------------------------------------------------------------------------- byte accounting
+def algorithmic_bytes(tables, lens, bs, B, H_q, H_kv, D, s_kv, s_q, T_append, s_src):
+    """Bytes the step must move at minimum.
+
+    decode: K and V of every distinct physical block the batch touches (the token positions
+    some sequence attends to), q, the fp32 output, the used table entries, the lengths and the
+    fp8 scales.  append: this step's K/V rows read and written, plus their slots.
+    """
+    used = {}
+    logical_tok = 0
+    tab_entries = 0
+    for row, n in zip(tables, lens):
+        n = int(n)
+        logical_tok += n
+        nb = -(-n // bs)
+        tab_entries += nb
+        for j in range(nb):
+            blk = int(row[j])
+            used[blk] = max(used.get(blk, 0), min(bs, n - j * bs))
+    per_tok = H_kv * D * 2 * s_kv
+    kv_unique = sum(used.values()) * per_tok
+    kv_logical = logical_tok * per_tok
+    other = B * H_q * D * s_q + B * H_q * D * 4 + tab_entries * 4 + B * 4 + (2 * H_kv * 4 if s_kv == 1 else 0)
+    append = T_append * H_kv * D * 2 * (s_src + s_kv) + T_append * 8
+    return dict(kv_unique=kv_unique, kv_logical=kv_logical, decode=kv_unique + other,
+                decode_logical=kv_logical + other, append=append)
+
+
+def source_hash(path):
+    return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
+
+
+def measured_traffic(workload):
+    """HBM bytes per decode launch from committed rocprofv3 counter runs, if they were taken
+    on the current kernel source and this workload; else None."""
+    try:
+        rec = json.load(open(COUNTERS))
+    except (OSError, ValueError):
+        return None
+    ent = rec.get(workload)
+    if not ent or ent.get("source_sha256_16") != source_hash(KERNEL_SOURCE):
+        return None
+    return ent.get("hbm_bytes_per_launch")
+
+
+# ----------------------------------------------------------------------------- main
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the decode path is not sharded "
+              "across GPUs in this build.", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    import paged_kv_cache_223_amd as pkv
+    import workloads
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = "cuda"
+    t_setup = time.time()
+    wname, kw = WORKLOADS[args.workload]
+    case = workloads.BUILDERS[wname](**kw)
+    if args.identity_tables:
+        case.initial_free_order = np.arange(case.NB, dtype=np.int32)
+    spec = case.spec
+    mat = workloads.materialize(case, pkv.Allocator(case.NB, case.bs, case.initial_free_order))
+    kvd = {"bf16": pkv.BF16, "e4m3": pkv.FP8_E4M3, "f32": pkv.F32}[spec.kv_dtype]
+    ks, vs = pkv.pool_shapes(case.NB, spec.H_kv, spec.d, case.bs, kvd)
+    pool_dt = {"bf16": torch.bfloat16, "e4m3": torch.uint8, "f32": torch.float32}[spec.kv_dtype]
+    k_pool = torch.zeros(ks, dtype=pool_dt, device=dev)
+    v_pool = torch.zeros(vs, dtype=pool_dt, device=dev)
+
+    def up(a, dt):
+        a = np.ascontiguousarray(a)
+        if dt == "bf16":
+            return torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
+        return torch.from_numpy(a).to(dev)
+
+    sd = "f32" if spec.kv_dtype == "f32" else "bf16"
+    k_scale = None if case.k_scale is None else torch.from_numpy(case.k_scale).to(dev)
+    v_scale = None if case.v_scale is None else torch.from_numpy(case.v_scale).to(dev)
+    CH = 65536
+    for i in range(0, len(mat.slots), CH):  # prefill the pools through the library's own append
+        pkv.kv_append(up(mat.k_src[i:i + CH], sd), up(mat.v_src[i:i + CH], sd),
+                      torch.from_numpy(mat.slots[i:i + CH]).to(dev), k_pool, v_pool, k_scale, v_scale)
+    step_k, step_v = up(mat.step_k, sd), up(mat.step_v, sd)
+    step_slots = torch.from_numpy(mat.step_slots).to(dev)
+    q = up(case.q, spec.q_dtype)
+    tables = torch.from_numpy(mat.block_tables).to(dev)
+    lens = torch.from_numpy(mat.context_lens).to(dev)
+    B, H_q, H_kv, D = case.B, spec.H_q, spec.H_kv, spec.d
+    mcl = case.max_context_len
+    out = torch.empty((B, H_q, D), dtype=torch.float32, device=dev)
+    wsb = pkv.decode_workspace_bytes(B, H_q, H_kv, D, mcl, case.bs)
+    ws = torch.empty(max(wsb, 256), dtype=torch.uint8, device=dev)
+    torch.cuda.synchronize()
+    print(f"# setup {time.time() - t_setup:.1f}s: {wname} B={B} NB={case.NB} pool {2 * k_pool.numel() * k_pool.element_size() / 1e9:.2f} GB",
+          file=sys.stderr, flush=True)
+
+    def step(e0=None, e1=None, e2=None):
+        if e0 is not None:
+            e0.record()
+        if len(mat.step_slots):
+            pkv.kv_append(step_k, step_v, step_slots, k_pool, v_pool, k_scale, v_scale)
+        if e1 is not None:
+            e1.record()
+        pkv.paged_attn_decode(q, k_pool, v_pool, tables, lens, float(case.scale), mcl, k_scale, v_scale,
+                              out=out, workspace=ws)
+        if e2 is not None:
+            e2.record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    K = args.steps
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
+    t0 = time.perf_counter()
+    for i in range(K):
+        step(*ev[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    append_ms = np.array([e[0].elapsed_time(e[1]) for e in ev])
+    decode_ms = np.array([e[1].elapsed_time(e[2]) for e in ev])
+    step_ms = ev[0][0].elapsed_time(ev[-1][2]) / K
+    print(f"# timed {K} steps in {wall:.3f}s wall; decode p10/p50/p90 "
+          f"{np.percentile(decode_ms, 10) * 1e3:.1f}/{np.median(decode_ms) * 1e3:.1f}/{np.percentile(decode_ms, 90) * 1e3:.1f} us",
+          file=sys.stderr, flush=True)
+
+    s_kv = {"bf16": 2, "e4m3": 1, "f32": 4}[spec.kv_dtype]
+    s_q = 4 if spec.q_dtype == "f32" else 2
+    s_src = 4 if sd == "f32" else 2
+    by = algorithmic_bytes(mat.block_tables, mat.context_lens, case.bs, B, H_q, H_kv, D, s_kv, s_q,
+                           len(mat.step_slots), s_src)
+    dec_avg_s = decode_ms.mean() / 1e3
+    dec_gbps = by["decode"] / dec_avg_s / 1e9
+    step_gbps = (by["decode"] + by["append"]) / (step_ms / 1e3) / 1e9
+
+    # practical read ceiling: the library's 16-byte streaming read over 4 GiB
+    buf = torch.empty(4 << 30, dtype=torch.uint8, device=dev)
+    sink = pkv.stream_read(buf)
+    torch.cuda.synchronize()
+    r0, r1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    r0.record()
+    for _ in range(10):
+        pkv.stream_read(buf, sink)
+    r1.record()
+    torch.cuda.synchronize()
+    ceiling = buf.numel() * 10 / (r0.elapsed_time(r1) / 1e3) / 1e9
+    del buf
+
+    res = {
+        "metric": METRIC,
+        "value": round(step_gbps, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(step_ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": spec.kv_dtype,
+        "data": "synthetic (seeded N(0,1) K/V/q rounded to the KV dtype; allocator-scattered block tables)",
+        "config": {
+            "workload": spec.desc, "batch": B, "H_q": H_q, "H_kv": H_kv, "head_dim": D, "block_size": case.bs,
+            "max_context": mcl, "mean_context": float(np.mean(mat.context_lens)), "pool_blocks": case.NB,
+            "append_tokens_per_step": int(len(mat.step_slots)),
+            "tables": "identity" if args.identity_tables else "scattered",
+        },
+        "seqs_per_s": round(B / (step_ms / 1e3), 1),
+        "frac_of_hbm_peak": round(step_gbps / HBM_PEAK_GBPS, 4),
+        "decode_us_p50": round(float(np.median(decode_ms)) * 1e3, 2),
+        "append_us_p50": round(float(np.median(append_ms)) * 1e3, 2),
+        "decode_GBps_unique": round(dec_gbps, 1),
+        "decode_GBps_logical": round(by["decode_logical"] / dec_avg_s / 1e9, 1),
+        "kv_bytes_unique": by["kv_unique"],
+        "kv_bytes_logical": by["kv_logical"],
+        "read_ceiling_GBps": round(ceiling, 1),
+        "frac_of_read_ceiling": round(step_gbps / ceiling, 4),
+    }
+    traffic = measured_traffic(args.workload)
+    res["roofline"] = {
+        "bound": "hbm", "kernel": "paged_attn_decode (context-split partition + split merge)",
+        "achieved": round(dec_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+        "frac": round(dec_gbps / HBM_PEAK_GBPS, 4),
+        "algorithmic_bytes_per_launch": by["decode"],
+        "avg_launch_us": round(dec_avg_s * 1e6, 2),
+        "traffic": traffic,
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(case, mat, out, args.cpu_seconds, by, B)
+    print(json.dumps(res), flush=True)
+
+
+def cpu_baseline(case, mat, out_dev, budget_s, by, B):
+    """The oracle (numpy fp64 gather-then-attend) on a bounded sample of the same batch."""
+    import oracle
+
+    spec = case.spec
+    sd = "f32" if spec.kv_dtype == "f32" else "bf16"
+    sample = list(range(0, B, max(1, B // 16)))[:16]  # up to 16 sequences spread over the batch
+    used = set()
+    for b in sample:
+        used.update(int(x) for x in mat.block_tables[b, :-(-int(mat.context_lens[b]) // case.bs)])
+    used = np.array(sorted(used), np.int64)
+    kp, vp = oracle.empty_pools(case.NB, spec.H_kv, spec.d, case.bs, spec.kv_dtype)
+    for k, v, s in ((mat.k_src, mat.v_src, mat.slots), (mat.step_k, mat.step_v, mat.step_slots)):
+        if len(s):
+            keep = np.isin(s // case.bs, used)
+            kp, vp = oracle.ref_append(kp, vp, k[keep], v[keep], sd, s[keep], case.bs, spec.kv_dtype,
+                                       case.k_scale, case.v_scale)
+    got = out_dev.cpu().numpy().astype(np.float64)
+    rows, errs = [], []
+    t0 = time.perf_counter()
+    for b in sample:
+        ref = oracle.ref_decode(case.q, spec.q_dtype, kp, vp, spec.kv_dtype, mat.block_tables, mat.context_lens,
+                                case.scale, case.bs, case.k_scale, case.v_scale, rows=[b])
+        rows.append(b)
+        den = np.abs(ref[b]).max(-1)
+        errs.append(float((np.abs(got[b] - ref[b]).max(-1) / den).max()))
+        if time.perf_counter() - t0 > budget_s:
+            break
+    dt = time.perf_counter() - t0
+    toks = int(sum(int(mat.context_lens[b]) for b in rows))
+    kv = toks * spec.H_kv * spec.d * 2 * {"bf16": 2, "e4m3": 1, "f32": 4}[spec.kv_dtype]
+    try:
+        from threadpoolctl import threadpool_info
+        blas = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
+    except Exception:  # threadpoolctl missing: report the process's CPU affinity
+        blas = len(os.sched_getaffinity(0))
+    return {
+        "value": round(len(rows) / dt, 3), "unit": "sequences/s", "cores": int(blas), "kind": "oracle",
+        "sample": f"{len(rows)} of {B} sequences ({toks} tokens, all heads), numpy fp64 gather-then-attend",
+        "kv_GBps": round(kv / dt / 1e9, 3), "seconds": round(dt, 2), "host_cpus": os.cpu_count(),
+        "affinity_cpus": len(os.sched_getaffinity(0)),
+        "gpu_vs_oracle_max_row_rel_err": float(max(errs)),
+    }
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,199 @@
+/*
+ * pkv.h — C ABI of the paged-KV decode-attention library for AMD MI355X (gfx950).
+ *
+ * The method ("KV Cache Fragmentation" field guide, defragging.ai, section
+ * "Definition"; "Paged Attention and KV Cache Fragmentation",
+ * inferenceengineering.co, section "How PagedAttention maps an OS concept onto
+ * GPU memory"): the KV cache lives in one pool of fixed-size physical blocks;
+ * each sequence owns a block table mapping its logical block j to a physical
+ * block; blocks are taken only as a sequence grows, returned when it finishes,
+ * and may be shared by several sequences (a common prefix, a fork).  The
+ * attention kernel walks the table.
+ *
+ * Three groups of calls:
+ *   pkv_kv_append          scatter this step's K/V rows into their slots
+ *   pkv_paged_attn_decode  one query token per sequence attends over its paged KV
+ *   pkv_alloc_* / pkv_seq_* host-side fixed-block free-list allocator
+ *
+ * ---------------------------------------------------------------------------
+ * Conventions
+ *   - Every call returns an int status (PKV_OK or a negative PKV_ERR_*);
+ *     pkv_last_error() returns a thread-local message for the last failure.
+ *   - Device pointers are owned by the caller (e.g. torch tensors), must be
+ *     contiguous in the layouts below and live on the current HIP device.
+ *     The library never allocates device memory: scratch for the decode's
+ *     split-context partials is passed in as `workspace`.
+ *   - Device calls are asynchronous on the caller's stream (`stream` is a
+ *     hipStream_t passed as void*; NULL = the null stream) and never
+ *     synchronize.  Scalar arguments are validated on the host before any
+ *     launch; an invalid call launches nothing.  Device-resident contents
+ *     (slots, block ids, lengths) are not validated for meaning, but the
+ *     kernels never read or write outside the buffers described here:
+ *     an out-of-range slot is skipped, an out-of-range block id is read as
+ *     block 0, a length beyond the table or beyond max_context_len is cut to
+ *     it.  Such inputs are caller errors with unspecified results.
+ *   - The allocator object is host memory only and is not thread-safe.
+ *
+ * Element types (PKV_*): fp32, bf16, and OCP FP8 E4M3FN (1 sign, 4 exponent
+ * bits with bias 7, 3 mantissa bits, no infinities, S.1111.111 = NaN, max 448).
+ * An E4M3 pool carries one fp32 scale per KV head for K and one for V
+ * (real value = code value * scale), device arrays of H_kv floats.
+ *
+ * Pool layout.  NB physical blocks of bs tokens; inside a block every KV
+ * head owns a contiguous tile (D = head dim, X = 16 bytes / element size):
+ *     K pool  [NB][H_kv][D/X][bs][X]
+ *     V pool  [NB][H_kv][D][bs]
+ * Token position p of a sequence with table row T lives at slot
+ * s = T[p / bs] * bs + p % bs (block s / bs, offset s % bs).
+ * GQA: query head h reads KV head h / (H_q / H_kv).
+ */
+#ifndef PKV_H
+#define PKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum pkv_status {
+  PKV_OK = 0,
+  PKV_ERR_INVALID_ARG = -1,   /* bad pointer, size, shape or id */
+  PKV_ERR_UNSUPPORTED = -2,   /* valid but not implemented (dtype / bs / D / G combination) */
+  PKV_ERR_OUT_OF_BLOCKS = -3, /* the pool cannot hold the request; allocator state unchanged */
+  PKV_ERR_UNKNOWN_SEQ = -4,   /* sequence id not present */
+  PKV_ERR_SHARED_BLOCK = -5,  /* growth would write into a shared, partly filled block */
+  PKV_ERR_HIP = -6            /* the HIP runtime reported an error (message has details) */
+};
+
+enum pkv_dtype { PKV_F32 = 0, PKV_BF16 = 1, PKV_FP8_E4M3 = 2 };
+
+/* Thread-local text of the last error set by a call on this thread ("" if none). */
+const char* pkv_last_error(void);
+
+/* ABI version (bumped on incompatible changes). */
+int pkv_abi_version(void);
+
+/*
+ * pkv_kv_append — write T tokens' K and V rows into their slots.
+ * ("Paged Attention and KV Cache Fragmentation", section "How PagedAttention
+ * maps an OS concept onto GPU memory": a sequence's new tokens go into the
+ * blocks its table maps them to.)
+ *
+ *   k, v           device, [T][H_kv][D] of src_dtype, row-major
+ *   slot_mapping   device int64 [T]; slot < 0 = padding, skipped;
+ *                  slot >= NB*bs is skipped (caller error); duplicate slots
+ *                  within one call are a caller error (unspecified winner)
+ *   k_pool, v_pool device, layouts above, pool_dtype
+ *   k_scale, v_scale device fp32 [H_kv], required iff pool_dtype = E4M3
+ *   Supported (src -> pool): F32->F32, BF16->BF16, E4M3->E4M3 (copy),
+ *   BF16->E4M3 (quantise: y = fp32(x) / scale[h] with IEEE fp32 division,
+ *   then round to nearest even E4M3; |y| >= 448 and +-inf saturate to +-448,
+ *   NaN becomes 0x7F with the input's sign).
+ *   D must be a multiple of 16 and <= 512; bs in 1..256.
+ */
+int pkv_kv_append(const void* k, const void* v, int src_dtype, const int64_t* slot_mapping,
+                  int32_t T, void* k_pool, void* v_pool, int pool_dtype, int32_t NB, int32_t bs,
+                  int32_t H_kv, int32_t D, const float* k_scale, const float* v_scale,
+                  void* stream);
+
+/*
+ * pkv_decode_workspace_bytes — size of the scratch buffer pkv_paged_attn_decode
+ * needs for these sizes (0 is possible).  The same arguments must be passed to
+ * the decode call.  Returns 0 and sets the last error for invalid sizes.
+ */
+size_t pkv_decode_workspace_bytes(int32_t B, int32_t H_q, int32_t H_kv, int32_t D,
+                                  int32_t max_context_len, int32_t bs);
+
+/*
+ * pkv_paged_attn_decode — one query token per sequence attends over its paged KV.
+ * For sequence b with n = context_lens[b] and query head h (KV head g):
+ *     out[b][h] = sum_{t<n} softmax_t(scale * <q[b][h], K_b[g][t]>) V_b[g][t]
+ * where K_b, V_b are the sequence's tokens in logical order reached through
+ * block_tables[b] (the kernel never materialises the scores in device memory:
+ * an online softmax per context split, then a merge of the splits).  n = 0
+ * gives a zero row.  context_lens counts the token appended this step.
+ *
+ *   out            device fp32 [B][H_q][D]
+ *   q              device [B][H_q][D], q_dtype F32 or BF16
+ *   k_pool, v_pool device, kv_dtype, layouts above
+ *   block_tables   device int32 [B][max_blocks_per_seq]; entries past
+ *                  ceil(n/bs) are ignored (may be -1)
+ *   context_lens   device int32 [B]
+ *   max_context_len host hint >= max(context_lens) (sizes the launch without
+ *                  a device->host read); lengths above it are cut to it
+ *   scale          softmax scale (e.g. 1/sqrt(D)), applied to q.k in fp32
+ *   k_scale, v_scale device fp32 [H_kv], required iff kv_dtype = E4M3
+ *   workspace      device scratch of >= pkv_decode_workspace_bytes(...) bytes,
+ *                  256-byte aligned; contents need no initialisation and are
+ *                  clobbered; calls that share a workspace must be ordered
+ *   Requires H_q % H_kv == 0, D in {64, 128, 256}, bs in {8, 16, 32}.
+ *   bf16 q with bf16/E4M3 KV, H_q/H_kv <= 16 and D in {64, 128} take the
+ *   matrix-core path; other supported combinations take a vector path.
+ *   All accumulation is fp32.
+ */
+int pkv_paged_attn_decode(float* out, const void* q, int q_dtype, const void* k_pool,
+                          const void* v_pool, int kv_dtype, const int32_t* block_tables,
+                          int32_t max_blocks_per_seq, const int32_t* context_lens,
+                          int32_t max_context_len, int32_t B, int32_t H_q, int32_t H_kv,
+                          int32_t D, int32_t NB, int32_t bs, float scale, const float* k_scale,
+                          const float* v_scale, void* workspace, size_t workspace_bytes,
+                          void* stream);
+
+/* ---------------------------------------------------------------------------
+ * Host allocator: fixed-size blocks, LIFO free list, per-block refcounts.
+ * ("Paged Attention and KV Cache Fragmentation", section "How PagedAttention
+ * maps an OS concept onto GPU memory": new blocks only as a sequence grows,
+ * freed the moment it finishes; every block has the same size so a freed
+ * block always fits; shared prefixes point at the same physical blocks.
+ * "KV Cache Fragmentation" field guide, section "Why it matters": cheap forks.)
+ *
+ * Semantics (deterministic, so block ids are reproducible):
+ *   - the free list is a stack; initially the first pops return
+ *     initial_free_order[0], [1], ... (NULL = 0, 1, ..., NB-1);
+ *   - append of n tokens to a sequence of length L takes
+ *     ceil((L+n)/bs) - ceil(L/bs) blocks, popped in logical order;
+ *     it is all-or-nothing: on PKV_ERR_OUT_OF_BLOCKS nothing changes;
+ *     if L % bs != 0, n > 0 and the last block is shared (refcount > 1)
+ *     it fails with PKV_ERR_SHARED_BLOCK and nothing changes;
+ *   - fork: the child (a new id) gets the parent's blocks and length, and
+ *     each of those blocks' refcount goes up by one;
+ *   - free: the sequence's blocks are visited last to first, refcount goes
+ *     down, blocks reaching zero are pushed on the free list.
+ * -------------------------------------------------------------------------*/
+typedef struct pkv_allocator pkv_allocator;
+
+int pkv_alloc_create(int32_t NB, int32_t bs, const int32_t* initial_free_order /* host, NB, or NULL */,
+                     pkv_allocator** out);
+void pkv_alloc_destroy(pkv_allocator* a);
+int32_t pkv_alloc_num_free(const pkv_allocator* a);
+int pkv_seq_add(pkv_allocator* a, int64_t seq); /* PKV_ERR_INVALID_ARG if seq exists */
+/* slots_out: host int64 [n] (may be NULL when n == 0) receives the new tokens' slots. */
+int pkv_seq_append_slots(pkv_allocator* a, int64_t seq, int32_t n, int64_t* slots_out);
+int pkv_seq_fork(pkv_allocator* a, int64_t parent, int64_t child);
+int pkv_seq_free(pkv_allocator* a, int64_t seq);
+int pkv_seq_len(const pkv_allocator* a, int64_t seq, int32_t* len_out);
+/* table_out: host int32 [n][max_blocks], padded with -1; lens_out: host int32 [n].
+ * PKV_ERR_INVALID_ARG if a sequence holds more than max_blocks blocks. */
+int pkv_block_tables(const pkv_allocator* a, const int64_t* seqs, int32_t n, int32_t max_blocks,
+                     int32_t* table_out, int32_t* lens_out);
+/* Refcount of a physical block (0 = free); -1 for an id outside the pool. */
+int32_t pkv_block_refcount(const pkv_allocator* a, int32_t block);
+
+/* ---------------------------------------------------------------------------
+ * Measurement helpers (not part of the method).
+ * pkv_stream_read: reads `bytes` (multiple of 16) from `src` with the
+ * library's load pattern and writes one fp32 per workgroup to `sink`
+ * (device, >= pkv_stream_read_sink_floats(bytes) floats): a read-bandwidth
+ * ceiling for the decode kernels.  pkv_copy: dst[0:bytes) = src[0:bytes),
+ * a plain copy of known size used to calibrate memory counters.
+ * -------------------------------------------------------------------------*/
+size_t pkv_stream_read_sink_floats(size_t bytes);
+int pkv_stream_read(const void* src, size_t bytes, float* sink, void* stream);
+int pkv_copy(void* dst, const void* src, size_t bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* PKV_H */

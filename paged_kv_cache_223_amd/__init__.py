@@ -1,0 +1,301 @@
+"""paged_kv_cache_223_amd — paged-KV decode attention for AMD MI355X (gfx950).
+
+Thin ctypes binding over libpkv.so (C ABI in include/pkv.h).  This module
+only marshals arguments: it checks shapes and dtypes of torch tensors, passes
+their device pointers and the current HIP stream, and turns status codes into
+exceptions.  Every step of the computation runs in the library's HIP kernels;
+if the library is not built, importing this package fails.
+
+    kv_append(k, v, slot_mapping, k_pool, v_pool, k_scale=None, v_scale=None)
+    paged_attn_decode(q, k_pool, v_pool, block_tables, context_lens, scale,
+                      max_context_len, k_scale=None, v_scale=None) -> out
+    Allocator(NB, bs, initial_free_order=None)
+
+Pool layout (see pkv.h): K [NB, H_kv, D // X, bs, X], V [NB, H_kv, D, bs],
+X = 16 bytes / element size; E4M3 pools are uint8 (or float8_e4m3fn) tensors.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+# torch ships its own HIP runtime (libamdhip64.so.7).  It must be the one libpkv.so binds to:
+# loading torch first makes the dynamic loader satisfy libpkv's libamdhip64.so.7 dependency
+# with torch's already-loaded copy, so device pointers and stream handles mean the same
+# thing on both sides.  (Loading libpkv first would pull in a second runtime.)
+import torch  # noqa: E402,F401
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libpkv.so")
+
+OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_OUT_OF_BLOCKS, ERR_UNKNOWN_SEQ, ERR_SHARED_BLOCK, ERR_HIP = \
+    0, -1, -2, -3, -4, -5, -6
+F32, BF16, FP8_E4M3 = 0, 1, 2
+ELEM_BYTES = {F32: 4, BF16: 2, FP8_E4M3: 1}
+
+# every symbol include/pkv.h declares: name -> (restype, argtypes)
+_P = ctypes.c_void_p
+_I32 = ctypes.c_int32
+_I64 = ctypes.c_int64
+_SZ = ctypes.c_size_t
+SIGNATURES = {
+    "pkv_last_error": (ctypes.c_char_p, []),
+    "pkv_abi_version": (ctypes.c_int, []),
+    "pkv_kv_append": (ctypes.c_int, [_P, _P, ctypes.c_int, _P, _I32, _P, _P, ctypes.c_int, _I32, _I32, _I32,
+                                     _I32, _P, _P, _P]),
+    "pkv_decode_workspace_bytes": (_SZ, [_I32, _I32, _I32, _I32, _I32, _I32]),
+    "pkv_paged_attn_decode": (ctypes.c_int, [_P, _P, ctypes.c_int, _P, _P, ctypes.c_int, _P, _I32, _P, _I32,
+                                             _I32, _I32, _I32, _I32, _I32, _I32, ctypes.c_float, _P, _P, _P,
+                                             _SZ, _P]),
+    "pkv_alloc_create": (ctypes.c_int, [_I32, _I32, _P, ctypes.POINTER(_P)]),
+    "pkv_alloc_destroy": (None, [_P]),
+    "pkv_alloc_num_free": (_I32, [_P]),
+    "pkv_seq_add": (ctypes.c_int, [_P, _I64]),
+    "pkv_seq_append_slots": (ctypes.c_int, [_P, _I64, _I32, _P]),
+    "pkv_seq_fork": (ctypes.c_int, [_P, _I64, _I64]),
+    "pkv_seq_free": (ctypes.c_int, [_P, _I64]),
+    "pkv_seq_len": (ctypes.c_int, [_P, _I64, _P]),
+    "pkv_block_tables": (ctypes.c_int, [_P, _P, _I32, _I32, _P, _P]),
+    "pkv_block_refcount": (_I32, [_P, _I32]),
+    "pkv_stream_read_sink_floats": (_SZ, [_SZ]),
+    "pkv_stream_read": (ctypes.c_int, [_P, _SZ, _P, _P]),
+    "pkv_copy": (ctypes.c_int, [_P, _P, _SZ, _P]),
+}
+
+
+def _hip_runtimes():
+    """Distinct libamdhip64 files mapped into this process."""
+    paths = set()
+    try:
+        with open("/proc/self/maps") as f:
+            for line in f:
+                p = line.split()[-1] if line.strip() else ""
+                if "libamdhip64.so" in p:
+                    paths.add(os.path.realpath(p))
+    except OSError:
+        pass
+    return paths
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is not built; run `python paged_kv_cache_223_amd/build.py`")
+    lib = ctypes.CDLL(LIB_PATH)
+    rts = _hip_runtimes()
+    if len(rts) > 1:
+        raise ImportError(f"two HIP runtimes are loaded ({sorted(rts)}); import torch before anything that "
+                          "loads /opt/rocm's libamdhip64, so that libpkv.so shares torch's runtime")
+    for name, (res, args) in SIGNATURES.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    return lib
+
+
+lib = _load()
+
+
+class PkvError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"pkv status {status}: {msg}")
+        self.status = status
+
+
+def last_error() -> str:
+    return (lib.pkv_last_error() or b"").decode()
+
+
+def _check(st: int):
+    if st != OK:
+        raise PkvError(st, last_error())
+
+
+# ---------------------------------------------------------------------------
+# device ops
+# ---------------------------------------------------------------------------
+def _torch():
+    return torch
+
+
+def dtype_code(t) -> int:
+    torch = _torch()
+    if t.dtype == torch.float32:
+        return F32
+    if t.dtype == torch.bfloat16:
+        return BF16
+    if t.dtype in (torch.uint8, torch.float8_e4m3fn):
+        return FP8_E4M3
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def pool_shapes(NB: int, H_kv: int, D: int, bs: int, kv_dtype: int):
+    X = 16 // ELEM_BYTES[kv_dtype]
+    if D % X:
+        raise ValueError(f"D={D} is not a multiple of {X}")
+    return (NB, H_kv, D // X, bs, X), (NB, H_kv, D, bs)
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else None
+
+
+def _stream():
+    return ctypes.c_void_p(_torch().cuda.current_stream().cuda_stream)
+
+
+def _dev(*ts):
+    for t in ts:
+        if t is not None:
+            if not t.is_cuda:
+                raise ValueError("tensor is not on a GPU")
+            if not t.is_contiguous():
+                raise ValueError("tensor is not contiguous")
+
+
+def _pool_dims(k_pool, v_pool):
+    kv = dtype_code(k_pool)
+    if dtype_code(v_pool) != kv:
+        raise TypeError("k_pool and v_pool dtypes differ")
+    if k_pool.dim() != 5 or v_pool.dim() != 4:
+        raise ValueError("k_pool must be [NB, H_kv, D/X, bs, X] and v_pool [NB, H_kv, D, bs]")
+    NB, H_kv, DX, bs, X = k_pool.shape
+    D = DX * X
+    if X != 16 // ELEM_BYTES[kv] or tuple(v_pool.shape) != (NB, H_kv, D, bs):
+        raise ValueError(f"pool shapes {tuple(k_pool.shape)} / {tuple(v_pool.shape)} do not match the layout")
+    return kv, NB, H_kv, D, bs
+
+
+def kv_append(k, v, slot_mapping, k_pool, v_pool, k_scale=None, v_scale=None):
+    """Write k[t], v[t] ([T, H_kv, D]) into slot slot_mapping[t] (int64; < 0 skipped)."""
+    torch = _torch()
+    _dev(k, v, slot_mapping, k_pool, v_pool, k_scale, v_scale)
+    kv, NB, H_kv, D, bs = _pool_dims(k_pool, v_pool)
+    src = dtype_code(k)
+    if dtype_code(v) != src or k.shape != v.shape or k.dim() != 3 or k.shape[1:] != (H_kv, D):
+        raise ValueError("k and v must both be [T, H_kv, D] of one dtype")
+    if slot_mapping.dtype != torch.int64 or slot_mapping.shape != (k.shape[0],):
+        raise ValueError("slot_mapping must be int64 [T]")
+    for s in (k_scale, v_scale):
+        if s is not None and (s.dtype != torch.float32 or s.shape != (H_kv,)):
+            raise ValueError("scales must be fp32 [H_kv]")
+    _check(lib.pkv_kv_append(_ptr(k), _ptr(v), src, _ptr(slot_mapping), k.shape[0], _ptr(k_pool), _ptr(v_pool),
+                             kv, NB, bs, H_kv, D, _ptr(k_scale), _ptr(v_scale), _stream()))
+
+
+def decode_workspace_bytes(B: int, H_q: int, H_kv: int, D: int, max_context_len: int, bs: int) -> int:
+    return int(lib.pkv_decode_workspace_bytes(B, H_q, H_kv, D, max_context_len, bs))
+
+
+def paged_attn_decode(q, k_pool, v_pool, block_tables, context_lens, scale: float, max_context_len: int,
+                      k_scale=None, v_scale=None, out=None, workspace=None):
+    """Decode attention of one query token per sequence over its paged KV; fp32 [B, H_q, D]."""
+    torch = _torch()
+    _dev(q, k_pool, v_pool, block_tables, context_lens, k_scale, v_scale, out, workspace)
+    kv, NB, H_kv, D, bs = _pool_dims(k_pool, v_pool)
+    if q.dim() != 3 or q.shape[2] != D:
+        raise ValueError("q must be [B, H_q, D]")
+    B, H_q, _ = q.shape
+    if block_tables.dtype != torch.int32 or block_tables.dim() != 2 or block_tables.shape[0] != B:
+        raise ValueError("block_tables must be int32 [B, max_blocks]")
+    if context_lens.dtype != torch.int32 or context_lens.shape != (B,):
+        raise ValueError("context_lens must be int32 [B]")
+    if out is None:
+        out = torch.empty((B, H_q, D), dtype=torch.float32, device=q.device)
+    elif out.dtype != torch.float32 or tuple(out.shape) != (B, H_q, D):
+        raise ValueError("out must be fp32 [B, H_q, D]")
+    need = decode_workspace_bytes(B, H_q, H_kv, D, max_context_len, bs)
+    if workspace is None and need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(lib.pkv_paged_attn_decode(
+        _ptr(out), _ptr(q), dtype_code(q), _ptr(k_pool), _ptr(v_pool), kv, _ptr(block_tables),
+        block_tables.shape[1], _ptr(context_lens), int(max_context_len), B, H_q, H_kv, D, NB, bs,
+        float(scale), _ptr(k_scale), _ptr(v_scale), _ptr(workspace), ws_bytes, _stream()))
+    return out
+
+
+def stream_read(src, sink=None):
+    """Read all of `src` (bytes multiple of 16) once; returns the per-workgroup sink."""
+    torch = _torch()
+    _dev(src)
+    nbytes = src.numel() * src.element_size()
+    if sink is None:
+        sink = torch.empty(int(lib.pkv_stream_read_sink_floats(nbytes)), dtype=torch.float32, device=src.device)
+    _check(lib.pkv_stream_read(_ptr(src), nbytes, _ptr(sink), _stream()))
+    return sink
+
+
+def copy_(dst, src):
+    _dev(dst, src)
+    nbytes = src.numel() * src.element_size()
+    if dst.numel() * dst.element_size() < nbytes:
+        raise ValueError("dst too small")
+    _check(lib.pkv_copy(_ptr(dst), _ptr(src), nbytes, _stream()))
+
+
+# ---------------------------------------------------------------------------
+# host allocator
+# ---------------------------------------------------------------------------
+class Allocator:
+    """Fixed-block free-list allocator with refcounted shared blocks (host only).
+
+    Methods return the C status code (0 = OK) like the C ABI, so scripts can react
+    to PKV_ERR_OUT_OF_BLOCKS; append_slots and block_tables also return arrays.
+    """
+
+    def __init__(self, NB: int, bs: int, initial_free_order=None):
+        self.NB, self.bs = int(NB), int(bs)
+        self._h = ctypes.c_void_p()
+        order = None
+        if initial_free_order is not None:
+            order = np.ascontiguousarray(initial_free_order, dtype=np.int32)
+            if order.shape != (self.NB,):
+                raise ValueError("initial_free_order must have NB entries")
+        _check(lib.pkv_alloc_create(self.NB, self.bs, order.ctypes.data if order is not None else None,
+                                    ctypes.byref(self._h)))
+
+    def __del__(self):
+        h = getattr(self, "_h", None)
+        if h:
+            lib.pkv_alloc_destroy(h)
+            self._h = None
+
+    def num_free(self) -> int:
+        return int(lib.pkv_alloc_num_free(self._h))
+
+    def seq_add(self, seq) -> int:
+        return int(lib.pkv_seq_add(self._h, int(seq)))
+
+    def append_slots(self, seq, n: int):
+        out = np.empty(max(int(n), 0), np.int64)
+        st = int(lib.pkv_seq_append_slots(self._h, int(seq), int(n), out.ctypes.data if n > 0 else None))
+        return st, (out if st == OK else None)
+
+    def fork(self, parent, child) -> int:
+        return int(lib.pkv_seq_fork(self._h, int(parent), int(child)))
+
+    def free(self, seq) -> int:
+        return int(lib.pkv_seq_free(self._h, int(seq)))
+
+    def seq_len(self, seq):
+        n = ctypes.c_int32()
+        st = int(lib.pkv_seq_len(self._h, int(seq), ctypes.byref(n)))
+        return st, (n.value if st == OK else None)
+
+    def block_tables(self, seqs, max_blocks: int):
+        s = np.ascontiguousarray(seqs, dtype=np.int64)
+        table = np.empty((len(s), int(max_blocks)), np.int32)
+        lens = np.empty(len(s), np.int32)
+        st = int(lib.pkv_block_tables(self._h, s.ctypes.data, len(s), int(max_blocks), table.ctypes.data,
+                                      lens.ctypes.data))
+        return st, (table if st == OK else None), (lens if st == OK else None)
+
+    def refcount(self, block: int) -> int:
+        return int(lib.pkv_block_refcount(self._h, int(block)))
+
+
+__all__ = ["lib", "LIB_PATH", "PkvError", "last_error", "kv_append", "paged_attn_decode", "decode_workspace_bytes",
+           "pool_shapes", "dtype_code", "stream_read", "copy_", "Allocator", "SIGNATURES",
+           "F32", "BF16", "FP8_E4M3"]

@@ -1,0 +1,198 @@
+// C ABI entry points: argument validation, launch planning, error reporting.
+// Every check happens on the host before any launch; see pkv.h for contracts.
+
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <cmath>
+
+#include "internal.h"
+
+namespace pkv {
+
+static thread_local char g_err[512] = "";
+
+void set_error(const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof g_err, fmt, ap);
+  va_end(ap);
+}
+
+int hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return PKV_OK;
+  set_error("%s: HIP error %d (%s)", what, (int)e, hipGetErrorString(e));
+  return PKV_ERR_HIP;
+}
+
+static bool valid_dtype(int dt) { return dt == PKV_F32 || dt == PKV_BF16 || dt == PKV_FP8_E4M3; }
+
+}  // namespace pkv
+
+using namespace pkv;
+
+extern "C" {
+
+const char* pkv_last_error(void) { return g_err; }
+
+int pkv_abi_version(void) { return 1; }
+
+int pkv_kv_append(const void* k, const void* v, int src_dtype, const int64_t* slot_mapping, int32_t T,
+                  void* k_pool, void* v_pool, int pool_dtype, int32_t NB, int32_t bs, int32_t H_kv, int32_t D,
+                  const float* k_scale, const float* v_scale, void* stream) {
+  g_err[0] = 0;
+  if (T < 0 || NB <= 0 || bs <= 0 || bs > 256 || H_kv <= 0 || D <= 0) {
+    set_error("kv_append: bad sizes T=%d NB=%d bs=%d H_kv=%d D=%d", T, NB, bs, H_kv, D);
+    return PKV_ERR_INVALID_ARG;
+  }
+  if (D % 16 != 0 || D > 512) {
+    set_error("kv_append: D=%d must be a multiple of 16 and <= 512", D);
+    return PKV_ERR_UNSUPPORTED;
+  }
+  if (!valid_dtype(src_dtype) || !valid_dtype(pool_dtype)) {
+    set_error("kv_append: unknown dtype (src %d, pool %d)", src_dtype, pool_dtype);
+    return PKV_ERR_INVALID_ARG;
+  }
+  const bool ok_pair = (src_dtype == pool_dtype) || (src_dtype == PKV_BF16 && pool_dtype == PKV_FP8_E4M3);
+  if (!ok_pair) {
+    set_error("kv_append: unsupported conversion %d -> %d", src_dtype, pool_dtype);
+    return PKV_ERR_UNSUPPORTED;
+  }
+  if (T == 0) return PKV_OK;
+  if (!k || !v || !slot_mapping || !k_pool || !v_pool) {
+    set_error("kv_append: null pointer");
+    return PKV_ERR_INVALID_ARG;
+  }
+  if (src_dtype == PKV_BF16 && pool_dtype == PKV_FP8_E4M3 && (!k_scale || !v_scale)) {
+    set_error("kv_append: quantising to E4M3 needs k_scale and v_scale");
+    return PKV_ERR_INVALID_ARG;
+  }
+  if ((long long)T * H_kv * (D / 8) > (long long)0x7FFFFFFF * 256) {
+    set_error("kv_append: T too large for one launch");
+    return PKV_ERR_INVALID_ARG;
+  }
+  AppendArgs a{k, v, slot_mapping, k_pool, v_pool, k_scale, v_scale, T, H_kv, D, bs, (long long)NB * bs,
+               src_dtype, pool_dtype};
+  return hip_status(launch_kv_append(a, (hipStream_t)stream), "kv_append launch");
+}
+
+size_t pkv_decode_workspace_bytes(int32_t B, int32_t H_q, int32_t H_kv, int32_t D, int32_t max_context_len,
+                                  int32_t bs) {
+  g_err[0] = 0;
+  if (B < 0 || H_q <= 0 || H_kv <= 0 || D <= 0 || max_context_len < 0 || bs <= 0) {
+    set_error("decode_workspace_bytes: bad sizes");
+    return 0;
+  }
+  return workspace_bytes_for(B, H_q, D, plan_splits(B, H_kv, max_context_len));
+}
+
+int pkv_paged_attn_decode(float* out, const void* q, int q_dtype, const void* k_pool, const void* v_pool,
+                          int kv_dtype, const int32_t* block_tables, int32_t max_blocks_per_seq,
+                          const int32_t* context_lens, int32_t max_context_len, int32_t B, int32_t H_q, int32_t H_kv,
+                          int32_t D, int32_t NB, int32_t bs, float scale, const float* k_scale,
+                          const float* v_scale, void* workspace, size_t workspace_bytes, void* stream) {
+  g_err[0] = 0;
+  if (B < 0 || H_q <= 0 || H_kv <= 0 || NB <= 0 || max_blocks_per_seq <= 0 || max_context_len < 0) {
+    set_error("decode: bad sizes B=%d H_q=%d H_kv=%d NB=%d max_blocks=%d max_context_len=%d", B, H_q, H_kv, NB,
+              max_blocks_per_seq, max_context_len);
+    return PKV_ERR_INVALID_ARG;
+  }
+  if (H_q % H_kv != 0) {
+    set_error("decode: H_q=%d is not a multiple of H_kv=%d", H_q, H_kv);
+    return PKV_ERR_INVALID_ARG;
+  }
+  if (!(D == 64 || D == 128 || D == 256) || !(bs == 8 || bs == 16 || bs == 32)) {
+    set_error("decode: unsupported D=%d / bs=%d (D in {64,128,256}, bs in {8,16,32})", D, bs);
+    return PKV_ERR_UNSUPPORTED;
+  }
+  if (!(q_dtype == PKV_F32 || q_dtype == PKV_BF16) || !valid_dtype(kv_dtype)) {
+    set_error("decode: unsupported dtypes q=%d kv=%d", q_dtype, kv_dtype);
+    return PKV_ERR_UNSUPPORTED;
+  }
+  if (!std::isfinite(scale)) {
+    set_error("decode: scale is not finite");
+    return PKV_ERR_INVALID_ARG;
+  }
+  if (B == 0) return PKV_OK;
+  if (!out || !q || !k_pool || !v_pool || !block_tables || !context_lens) {
+    set_error("decode: null pointer");
+    return PKV_ERR_INVALID_ARG;
+  }
+  if (kv_dtype == PKV_FP8_E4M3 && (!k_scale || !v_scale)) {
+    set_error("decode: E4M3 KV needs k_scale and v_scale");
+    return PKV_ERR_INVALID_ARG;
+  }
+  const SplitPlan plan = plan_splits(B, H_kv, max_context_len);
+  const size_t need = workspace_bytes_for(B, H_q, D, plan);
+  if (need > 0 && (!workspace || workspace_bytes < need || ((uintptr_t)workspace & 255u))) {
+    set_error("decode: workspace needs %zu bytes, 256-byte aligned (got %zu at %p)", need, workspace_bytes,
+              workspace);
+    return PKV_ERR_INVALID_ARG;
+  }
+  const int G = H_q / H_kv;
+  const bool fast = decode_fast_path_supported(q_dtype, kv_dtype, G, D, bs);
+  const long long items = (long long)B * plan.max_splits * (fast ? H_kv : H_q);
+  if (items > 0x7FFFFFFFLL) {
+    set_error("decode: launch too large (%lld work items)", items);
+    return PKV_ERR_INVALID_ARG;
+  }
+  DecodeArgs a{};
+  a.out = out;
+  a.q = q;
+  a.k_pool = k_pool;
+  a.v_pool = v_pool;
+  a.block_tables = block_tables;
+  a.context_lens = context_lens;
+  a.k_scale = k_scale;
+  a.v_scale = v_scale;
+  if (need > 0) {
+    size_t per = (size_t)B * H_q * plan.max_splits;
+    size_t o = (per * D * sizeof(float) + 255) / 256 * 256;
+    a.ws_o = (float*)workspace;
+    a.ws_ml = (float*)((char*)workspace + o);
+  }
+  a.B = B;
+  a.H_q = H_q;
+  a.H_kv = H_kv;
+  a.G = G;
+  a.D = D;
+  a.NB = NB;
+  a.bs = bs;
+  a.max_blocks = max_blocks_per_seq;
+  const long long cap = (long long)max_blocks_per_seq * bs;
+  a.len_cap = (int)(cap < max_context_len ? cap : max_context_len);
+  a.split_tokens = plan.split_tokens;
+  a.max_splits = plan.max_splits;
+  a.scale_log2 = scale * 1.4426950408889634f;
+  a.q_dtype = q_dtype;
+  a.kv_dtype = kv_dtype;
+  hipStream_t s = (hipStream_t)stream;
+  int st = hip_status(fast ? launch_decode_mfma(a, s) : launch_decode_vector(a, s), "decode launch");
+  if (st != PKV_OK || plan.max_splits <= 1) return st;
+  return hip_status(launch_split_reduce(a, s), "split reduce launch");
+}
+
+size_t pkv_stream_read_sink_floats(size_t bytes) { return stream_read_blocks(bytes); }
+
+int pkv_stream_read(const void* src, size_t bytes, float* sink, void* stream) {
+  g_err[0] = 0;
+  if (!src || !sink || bytes % 16 != 0) {
+    set_error("stream_read: null pointer or size not a multiple of 16");
+    return PKV_ERR_INVALID_ARG;
+  }
+  if (bytes == 0) return PKV_OK;
+  return hip_status(launch_stream_read(src, bytes, sink, (hipStream_t)stream), "stream_read launch");
+}
+
+int pkv_copy(void* dst, const void* src, size_t bytes, void* stream) {
+  g_err[0] = 0;
+  if (!src || !dst || bytes % 16 != 0) {
+    set_error("copy: null pointer or size not a multiple of 16");
+    return PKV_ERR_INVALID_ARG;
+  }
+  if (bytes == 0) return PKV_OK;
+  return hip_status(launch_copy(dst, src, bytes, (hipStream_t)stream), "copy launch");
+}
+
+}  // extern "C"

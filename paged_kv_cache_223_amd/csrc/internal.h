@@ -1,0 +1,98 @@
+// Internal declarations shared by the C ABI (api.cpp) and the HIP launchers.
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#include "pkv.h"
+
+namespace pkv {
+
+void set_error(const char* fmt, ...);
+int hip_status(hipError_t e, const char* what);
+
+inline int elem_bytes(int dt) { return dt == PKV_F32 ? 4 : dt == PKV_BF16 ? 2 : 1; }
+
+// Context-split plan shared by the workspace query and the decode call.  A work
+// item is (sequence, context split, KV head); a split covers `split_tokens`
+// consecutive logical tokens (a multiple of 256).  The split length aims at
+// kTargetItems items for the batch's upper-bound token count, between
+// kMinSplit and kMaxSplit tokens so that no item runs much longer than the rest.
+struct SplitPlan {
+  int split_tokens;
+  int max_splits;  // splits of the longest admissible sequence
+};
+
+constexpr int kTargetItems = 2048;
+constexpr int kMinSplit = 256;
+constexpr int kMaxSplit = 2048;
+
+inline SplitPlan plan_splits(int B, int H_kv, int max_ctx) {
+  long long total = (long long)B * H_kv * (max_ctx > 0 ? max_ctx : 1);
+  long long s = (total + kTargetItems - 1) / kTargetItems;
+  s = (s + 255) / 256 * 256;
+  if (s < kMinSplit) s = kMinSplit;
+  if (s > kMaxSplit) s = kMaxSplit;
+  SplitPlan p;
+  p.split_tokens = (int)s;
+  p.max_splits = max_ctx > 0 ? (int)((max_ctx + s - 1) / s) : 1;
+  return p;
+}
+
+inline size_t workspace_bytes_for(int B, int H_q, int D, const SplitPlan& p) {
+  if (p.max_splits <= 1) return 0;
+  size_t per = (size_t)B * H_q * p.max_splits;
+  size_t o = per * D * sizeof(float);
+  o = (o + 255) / 256 * 256;
+  return o + per * 2 * sizeof(float);
+}
+
+struct DecodeArgs {
+  float* out;
+  const void* q;
+  const void* k_pool;
+  const void* v_pool;
+  const int32_t* block_tables;
+  const int32_t* context_lens;
+  const float* k_scale;
+  const float* v_scale;
+  float* ws_o;   // [B][H_q][max_splits][D] split partial outputs (unnormalised)
+  float* ws_ml;  // [B][H_q][max_splits][2]  split running max (log2 units) and sum
+  int B, H_q, H_kv, G, D, NB, bs;
+  int max_blocks;    // table row stride
+  int len_cap;       // min(max_context_len, max_blocks * bs)
+  int split_tokens;
+  int max_splits;
+  float scale_log2;  // scale * log2(e)
+  int q_dtype, kv_dtype;
+};
+
+// Kernel launchers (paged_decode.hip).  Return hipError_t of the launch.
+bool decode_fast_path_supported(int q_dtype, int kv_dtype, int G, int D, int bs);
+hipError_t launch_decode_mfma(const DecodeArgs& a, hipStream_t s);
+hipError_t launch_decode_vector(const DecodeArgs& a, hipStream_t s);
+hipError_t launch_split_reduce(const DecodeArgs& a, hipStream_t s);
+
+// kv_append.hip
+struct AppendArgs {
+  const void* k;
+  const void* v;
+  const int64_t* slots;
+  void* k_pool;
+  void* v_pool;
+  const float* k_scale;
+  const float* v_scale;
+  int T, H_kv, D, bs;
+  long long n_slots;  // NB * bs
+  int src_dtype, pool_dtype;
+};
+hipError_t launch_kv_append(const AppendArgs& a, hipStream_t s);
+
+// stream.hip
+size_t stream_read_blocks(size_t bytes);
+hipError_t launch_stream_read(const void* src, size_t bytes, float* sink, hipStream_t s);
+hipError_t launch_copy(void* dst, const void* src, size_t bytes, hipStream_t s);
+
+}  // namespace pkv

@@ -1,0 +1,624 @@
+// Paged-KV decode attention for gfx950 (CDNA4).
+//
+// Method: "KV Cache Fragmentation" field guide (defragging.ai), section
+// "Definition" — the cache is cut into fixed-size pages and the attention
+// kernel walks the per-request table from logical to physical pages;
+// "Paged Attention and KV Cache Fragmentation" (inferenceengineering.co),
+// sections "How PagedAttention maps an OS concept onto GPU memory" and "The
+// non-contiguous memory layout PagedAttention introduces and its overhead"
+// — every attention step follows the block table, and gathering scattered
+// pages is the cost to keep small.  Scores are never written to memory (the
+// fused-attention property named in the section on block-level eviction).
+//
+// Work decomposition: a work item is (sequence b, context split, KV head g).
+// Items are numbered sequence-major; every workgroup scans the context
+// lengths to find its item, so sequences of very different length get a
+// number of items proportional to their length and no item is idle.
+//
+// Matrix-core path (bf16 q; bf16 or E4M3 KV; G = H_q/H_kv <= 16; D 64/128):
+// one workgroup = 4 waves; a wave owns 32-token chunks of the split (chunk
+// w, w+4, ...).  Per chunk:
+//   S^T[16 tok][16 heads] = K[16 tok][D] . Q^T[D][16 heads]   two
+//     v_mfma_f32_16x16x32_bf16 chains (one per 16-token half); A = K rows
+//     straight from the pool, B = the wave's resident Q (heads >= G zero).
+//   online softmax in log2 units on the MFMA accumulator layout (lane l holds
+//     head l%16, tokens 4*(l/16)+i): the running maximum only moves when a
+//     chunk exceeds it by more than 2^8, so the rescale of the accumulators is
+//     rare; the sum stays per lane until the end.
+//   O[16 heads][D] += P[16 heads][32 tok] . V[32 tok][D] with P split into
+//     bf16 hi + lo parts (two MFMAs per tile) so P keeps ~16 bits: the
+//     accumulator layout of S^T is exactly the A-operand layout P needs.
+// The pool layout makes every MFMA operand a 16- or 8-byte lane load: the K
+// tile is [D/X][bs][X] (16 tokens x 16 bytes contiguous per 16 lanes) and the
+// V tile is [D][bs] (4 consecutive tokens of one column per lane), so no LDS
+// staging or transposition is needed on the hot loop; LDS only merges the
+// four waves at the end.
+//
+// Vector path: one wave per (sequence, split, query head), fp32 VALU; used for
+// fp32 q or KV, G > 16 or D = 256.
+//
+// Splits: each item writes its unnormalised output and (max, sum) to the
+// workspace unless the sequence has a single split, in which case it writes
+// the final row; split_reduce merges multi-split rows.
+
+#include <hip/hip_runtime.h>
+
+#include <math.h>
+
+#include <type_traits>
+
+#include "internal.h"
+
+namespace pkv {
+namespace {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+constexpr float kRescaleLog2 = 8.0f;
+
+__device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+
+__device__ __forceinline__ int elem_bytes_dev(int dt) { return dt == PKV_F32 ? 4 : dt == PKV_BF16 ? 2 : 1; }
+
+__device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
+
+// number of context splits of a sequence of length n (a zero-length sequence
+// still owns one item, which writes its zero row)
+__device__ __forceinline__ int splits_of(int n, int cap, int split_tokens) {
+  n = n < 0 ? 0 : (n > cap ? cap : n);
+  return n == 0 ? 1 : (n + split_tokens - 1) / split_tokens;
+}
+
+// Map work index `target` (over sequences, sequence-major) to (b, split).
+// All NT threads of the block take part; the result is block-uniform.
+template <int NT>
+__device__ bool find_item(const int32_t* __restrict__ lens, int B, int cap, int split_tokens,
+                          int target, int& b_out, int& split_out) {
+  constexpr int NWv = NT / 64;
+  __shared__ int sh_wsum[NWv];
+  __shared__ int sh_res[2];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  if (tid == 0) sh_res[0] = -1;
+  int carry = 0;
+  for (int base = 0; base < B; base += NT) {
+    const int b = base + tid;
+    const int ns = b < B ? splits_of(lens[b], cap, split_tokens) : 0;
+    int x = ns;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      int y = __shfl_up(x, off, 64);
+      if (lane >= off) x += y;
+    }
+    if (lane == 63) sh_wsum[w] = x;
+    __syncthreads();
+    int pre = carry, tot = carry;
+#pragma unroll
+    for (int i = 0; i < NWv; ++i) {
+      pre += i < w ? sh_wsum[i] : 0;
+      tot += sh_wsum[i];
+    }
+    const int incl = pre + x, excl = incl - ns;
+    if (b < B && target >= excl && target < incl) {
+      sh_res[0] = b;
+      sh_res[1] = target - excl;
+    }
+    carry = tot;
+    __syncthreads();
+    if (sh_res[0] >= 0) break;
+  }
+  b_out = uniform(sh_res[0]);
+  split_out = uniform(sh_res[1]);
+  return b_out >= 0;
+}
+
+__device__ __forceinline__ int seq_len(const int32_t* __restrict__ lens, int b, int cap) {
+  int n = lens[b];
+  return n < 0 ? 0 : (n > cap ? cap : n);
+}
+
+// physical block of logical block j (clamped to the sequence's last block; an
+// id outside the pool is read as block 0 so that no access leaves the pool)
+__device__ __forceinline__ int block_id(const int32_t* __restrict__ tab, int j, int last, int NB) {
+  j = j > last ? last : j;
+  const int id = tab[j];
+  return (unsigned)id < (unsigned)NB ? id : 0;
+}
+
+// ---------------------------------------------------------------------------
+// matrix-core path
+// ---------------------------------------------------------------------------
+template <int KVT>
+struct KvTraits;
+template <>
+struct KvTraits<PKV_BF16> {
+  static constexpr int kBytes = 2;
+};
+template <>
+struct KvTraits<PKV_FP8_E4M3> {
+  static constexpr int kBytes = 1;
+};
+
+// head-dim offset of the 8 k-slots lane group kg feeds into QK MFMA number c
+template <int KVT>
+__device__ __forceinline__ constexpr int qk_dofs(int c, int kg) {
+  return KVT == PKV_BF16 ? 32 * c + 8 * kg : 64 * (c / 2) + 16 * kg + 8 * (c % 2);
+}
+
+// E4M3 (OCP) pair -> bf16 pair, exact; `hi` picks bytes 2,3 instead of 0,1
+__device__ __forceinline__ uint32_t e4m3x2_to_bf16x2(uint32_t w, bool hi) {
+  bf16x2 r = hi ? __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, true)
+                : __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, false);
+  return __builtin_bit_cast(uint32_t, r);
+}
+
+__device__ __forceinline__ u32x4 e4m3x8_to_bf16x8(uint32_t w0, uint32_t w1) {
+  return u32x4{e4m3x2_to_bf16x2(w0, false), e4m3x2_to_bf16x2(w0, true), e4m3x2_to_bf16x2(w1, false),
+               e4m3x2_to_bf16x2(w1, true)};
+}
+
+__device__ __forceinline__ f32x4 mfma16x16x32(u32x4 a, u32x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c,
+                                                 0, 0, 0);
+}
+
+template <int D, int BS, int KVT>
+struct Chunk {
+  static constexpr int kKLoads = KVT == PKV_BF16 ? D / 32 : D / 64;  // 16-byte K loads per half
+  u32x4 k[2][kKLoads];
+  // V operand words per output tile: bf16 -> 4 words, e4m3 -> 2 words (codes)
+  typename std::conditional<KVT == PKV_BF16, u32x4, u32x2>::type v[D / 16];
+};
+
+template <int NBCH>
+__device__ __forceinline__ int pick(const int (&ids)[NBCH], int idx) {
+  int r = ids[0];
+#pragma unroll
+  for (int i = 1; i < NBCH; ++i) r = idx == i ? ids[i] : r;
+  return r;
+}
+
+template <int D, int BS, int KVT>
+__device__ __forceinline__ void load_chunk(Chunk<D, BS, KVT>& ch, const char* __restrict__ kpool,
+                                           const char* __restrict__ vpool, const int32_t* __restrict__ tab,
+                                           int chunk, int last_blk, int NB, int H_kv, int g, int lane) {
+  constexpr int S = KvTraits<KVT>::kBytes;
+  constexpr int NBCH = BS >= 32 ? 1 : 32 / BS;
+  constexpr size_t kTile = (size_t)D * BS * S;
+  const int cs = chunk * 32;
+  int ids[NBCH];
+#pragma unroll
+  for (int i = 0; i < NBCH; ++i) ids[i] = block_id(tab, cs / BS + i, last_blk, NB);
+  const int m = lane & 15, kg = lane >> 4;
+  const size_t gofs = (size_t)g * kTile;
+  const size_t bstride = (size_t)H_kv * kTile;
+#pragma unroll
+  for (int a = 0; a < 2; ++a) {
+    const int tk = 16 * a + m;  // token within the chunk this lane's K row belongs to
+    const int id = pick<NBCH>(ids, BS >= 32 ? 0 : tk / BS);
+    const char* base = kpool + (size_t)id * bstride + gofs + (size_t)(kg * BS + tk % BS) * 16;
+#pragma unroll
+    for (int c = 0; c < Chunk<D, BS, KVT>::kKLoads; ++c)
+      ch.k[a][c] = *(const u32x4*)(base + (size_t)c * 64 * BS);
+  }
+  const int n = lane & 15, qg = lane >> 4;
+#pragma unroll
+  for (int a = 0; a < 2; ++a) {
+    const int tv = 16 * a + 4 * qg;  // first of the 4 tokens this lane's V words hold
+    const int id = pick<NBCH>(ids, BS >= 32 ? 0 : tv / BS);
+    const char* base = vpool + (size_t)id * bstride + gofs + ((size_t)n * BS + tv % BS) * S;
+#pragma unroll
+    for (int t = 0; t < D / 16; ++t) {
+      const char* p = base + (size_t)t * 16 * BS * S;
+      if constexpr (KVT == PKV_BF16) {
+        u32x2 x = *(const u32x2*)p;
+        ch.v[t][2 * a] = x.x;
+        ch.v[t][2 * a + 1] = x.y;
+      } else {
+        ch.v[t][a] = *(const uint32_t*)p;
+      }
+    }
+  }
+}
+
+struct WaveState {
+  float m;  // running max of head (lane & 15), log2 units, same in the head's 4 lanes
+  float l;  // this lane's share of the running sum
+};
+
+template <int D, int BS, int KVT>
+__device__ __forceinline__ void process_chunk(const Chunk<D, BS, KVT>& ch, const u32x4 (&qop)[D / 32],
+                                              f32x4 (&acc)[D / 16], WaveState& st, int chunk, int n,
+                                              float sl, int lane) {
+  const int cs = chunk * 32;
+  const int kg = lane >> 4;
+  const bool tail = cs + 32 > n;  // wave-uniform
+  // ---- S^T = K Q^T for the two 16-token halves
+  f32x4 s[2];
+#pragma unroll
+  for (int a = 0; a < 2; ++a) {
+    s[a] = f32x4{0.f, 0.f, 0.f, 0.f};
+    if constexpr (KVT == PKV_BF16) {
+#pragma unroll
+      for (int c = 0; c < D / 32; ++c) s[a] = mfma16x16x32(ch.k[a][c], qop[c], s[a]);
+    } else {
+#pragma unroll
+      for (int u = 0; u < D / 64; ++u) {
+        const u32x4 w = ch.k[a][u];
+        s[a] = mfma16x16x32(e4m3x8_to_bf16x8(w.x, w.y), qop[2 * u], s[a]);
+        s[a] = mfma16x16x32(e4m3x8_to_bf16x8(w.z, w.w), qop[2 * u + 1], s[a]);
+      }
+    }
+  }
+  float x[8];
+#pragma unroll
+  for (int a = 0; a < 2; ++a)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      float v = s[a][i] * sl;
+      if (tail) v = (cs + 16 * a + 4 * kg + i < n) ? v : -INFINITY;
+      x[4 * a + i] = v;
+    }
+  // ---- chunk max per head: 8 values in the lane, then the head's 4 lanes
+  float cm = x[0];
+#pragma unroll
+  for (int j = 1; j < 8; ++j) cm = fmaxf(cm, x[j]);
+  cm = fmaxf(cm, __shfl_xor(cm, 16, 64));
+  cm = fmaxf(cm, __shfl_xor(cm, 32, 64));
+  const bool need = cm > st.m + kRescaleLog2;
+  if (__ballot(need)) {
+    const float mu = need ? cm : st.m;
+    const float alpha = exp2_fast(st.m - mu);
+    st.l *= alpha;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float ai = __shfl(alpha, 4 * kg + i, 64);  // alpha of accumulator row 4*kg+i
+#pragma unroll
+      for (int t = 0; t < D / 16; ++t) acc[t][i] *= ai;
+    }
+    st.m = mu;
+  }
+  // ---- P = exp2(x - m): keep fp32 sum, split into bf16 hi + lo for the MFMA
+  uint32_t hb[8];
+  float lo[8];
+  float psum = 0.f;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const float p = exp2_fast(x[j] - st.m);
+    psum += p;
+    const uint32_t bits = __builtin_bit_cast(uint32_t, p);
+    hb[j] = bits;
+    lo[j] = p - __builtin_bit_cast(float, bits & 0xFFFF0000u);
+  }
+  st.l += psum;
+  u32x4 ph, pl;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    ph[w] = __builtin_amdgcn_perm(hb[2 * w + 1], hb[2 * w], 0x07060302u);
+    pl[w] = __builtin_amdgcn_perm(__builtin_bit_cast(uint32_t, lo[2 * w + 1]),
+                                  __builtin_bit_cast(uint32_t, lo[2 * w]), 0x07060302u);
+  }
+  // ---- V tail mask: k-slot j of lane group kg is token (j<4 ? 4kg+j : 16+4kg+j-4)
+  u32x4 vmask = u32x4{~0u, ~0u, ~0u, ~0u};
+  if (tail) {
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const int j0 = 2 * w, j1 = 2 * w + 1;
+      const int t0 = cs + (j0 < 4 ? 4 * kg + j0 : 16 + 4 * kg + j0 - 4);
+      const int t1 = cs + (j1 < 4 ? 4 * kg + j1 : 16 + 4 * kg + j1 - 4);
+      vmask[w] = (t0 < n ? 0x0000FFFFu : 0u) | (t1 < n ? 0xFFFF0000u : 0u);
+    }
+  }
+  // ---- O += P V
+#pragma unroll
+  for (int t = 0; t < D / 16; ++t) {
+    u32x4 vop;
+    if constexpr (KVT == PKV_BF16) {
+      vop = ch.v[t];
+    } else {
+      vop = e4m3x8_to_bf16x8(ch.v[t][0], ch.v[t][1]);
+    }
+    if (tail) vop &= vmask;
+    acc[t] = mfma16x16x32(ph, vop, acc[t]);
+    acc[t] = mfma16x16x32(pl, vop, acc[t]);
+  }
+}
+
+template <int D, int BS, int KVT>
+__global__ __launch_bounds__(256, 2) void decode_mfma_kernel(DecodeArgs a) {
+  constexpr int NW = 4;
+  __shared__ float sh_acc[NW][16][D];
+  __shared__ float sh_m[NW][16];
+  __shared__ float sh_l[NW][16];
+
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int g = blockIdx.x % a.H_kv;
+  int b, split;
+  if (!find_item<256>(a.context_lens, a.B, a.len_cap, a.split_tokens, blockIdx.x / a.H_kv, b, split)) return;
+  const int G = a.G;
+  const int hq0 = g * G;
+  const int n = uniform(seq_len(a.context_lens, b, a.len_cap));
+  const int nsplit = n == 0 ? 1 : (n + a.split_tokens - 1) / a.split_tokens;
+  const size_t orow = ((size_t)b * a.H_q + hq0) * D;
+  if (n == 0) {
+    for (int e = tid; e < G * D; e += 256) a.out[orow + e] = 0.f;
+    return;
+  }
+  const int t_begin = split * a.split_tokens;
+  const int t_end = min(n, t_begin + a.split_tokens);
+  const int c_begin = t_begin / 32, c_end = (t_end + 31) / 32;
+  const int last_blk = (n + BS - 1) / BS - 1;
+  const int32_t* tab = a.block_tables + (size_t)b * a.max_blocks;
+  const char* kpool = (const char*)a.k_pool;
+  const char* vpool = (const char*)a.v_pool;
+
+  // resident Q operand: lane holds head (lane & 15), 8 head-dim values per MFMA
+  const int h = lane & 15, kg = lane >> 4;
+  u32x4 qop[D / 32];
+  {
+    const uint16_t* qrow = (const uint16_t*)a.q + ((size_t)b * a.H_q + hq0 + h) * D;
+#pragma unroll
+    for (int c = 0; c < D / 32; ++c) {
+      u32x4 v = u32x4{0u, 0u, 0u, 0u};
+      if (h < G) v = *(const u32x4*)(qrow + qk_dofs<KVT>(c, kg));
+      qop[c] = v;
+    }
+  }
+  float sl = a.scale_log2;
+  if constexpr (KVT == PKV_FP8_E4M3) sl *= a.k_scale[g];
+
+  f32x4 acc[D / 16];
+#pragma unroll
+  for (int t = 0; t < D / 16; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+  WaveState st{-INFINITY, 0.f};
+
+  // chunks c_begin + w, +NW, ... ; double-buffered: the next chunk's loads are
+  // in flight while the current one is computed
+  const int first = c_begin + w;
+  const int cnt = first < c_end ? (c_end - first + NW - 1) / NW : 0;
+  if (cnt > 0) {
+    Chunk<D, BS, KVT> A, Bf;
+    int c = first;
+    load_chunk(A, kpool, vpool, tab, c, last_blk, a.NB, a.H_kv, g, lane);
+    int k = 0;
+    for (; k + 2 < cnt; k += 2) {
+      load_chunk(Bf, kpool, vpool, tab, c + NW, last_blk, a.NB, a.H_kv, g, lane);
+      process_chunk(A, qop, acc, st, c, n, sl, lane);
+      load_chunk(A, kpool, vpool, tab, c + 2 * NW, last_blk, a.NB, a.H_kv, g, lane);
+      process_chunk(Bf, qop, acc, st, c + NW, n, sl, lane);
+      c += 2 * NW;
+    }
+    if (k + 1 < cnt) {
+      load_chunk(Bf, kpool, vpool, tab, c + NW, last_blk, a.NB, a.H_kv, g, lane);
+      process_chunk(A, qop, acc, st, c, n, sl, lane);
+      process_chunk(Bf, qop, acc, st, c + NW, n, sl, lane);
+    } else {
+      process_chunk(A, qop, acc, st, c, n, sl, lane);
+    }
+  }
+
+  // ---- merge the four waves through LDS
+  float lt = st.l;
+  lt += __shfl_xor(lt, 16, 64);
+  lt += __shfl_xor(lt, 32, 64);
+  if (lane < 16) {
+    sh_m[w][lane] = st.m;
+    sh_l[w][lane] = lt;
+  }
+#pragma unroll
+  for (int t = 0; t < D / 16; ++t)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) sh_acc[w][4 * kg + i][16 * t + (lane & 15)] = acc[t][i];
+  __syncthreads();
+
+  const float vs = KVT == PKV_FP8_E4M3 ? a.v_scale[g] : 1.f;
+  for (int e = tid; e < G * D; e += 256) {
+    const int hh = e / D, col = e % D;
+    float M = sh_m[0][hh];
+#pragma unroll
+    for (int i = 1; i < NW; ++i) M = fmaxf(M, sh_m[i][hh]);
+    float L = 0.f, O = 0.f;
+#pragma unroll
+    for (int i = 0; i < NW; ++i) {
+      const float wt = exp2_fast(sh_m[i][hh] - M);
+      L += wt * sh_l[i][hh];
+      O += wt * sh_acc[i][hh][col];
+    }
+    O *= vs;
+    if (nsplit == 1) {
+      a.out[orow + e] = O / L;
+    } else {
+      const size_t pr = ((size_t)b * a.H_q + hq0 + hh) * a.max_splits + split;
+      a.ws_o[pr * D + col] = O;
+      if (col == 0) {
+        a.ws_ml[2 * pr] = M;
+        a.ws_ml[2 * pr + 1] = L;
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// vector path
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float e4m3_value(uint32_t c) {
+  const uint32_t e = (c >> 3) & 15u, m = c & 7u;
+  float mag = e ? ldexpf((float)(8u + m), (int)e - 10) : ldexpf((float)m, -9);
+  if (e == 15u && m == 7u) mag = NAN;
+  return (c & 0x80u) ? -mag : mag;
+}
+
+__device__ __forceinline__ float load_elem(const void* p, size_t idx, int dt) {
+  if (dt == PKV_F32) return ((const float*)p)[idx];
+  if (dt == PKV_BF16) return __builtin_bit_cast(float, (uint32_t)((const uint16_t*)p)[idx] << 16);
+  return e4m3_value(((const uint8_t*)p)[idx]);
+}
+
+template <int D>
+__global__ __launch_bounds__(64) void decode_vector_kernel(DecodeArgs a) {
+  constexpr int KD = D / 64;
+  __shared__ float sh_q[D];
+  __shared__ float sh_p[64];
+  __shared__ int sh_blk[64];
+  __shared__ int sh_off[64];
+  const int lane = threadIdx.x;
+  const int hq = blockIdx.x % a.H_q;
+  int b, split;
+  if (!find_item<64>(a.context_lens, a.B, a.len_cap, a.split_tokens, blockIdx.x / a.H_q, b, split)) return;
+  const int g = hq / a.G;
+  const int n = uniform(seq_len(a.context_lens, b, a.len_cap));
+  const int nsplit = n == 0 ? 1 : (n + a.split_tokens - 1) / a.split_tokens;
+  const size_t orow = ((size_t)b * a.H_q + hq) * D;
+  if (n == 0) {
+    for (int d = lane; d < D; d += 64) a.out[orow + d] = 0.f;
+    return;
+  }
+  const int bs = a.bs, kvt = a.kv_dtype;
+  const int X = 16 / elem_bytes_dev(kvt);
+  const int t_begin = split * a.split_tokens;
+  const int t_end = min(n, t_begin + a.split_tokens);
+  const int last_blk = (n + bs - 1) / bs - 1;
+  const int32_t* tab = a.block_tables + (size_t)b * a.max_blocks;
+  for (int d = lane; d < D; d += 64) sh_q[d] = load_elem(a.q, orow + d, a.q_dtype);
+  __syncthreads();
+  float sl = a.scale_log2;
+  float vs = 1.f;
+  if (kvt == PKV_FP8_E4M3) {
+    sl *= a.k_scale[g];
+    vs = a.v_scale[g];
+  }
+  float m = -INFINITY, l = 0.f, acc[KD];
+#pragma unroll
+  for (int k = 0; k < KD; ++k) acc[k] = 0.f;
+  for (int t0 = t_begin; t0 < t_end; t0 += 64) {
+    const int tok = t0 + lane;
+    const bool valid = tok < t_end;
+    float s = -INFINITY;
+    int blk = 0, off = 0;
+    if (valid) {
+      blk = block_id(tab, tok / bs, last_blk, a.NB);
+      off = tok % bs;
+      const size_t tile = ((size_t)blk * a.H_kv + g) * (size_t)D * bs;
+      float dot = 0.f;
+      for (int d = 0; d < D; ++d)
+        dot += sh_q[d] * load_elem(a.k_pool, tile + ((size_t)(d / X) * bs + off) * X + d % X, kvt);
+      s = dot * sl;
+    }
+    float tm = s;
+    for (int o = 32; o; o >>= 1) tm = fmaxf(tm, __shfl_xor(tm, o, 64));
+    const float mn = fmaxf(m, tm);
+    const float alpha = exp2_fast(m - mn);
+    const float p = valid ? exp2_fast(s - mn) : 0.f;
+    float ps = p;
+    for (int o = 32; o; o >>= 1) ps += __shfl_xor(ps, o, 64);
+    l = l * alpha + ps;
+    sh_p[lane] = p;
+    sh_blk[lane] = blk;
+    sh_off[lane] = off;
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < KD; ++k) acc[k] *= alpha;
+    const int cnt = min(64, t_end - t0);
+    for (int tt = 0; tt < cnt; ++tt) {
+      const float pp = sh_p[tt];
+      const size_t tile = ((size_t)sh_blk[tt] * a.H_kv + g) * (size_t)D * bs;
+#pragma unroll
+      for (int k = 0; k < KD; ++k)
+        acc[k] += pp * load_elem(a.v_pool, tile + (size_t)(lane + 64 * k) * bs + sh_off[tt], kvt);
+    }
+    m = mn;
+    __syncthreads();
+  }
+#pragma unroll
+  for (int k = 0; k < KD; ++k) {
+    const int d = lane + 64 * k;
+    if (nsplit == 1) {
+      a.out[orow + d] = acc[k] * vs / l;
+    } else {
+      const size_t pr = ((size_t)b * a.H_q + hq) * a.max_splits + split;
+      a.ws_o[pr * D + d] = acc[k] * vs;
+      if (d == 0) {
+        a.ws_ml[2 * pr] = m;
+        a.ws_ml[2 * pr + 1] = l;
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// split merge: o = sum_i 2^(m_i - M) o_i / sum_i 2^(m_i - M) l_i
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(64) void split_reduce_kernel(DecodeArgs a) {
+  const int b = blockIdx.x / a.H_q, hq = blockIdx.x % a.H_q;
+  const int n = seq_len(a.context_lens, b, a.len_cap);
+  const int nsplit = n == 0 ? 1 : (n + a.split_tokens - 1) / a.split_tokens;
+  if (nsplit <= 1) return;
+  const size_t pr0 = ((size_t)b * a.H_q + hq) * a.max_splits;
+  const float* ml = a.ws_ml + 2 * pr0;
+  float M = -INFINITY;
+  for (int s = 0; s < nsplit; ++s) M = fmaxf(M, ml[2 * s]);
+  float L = 0.f;
+  for (int s = 0; s < nsplit; ++s) L += exp2_fast(ml[2 * s] - M) * ml[2 * s + 1];
+  const float inv = 1.f / L;
+  for (int d = threadIdx.x; d < a.D; d += 64) {
+    float O = 0.f;
+    for (int s = 0; s < nsplit; ++s) O += exp2_fast(ml[2 * s] - M) * a.ws_o[(pr0 + s) * a.D + d];
+    a.out[((size_t)b * a.H_q + hq) * a.D + d] = O * inv;
+  }
+}
+
+template <int D, int BS, int KVT>
+hipError_t launch_mfma_t(const DecodeArgs& a, hipStream_t s) {
+  const long long grid = (long long)a.B * a.max_splits * a.H_kv;
+  hipLaunchKernelGGL((decode_mfma_kernel<D, BS, KVT>), dim3((unsigned)grid), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+template <int D, int KVT>
+hipError_t launch_mfma_bs(const DecodeArgs& a, hipStream_t s) {
+  switch (a.bs) {
+    case 8: return launch_mfma_t<D, 8, KVT>(a, s);
+    case 16: return launch_mfma_t<D, 16, KVT>(a, s);
+    case 32: return launch_mfma_t<D, 32, KVT>(a, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+bool decode_fast_path_supported(int q_dtype, int kv_dtype, int G, int D, int bs) {
+  return q_dtype == PKV_BF16 && (kv_dtype == PKV_BF16 || kv_dtype == PKV_FP8_E4M3) && G >= 1 && G <= 16 &&
+         (D == 64 || D == 128) && (bs == 8 || bs == 16 || bs == 32);
+}
+
+hipError_t launch_decode_mfma(const DecodeArgs& a, hipStream_t s) {
+  if (a.kv_dtype == PKV_BF16) {
+    if (a.D == 64) return launch_mfma_bs<64, PKV_BF16>(a, s);
+    if (a.D == 128) return launch_mfma_bs<128, PKV_BF16>(a, s);
+  } else {
+    if (a.D == 64) return launch_mfma_bs<64, PKV_FP8_E4M3>(a, s);
+    if (a.D == 128) return launch_mfma_bs<128, PKV_FP8_E4M3>(a, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_decode_vector(const DecodeArgs& a, hipStream_t s) {
+  const long long grid = (long long)a.B * a.max_splits * a.H_q;
+  switch (a.D) {
+    case 64: hipLaunchKernelGGL(decode_vector_kernel<64>, dim3((unsigned)grid), dim3(64), 0, s, a); break;
+    case 128: hipLaunchKernelGGL(decode_vector_kernel<128>, dim3((unsigned)grid), dim3(64), 0, s, a); break;
+    case 256: hipLaunchKernelGGL(decode_vector_kernel<256>, dim3((unsigned)grid), dim3(64), 0, s, a); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_split_reduce(const DecodeArgs& a, hipStream_t s) {
+  hipLaunchKernelGGL(split_reduce_kernel, dim3((unsigned)(a.B * a.H_q)), dim3(64), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace pkv

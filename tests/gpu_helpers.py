@@ -1,0 +1,80 @@
+"""GPU-side test plumbing: upload oracle-made inputs and run the library through its binding."""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+import paged_kv_cache_223_amd as pkv
+
+DEV = "cuda"
+
+
+def to_dev(arr: np.ndarray, dtype: str):
+    """numpy storage array (fp32 values / bf16 bits / e4m3 codes / ints) -> device tensor."""
+    arr = np.ascontiguousarray(arr)
+    if dtype == "bf16":
+        return torch.from_numpy(arr.view(np.int16)).to(DEV).view(torch.bfloat16)
+    if dtype == "e4m3":
+        return torch.from_numpy(arr.view(np.uint8)).to(DEV)
+    return torch.from_numpy(arr).to(DEV)
+
+
+def from_dev(t) -> np.ndarray:
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).cpu().numpy().view(np.uint16)
+    return t.cpu().numpy()
+
+
+def src_dtype(case) -> str:
+    return "f32" if case.spec.kv_dtype == "f32" else "bf16"
+
+
+def device_inputs(case, mat, kp, vp):
+    spec = case.spec
+    d = dict(
+        q=to_dev(case.q, spec.q_dtype),
+        k_pool=to_dev(kp, spec.kv_dtype),
+        v_pool=to_dev(vp, spec.kv_dtype),
+        block_tables=torch.from_numpy(np.ascontiguousarray(mat.block_tables, np.int32)).to(DEV),
+        context_lens=torch.from_numpy(np.ascontiguousarray(mat.context_lens, np.int32)).to(DEV),
+        k_scale=None if case.k_scale is None else torch.from_numpy(case.k_scale).to(DEV),
+        v_scale=None if case.v_scale is None else torch.from_numpy(case.v_scale).to(DEV),
+    )
+    return d
+
+
+def gpu_pools_by_append(case, mat, chunk=65536):
+    """Device pools filled through the library's kv_append over NaN-poisoned memory
+    (E4M3: code 0x7F), for full-size runs."""
+    spec = case.spec
+    kvd = {"bf16": pkv.BF16, "e4m3": pkv.FP8_E4M3, "f32": pkv.F32}[spec.kv_dtype]
+    ks, vs = pkv.pool_shapes(case.NB, spec.H_kv, spec.d, case.bs, kvd)
+    if spec.kv_dtype == "e4m3":
+        kp = torch.full(ks, 0x7F, dtype=torch.uint8, device=DEV)
+        vp = torch.full(vs, 0x7F, dtype=torch.uint8, device=DEV)
+    else:
+        dt = torch.bfloat16 if spec.kv_dtype == "bf16" else torch.float32
+        kp = torch.full(ks, float("nan"), dtype=dt, device=DEV)
+        vp = torch.full(vs, float("nan"), dtype=dt, device=DEV)
+    sd = src_dtype(case)
+    k_s = None if case.k_scale is None else torch.from_numpy(case.k_scale).to(DEV)
+    v_s = None if case.v_scale is None else torch.from_numpy(case.v_scale).to(DEV)
+    for k, v, s in ((mat.k_src, mat.v_src, mat.slots), (mat.step_k, mat.step_v, mat.step_slots)):
+        for i in range(0, len(s), chunk):
+            pkv.kv_append(to_dev(k[i:i + chunk], sd), to_dev(v[i:i + chunk], sd),
+                          torch.from_numpy(np.ascontiguousarray(s[i:i + chunk])).to(DEV), kp, vp, k_s, v_s)
+    torch.cuda.synchronize()
+    return kp, vp
+
+
+def decode(case, dev, max_context_len=None):
+    mcl = case.max_context_len if max_context_len is None else max_context_len
+    out = pkv.paged_attn_decode(dev["q"], dev["k_pool"], dev["v_pool"], dev["block_tables"], dev["context_lens"],
+                                float(case.scale), mcl, dev["k_scale"], dev["v_scale"])
+    torch.cuda.synchronize()
+    return out.cpu().numpy().astype(np.float64)
+
+
+def tol(case) -> float:
+    """Max per-row relative error allowed: 2e-3 with bf16 (or fp32) KV, 2e-2 with fp8 KV."""
+    return 2e-2 if case.spec.kv_dtype == "e4m3" else 2e-3

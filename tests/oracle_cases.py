@@ -30,6 +30,25 @@ def oracle_pools(case, mat, include_step=True):
     return kp, vp
 
 
+def oracle_pools_for_rows(case, mat, rows):
+    """Zero pools holding only the tokens stored in blocks that `rows` reference (enough for
+    the oracle to decode those rows at full size without quantising the whole batch)."""
+    spec = case.spec
+    used = set()
+    for b in rows:
+        nb = -(-int(mat.context_lens[b]) // case.bs)
+        used.update(int(x) for x in mat.block_tables[b, :nb])
+    used = np.array(sorted(used), np.int64)
+    kp, vp = oracle.empty_pools(case.NB, spec.H_kv, spec.d, case.bs, spec.kv_dtype)
+    for k, v, s in ((mat.k_src, mat.v_src, mat.slots), (mat.step_k, mat.step_v, mat.step_slots)):
+        if not len(s):
+            continue
+        keep = np.isin(np.asarray(s) // case.bs, used)
+        kp, vp = oracle.ref_append(kp, vp, k[keep], v[keep], src_dtype(case), s[keep], case.bs, spec.kv_dtype,
+                                   case.k_scale, case.v_scale)
+    return kp, vp
+
+
 def oracle_decode(case, mat, kp, vp, rows=None):
     spec = case.spec
     return oracle.ref_decode(case.q, spec.q_dtype, kp, vp, spec.kv_dtype, mat.block_tables,

@@ -287,6 +287,25 @@ def bf16_bits_as_f32(bits: np.ndarray) -> np.ndarray:
     return (np.asarray(bits, np.uint16).astype(np.uint32) << 16).view(np.float32)
 
 
+def custom(name, B, H_q, H_kv, d, bs, kv_dtype, q_dtype, lens, seed, fill="noise", NB=None):
+    """A one-off workload of given shapes and lengths (test coverage beyond the five above)."""
+    spec = Spec(name, B, H_q, H_kv, d, bs, kv_dtype, q_dtype, seed, "custom")
+    assert len(lens) == B
+    need = sum(_blocks(n, bs) for n in lens)
+    case = _plain_case(spec, bs, list(lens), NB if NB is not None else need + 3, fill)
+    if kv_dtype == "e4m3":
+        amax_k = np.zeros(H_kv, np.float32)
+        amax_v = np.zeros(H_kv, np.float32)
+        for b in range(B):
+            k, v = case.stream_kv(b)
+            if len(k):
+                amax_k = np.maximum(amax_k, np.abs(bf16_bits_as_f32(k)).max(axis=(0, 2)))
+                amax_v = np.maximum(amax_v, np.abs(bf16_bits_as_f32(v)).max(axis=(0, 2)))
+        case.k_scale = np.maximum(amax_k, np.float32(1e-3)) / np.float32(448.0)
+        case.v_scale = np.maximum(amax_v, np.float32(1e-3)) / np.float32(448.0)
+    return case
+
+
 BUILDERS = {
     "tiny_f32": tiny_f32,
     "llama8b_bf16": llama8b_bf16,
