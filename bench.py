@@ -49,6 +49,11 @@ def parse():
     p.add_argument("--workload", default="llama70b", choices=sorted(WORKLOADS))
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the oracle baseline sample")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                   help="only run the library's plain copy kernel over MIB MiB, 5 times (calibrates the "
+                        "FETCH_SIZE / WRITE_SIZE memory counters against a known byte count) and exit")
+    p.add_argument("--eager", action="store_true",
+                   help="launch the step's kernels one by one instead of replaying a captured HIP graph")
     p.add_argument("--identity-tables", action="store_true",
                    help="lay every sequence out contiguously (identity block order) instead of scattered")
     return p.parse_args()
@@ -113,6 +118,15 @@ def main():
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     dev = "cuda"
+    if args.copy_calibration:
+        n = args.copy_calibration << 20
+        src = torch.ones(n, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            pkv.copy_(dst, src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes_per_launch": n, "launches": 5}), flush=True)
+        return
     t_setup = time.time()
     wname, kw = WORKLOADS[args.workload]
     case = workloads.BUILDERS[wname](**kw)
@@ -147,8 +161,7 @@ def main():
     B, H_q, H_kv, D = case.B, spec.H_q, spec.H_kv, spec.d
     mcl = case.max_context_len
     out = torch.empty((B, H_q, D), dtype=torch.float32, device=dev)
-    wsb = pkv.decode_workspace_bytes(B, H_q, H_kv, D, mcl, case.bs)
-    ws = torch.empty(max(wsb, 256), dtype=torch.uint8, device=dev)
+    ws = pkv.decode_workspace(B, H_q, H_kv, D, mcl, case.bs, device=dev)
     torch.cuda.synchronize()
     print(f"# setup {time.time() - t_setup:.1f}s: {wname} B={B} NB={case.NB} pool {2 * k_pool.numel() * k_pool.element_size() / 1e9:.2f} GB",
           file=sys.stderr, flush=True)
@@ -169,16 +182,33 @@ def main():
         step()
     torch.cuda.synchronize()
     K = args.steps
+    # decode alone, eager launches: per-call duration of the dominant kernel(s) on the launch stream
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
-    t0 = time.perf_counter()
     for i in range(K):
         step(*ev[i])
     torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
     append_ms = np.array([e[0].elapsed_time(e[1]) for e in ev])
     decode_ms = np.array([e[1].elapsed_time(e[2]) for e in ev])
-    step_ms = ev[0][0].elapsed_time(ev[-1][2]) / K
-    print(f"# timed {K} steps in {wall:.3f}s wall; decode p10/p50/p90 "
+    eager_step_ms = ev[0][0].elapsed_time(ev[-1][2]) / K
+    # the timed region: K whole steps (kv_append + decode), replayed from one captured HIP graph
+    graph = None
+    if not args.eager:
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            step()
+        for _ in range(args.warmup):
+            graph.replay()
+    torch.cuda.synchronize()
+    g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    g0.record()
+    for i in range(K):
+        graph.replay() if graph is not None else step()
+    g1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    step_ms = g0.elapsed_time(g1) / K
+    print(f"# timed {K} steps in {wall:.3f}s wall ({'eager' if graph is None else 'graph'}); eager decode p10/p50/p90 "
           f"{np.percentile(decode_ms, 10) * 1e3:.1f}/{np.median(decode_ms) * 1e3:.1f}/{np.percentile(decode_ms, 90) * 1e3:.1f} us",
           file=sys.stderr, flush=True)
 
@@ -227,6 +257,8 @@ def main():
         "frac_of_hbm_peak": round(step_gbps / HBM_PEAK_GBPS, 4),
         "decode_us_p50": round(float(np.median(decode_ms)) * 1e3, 2),
         "append_us_p50": round(float(np.median(append_ms)) * 1e3, 2),
+        "eager_ms_per_step": round(eager_step_ms, 5),
+        "step_launch": "eager" if graph is None else "hip_graph",
         "decode_GBps_unique": round(dec_gbps, 1),
         "decode_GBps_logical": round(by["decode_logical"] / dec_avg_s / 1e9, 1),
         "kv_bytes_unique": by["kv_unique"],
@@ -268,14 +300,15 @@ def cpu_baseline(case, mat, out_dev, budget_s, by, B):
     got = out_dev.cpu().numpy().astype(np.float64)
     rows, errs = [], []
     t0 = time.perf_counter()
-    for b in sample:
-        ref = oracle.ref_decode(case.q, spec.q_dtype, kp, vp, spec.kv_dtype, mat.block_tables, mat.context_lens,
-                                case.scale, case.bs, case.k_scale, case.v_scale, rows=[b])
-        rows.append(b)
-        den = np.abs(ref[b]).max(-1)
-        errs.append(float((np.abs(got[b] - ref[b]).max(-1) / den).max()))
-        if time.perf_counter() - t0 > budget_s:
-            break
+    while time.perf_counter() - t0 < budget_s:  # passes over the sample until the budget is spent
+        for b in sample:
+            ref = oracle.ref_decode(case.q, spec.q_dtype, kp, vp, spec.kv_dtype, mat.block_tables,
+                                    mat.context_lens, case.scale, case.bs, case.k_scale, case.v_scale, rows=[b])
+            rows.append(b)
+            den = np.abs(ref[b]).max(-1)
+            errs.append(float((np.abs(got[b] - ref[b]).max(-1) / den).max()))
+            if time.perf_counter() - t0 > budget_s:
+                break
     dt = time.perf_counter() - t0
     toks = int(sum(int(mat.context_lens[b]) for b in rows))
     kv = toks * spec.H_kv * spec.d * 2 * {"bf16": 2, "e4m3": 1, "f32": 4}[spec.kv_dtype]
@@ -286,7 +319,8 @@ def cpu_baseline(case, mat, out_dev, budget_s, by, B):
         blas = len(os.sched_getaffinity(0))
     return {
         "value": round(len(rows) / dt, 3), "unit": "sequences/s", "cores": int(blas), "kind": "oracle",
-        "sample": f"{len(rows)} of {B} sequences ({toks} tokens, all heads), numpy fp64 gather-then-attend",
+        "sample": f"{len(rows)} sequence decodes drawn from {len(sample)} of the {B} sequences ({toks} tokens, "
+                  f"all heads), numpy fp64 gather-then-attend",
         "kv_GBps": round(kv / dt / 1e9, 3), "seconds": round(dt, 2), "host_cpus": os.cpu_count(),
         "affinity_cpus": len(os.sched_getaffinity(0)),
         "gpu_vs_oracle_max_row_rel_err": float(max(errs)),

@@ -111,9 +111,11 @@ size_t pkv_decode_workspace_bytes(int32_t B, int32_t H_q, int32_t H_kv, int32_t 
  * For sequence b with n = context_lens[b] and query head h (KV head g):
  *     out[b][h] = sum_{t<n} softmax_t(scale * <q[b][h], K_b[g][t]>) V_b[g][t]
  * where K_b, V_b are the sequence's tokens in logical order reached through
- * block_tables[b] (the kernel never materialises the scores in device memory:
- * an online softmax per context split, then a merge of the splits).  n = 0
- * gives a zero row.  context_lens counts the token appended this step.
+ * block_tables[b].  Each (context split, sequence, KV head) work item runs
+ * an online softmax over its tokens without writing scores to memory; when
+ * a sequence has several splits a second small launch merges their partial
+ * results.  n = 0 gives a zero row.  context_lens counts the token appended
+ * this step.
  *
  *   out            device fp32 [B][H_q][D]
  *   q              device [B][H_q][D], q_dtype F32 or BF16
@@ -126,8 +128,10 @@ size_t pkv_decode_workspace_bytes(int32_t B, int32_t H_q, int32_t H_kv, int32_t 
  *   scale          softmax scale (e.g. 1/sqrt(D)), applied to q.k in fp32
  *   k_scale, v_scale device fp32 [H_kv], required iff kv_dtype = E4M3
  *   workspace      device scratch of >= pkv_decode_workspace_bytes(...) bytes,
- *                  256-byte aligned; contents need no initialisation and are
- *                  clobbered; calls that share a workspace must be ordered
+ *                  256-byte aligned (may be NULL when that size is 0); its
+ *                  contents need no initialisation and are overwritten.
+ *                  Calls that share a workspace must be ordered (one stream,
+ *                  or synchronised); concurrent calls on one workspace race.
  *   Requires H_q % H_kv == 0, D in {64, 128, 256}, bs in {8, 16, 32}.
  *   bf16 q with bf16/E4M3 KV, H_q/H_kv <= 16 and D in {64, 128} take the
  *   matrix-core path; other supported combinations take a vector path.

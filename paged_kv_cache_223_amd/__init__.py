@@ -188,6 +188,25 @@ def decode_workspace_bytes(B: int, H_q: int, H_kv: int, D: int, max_context_len:
     return int(lib.pkv_decode_workspace_bytes(B, H_q, H_kv, D, max_context_len, bs))
 
 
+def decode_workspace(B: int, H_q: int, H_kv: int, D: int, max_context_len: int, bs: int, device="cuda"):
+    """A workspace for these sizes (contents need no initialisation)."""
+    n = decode_workspace_bytes(B, H_q, H_kv, D, max_context_len, bs)
+    return torch.empty(max(n, 256), dtype=torch.uint8, device=device)
+
+
+_ws_cache = {}
+
+
+def _cached_workspace(device, need: int):
+    """Per-device workspace reused by calls that pass none (ordered on torch's current stream)."""
+    key = (device.type, device.index)
+    ws = _ws_cache.get(key)
+    if ws is None or ws.numel() < need:
+        ws = torch.empty(max(need, 1 << 20), dtype=torch.uint8, device=device)
+        _ws_cache[key] = ws
+    return ws
+
+
 def paged_attn_decode(q, k_pool, v_pool, block_tables, context_lens, scale: float, max_context_len: int,
                       k_scale=None, v_scale=None, out=None, workspace=None):
     """Decode attention of one query token per sequence over its paged KV; fp32 [B, H_q, D]."""
@@ -207,7 +226,7 @@ def paged_attn_decode(q, k_pool, v_pool, block_tables, context_lens, scale: floa
         raise ValueError("out must be fp32 [B, H_q, D]")
     need = decode_workspace_bytes(B, H_q, H_kv, D, max_context_len, bs)
     if workspace is None and need:
-        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+        workspace = _cached_workspace(q.device, need)
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     _check(lib.pkv_paged_attn_decode(
         _ptr(out), _ptr(q), dtype_code(q), _ptr(k_pool), _ptr(v_pool), kv, _ptr(block_tables),
@@ -297,5 +316,6 @@ class Allocator:
 
 
 __all__ = ["lib", "LIB_PATH", "PkvError", "last_error", "kv_append", "paged_attn_decode", "decode_workspace_bytes",
+           "decode_workspace",
            "pool_shapes", "dtype_code", "stream_read", "copy_", "Allocator", "SIGNATURES",
            "F32", "BF16", "FP8_E4M3"]

@@ -28,6 +28,18 @@ int hip_status(hipError_t e, const char* what) {
 
 static bool valid_dtype(int dt) { return dt == PKV_F32 || dt == PKV_BF16 || dt == PKV_FP8_E4M3; }
 
+// compute units of the current device (256 on MI355X when no device is visible,
+// e.g. when only sizes are queried on a host without a GPU)
+static int current_num_cus() {
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) {
+    (void)hipGetLastError();
+    return 256;
+  }
+  return cus;
+}
+
 }  // namespace pkv
 
 using namespace pkv;
@@ -84,7 +96,7 @@ size_t pkv_decode_workspace_bytes(int32_t B, int32_t H_q, int32_t H_kv, int32_t 
     set_error("decode_workspace_bytes: bad sizes");
     return 0;
   }
-  return workspace_bytes_for(B, H_q, D, plan_splits(B, H_kv, max_context_len));
+  return workspace_bytes_for(B, H_q, D, plan_splits(B, H_kv, max_context_len), current_num_cus());
 }
 
 int pkv_paged_attn_decode(float* out, const void* q, int q_dtype, const void* k_pool, const void* v_pool,
@@ -124,7 +136,8 @@ int pkv_paged_attn_decode(float* out, const void* q, int q_dtype, const void* k_
     return PKV_ERR_INVALID_ARG;
   }
   const SplitPlan plan = plan_splits(B, H_kv, max_context_len);
-  const size_t need = workspace_bytes_for(B, H_q, D, plan);
+  const int num_cus = current_num_cus();
+  const size_t need = workspace_bytes_for(B, H_q, D, plan, num_cus);
   if (need > 0 && (!workspace || workspace_bytes < need || ((uintptr_t)workspace & 255u))) {
     set_error("decode: workspace needs %zu bytes, 256-byte aligned (got %zu at %p)", need, workspace_bytes,
               workspace);
@@ -147,10 +160,9 @@ int pkv_paged_attn_decode(float* out, const void* q, int q_dtype, const void* k_
   a.k_scale = k_scale;
   a.v_scale = v_scale;
   if (need > 0) {
-    size_t per = (size_t)B * H_q * plan.max_splits;
-    size_t o = (per * D * sizeof(float) + 255) / 256 * 256;
-    a.ws_o = (float*)workspace;
-    a.ws_ml = (float*)((char*)workspace + o);
+    const WorkspaceLayout wl = workspace_layout(B, H_q, D, plan, num_cus);
+    a.ws_o = (float*)((char*)workspace + wl.o);
+    a.ws_ml = (float*)((char*)workspace + wl.ml);
   }
   a.B = B;
   a.H_q = H_q;
@@ -167,10 +179,12 @@ int pkv_paged_attn_decode(float* out, const void* q, int q_dtype, const void* k_
   a.scale_log2 = scale * 1.4426950408889634f;
   a.q_dtype = q_dtype;
   a.kv_dtype = kv_dtype;
+  a.num_cus = num_cus;
   hipStream_t s = (hipStream_t)stream;
-  int st = hip_status(fast ? launch_decode_mfma(a, s) : launch_decode_vector(a, s), "decode launch");
+  if (fast) return hip_status(launch_decode_mfma(a, s), "decode launch");
+  const int st = hip_status(launch_decode_vector(a, s), "decode launch");
   if (st != PKV_OK || plan.max_splits <= 1) return st;
-  return hip_status(launch_split_reduce(a, s), "split reduce launch");
+  return hip_status(launch_split_merge(a, s), "split merge launch");
 }
 
 size_t pkv_stream_read_sink_floats(size_t bytes) { return stream_read_blocks(bytes); }

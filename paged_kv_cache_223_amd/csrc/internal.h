@@ -41,12 +41,33 @@ inline SplitPlan plan_splits(int B, int H_kv, int max_ctx) {
   return p;
 }
 
-inline size_t workspace_bytes_for(int B, int H_q, int D, const SplitPlan& p) {
-  if (p.max_splits <= 1) return 0;
-  size_t per = (size_t)B * H_q * p.max_splits;
-  size_t o = per * D * sizeof(float);
-  o = (o + 255) / 256 * 256;
-  return o + per * 2 * sizeof(float);
+// The matrix-core path launches one round of 4-wave workgroups: at most this
+// many per CU; each owns two partial slots of 16 heads.
+constexpr int kStreamKMaxGroupsPerCU = 4;
+
+// Workspace layout, large enough for either path:
+//   [partial outputs fp32: max(vector path B*H_q*max_splits*D,
+//                              matrix path CUs*4 groups*2 slots*16 heads*D)][pad to 256]
+//   [partial (max, sum) fp32: the same count of rows * 2]
+struct WorkspaceLayout {
+  size_t o, ml, total;
+};
+
+inline size_t align256(size_t x) { return (x + 255) / 256 * 256; }
+
+inline WorkspaceLayout workspace_layout(int B, int H_q, int D, const SplitPlan& p, int num_cus) {
+  const size_t vec_rows = p.max_splits > 1 ? (size_t)B * H_q * p.max_splits : 0;
+  const size_t mfma_rows = (size_t)num_cus * kStreamKMaxGroupsPerCU * 2 * 16;
+  const size_t rows = vec_rows > mfma_rows ? vec_rows : mfma_rows;
+  WorkspaceLayout w;
+  w.o = 0;
+  w.ml = align256(rows * D * sizeof(float));
+  w.total = w.ml + rows * 2 * sizeof(float);
+  return w;
+}
+
+inline size_t workspace_bytes_for(int B, int H_q, int D, const SplitPlan& p, int num_cus) {
+  return workspace_layout(B, H_q, D, p, num_cus).total;
 }
 
 struct DecodeArgs {
@@ -67,13 +88,14 @@ struct DecodeArgs {
   int max_splits;
   float scale_log2;  // scale * log2(e)
   int q_dtype, kv_dtype;
+  int num_cus;       // compute units of the device (sizes the matrix-core launch)
 };
 
 // Kernel launchers (paged_decode.hip).  Return hipError_t of the launch.
 bool decode_fast_path_supported(int q_dtype, int kv_dtype, int G, int D, int bs);
 hipError_t launch_decode_mfma(const DecodeArgs& a, hipStream_t s);
 hipError_t launch_decode_vector(const DecodeArgs& a, hipStream_t s);
-hipError_t launch_split_reduce(const DecodeArgs& a, hipStream_t s);
+hipError_t launch_split_merge(const DecodeArgs& a, hipStream_t s);
 
 // kv_append.hip
 struct AppendArgs {

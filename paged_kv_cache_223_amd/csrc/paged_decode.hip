@@ -10,10 +10,14 @@
 // pages is the cost to keep small.  Scores are never written to memory (the
 // fused-attention property named in the section on block-level eviction).
 //
-// Work decomposition: a work item is (sequence b, context split, KV head g).
-// Items are numbered sequence-major; every workgroup scans the context
-// lengths to find its item, so sequences of very different length get a
-// number of items proportional to their length and no item is idle.
+// Work decomposition: a work item is (context split s, sequence b, KV head g),
+// numbered ((s * B) + b) * H_kv + g.  The grid covers the longest admissible
+// sequence; an item past its sequence's last split exits after one load of
+// the (cached) length.  Split-major order makes the first splits of all
+// sequences run together, so sequences that share prefix blocks read them at
+// about the same time, and KV head g of every item lands on the same XCD
+// (workgroups are dealt to the 8 XCDs round-robin), whose L2 then serves the
+// shared blocks again.
 //
 // Matrix-core path (bf16 q; bf16 or E4M3 KV; G = H_q/H_kv <= 16; D 64/128):
 // one workgroup = 4 waves; a wave owns 32-token chunks of the split (chunk
@@ -37,9 +41,13 @@
 // Vector path: one wave per (sequence, split, query head), fp32 VALU; used for
 // fp32 q or KV, G > 16 or D = 256.
 //
-// Splits: each item writes its unnormalised output and (max, sum) to the
-// workspace unless the sequence has a single split, in which case it writes
-// the final row; split_reduce merges multi-split rows.
+// Splits: a sequence with one split writes its final rows directly.  With
+// several splits each item writes its unnormalised output and (max, sum) to
+// the workspace, and split_merge (a second, small launch) combines them:
+//     o = sum_i 2^(m_i - M) o_i / sum_i 2^(m_i - M) l_i,  M = max_i m_i.
+// (Merging inside the partition kernel by the last-arriving workgroup needs a
+// device-scope release/acquire per workgroup; on gfx950 those are whole-L2
+// writeback/invalidate operations, which cost far more than the launch.)
 
 #include <hip/hip_runtime.h>
 
@@ -71,48 +79,6 @@ __device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirs
 __device__ __forceinline__ int splits_of(int n, int cap, int split_tokens) {
   n = n < 0 ? 0 : (n > cap ? cap : n);
   return n == 0 ? 1 : (n + split_tokens - 1) / split_tokens;
-}
-
-// Map work index `target` (over sequences, sequence-major) to (b, split).
-// All NT threads of the block take part; the result is block-uniform.
-template <int NT>
-__device__ bool find_item(const int32_t* __restrict__ lens, int B, int cap, int split_tokens,
-                          int target, int& b_out, int& split_out) {
-  constexpr int NWv = NT / 64;
-  __shared__ int sh_wsum[NWv];
-  __shared__ int sh_res[2];
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  if (tid == 0) sh_res[0] = -1;
-  int carry = 0;
-  for (int base = 0; base < B; base += NT) {
-    const int b = base + tid;
-    const int ns = b < B ? splits_of(lens[b], cap, split_tokens) : 0;
-    int x = ns;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-      int y = __shfl_up(x, off, 64);
-      if (lane >= off) x += y;
-    }
-    if (lane == 63) sh_wsum[w] = x;
-    __syncthreads();
-    int pre = carry, tot = carry;
-#pragma unroll
-    for (int i = 0; i < NWv; ++i) {
-      pre += i < w ? sh_wsum[i] : 0;
-      tot += sh_wsum[i];
-    }
-    const int incl = pre + x, excl = incl - ns;
-    if (b < B && target >= excl && target < incl) {
-      sh_res[0] = b;
-      sh_res[1] = target - excl;
-    }
-    carry = tot;
-    __syncthreads();
-    if (sh_res[0] >= 0) break;
-  }
-  b_out = uniform(sh_res[0]);
-  split_out = uniform(sh_res[1]);
-  return b_out >= 0;
 }
 
 __device__ __forceinline__ int seq_len(const int32_t* __restrict__ lens, int b, int cap) {
@@ -202,7 +168,7 @@ __device__ __forceinline__ void load_chunk(Chunk<D, BS, KVT>& ch, const char* __
     const char* base = kpool + (size_t)id * bstride + gofs + (size_t)(kg * BS + tk % BS) * 16;
 #pragma unroll
     for (int c = 0; c < Chunk<D, BS, KVT>::kKLoads; ++c)
-      ch.k[a][c] = *(const u32x4*)(base + (size_t)c * 64 * BS);
+      ch.k[a][c] = __builtin_nontemporal_load((const u32x4*)(base + (size_t)c * 64 * BS));
   }
   const int n = lane & 15, qg = lane >> 4;
 #pragma unroll
@@ -214,11 +180,11 @@ __device__ __forceinline__ void load_chunk(Chunk<D, BS, KVT>& ch, const char* __
     for (int t = 0; t < D / 16; ++t) {
       const char* p = base + (size_t)t * 16 * BS * S;
       if constexpr (KVT == PKV_BF16) {
-        u32x2 x = *(const u32x2*)p;
+        u32x2 x = __builtin_nontemporal_load((const u32x2*)p);
         ch.v[t][2 * a] = x.x;
         ch.v[t][2 * a + 1] = x.y;
       } else {
-        ch.v[t][a] = *(const uint32_t*)p;
+        ch.v[t][a] = __builtin_nontemporal_load((const uint32_t*)p);
       }
     }
   }
@@ -327,39 +293,64 @@ __device__ __forceinline__ void process_chunk(const Chunk<D, BS, KVT>& ch, const
   }
 }
 
-template <int D, int BS, int KVT>
-__global__ __launch_bounds__(256, 2) void decode_mfma_kernel(DecodeArgs a) {
-  constexpr int NW = 4;
-  __shared__ float sh_acc[NW][16][D];
-  __shared__ float sh_m[NW][16];
-  __shared__ float sh_l[NW][16];
+// ---------------------------------------------------------------------------
+// matrix-core path, stream-K decomposition
+//
+// The batch's work is a row of units (sequence b, KV head g, 32-token chunk),
+// ordered b-major, then g, then chunk; sequence b contributes H_kv segments of
+// c_b = ceil(n_b / 32) units.  The grid is one round of 4-wave workgroups (as
+// many as the GPU holds at once) and workgroup i takes the contiguous units
+// [i*upw, (i+1)*upw), upw = ceil(total / workgroups), so every workgroup
+// streams the same number of KV bytes whatever the mix of lengths, and there
+// is no second round.  A workgroup walks its range segment by segment (its 4
+// waves take a piece's chunks round-robin and merge through LDS): a segment
+// it covers whole gets its final rows written directly; the at most two
+// segments cut by its range ends get partial results in its two workspace
+// slots, merged afterwards by streamk_merge.
+// ---------------------------------------------------------------------------
+constexpr int kMinUnits = 8;
 
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int g = blockIdx.x % a.H_kv;
-  int b, split;
-  if (!find_item<256>(a.context_lens, a.B, a.len_cap, a.split_tokens, blockIdx.x / a.H_kv, b, split)) return;
-  const int G = a.G;
-  const int hq0 = g * G;
-  const int n = uniform(seq_len(a.context_lens, b, a.len_cap));
-  const int nsplit = n == 0 ? 1 : (n + a.split_tokens - 1) / a.split_tokens;
-  const size_t orow = ((size_t)b * a.H_q + hq0) * D;
-  if (n == 0) {
-    for (int e = tid; e < G * D; e += 256) a.out[orow + e] = 0.f;
-    return;
+__device__ __forceinline__ int chunks_of(int n, int cap) {
+  n = n < 0 ? 0 : (n > cap ? cap : n);
+  return (n + 31) / 32;
+}
+
+__device__ __forceinline__ int wave_sum(int x) {
+#pragma unroll
+  for (int o = 32; o; o >>= 1) x += __shfl_xor(x, o, 64);
+  return x;
+}
+
+__device__ __forceinline__ int wave_incl_scan(int x, int lane) {
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(x, o, 64);
+    if (lane >= o) x += y;
   }
-  const int t_begin = split * a.split_tokens;
-  const int t_end = min(n, t_begin + a.split_tokens);
-  const int c_begin = t_begin / 32, c_end = (t_end + 31) / 32;
+  return x;
+}
+
+// The wave's share of one piece: chunks c_first + w, + 4, ... below c_end of
+// segment (b, g), with the next chunk's loads in flight while one is computed.
+template <int D, int BS, int KVT>
+__device__ __forceinline__ void run_piece(const DecodeArgs& a, int b, int g, int n, int first, int c_end,
+                                          f32x4 (&acc)[D / 16], WaveState& st, int lane) {
+  constexpr int NW = 4;
+  const int G = a.G;
   const int last_blk = (n + BS - 1) / BS - 1;
   const int32_t* tab = a.block_tables + (size_t)b * a.max_blocks;
   const char* kpool = (const char*)a.k_pool;
   const char* vpool = (const char*)a.v_pool;
-
+#pragma unroll
+  for (int t = 0; t < D / 16; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+  st = WaveState{-INFINITY, 0.f};
+  const int cnt = first < c_end ? (c_end - first + NW - 1) / NW : 0;
+  if (cnt == 0) return;
   // resident Q operand: lane holds head (lane & 15), 8 head-dim values per MFMA
   const int h = lane & 15, kg = lane >> 4;
   u32x4 qop[D / 32];
   {
-    const uint16_t* qrow = (const uint16_t*)a.q + ((size_t)b * a.H_q + hq0 + h) * D;
+    const uint16_t* qrow = (const uint16_t*)a.q + ((size_t)b * a.H_q + g * G + h) * D;
 #pragma unroll
     for (int c = 0; c < D / 32; ++c) {
       u32x4 v = u32x4{0u, 0u, 0u, 0u};
@@ -369,75 +360,234 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(DecodeArgs a) {
   }
   float sl = a.scale_log2;
   if constexpr (KVT == PKV_FP8_E4M3) sl *= a.k_scale[g];
+  Chunk<D, BS, KVT> A, Bf;
+  int c = first;
+  load_chunk(A, kpool, vpool, tab, c, last_blk, a.NB, a.H_kv, g, lane);
+  int k = 0;
+  for (; k + 2 < cnt; k += 2) {
+    load_chunk(Bf, kpool, vpool, tab, c + NW, last_blk, a.NB, a.H_kv, g, lane);
+    process_chunk(A, qop, acc, st, c, n, sl, lane);
+    load_chunk(A, kpool, vpool, tab, c + 2 * NW, last_blk, a.NB, a.H_kv, g, lane);
+    process_chunk(Bf, qop, acc, st, c + NW, n, sl, lane);
+    c += 2 * NW;
+  }
+  if (k + 1 < cnt) {
+    load_chunk(Bf, kpool, vpool, tab, c + NW, last_blk, a.NB, a.H_kv, g, lane);
+    process_chunk(A, qop, acc, st, c, n, sl, lane);
+    process_chunk(Bf, qop, acc, st, c + NW, n, sl, lane);
+  } else {
+    process_chunk(A, qop, acc, st, c, n, sl, lane);
+  }
+}
 
+template <int D, int BS, int KVT>
+__global__ __launch_bounds__(256, 2) void decode_streamk_kernel(DecodeArgs a) {
+  constexpr int NW = 4;
+  __shared__ float sh_acc[NW][16][D];
+  __shared__ float sh_m[NW][16];
+  __shared__ float sh_l[NW][16];
+  const int tid = threadIdx.x, lane = tid & 63, w = uniform(tid >> 6);
+  const int wg = blockIdx.x, nwg = gridDim.x;
+  const int B = a.B, H_kv = a.H_kv, G = a.G, cap = a.len_cap;
+  // sequences with no tokens: zero rows, written by workgroup b % nwg
+  for (int b0 = wg; b0 < B; b0 += nwg) {
+    if (uniform(seq_len(a.context_lens, b0, cap)) == 0)
+      for (int e = tid; e < a.H_q * D; e += 256) a.out[(size_t)b0 * a.H_q * D + e] = 0.f;
+  }
+  // total units and this workgroup's range (every wave computes the same values)
+  int part = 0;
+  for (int b0 = lane; b0 < B; b0 += 64) part += chunks_of(a.context_lens[b0], cap);
+  const int total = uniform(wave_sum(part)) * H_kv;
+  int upw = (total + nwg - 1) / nwg;
+  upw = upw < kMinUnits ? kMinUnits : upw;
+  const int u_begin = wg * upw;
+  if (u_begin >= total) return;
+  const int u_end = min(total, u_begin + upw);
+  // the sequence holding unit u_begin, and P = chunks of the sequences before it
+  int b = -1, P = 0;
+  {
+    int base = 0;
+    for (int b0 = 0; b0 < B && b < 0; b0 += 64) {
+      const int cb = b0 + lane < B ? chunks_of(a.context_lens[b0 + lane], cap) : 0;
+      const int incl = wave_incl_scan(cb, lane);
+      const bool hit = cb > 0 && (base + incl - cb) * H_kv <= u_begin && u_begin < (base + incl) * H_kv;
+      const unsigned long long m = __ballot(hit);
+      if (m) {
+        const int src = __ffsll((long long)m) - 1;
+        b = b0 + src;
+        P = __shfl(base + incl - cb, src, 64);
+      }
+      base += __shfl(incl, 63, 64);
+    }
+  }
+  b = uniform(b);
+  P = uniform(P);
+  const int kg = lane >> 4;
   f32x4 acc[D / 16];
-#pragma unroll
-  for (int t = 0; t < D / 16; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-  WaveState st{-INFINITY, 0.f};
-
-  // chunks c_begin + w, +NW, ... ; double-buffered: the next chunk's loads are
-  // in flight while the current one is computed
-  const int first = c_begin + w;
-  const int cnt = first < c_end ? (c_end - first + NW - 1) / NW : 0;
-  if (cnt > 0) {
-    Chunk<D, BS, KVT> A, Bf;
-    int c = first;
-    load_chunk(A, kpool, vpool, tab, c, last_blk, a.NB, a.H_kv, g, lane);
-    int k = 0;
-    for (; k + 2 < cnt; k += 2) {
-      load_chunk(Bf, kpool, vpool, tab, c + NW, last_blk, a.NB, a.H_kv, g, lane);
-      process_chunk(A, qop, acc, st, c, n, sl, lane);
-      load_chunk(A, kpool, vpool, tab, c + 2 * NW, last_blk, a.NB, a.H_kv, g, lane);
-      process_chunk(Bf, qop, acc, st, c + NW, n, sl, lane);
-      c += 2 * NW;
+  WaveState st;
+  int u = u_begin;
+  int slot = 0;
+  while (u < u_end) {
+    const int n = uniform(seq_len(a.context_lens, b, cap));
+    const int cb = (n + 31) / 32;
+    const int seg0 = P * H_kv;  // first unit of sequence b
+    const int g = (u - seg0) / cb;
+    const int s_begin = seg0 + g * cb;
+    const int c_first = u - s_begin;
+    const int c_end = min(u_end, s_begin + cb) - s_begin;
+    run_piece<D, BS, KVT>(a, b, g, n, c_first + w, c_end, acc, st, lane);
+    // ---- merge the four waves' shares through LDS
+    float lt = st.l;
+    lt += __shfl_xor(lt, 16, 64);
+    lt += __shfl_xor(lt, 32, 64);
+    if (lane < 16) {
+      sh_m[w][lane] = st.m;
+      sh_l[w][lane] = lt;
     }
-    if (k + 1 < cnt) {
-      load_chunk(Bf, kpool, vpool, tab, c + NW, last_blk, a.NB, a.H_kv, g, lane);
-      process_chunk(A, qop, acc, st, c, n, sl, lane);
-      process_chunk(Bf, qop, acc, st, c + NW, n, sl, lane);
-    } else {
-      process_chunk(A, qop, acc, st, c, n, sl, lane);
-    }
-  }
-
-  // ---- merge the four waves through LDS
-  float lt = st.l;
-  lt += __shfl_xor(lt, 16, 64);
-  lt += __shfl_xor(lt, 32, 64);
-  if (lane < 16) {
-    sh_m[w][lane] = st.m;
-    sh_l[w][lane] = lt;
-  }
 #pragma unroll
-  for (int t = 0; t < D / 16; ++t)
+    for (int t = 0; t < D / 16; ++t)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) sh_acc[w][4 * kg + i][16 * t + (lane & 15)] = acc[t][i];
-  __syncthreads();
-
-  const float vs = KVT == PKV_FP8_E4M3 ? a.v_scale[g] : 1.f;
-  for (int e = tid; e < G * D; e += 256) {
-    const int hh = e / D, col = e % D;
-    float M = sh_m[0][hh];
+      for (int i = 0; i < 4; ++i) sh_acc[w][4 * kg + i][16 * t + (lane & 15)] = acc[t][i];
+    __syncthreads();
+    const float vs = KVT == PKV_FP8_E4M3 ? a.v_scale[g] : 1.f;
+    const bool whole = c_first == 0 && c_end == cb;
+    const size_t orow = ((size_t)b * a.H_q + g * G) * D;
+    const size_t prow = ((size_t)wg * 2 + slot) * 16;
+    for (int e = tid; e < G * D; e += 256) {
+      const int hh = e / D, col = e % D;
+      float M = sh_m[0][hh];
 #pragma unroll
-    for (int i = 1; i < NW; ++i) M = fmaxf(M, sh_m[i][hh]);
-    float L = 0.f, O = 0.f;
+      for (int i = 1; i < NW; ++i) M = fmaxf(M, sh_m[i][hh]);
+      float L = 0.f, O = 0.f;
 #pragma unroll
-    for (int i = 0; i < NW; ++i) {
-      const float wt = exp2_fast(sh_m[i][hh] - M);
-      L += wt * sh_l[i][hh];
-      O += wt * sh_acc[i][hh][col];
-    }
-    O *= vs;
-    if (nsplit == 1) {
-      a.out[orow + e] = O / L;
-    } else {
-      const size_t pr = ((size_t)b * a.H_q + hq0 + hh) * a.max_splits + split;
-      a.ws_o[pr * D + col] = O;
-      if (col == 0) {
-        a.ws_ml[2 * pr] = M;
-        a.ws_ml[2 * pr + 1] = L;
+      for (int i = 0; i < NW; ++i) {
+        const float wt = exp2_fast(sh_m[i][hh] - M);
+        L += wt * sh_l[i][hh];
+        O += wt * sh_acc[i][hh][col];
+      }
+      O *= vs;
+      if (whole) {
+        a.out[orow + e] = O / L;
+      } else {
+        a.ws_o[(prow + hh) * D + col] = O;
+        if (col == 0) {
+          a.ws_ml[2 * (prow + hh)] = M;
+          a.ws_ml[2 * (prow + hh) + 1] = L;
+        }
       }
     }
+    __syncthreads();  // LDS is reused by the next piece
+    slot = 1;
+    u = s_begin + c_end;
+    if (u >= seg0 + H_kv * cb) {  // next non-empty sequence
+      P += cb;
+      do {
+        ++b;
+      } while (b < B && uniform(chunks_of(a.context_lens[b], cap)) == 0);
+    }
+  }
+}
+
+// Merge the pieces of the segments that workgroup ranges cut; one workgroup per
+// (sequence, KV head).  Recomputes the unit layout of the kernel above.  All
+// piece loads are independent of each other.
+__global__ __launch_bounds__(256) void streamk_merge_kernel(DecodeArgs a, int nwg) {
+  __shared__ int sh_part[2][4];
+  __shared__ float sh_red[4][16][2];
+  __shared__ float sh_M[16], sh_iL[16];
+  __shared__ float sh_o[256];
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int b = blockIdx.x / a.H_kv, g = blockIdx.x % a.H_kv;
+  const int cap = a.len_cap, B = a.B, G = a.G, D = a.D;
+  const int cb = chunks_of(a.context_lens[b], cap);
+  if (cb == 0) return;
+  int tot = 0, before = 0;
+  for (int b0 = tid; b0 < B; b0 += 256) {
+    const int c = chunks_of(a.context_lens[b0], cap);
+    tot += c;
+    before += b0 < b ? c : 0;
+  }
+  tot = wave_sum(tot);
+  before = wave_sum(before);
+  if (lane == 0) {
+    sh_part[0][wv] = tot;
+    sh_part[1][wv] = before;
+  }
+  __syncthreads();
+  const int total = (sh_part[0][0] + sh_part[0][1] + sh_part[0][2] + sh_part[0][3]) * a.H_kv;
+  const int P = sh_part[1][0] + sh_part[1][1] + sh_part[1][2] + sh_part[1][3];
+  int upw = (total + nwg - 1) / nwg;
+  upw = upw < kMinUnits ? kMinUnits : upw;
+  const int s_begin = P * a.H_kv + g * cb, s_end = s_begin + cb;
+  const int w0 = s_begin / upw, w1 = (s_end - 1) / upw;
+  if (w0 == w1) return;  // one workgroup covered the segment and wrote it
+  const int np = w1 - w0 + 1;
+  // piece p belongs to workgroup w0 + p: slot 1 if that workgroup began in an earlier segment
+  auto prow = [&](int p) -> size_t {
+    const int w = w0 + p;
+    const int slot = (p == 0 && w * upw < s_begin) ? 1 : 0;
+    return ((size_t)w * 2 + slot) * 16;
+  };
+  // ---- per head: M = max m_p, L = sum 2^(m_p - M) l_p, threads strided over pieces
+  for (int h = 0; h < G; ++h) {
+    float m = -INFINITY, l = 0.f;
+    for (int p = tid; p < np; p += 256) {
+      const float mp = a.ws_ml[2 * (prow(p) + h)], lp = a.ws_ml[2 * (prow(p) + h) + 1];
+      const float mn = fmaxf(m, mp);
+      l = l * exp2_fast(m - mn) + lp * exp2_fast(mp - mn);
+      m = mn;
+    }
+#pragma unroll
+    for (int o = 32; o; o >>= 1) {
+      const float m2 = __shfl_xor(m, o, 64), l2 = __shfl_xor(l, o, 64);
+      const float mn = fmaxf(m, m2);
+      l = (m == -INFINITY ? 0.f : l * exp2_fast(m - mn)) + (m2 == -INFINITY ? 0.f : l2 * exp2_fast(m2 - mn));
+      m = mn;
+    }
+    if (lane == 0 && h < 16) {
+      sh_red[wv][h][0] = m;
+      sh_red[wv][h][1] = l;
+    }
+  }
+  __syncthreads();
+  if (tid < G) {
+    float M = sh_red[0][tid][0];
+    for (int i = 1; i < 4; ++i) M = fmaxf(M, sh_red[i][tid][0]);
+    float L = 0.f;
+    for (int i = 0; i < 4; ++i)
+      if (sh_red[i][tid][0] != -INFINITY) L += sh_red[i][tid][1] * exp2_fast(sh_red[i][tid][0] - M);
+    sh_M[tid] = M;
+    sh_iL[tid] = 1.f / L;
+  }
+  __syncthreads();
+  // ---- outputs: thread = (column, piece group); sum pieces of its group, then across groups
+  const int ngrp = 256 / D;  // D divides 256 here (64 or 128)
+  const int col = tid % D, grp = tid / D;
+  const size_t orow = (size_t)b * a.H_q + g * G;
+  for (int h = 0; h < G; ++h) {
+    const float M = sh_M[h];
+    float O = 0.f;
+    int p = grp;
+    for (; p + 3 * ngrp < np; p += 4 * ngrp) {  // four independent piece loads in flight
+      const size_t r0 = prow(p) + h, r1 = prow(p + ngrp) + h, r2 = prow(p + 2 * ngrp) + h,
+                   r3 = prow(p + 3 * ngrp) + h;
+      const float o0 = a.ws_o[r0 * D + col], o1 = a.ws_o[r1 * D + col];
+      const float o2 = a.ws_o[r2 * D + col], o3 = a.ws_o[r3 * D + col];
+      O += exp2_fast(a.ws_ml[2 * r0] - M) * o0 + exp2_fast(a.ws_ml[2 * r1] - M) * o1 +
+           exp2_fast(a.ws_ml[2 * r2] - M) * o2 + exp2_fast(a.ws_ml[2 * r3] - M) * o3;
+    }
+    for (; p < np; p += ngrp) {
+      const size_t r = prow(p) + h;
+      O += exp2_fast(a.ws_ml[2 * r] - M) * a.ws_o[r * D + col];
+    }
+    sh_o[tid] = O;
+    __syncthreads();
+    if (grp == 0) {
+      float s = 0.f;
+      for (int q = 0; q < ngrp; ++q) s += sh_o[q * D + col];
+      a.out[(orow + h) * D + col] = s * sh_iL[h];
+    }
+    __syncthreads();
   }
 }
 
@@ -466,11 +616,12 @@ __global__ __launch_bounds__(64) void decode_vector_kernel(DecodeArgs a) {
   __shared__ int sh_off[64];
   const int lane = threadIdx.x;
   const int hq = blockIdx.x % a.H_q;
-  int b, split;
-  if (!find_item<64>(a.context_lens, a.B, a.len_cap, a.split_tokens, blockIdx.x / a.H_q, b, split)) return;
+  const int b = (blockIdx.x / a.H_q) % a.B;
+  const int split = blockIdx.x / (a.H_q * a.B);
   const int g = hq / a.G;
   const int n = uniform(seq_len(a.context_lens, b, a.len_cap));
   const int nsplit = n == 0 ? 1 : (n + a.split_tokens - 1) / a.split_tokens;
+  if (split >= nsplit) return;
   const size_t orow = ((size_t)b * a.H_q + hq) * D;
   if (n == 0) {
     for (int d = lane; d < D; d += 64) a.out[orow + d] = 0.f;
@@ -549,31 +700,70 @@ __global__ __launch_bounds__(64) void decode_vector_kernel(DecodeArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// split merge: o = sum_i 2^(m_i - M) o_i / sum_i 2^(m_i - M) l_i
+// split merge: one workgroup per (sequence, KV head) with more than one split
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(64) void split_reduce_kernel(DecodeArgs a) {
-  const int b = blockIdx.x / a.H_q, hq = blockIdx.x % a.H_q;
+__global__ __launch_bounds__(256) void split_merge_kernel(DecodeArgs a) {
+  constexpr int kHeads = 64;  // heads merged per pass
+  __shared__ float sh_M[kHeads], sh_iL[kHeads];
+  const int b = blockIdx.x / a.H_kv, g = blockIdx.x % a.H_kv;
   const int n = seq_len(a.context_lens, b, a.len_cap);
   const int nsplit = n == 0 ? 1 : (n + a.split_tokens - 1) / a.split_tokens;
   if (nsplit <= 1) return;
-  const size_t pr0 = ((size_t)b * a.H_q + hq) * a.max_splits;
-  const float* ml = a.ws_ml + 2 * pr0;
-  float M = -INFINITY;
-  for (int s = 0; s < nsplit; ++s) M = fmaxf(M, ml[2 * s]);
-  float L = 0.f;
-  for (int s = 0; s < nsplit; ++s) L += exp2_fast(ml[2 * s] - M) * ml[2 * s + 1];
-  const float inv = 1.f / L;
-  for (int d = threadIdx.x; d < a.D; d += 64) {
-    float O = 0.f;
-    for (int s = 0; s < nsplit; ++s) O += exp2_fast(ml[2 * s] - M) * a.ws_o[(pr0 + s) * a.D + d];
-    a.out[((size_t)b * a.H_q + hq) * a.D + d] = O * inv;
+  const int D = a.D, tid = threadIdx.x;
+  for (int h0 = 0; h0 < a.G; h0 += kHeads) {
+    const int nh = min(kHeads, a.G - h0);
+    const size_t row0 = (size_t)b * a.H_q + g * a.G + h0;
+    if (tid < nh) {
+      const float* ml = a.ws_ml + 2 * (row0 + tid) * a.max_splits;
+      float M = -INFINITY;
+      for (int i = 0; i < nsplit; ++i) M = fmaxf(M, ml[2 * i]);
+      float L = 0.f;
+      for (int i = 0; i < nsplit; ++i) L += exp2_fast(ml[2 * i] - M) * ml[2 * i + 1];
+      sh_M[tid] = M;
+      sh_iL[tid] = 1.f / L;
+    }
+    __syncthreads();
+    for (int e = tid; e < nh * D; e += 256) {
+      const int h = e / D, col = e % D;
+      const size_t pr0 = (row0 + h) * a.max_splits;
+      const float* ml = a.ws_ml + 2 * pr0;
+      const float* o = a.ws_o + pr0 * D + col;
+      const float M = sh_M[h];
+      float acc = 0.f;
+      int i = 0;
+      for (; i + 4 <= nsplit; i += 4) {  // four independent loads in flight
+        const float o0 = o[(size_t)i * D], o1 = o[(size_t)(i + 1) * D];
+        const float o2 = o[(size_t)(i + 2) * D], o3 = o[(size_t)(i + 3) * D];
+        acc += exp2_fast(ml[2 * i] - M) * o0 + exp2_fast(ml[2 * i + 2] - M) * o1 +
+               exp2_fast(ml[2 * i + 4] - M) * o2 + exp2_fast(ml[2 * i + 6] - M) * o3;
+      }
+      for (; i < nsplit; ++i) acc += exp2_fast(ml[2 * i] - M) * o[(size_t)i * D];
+      a.out[(row0 + h) * D + col] = acc * sh_iL[h];
+    }
+    __syncthreads();
   }
+}
+
+// workgroups of decode_streamk_kernel<D, BS, KVT> one CU holds at once
+template <int D, int BS, int KVT>
+int streamk_groups_per_cu() {
+  static const int per_cu = [] {
+    int nb = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, decode_streamk_kernel<D, BS, KVT>, 256, 0) != hipSuccess ||
+        nb <= 0)
+      nb = 2;
+    return nb > kStreamKMaxGroupsPerCU ? kStreamKMaxGroupsPerCU : nb;
+  }();
+  return per_cu;
 }
 
 template <int D, int BS, int KVT>
 hipError_t launch_mfma_t(const DecodeArgs& a, hipStream_t s) {
-  const long long grid = (long long)a.B * a.max_splits * a.H_kv;
-  hipLaunchKernelGGL((decode_mfma_kernel<D, BS, KVT>), dim3((unsigned)grid), dim3(256), 0, s, a);
+  const int groups = streamk_groups_per_cu<D, BS, KVT>() * a.num_cus;
+  hipLaunchKernelGGL((decode_streamk_kernel<D, BS, KVT>), dim3((unsigned)groups), dim3(256), 0, s, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(streamk_merge_kernel, dim3((unsigned)(a.B * a.H_kv)), dim3(256), 0, s, a, groups);
   return hipGetLastError();
 }
 
@@ -588,6 +778,11 @@ hipError_t launch_mfma_bs(const DecodeArgs& a, hipStream_t s) {
 }
 
 }  // namespace
+
+hipError_t launch_split_merge(const DecodeArgs& a, hipStream_t s) {
+  hipLaunchKernelGGL(split_merge_kernel, dim3((unsigned)(a.B * a.H_kv)), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
 
 bool decode_fast_path_supported(int q_dtype, int kv_dtype, int G, int D, int bs) {
   return q_dtype == PKV_BF16 && (kv_dtype == PKV_BF16 || kv_dtype == PKV_FP8_E4M3) && G >= 1 && G <= 16 &&
@@ -606,18 +801,13 @@ hipError_t launch_decode_mfma(const DecodeArgs& a, hipStream_t s) {
 }
 
 hipError_t launch_decode_vector(const DecodeArgs& a, hipStream_t s) {
-  const long long grid = (long long)a.B * a.max_splits * a.H_q;
+  const long long grid = (long long)a.max_splits * a.B * a.H_q;
   switch (a.D) {
     case 64: hipLaunchKernelGGL(decode_vector_kernel<64>, dim3((unsigned)grid), dim3(64), 0, s, a); break;
     case 128: hipLaunchKernelGGL(decode_vector_kernel<128>, dim3((unsigned)grid), dim3(64), 0, s, a); break;
     case 256: hipLaunchKernelGGL(decode_vector_kernel<256>, dim3((unsigned)grid), dim3(64), 0, s, a); break;
     default: return hipErrorInvalidValue;
   }
-  return hipGetLastError();
-}
-
-hipError_t launch_split_reduce(const DecodeArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL(split_reduce_kernel, dim3((unsigned)(a.B * a.H_q)), dim3(64), 0, s, a);
   return hipGetLastError();
 }
 

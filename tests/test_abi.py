@@ -70,7 +70,7 @@ def _decode(**kw):
     (dict(out=None), pkv.ERR_INVALID_ARG),
     (dict(tab=None), pkv.ERR_INVALID_ARG),
     (dict(kv=pkv.FP8_E4M3), pkv.ERR_INVALID_ARG),  # scales missing
-    (dict(mcl=100000), pkv.ERR_INVALID_ARG),  # needs a workspace, none given
+    (dict(), pkv.ERR_INVALID_ARG),  # needs a workspace, none given
     (dict(mcl=100000, ws=ctypes.c_void_p(0x1008), wsb=1 << 40), pkv.ERR_INVALID_ARG),  # misaligned
 ])
 def test_decode_rejects_bad_arguments_before_launch(kw, status):
@@ -82,10 +82,11 @@ def test_decode_empty_batch_is_a_no_op():
     assert _decode(B=0) == pkv.OK
 
 
-def test_workspace_size_follows_the_split_plan():
-    assert pkv.decode_workspace_bytes(4, 64, 8, 128, 200, 16) == 0  # one split
-    n = pkv.decode_workspace_bytes(4, 64, 8, 128, 131072, 32)
-    assert n > 0 and n % 4 == 0
+def test_workspace_size_covers_both_paths():
+    small = pkv.decode_workspace_bytes(4, 64, 8, 128, 200, 16)
+    assert small > 0 and small % 4 == 0  # the matrix-core path always keeps its partial slots
+    big = pkv.decode_workspace_bytes(4096, 64, 8, 128, 131072, 32)  # vector-path splits dominate
+    assert big > small
     assert pkv.decode_workspace_bytes(-1, 64, 8, 128, 10, 16) == 0 and pkv.last_error()
 
 

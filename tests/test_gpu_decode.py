@@ -188,3 +188,61 @@ def test_every_e4m3_code_decodes_exactly():
     got = out.cpu().numpy().reshape(-1)
     want = oracle.e4m3_decode(codes).astype(np.float32)
     assert (got == want).all()
+
+
+def test_workspace_reused_across_calls_and_shapes():
+    """One workspace serves consecutive calls of different batch shapes; stale partials left
+    by an earlier, larger call never leak into a later one."""
+    import paged_kv_cache_223_amd as pkv
+    big = workloads.long128k_bf16(B=3, ctx=5000)
+    small = workloads.llama8b_bf16(B=5, lo=600, hi=2500)
+    ws = torch.full((64 << 20,), 0x7F, dtype=torch.uint8, device=DEV)  # garbage (NaN-ish) contents
+    runs = []
+    for case in (big, small, big, small):
+        mat = materialize_with_model(case)
+        kp, vp = oracle_pools(case, mat)
+        dev = device_inputs(case, mat, kp, vp)
+        assert pkv.decode_workspace_bytes(case.B, case.spec.H_q, case.spec.H_kv, case.spec.d,
+                                          case.max_context_len, case.bs) > 0
+        out = pkv.paged_attn_decode(dev["q"], dev["k_pool"], dev["v_pool"], dev["block_tables"],
+                                    dev["context_lens"], float(case.scale), case.max_context_len, workspace=ws)
+        torch.cuda.synchronize()
+        got = out.cpu().numpy().astype(np.float64)
+        assert row_rel_err(got, oracle_decode(case, mat, kp, vp)) <= tol(case)
+        runs.append(got)
+    assert (runs[0] == runs[2]).all() and (runs[1] == runs[3]).all()
+
+
+def test_captured_step_replays_match_eager():
+    """A decode step (kv_append + decode + split merge) captured in a HIP graph and replayed,
+    with eager work and synchronisations between replays: every replay equals the eager step."""
+    import paged_kv_cache_223_amd as pkv
+    case = workloads.llama70b_bf16(B=4, ctx=2600, prefix=512)
+    mat = materialize_with_model(case)
+    kp, vp = oracle_pools(case, mat, include_step=False)
+    dev = device_inputs(case, mat, kp, vp)
+    step_k = to_dev(mat.step_k, "bf16")
+    step_v = to_dev(mat.step_v, "bf16")
+    slots = torch.from_numpy(mat.step_slots).to(DEV)
+    ws = pkv.decode_workspace(case.B, 64, 8, 128, case.max_context_len, case.bs)
+    out = torch.empty((case.B, 64, 128), dtype=torch.float32, device=DEV)
+
+    def step():
+        pkv.kv_append(step_k, step_v, slots, dev["k_pool"], dev["v_pool"])
+        pkv.paged_attn_decode(dev["q"], dev["k_pool"], dev["v_pool"], dev["block_tables"], dev["context_lens"],
+                              float(case.scale), case.max_context_len, out=out, workspace=ws)
+
+    step()
+    torch.cuda.synchronize()
+    eager = out.clone()
+    ref = oracle_decode(case, mat, *oracle_pools(case, mat))
+    assert row_rel_err(eager.cpu().numpy(), ref) <= 2e-3
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    for i in range(4):
+        out.fill_(float("nan"))  # eager work between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, eager), f"replay {i} differs from the eager step"
