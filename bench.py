@@ -221,7 +221,7 @@ def main():
     dec_gbps = by["decode"] / dec_avg_s / 1e9
     step_gbps = (by["decode"] + by["append"]) / (step_ms / 1e3) / 1e9
 
-    # practical read ceiling: the library's 16-byte streaming read over 4 GiB
+    # practical read ceiling: the library's non-temporal 16-byte streaming read over 4 GiB
     buf = torch.empty(4 << 30, dtype=torch.uint8, device=dev)
     sink = pkv.stream_read(buf)
     torch.cuda.synchronize()
@@ -268,7 +268,7 @@ def main():
     }
     traffic = measured_traffic(args.workload)
     res["roofline"] = {
-        "bound": "hbm", "kernel": "paged_attn_decode (context-split partition + split merge)",
+        "bound": "hbm", "kernel": "paged_attn_decode call = decode_streamk_kernel + streamk_merge_kernel",
         "achieved": round(dec_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
         "frac": round(dec_gbps / HBM_PEAK_GBPS, 4),
         "algorithmic_bytes_per_launch": by["decode"],

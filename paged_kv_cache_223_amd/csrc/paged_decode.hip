@@ -493,9 +493,8 @@ __global__ __launch_bounds__(256, 2) void decode_streamk_kernel(DecodeArgs a) {
 // piece loads are independent of each other.
 __global__ __launch_bounds__(256) void streamk_merge_kernel(DecodeArgs a, int nwg) {
   __shared__ int sh_part[2][4];
-  __shared__ float sh_red[4][16][2];
+  __shared__ float sh_red[16][16][2];
   __shared__ float sh_M[16], sh_iL[16];
-  __shared__ float sh_o[256];
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int b = blockIdx.x / a.H_kv, g = blockIdx.x % a.H_kv;
   const int cap = a.len_cap, B = a.B, G = a.G, D = a.D;
@@ -528,66 +527,53 @@ __global__ __launch_bounds__(256) void streamk_merge_kernel(DecodeArgs a, int nw
     const int slot = (p == 0 && w * upw < s_begin) ? 1 : 0;
     return ((size_t)w * 2 + slot) * 16;
   };
-  // ---- per head: M = max m_p, L = sum 2^(m_p - M) l_p, threads strided over pieces
-  for (int h = 0; h < G; ++h) {
+  // ---- per head h: M = max_p m_p, L = sum_p 2^(m_p - M) l_p.  Thread t takes head t % 16
+  // and pieces t / 16, t / 16 + 16, ...; the 16 partial results of a head meet in LDS.
+  {
+    const int h = tid & 15, p0 = tid >> 4;
     float m = -INFINITY, l = 0.f;
-    for (int p = tid; p < np; p += 256) {
-      const float mp = a.ws_ml[2 * (prow(p) + h)], lp = a.ws_ml[2 * (prow(p) + h) + 1];
-      const float mn = fmaxf(m, mp);
-      l = l * exp2_fast(m - mn) + lp * exp2_fast(mp - mn);
-      m = mn;
+    if (h < G) {
+      for (int p = p0; p < np; p += 16) {
+        const size_t r = prow(p) + h;
+        const float mp = a.ws_ml[2 * r], lp = a.ws_ml[2 * r + 1];
+        const float mn = fmaxf(m, mp);
+        l = (m == -INFINITY ? 0.f : l * exp2_fast(m - mn)) + lp * exp2_fast(mp - mn);
+        m = mn;
+      }
     }
-#pragma unroll
-    for (int o = 32; o; o >>= 1) {
-      const float m2 = __shfl_xor(m, o, 64), l2 = __shfl_xor(l, o, 64);
-      const float mn = fmaxf(m, m2);
-      l = (m == -INFINITY ? 0.f : l * exp2_fast(m - mn)) + (m2 == -INFINITY ? 0.f : l2 * exp2_fast(m2 - mn));
-      m = mn;
-    }
-    if (lane == 0 && h < 16) {
-      sh_red[wv][h][0] = m;
-      sh_red[wv][h][1] = l;
-    }
+    sh_red[p0][h][0] = m;
+    sh_red[p0][h][1] = l;
   }
   __syncthreads();
   if (tid < G) {
-    float M = sh_red[0][tid][0];
-    for (int i = 1; i < 4; ++i) M = fmaxf(M, sh_red[i][tid][0]);
+    float M = -INFINITY;
+    for (int i = 0; i < 16; ++i) M = fmaxf(M, sh_red[i][tid][0]);
     float L = 0.f;
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < 16; ++i)
       if (sh_red[i][tid][0] != -INFINITY) L += sh_red[i][tid][1] * exp2_fast(sh_red[i][tid][0] - M);
     sh_M[tid] = M;
     sh_iL[tid] = 1.f / L;
   }
   __syncthreads();
-  // ---- outputs: thread = (column, piece group); sum pieces of its group, then across groups
-  const int ngrp = 256 / D;  // D divides 256 here (64 or 128)
-  const int col = tid % D, grp = tid / D;
+  // ---- outputs: each thread owns (head, column) elements and sums their pieces
   const size_t orow = (size_t)b * a.H_q + g * G;
-  for (int h = 0; h < G; ++h) {
+  for (int e = tid; e < G * D; e += 256) {
+    const int h = e / D, col = e % D;
     const float M = sh_M[h];
     float O = 0.f;
-    int p = grp;
-    for (; p + 3 * ngrp < np; p += 4 * ngrp) {  // four independent piece loads in flight
-      const size_t r0 = prow(p) + h, r1 = prow(p + ngrp) + h, r2 = prow(p + 2 * ngrp) + h,
-                   r3 = prow(p + 3 * ngrp) + h;
+    int p = 0;
+    for (; p + 4 <= np; p += 4) {  // four independent piece loads in flight
+      const size_t r0 = prow(p) + h, r1 = prow(p + 1) + h, r2 = prow(p + 2) + h, r3 = prow(p + 3) + h;
       const float o0 = a.ws_o[r0 * D + col], o1 = a.ws_o[r1 * D + col];
       const float o2 = a.ws_o[r2 * D + col], o3 = a.ws_o[r3 * D + col];
       O += exp2_fast(a.ws_ml[2 * r0] - M) * o0 + exp2_fast(a.ws_ml[2 * r1] - M) * o1 +
            exp2_fast(a.ws_ml[2 * r2] - M) * o2 + exp2_fast(a.ws_ml[2 * r3] - M) * o3;
     }
-    for (; p < np; p += ngrp) {
+    for (; p < np; ++p) {
       const size_t r = prow(p) + h;
       O += exp2_fast(a.ws_ml[2 * r] - M) * a.ws_o[r * D + col];
     }
-    sh_o[tid] = O;
-    __syncthreads();
-    if (grp == 0) {
-      float s = 0.f;
-      for (int q = 0; q < ngrp; ++q) s += sh_o[q * D + col];
-      a.out[(orow + h) * D + col] = s * sh_iL[h];
-    }
-    __syncthreads();
+    a.out[(orow + h) * D + col] = O * sh_iL[h];
   }
 }
 

@@ -12,22 +12,27 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kUnroll = 8;
 
+// Each workgroup reads whole tiles of kThreads x kUnroll x 16 bytes with
+// non-temporal loads (the decode kernels' K/V loads are non-temporal too);
+// the tail that does not fill a tile is read by workgroup 0.
 __global__ __launch_bounds__(kThreads) void stream_read_kernel(const uint4* __restrict__ src, size_t n16,
                                                                float* __restrict__ sink) {
-  const size_t stride = (size_t)gridDim.x * kThreads;
-  size_t i = (size_t)blockIdx.x * kThreads + threadIdx.x;
+  typedef uint32_t v4u __attribute__((ext_vector_type(4)));
+  const v4u* s = (const v4u*)src;
+  constexpr size_t tile = (size_t)kThreads * kUnroll;
   uint32_t acc = 0;
-  for (; i + (kUnroll - 1) * stride < n16; i += kUnroll * stride) {
-    uint4 v[kUnroll];
+  for (size_t t = blockIdx.x; (t + 1) * tile <= n16; t += gridDim.x) {
+    v4u v[kUnroll];
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) v[u] = src[i + u * stride];
+    for (int u = 0; u < kUnroll; ++u) v[u] = __builtin_nontemporal_load(s + t * tile + u * kThreads + threadIdx.x);
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
   }
-  for (; i < n16; i += stride) {
-    const uint4 v = src[i];
-    acc ^= v.x ^ v.y ^ v.z ^ v.w;
-  }
+  if (blockIdx.x == 0)
+    for (size_t i = n16 / tile * tile + threadIdx.x; i < n16; i += kThreads) {
+      const v4u v = s[i];
+      acc ^= v.x ^ v.y ^ v.z ^ v.w;
+    }
   for (int o = 32; o; o >>= 1) acc ^= __shfl_xor(acc, o, 64);
   __shared__ uint32_t sh[kThreads / 64];
   if ((threadIdx.x & 63) == 0) sh[threadIdx.x >> 6] = acc;
@@ -49,8 +54,8 @@ __global__ __launch_bounds__(kThreads) void copy_kernel(uint4* __restrict__ dst,
 
 size_t stream_read_blocks(size_t bytes) {
   const size_t n16 = bytes / 16;
-  size_t blocks = (n16 + kThreads * kUnroll - 1) / (kThreads * kUnroll);
-  if (blocks > 256 * 16) blocks = 256 * 16;
+  size_t blocks = n16 / ((size_t)kThreads * kUnroll);
+  if (blocks > 256 * 8) blocks = 256 * 8;
   return blocks ? blocks : 1;
 }
 
