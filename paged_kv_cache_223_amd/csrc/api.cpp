@@ -96,7 +96,7 @@ size_t pkv_decode_workspace_bytes(int32_t B, int32_t H_q, int32_t H_kv, int32_t 
     set_error("decode_workspace_bytes: bad sizes");
     return 0;
   }
-  return workspace_bytes_for(B, H_q, D, plan_splits(B, H_kv, max_context_len), current_num_cus());
+  return workspace_bytes_for(B, H_q, H_kv, D, plan_splits(B, H_kv, max_context_len), current_num_cus());
 }
 
 int pkv_paged_attn_decode(float* out, const void* q, int q_dtype, const void* k_pool, const void* v_pool,
@@ -137,7 +137,7 @@ int pkv_paged_attn_decode(float* out, const void* q, int q_dtype, const void* k_
   }
   const SplitPlan plan = plan_splits(B, H_kv, max_context_len);
   const int num_cus = current_num_cus();
-  const size_t need = workspace_bytes_for(B, H_q, D, plan, num_cus);
+  const size_t need = workspace_bytes_for(B, H_q, H_kv, D, plan, num_cus);
   if (need > 0 && (!workspace || workspace_bytes < need || ((uintptr_t)workspace & 255u))) {
     set_error("decode: workspace needs %zu bytes, 256-byte aligned (got %zu at %p)", need, workspace_bytes,
               workspace);
@@ -145,7 +145,8 @@ int pkv_paged_attn_decode(float* out, const void* q, int q_dtype, const void* k_
   }
   const int G = H_q / H_kv;
   const bool fast = decode_fast_path_supported(q_dtype, kv_dtype, G, D, bs);
-  const long long items = (long long)B * plan.max_splits * (fast ? H_kv : H_q);
+  const long long items = fast ? (long long)num_cus * kMaxGroupsPerCU + (long long)B * H_kv
+                               : (long long)B * plan.max_splits * H_q;
   if (items > 0x7FFFFFFFLL) {
     set_error("decode: launch too large (%lld work items)", items);
     return PKV_ERR_INVALID_ARG;
@@ -160,7 +161,7 @@ int pkv_paged_attn_decode(float* out, const void* q, int q_dtype, const void* k_
   a.k_scale = k_scale;
   a.v_scale = v_scale;
   if (need > 0) {
-    const WorkspaceLayout wl = workspace_layout(B, H_q, D, plan, num_cus);
+    const WorkspaceLayout wl = workspace_layout(B, H_q, H_kv, D, plan, num_cus);
     a.ws_o = (float*)((char*)workspace + wl.o);
     a.ws_ml = (float*)((char*)workspace + wl.ml);
   }

@@ -41,13 +41,14 @@ inline SplitPlan plan_splits(int B, int H_kv, int max_ctx) {
   return p;
 }
 
-// The matrix-core path launches one round of 4-wave workgroups: at most this
-// many per CU; each owns two partial slots of 16 heads.
-constexpr int kStreamKMaxGroupsPerCU = 4;
+// The matrix-core path plans one round of 4-wave workgroups (at most this many
+// per CU) and launches up to that many plus B * H_kv pieces, each owning one
+// partial slot of 16 heads.
+constexpr int kMaxGroupsPerCU = 4;
 
 // Workspace layout, large enough for either path:
 //   [partial outputs fp32: max(vector path B*H_q*max_splits*D,
-//                              matrix path CUs*4 groups*2 slots*16 heads*D)][pad to 256]
+//                              matrix path (CUs*4 + B*H_kv) pieces*16 heads*D)][pad to 256]
 //   [partial (max, sum) fp32: the same count of rows * 2]
 struct WorkspaceLayout {
   size_t o, ml, total;
@@ -55,9 +56,9 @@ struct WorkspaceLayout {
 
 inline size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 
-inline WorkspaceLayout workspace_layout(int B, int H_q, int D, const SplitPlan& p, int num_cus) {
+inline WorkspaceLayout workspace_layout(int B, int H_q, int H_kv, int D, const SplitPlan& p, int num_cus) {
   const size_t vec_rows = p.max_splits > 1 ? (size_t)B * H_q * p.max_splits : 0;
-  const size_t mfma_rows = (size_t)num_cus * kStreamKMaxGroupsPerCU * 2 * 16;
+  const size_t mfma_rows = ((size_t)num_cus * kMaxGroupsPerCU + (size_t)B * H_kv) * 16;
   const size_t rows = vec_rows > mfma_rows ? vec_rows : mfma_rows;
   WorkspaceLayout w;
   w.o = 0;
@@ -66,8 +67,8 @@ inline WorkspaceLayout workspace_layout(int B, int H_q, int D, const SplitPlan& 
   return w;
 }
 
-inline size_t workspace_bytes_for(int B, int H_q, int D, const SplitPlan& p, int num_cus) {
-  return workspace_layout(B, H_q, D, p, num_cus).total;
+inline size_t workspace_bytes_for(int B, int H_q, int H_kv, int D, const SplitPlan& p, int num_cus) {
+  return workspace_layout(B, H_q, H_kv, D, p, num_cus).total;
 }
 
 struct DecodeArgs {

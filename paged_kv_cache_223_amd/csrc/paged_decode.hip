@@ -294,21 +294,24 @@ __device__ __forceinline__ void process_chunk(const Chunk<D, BS, KVT>& ch, const
 }
 
 // ---------------------------------------------------------------------------
-// matrix-core path, stream-K decomposition
+// matrix-core path: one piece per workgroup, pieces planned from the lengths
 //
-// The batch's work is a row of units (sequence b, KV head g, 32-token chunk),
-// ordered b-major, then g, then chunk; sequence b contributes H_kv segments of
-// c_b = ceil(n_b / 32) units.  The grid is one round of 4-wave workgroups (as
-// many as the GPU holds at once) and workgroup i takes the contiguous units
-// [i*upw, (i+1)*upw), upw = ceil(total / workgroups), so every workgroup
-// streams the same number of KV bytes whatever the mix of lengths, and there
-// is no second round.  A workgroup walks its range segment by segment (its 4
-// waves take a piece's chunks round-robin and merge through LDS): a segment
-// it covers whole gets its final rows written directly; the at most two
-// segments cut by its range ends get partial results in its two workspace
-// slots, merged afterwards by streamk_merge.
+// The batch's work is c_b = ceil(n_b / 32) chunks per (sequence b, KV head g)
+// segment.  Every workgroup derives the same plan from the lengths: with
+// total = H_kv * sum_b c_b units and T target pieces (the workgroups the GPU
+// holds at once), upw = ceil(total / T), and each segment of sequence b is cut
+// into np_b = ceil(c_b / upw) balanced pieces.  Workgroup i takes piece i,
+// counting sequence-major, then KV head, then piece.  A uniform batch thus
+// runs as exactly one round of equal pieces (no second-round bubble); a batch
+// of mixed lengths gets many segment-aligned pieces, at most upw chunks each,
+// which the hardware dispatcher balances.  Each workgroup runs a single piece,
+// which keeps register use (and so occupancy) at its single-piece minimum.
+// The 4 waves take the piece's chunks round-robin and merge through LDS; a
+// piece that is a whole segment writes its final rows, the others write
+// partials that piece_merge combines.
 // ---------------------------------------------------------------------------
 constexpr int kMinUnits = 8;
+constexpr int kLensInRegs = 16;  // lengths a lane keeps in registers (B <= 1024 in one pass)
 
 __device__ __forceinline__ int chunks_of(int n, int cap) {
   n = n < 0 ? 0 : (n > cap ? cap : n);
@@ -328,6 +331,62 @@ __device__ __forceinline__ int wave_incl_scan(int x, int lane) {
     if (lane >= o) x += y;
   }
   return x;
+}
+
+struct PiecePlan {
+  int b, g, n, lo, hi, np;  // piece [lo, hi) of segment (b, g); np pieces in the segment
+};
+
+// Plan step shared by the decode and merge kernels (one wave computes it).
+// Returns upw and, for `item` >= 0, the piece it names (b = -1 if none).
+__device__ int plan_piece(const DecodeArgs& a, int target, int item, int lane, PiecePlan& pp) {
+  const int B = a.B, H_kv = a.H_kv, cap = a.len_cap;
+  int c[kLensInRegs];
+  int part = 0;
+#pragma unroll
+  for (int k = 0; k < kLensInRegs; ++k) {
+    const int b0 = lane + 64 * k;
+    c[k] = b0 < B ? chunks_of(a.context_lens[b0], cap) : 0;
+    part += c[k];
+  }
+  for (int b0 = lane + 64 * kLensInRegs; b0 < B; b0 += 64) part += chunks_of(a.context_lens[b0], cap);
+  const int total = uniform(wave_sum(part)) * H_kv;
+  int upw = (total + target - 1) / target;
+  upw = upw < kMinUnits ? kMinUnits : upw;
+  pp.b = -1;
+  if (item < 0) return upw;
+  // locate: prefix over sequences of H_kv * np_b pieces
+  int base = 0;
+  for (int k = 0; k * 64 < B && pp.b < 0; ++k) {
+    const int b0 = lane + 64 * k;
+    int cb = 0;
+    if (k < kLensInRegs) {
+#pragma unroll
+      for (int kk = 0; kk < kLensInRegs; ++kk) cb = kk == k ? c[kk] : cb;
+    } else {
+      cb = b0 < B ? chunks_of(a.context_lens[b0], cap) : 0;
+    }
+    const int npb = (cb + upw - 1) / upw;
+    const int cnt = npb * H_kv;
+    const int incl = wave_incl_scan(cnt, lane);
+    const bool hit = cnt > 0 && base + incl - cnt <= item && item < base + incl;
+    const unsigned long long m = __ballot(hit);
+    if (m) {
+      const int src = __ffsll((long long)m) - 1;
+      const int b = 64 * k + src;
+      const int r = item - __shfl(base + incl - cnt, src, 64);
+      const int np = __shfl(npb, src, 64), cbb = __shfl(cb, src, 64);
+      const int j = r % np;
+      pp.b = b;
+      pp.g = r / np;
+      pp.np = np;
+      pp.lo = (int)((long long)j * cbb / np);
+      pp.hi = (int)((long long)(j + 1) * cbb / np);
+    }
+    base += __shfl(incl, 63, 64);
+  }
+  pp.b = uniform(pp.b);
+  return upw;
 }
 
 // The wave's share of one piece: chunks c_first + w, + 4, ... below c_end of
@@ -381,152 +440,96 @@ __device__ __forceinline__ void run_piece(const DecodeArgs& a, int b, int g, int
 }
 
 template <int D, int BS, int KVT>
-__global__ __launch_bounds__(256, 2) void decode_streamk_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(256, 2) void decode_piece_kernel(DecodeArgs a, int target) {
   constexpr int NW = 4;
   __shared__ float sh_acc[NW][16][D];
   __shared__ float sh_m[NW][16];
   __shared__ float sh_l[NW][16];
   const int tid = threadIdx.x, lane = tid & 63, w = uniform(tid >> 6);
-  const int wg = blockIdx.x, nwg = gridDim.x;
-  const int B = a.B, H_kv = a.H_kv, G = a.G, cap = a.len_cap;
-  // sequences with no tokens: zero rows, written by workgroup b % nwg
-  for (int b0 = wg; b0 < B; b0 += nwg) {
-    if (uniform(seq_len(a.context_lens, b0, cap)) == 0)
-      for (int e = tid; e < a.H_q * D; e += 256) a.out[(size_t)b0 * a.H_q * D + e] = 0.f;
-  }
-  // total units and this workgroup's range (every wave computes the same values)
-  int part = 0;
-  for (int b0 = lane; b0 < B; b0 += 64) part += chunks_of(a.context_lens[b0], cap);
-  const int total = uniform(wave_sum(part)) * H_kv;
-  int upw = (total + nwg - 1) / nwg;
-  upw = upw < kMinUnits ? kMinUnits : upw;
-  const int u_begin = wg * upw;
-  if (u_begin >= total) return;
-  const int u_end = min(total, u_begin + upw);
-  // the sequence holding unit u_begin, and P = chunks of the sequences before it
-  int b = -1, P = 0;
-  {
-    int base = 0;
-    for (int b0 = 0; b0 < B && b < 0; b0 += 64) {
-      const int cb = b0 + lane < B ? chunks_of(a.context_lens[b0 + lane], cap) : 0;
-      const int incl = wave_incl_scan(cb, lane);
-      const bool hit = cb > 0 && (base + incl - cb) * H_kv <= u_begin && u_begin < (base + incl) * H_kv;
-      const unsigned long long m = __ballot(hit);
-      if (m) {
-        const int src = __ffsll((long long)m) - 1;
-        b = b0 + src;
-        P = __shfl(base + incl - cb, src, 64);
-      }
-      base += __shfl(incl, 63, 64);
-    }
-  }
-  b = uniform(b);
-  P = uniform(P);
-  const int kg = lane >> 4;
+  const int item = blockIdx.x;
+  const int G = a.G, cap = a.len_cap;
+  // a sequence with no tokens: zero rows, written by workgroup b
+  if (item < a.B && uniform(seq_len(a.context_lens, item, cap)) == 0)
+    for (int e = tid; e < a.H_q * D; e += 256) a.out[(size_t)item * a.H_q * D + e] = 0.f;
+  PiecePlan pp;
+  plan_piece(a, target, item, lane, pp);
+  if (pp.b < 0) return;
+  const int b = pp.b, g = uniform(pp.g), np = uniform(pp.np);
+  const int lo = uniform(pp.lo), hi = uniform(pp.hi);
+  const int n = uniform(seq_len(a.context_lens, b, cap));
   f32x4 acc[D / 16];
   WaveState st;
-  int u = u_begin;
-  int slot = 0;
-  while (u < u_end) {
-    const int n = uniform(seq_len(a.context_lens, b, cap));
-    const int cb = (n + 31) / 32;
-    const int seg0 = P * H_kv;  // first unit of sequence b
-    const int g = (u - seg0) / cb;
-    const int s_begin = seg0 + g * cb;
-    const int c_first = u - s_begin;
-    const int c_end = min(u_end, s_begin + cb) - s_begin;
-    run_piece<D, BS, KVT>(a, b, g, n, c_first + w, c_end, acc, st, lane);
-    // ---- merge the four waves' shares through LDS
-    float lt = st.l;
-    lt += __shfl_xor(lt, 16, 64);
-    lt += __shfl_xor(lt, 32, 64);
-    if (lane < 16) {
-      sh_m[w][lane] = st.m;
-      sh_l[w][lane] = lt;
+  run_piece<D, BS, KVT>(a, b, g, n, lo + w, hi, acc, st, lane);
+  // ---- merge the four waves' shares through LDS
+  const int kg = lane >> 4;
+  float lt = st.l;
+  lt += __shfl_xor(lt, 16, 64);
+  lt += __shfl_xor(lt, 32, 64);
+  if (lane < 16) {
+    sh_m[w][lane] = st.m;
+    sh_l[w][lane] = lt;
+  }
+#pragma unroll
+  for (int t = 0; t < D / 16; ++t)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) sh_acc[w][4 * kg + i][16 * t + (lane & 15)] = acc[t][i];
+  __syncthreads();
+  const float vs = KVT == PKV_FP8_E4M3 ? a.v_scale[g] : 1.f;
+  const size_t orow = ((size_t)b * a.H_q + g * G) * D;
+  const size_t prow = (size_t)item * 16;
+  for (int e = tid; e < G * D; e += 256) {
+    const int hh = e / D, col = e % D;
+    float M = sh_m[0][hh];
+#pragma unroll
+    for (int i = 1; i < NW; ++i) M = fmaxf(M, sh_m[i][hh]);
+    float L = 0.f, O = 0.f;
+#pragma unroll
+    for (int i = 0; i < NW; ++i) {
+      const float wt = exp2_fast(sh_m[i][hh] - M);
+      L += wt * sh_l[i][hh];
+      O += wt * sh_acc[i][hh][col];
     }
-#pragma unroll
-    for (int t = 0; t < D / 16; ++t)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) sh_acc[w][4 * kg + i][16 * t + (lane & 15)] = acc[t][i];
-    __syncthreads();
-    const float vs = KVT == PKV_FP8_E4M3 ? a.v_scale[g] : 1.f;
-    const bool whole = c_first == 0 && c_end == cb;
-    const size_t orow = ((size_t)b * a.H_q + g * G) * D;
-    const size_t prow = ((size_t)wg * 2 + slot) * 16;
-    for (int e = tid; e < G * D; e += 256) {
-      const int hh = e / D, col = e % D;
-      float M = sh_m[0][hh];
-#pragma unroll
-      for (int i = 1; i < NW; ++i) M = fmaxf(M, sh_m[i][hh]);
-      float L = 0.f, O = 0.f;
-#pragma unroll
-      for (int i = 0; i < NW; ++i) {
-        const float wt = exp2_fast(sh_m[i][hh] - M);
-        L += wt * sh_l[i][hh];
-        O += wt * sh_acc[i][hh][col];
+    O *= vs;
+    if (np == 1) {
+      a.out[orow + e] = O / L;
+    } else {
+      a.ws_o[(prow + hh) * D + col] = O;
+      if (col == 0) {
+        a.ws_ml[2 * (prow + hh)] = M;
+        a.ws_ml[2 * (prow + hh) + 1] = L;
       }
-      O *= vs;
-      if (whole) {
-        a.out[orow + e] = O / L;
-      } else {
-        a.ws_o[(prow + hh) * D + col] = O;
-        if (col == 0) {
-          a.ws_ml[2 * (prow + hh)] = M;
-          a.ws_ml[2 * (prow + hh) + 1] = L;
-        }
-      }
-    }
-    __syncthreads();  // LDS is reused by the next piece
-    slot = 1;
-    u = s_begin + c_end;
-    if (u >= seg0 + H_kv * cb) {  // next non-empty sequence
-      P += cb;
-      do {
-        ++b;
-      } while (b < B && uniform(chunks_of(a.context_lens[b], cap)) == 0);
     }
   }
 }
 
-// Merge the pieces of the segments that workgroup ranges cut; one workgroup per
-// (sequence, KV head).  Recomputes the unit layout of the kernel above.  All
-// piece loads are independent of each other.
-__global__ __launch_bounds__(256) void streamk_merge_kernel(DecodeArgs a, int nwg) {
-  __shared__ int sh_part[2][4];
+// Merge the pieces of every segment cut into several; one workgroup per
+// (sequence, KV head).  Wave 0 recomputes the plan; all piece loads are
+// independent of each other.
+__global__ __launch_bounds__(256) void piece_merge_kernel(DecodeArgs a, int target) {
+  __shared__ int sh_info[2];
   __shared__ float sh_red[16][16][2];
   __shared__ float sh_M[16], sh_iL[16];
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
   const int b = blockIdx.x / a.H_kv, g = blockIdx.x % a.H_kv;
-  const int cap = a.len_cap, B = a.B, G = a.G, D = a.D;
+  const int cap = a.len_cap, G = a.G, D = a.D, H_kv = a.H_kv;
   const int cb = chunks_of(a.context_lens[b], cap);
   if (cb == 0) return;
-  int tot = 0, before = 0;
-  for (int b0 = tid; b0 < B; b0 += 256) {
-    const int c = chunks_of(a.context_lens[b0], cap);
-    tot += c;
-    before += b0 < b ? c : 0;
-  }
-  tot = wave_sum(tot);
-  before = wave_sum(before);
-  if (lane == 0) {
-    sh_part[0][wv] = tot;
-    sh_part[1][wv] = before;
+  if (tid < 64) {
+    PiecePlan pp;
+    const int upw = plan_piece(a, target, -1, lane, pp);
+    const int np = (cb + upw - 1) / upw;
+    // first piece id of sequence b: sum over b' < b of H_kv * np_b'
+    int before = 0;
+    for (int b0 = lane; b0 < b; b0 += 64) before += H_kv * ((chunks_of(a.context_lens[b0], cap) + upw - 1) / upw);
+    before = wave_sum(before);
+    if (lane == 0) {
+      sh_info[0] = np;
+      sh_info[1] = before + g * np;
+    }
   }
   __syncthreads();
-  const int total = (sh_part[0][0] + sh_part[0][1] + sh_part[0][2] + sh_part[0][3]) * a.H_kv;
-  const int P = sh_part[1][0] + sh_part[1][1] + sh_part[1][2] + sh_part[1][3];
-  int upw = (total + nwg - 1) / nwg;
-  upw = upw < kMinUnits ? kMinUnits : upw;
-  const int s_begin = P * a.H_kv + g * cb, s_end = s_begin + cb;
-  const int w0 = s_begin / upw, w1 = (s_end - 1) / upw;
-  if (w0 == w1) return;  // one workgroup covered the segment and wrote it
-  const int np = w1 - w0 + 1;
-  // piece p belongs to workgroup w0 + p: slot 1 if that workgroup began in an earlier segment
-  auto prow = [&](int p) -> size_t {
-    const int w = w0 + p;
-    const int slot = (p == 0 && w * upw < s_begin) ? 1 : 0;
-    return ((size_t)w * 2 + slot) * 16;
-  };
+  const int np = sh_info[0], first = sh_info[1];
+  if (np <= 1) return;  // the single piece wrote the final rows
   // ---- per head h: M = max_p m_p, L = sum_p 2^(m_p - M) l_p.  Thread t takes head t % 16
   // and pieces t / 16, t / 16 + 16, ...; the 16 partial results of a head meet in LDS.
   {
@@ -534,7 +537,7 @@ __global__ __launch_bounds__(256) void streamk_merge_kernel(DecodeArgs a, int nw
     float m = -INFINITY, l = 0.f;
     if (h < G) {
       for (int p = p0; p < np; p += 16) {
-        const size_t r = prow(p) + h;
+        const size_t r = (size_t)(first + p) * 16 + h;
         const float mp = a.ws_ml[2 * r], lp = a.ws_ml[2 * r + 1];
         const float mn = fmaxf(m, mp);
         l = (m == -INFINITY ? 0.f : l * exp2_fast(m - mn)) + lp * exp2_fast(mp - mn);
@@ -563,14 +566,14 @@ __global__ __launch_bounds__(256) void streamk_merge_kernel(DecodeArgs a, int nw
     float O = 0.f;
     int p = 0;
     for (; p + 4 <= np; p += 4) {  // four independent piece loads in flight
-      const size_t r0 = prow(p) + h, r1 = prow(p + 1) + h, r2 = prow(p + 2) + h, r3 = prow(p + 3) + h;
+      const size_t r0 = (size_t)(first + p) * 16 + h, r1 = r0 + 16, r2 = r0 + 32, r3 = r0 + 48;
       const float o0 = a.ws_o[r0 * D + col], o1 = a.ws_o[r1 * D + col];
       const float o2 = a.ws_o[r2 * D + col], o3 = a.ws_o[r3 * D + col];
       O += exp2_fast(a.ws_ml[2 * r0] - M) * o0 + exp2_fast(a.ws_ml[2 * r1] - M) * o1 +
            exp2_fast(a.ws_ml[2 * r2] - M) * o2 + exp2_fast(a.ws_ml[2 * r3] - M) * o3;
     }
     for (; p < np; ++p) {
-      const size_t r = prow(p) + h;
+      const size_t r = (size_t)(first + p) * 16 + h;
       O += exp2_fast(a.ws_ml[2 * r] - M) * a.ws_o[r * D + col];
     }
     a.out[(orow + h) * D + col] = O * sh_iL[h];
@@ -730,26 +733,29 @@ __global__ __launch_bounds__(256) void split_merge_kernel(DecodeArgs a) {
   }
 }
 
-// workgroups of decode_streamk_kernel<D, BS, KVT> one CU holds at once
+// workgroups of decode_piece_kernel<D, BS, KVT> one CU holds at once
 template <int D, int BS, int KVT>
-int streamk_groups_per_cu() {
+int piece_groups_per_cu() {
   static const int per_cu = [] {
     int nb = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, decode_streamk_kernel<D, BS, KVT>, 256, 0) != hipSuccess ||
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, decode_piece_kernel<D, BS, KVT>, 256, 0) != hipSuccess ||
         nb <= 0)
       nb = 2;
-    return nb > kStreamKMaxGroupsPerCU ? kStreamKMaxGroupsPerCU : nb;
+    return nb > kMaxGroupsPerCU ? kMaxGroupsPerCU : nb;
   }();
   return per_cu;
 }
 
 template <int D, int BS, int KVT>
 hipError_t launch_mfma_t(const DecodeArgs& a, hipStream_t s) {
-  const int groups = streamk_groups_per_cu<D, BS, KVT>() * a.num_cus;
-  hipLaunchKernelGGL((decode_streamk_kernel<D, BS, KVT>), dim3((unsigned)groups), dim3(256), 0, s, a);
+  // target pieces = one round of resident workgroups; the plan never makes more
+  // than target + B * H_kv pieces, which sizes the grid (the rest exit at once)
+  const int target = piece_groups_per_cu<D, BS, KVT>() * a.num_cus;
+  const long long grid = (long long)target + (long long)a.B * a.H_kv;
+  hipLaunchKernelGGL((decode_piece_kernel<D, BS, KVT>), dim3((unsigned)grid), dim3(256), 0, s, a, target);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(streamk_merge_kernel, dim3((unsigned)(a.B * a.H_kv)), dim3(256), 0, s, a, groups);
+  hipLaunchKernelGGL(piece_merge_kernel, dim3((unsigned)(a.B * a.H_kv)), dim3(256), 0, s, a, target);
   return hipGetLastError();
 }
 
