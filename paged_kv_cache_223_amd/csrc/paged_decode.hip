@@ -389,12 +389,11 @@ __device__ int plan_piece(const DecodeArgs& a, int target, int item, int lane, P
   return upw;
 }
 
-// The wave's share of one piece: chunks c_first + w, + 4, ... below c_end of
+// The wave's share of one piece: chunks first, first + NW, ... below c_end of
 // segment (b, g), with the next chunk's loads in flight while one is computed.
-template <int D, int BS, int KVT>
+template <int D, int BS, int KVT, int NW>
 __device__ __forceinline__ void run_piece(const DecodeArgs& a, int b, int g, int n, int first, int c_end,
                                           f32x4 (&acc)[D / 16], WaveState& st, int lane) {
-  constexpr int NW = 4;
   const int G = a.G;
   const int last_blk = (n + BS - 1) / BS - 1;
   const int32_t* tab = a.block_tables + (size_t)b * a.max_blocks;
@@ -439,18 +438,23 @@ __device__ __forceinline__ void run_piece(const DecodeArgs& a, int b, int g, int
   }
 }
 
-template <int D, int BS, int KVT>
-__global__ __launch_bounds__(256, 2) void decode_piece_kernel(DecodeArgs a, int target) {
-  constexpr int NW = 4;
+template <int D, int BS, int KVT, int NW>
+__global__ __launch_bounds__(64 * NW, 2) void decode_piece_kernel(DecodeArgs a, int target) {
+  constexpr int NT = 64 * NW;
   __shared__ float sh_acc[NW][16][D];
   __shared__ float sh_m[NW][16];
   __shared__ float sh_l[NW][16];
   const int tid = threadIdx.x, lane = tid & 63, w = uniform(tid >> 6);
   const int item = blockIdx.x;
   const int G = a.G, cap = a.len_cap;
-  // a sequence with no tokens: zero rows, written by workgroup b
+  // a sequence with no tokens: zero rows, written by workgroup b.
+  // Only float stores may come before the chunk loop: the compiler keeps the
+  // block-table and length reads on the scalar unit only while it can prove
+  // that no earlier store of the kernel overwrites them, and an int32 store
+  // (same type as the tables) would turn them into vector loads with a full
+  // wait for memory on every chunk.
   if (item < a.B && uniform(seq_len(a.context_lens, item, cap)) == 0)
-    for (int e = tid; e < a.H_q * D; e += 256) a.out[(size_t)item * a.H_q * D + e] = 0.f;
+    for (int e = tid; e < a.H_q * D; e += NT) a.out[(size_t)item * a.H_q * D + e] = 0.f;
   PiecePlan pp;
   plan_piece(a, target, item, lane, pp);
   if (pp.b < 0) return;
@@ -459,7 +463,7 @@ __global__ __launch_bounds__(256, 2) void decode_piece_kernel(DecodeArgs a, int 
   const int n = uniform(seq_len(a.context_lens, b, cap));
   f32x4 acc[D / 16];
   WaveState st;
-  run_piece<D, BS, KVT>(a, b, g, n, lo + w, hi, acc, st, lane);
+  run_piece<D, BS, KVT, NW>(a, b, g, n, lo + w, hi, acc, st, lane);
   // ---- merge the four waves' shares through LDS
   const int kg = lane >> 4;
   float lt = st.l;
@@ -477,7 +481,7 @@ __global__ __launch_bounds__(256, 2) void decode_piece_kernel(DecodeArgs a, int 
   const float vs = KVT == PKV_FP8_E4M3 ? a.v_scale[g] : 1.f;
   const size_t orow = ((size_t)b * a.H_q + g * G) * D;
   const size_t prow = (size_t)item * 16;
-  for (int e = tid; e < G * D; e += 256) {
+  for (int e = tid; e < G * D; e += NT) {
     const int hh = e / D, col = e % D;
     float M = sh_m[0][hh];
 #pragma unroll
@@ -733,14 +737,15 @@ __global__ __launch_bounds__(256) void split_merge_kernel(DecodeArgs a) {
   }
 }
 
-// workgroups of decode_piece_kernel<D, BS, KVT> one CU holds at once
-template <int D, int BS, int KVT>
+// workgroups of decode_piece_kernel<D, BS, KVT, NW> one CU holds at once
+template <int D, int BS, int KVT, int NW>
 int piece_groups_per_cu() {
   static const int per_cu = [] {
     int nb = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, decode_piece_kernel<D, BS, KVT>, 256, 0) != hipSuccess ||
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, decode_piece_kernel<D, BS, KVT, NW>, 64 * NW, 0) !=
+            hipSuccess ||
         nb <= 0)
-      nb = 2;
+      nb = 1;
     return nb > kMaxGroupsPerCU ? kMaxGroupsPerCU : nb;
   }();
   return per_cu;
@@ -749,10 +754,20 @@ int piece_groups_per_cu() {
 template <int D, int BS, int KVT>
 hipError_t launch_mfma_t(const DecodeArgs& a, hipStream_t s) {
   // target pieces = one round of resident workgroups; the plan never makes more
-  // than target + B * H_kv pieces, which sizes the grid (the rest exit at once)
-  const int target = piece_groups_per_cu<D, BS, KVT>() * a.num_cus;
-  const long long grid = (long long)target + (long long)a.B * a.H_kv;
-  hipLaunchKernelGGL((decode_piece_kernel<D, BS, KVT>), dim3((unsigned)grid), dim3(256), 0, s, a, target);
+  // than target + B * H_kv pieces, which sizes the grid (the rest exit at once).
+  // 8-wave workgroups when every (sequence, KV head) segment fits one round
+  // whole: a uniform batch then needs no partials at all; otherwise 4-wave
+  // workgroups, twice as many, so that piece boundaries of one workgroup
+  // overlap another's streaming on the same CU.
+  const long long segments = (long long)a.B * a.H_kv;
+  const int target8 = piece_groups_per_cu<D, BS, KVT, 8>() * a.num_cus;
+  const bool wide = segments <= target8;
+  const int target = wide ? target8 : piece_groups_per_cu<D, BS, KVT, 4>() * a.num_cus;
+  const long long grid = (long long)target + segments;
+  if (wide)
+    hipLaunchKernelGGL((decode_piece_kernel<D, BS, KVT, 8>), dim3((unsigned)grid), dim3(512), 0, s, a, target);
+  else
+    hipLaunchKernelGGL((decode_piece_kernel<D, BS, KVT, 4>), dim3((unsigned)grid), dim3(256), 0, s, a, target);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(piece_merge_kernel, dim3((unsigned)(a.B * a.H_kv)), dim3(256), 0, s, a, target);

@@ -246,3 +246,15 @@ def test_captured_step_replays_match_eager():
         g.replay()
         torch.cuda.synchronize()
         assert torch.equal(out, eager), f"replay {i} differs from the eager step"
+
+
+@pytest.mark.parametrize("kv", ["bf16", "e4m3"])
+def test_decode_many_segments_mixed_lengths(kv):
+    """More (sequence, KV head) segments than one round of wide workgroups holds: the
+    narrow-workgroup plan, with long sequences cut into pieces and short ones whole."""
+    rng = np.random.default_rng(31 if kv == "bf16" else 32)
+    lens = rng.integers(1, 400, size=48).tolist()
+    lens[3], lens[17], lens[40] = 5000, 2600, 0
+    case = workloads.custom(f"many_{kv}", 48, 32, 8, 128, 16, kv, "bf16", lens, seed=3100 + len(kv))
+    got, _, _ = _parity(case)
+    assert (got[40] == 0).all()
