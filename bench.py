@@ -3,10 +3,11 @@
 
 A step is one pass of the whole hot path over one batch: kv_append of this step's token
 for every sequence, then paged decode attention of every sequence's query over its paged
-KV (context-split partition kernel + split merge).  The default workload is a
+KV (piece kernel + piece merge).  The default workload is a
 Llama-3.1-70B-shaped layer: 32 sequences at 8192 tokens (16 of them share one refcounted
 2048-token prefix), H_q 64, H_kv 8, head dim 128, bf16 KV, 16-token blocks scattered by
-the allocator.  Inputs are synthetic and resident in HBM before the timed region.
+the allocator.  Inputs are synthetic and resident in HBM before the timed region.  A
+workload with less than 1 GB of KV rotates through copies of its inputs (--sets).
 
 Prints one JSON line.  `value` = algorithmic bytes of the step / step time in GB/s
 (KV counted once per distinct physical block).
@@ -18,6 +19,7 @@ import hashlib
 import json
 import math
 import os
+import re
 import sys
 import time
 
@@ -56,6 +58,9 @@ def parse():
                    help="launch the step's kernels one by one instead of replaying a captured HIP graph")
     p.add_argument("--identity-tables", action="store_true",
                    help="lay every sequence out contiguously (identity block order) instead of scattered")
+    p.add_argument("--sets", type=int, default=0,
+                   help="independent copies of the inputs the steps rotate through (0 = enough for 1 GB of "
+                        "KV, so the 256 MB last-level cache cannot hold the working set)")
     return p.parse_args()
 
 
@@ -88,7 +93,13 @@ def algorithmic_bytes(tables, lens, bs, B, H_q, H_kv, D, s_kv, s_q, T_append, s_
 
 
 def source_hash(path):
-    return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
+    """Hash of a C++/HIP source with comments and whitespace removed, so that the counters
+    taken on a kernel stay valid across comment-only edits."""
+    text = open(path).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", "", text)
+    text = re.sub(r"\s+", "", text)
+    return hashlib.sha256(text.encode()).hexdigest()[:16]
 
 
 def measured_traffic(workload):
@@ -99,7 +110,7 @@ def measured_traffic(workload):
     except (OSError, ValueError):
         return None
     ent = rec.get(workload)
-    if not ent or ent.get("source_sha256_16") != source_hash(KERNEL_SOURCE):
+    if not ent or ent.get("code_sha256_16") != source_hash(KERNEL_SOURCE):
         return None
     return ent.get("hbm_bytes_per_launch")
 
@@ -162,61 +173,72 @@ def main():
     mcl = case.max_context_len
     out = torch.empty((B, H_q, D), dtype=torch.float32, device=dev)
     ws = pkv.decode_workspace(B, H_q, H_kv, D, mcl, case.bs, device=dev)
-    torch.cuda.synchronize()
-    print(f"# setup {time.time() - t_setup:.1f}s: {wname} B={B} NB={case.NB} pool {2 * k_pool.numel() * k_pool.element_size() / 1e9:.2f} GB",
-          file=sys.stderr, flush=True)
-
-    def step(e0=None, e1=None, e2=None):
-        if e0 is not None:
-            e0.record()
-        if len(mat.step_slots):
-            pkv.kv_append(step_k, step_v, step_slots, k_pool, v_pool, k_scale, v_scale)
-        if e1 is not None:
-            e1.record()
-        pkv.paged_attn_decode(q, k_pool, v_pool, tables, lens, float(case.scale), mcl, k_scale, v_scale,
-                              out=out, workspace=ws)
-        if e2 is not None:
-            e2.record()
-
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    K = args.steps
-    # decode alone, eager launches: per-call duration of the dominant kernel(s) on the launch stream
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
-    for i in range(K):
-        step(*ev[i])
-    torch.cuda.synchronize()
-    append_ms = np.array([e[0].elapsed_time(e[1]) for e in ev])
-    decode_ms = np.array([e[1].elapsed_time(e[2]) for e in ev])
-    eager_step_ms = ev[0][0].elapsed_time(ev[-1][2]) / K
-    # the timed region: K whole steps (kv_append + decode), replayed from one captured HIP graph
-    graph = None
-    if not args.eager:
-        graph = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(graph):
-            step()
-        for _ in range(args.warmup):
-            graph.replay()
-    torch.cuda.synchronize()
-    g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    t0 = time.perf_counter()
-    g0.record()
-    for i in range(K):
-        graph.replay() if graph is not None else step()
-    g1.record()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    step_ms = g0.elapsed_time(g1) / K
-    print(f"# timed {K} steps in {wall:.3f}s wall ({'eager' if graph is None else 'graph'}); eager decode p10/p50/p90 "
-          f"{np.percentile(decode_ms, 10) * 1e3:.1f}/{np.median(decode_ms) * 1e3:.1f}/{np.percentile(decode_ms, 90) * 1e3:.1f} us",
-          file=sys.stderr, flush=True)
 
     s_kv = {"bf16": 2, "e4m3": 1, "f32": 4}[spec.kv_dtype]
     s_q = 4 if spec.q_dtype == "f32" else 2
     s_src = 4 if sd == "f32" else 2
     by = algorithmic_bytes(mat.block_tables, mat.context_lens, case.bs, B, H_q, H_kv, D, s_kv, s_q,
                            len(mat.step_slots), s_src)
+    # independent input sets (separate copies of the pools and per-step inputs) so that a
+    # workload smaller than 1 GB of KV is not served from the last-level cache on repeat
+    n_sets = args.sets if args.sets > 0 else max(1, math.ceil(1e9 / by["kv_logical"]))
+    sets = [(k_pool, v_pool, q, tables, lens, step_k, step_v, step_slots)]
+    for _ in range(n_sets - 1):
+        sets.append(tuple(t.clone() for t in sets[0]))
+    torch.cuda.synchronize()
+    print(f"# setup {time.time() - t_setup:.1f}s: {wname} B={B} NB={case.NB} pool {2 * k_pool.numel() * k_pool.element_size() / 1e9:.2f} GB"
+          f" x {n_sets} input set(s)", file=sys.stderr, flush=True)
+
+    def step(i=0, e0=None, e1=None, e2=None):
+        kp, vp, q_, tab, ln, sk, sv, ss = sets[i % n_sets]
+        if e0 is not None:
+            e0.record()
+        if len(mat.step_slots):
+            pkv.kv_append(sk, sv, ss, kp, vp, k_scale, v_scale)
+        if e1 is not None:
+            e1.record()
+        pkv.paged_attn_decode(q_, kp, vp, tab, ln, float(case.scale), mcl, k_scale, v_scale,
+                              out=out, workspace=ws)
+        if e2 is not None:
+            e2.record()
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    K = args.steps
+    # decode alone, eager launches: per-call duration of the dominant kernel(s) on the launch stream
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
+    for i in range(K):
+        step(i, *ev[i])
+    torch.cuda.synchronize()
+    append_ms = np.array([e[0].elapsed_time(e[1]) for e in ev])
+    decode_ms = np.array([e[1].elapsed_time(e[2]) for e in ev])
+    eager_step_ms = ev[0][0].elapsed_time(ev[-1][2]) / K
+    # the timed region: K whole steps (kv_append + decode), replayed from captured HIP graphs
+    graphs = None
+    if not args.eager:  # one captured step per input set, replayed in rotation
+        graphs = []
+        for i in range(n_sets):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                step(i)
+            graphs.append(g)
+        for i in range(args.warmup):
+            graphs[i % n_sets].replay()
+    torch.cuda.synchronize()
+    g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    g0.record()
+    for i in range(K):
+        graphs[i % n_sets].replay() if graphs is not None else step(i)
+    g1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    step_ms = g0.elapsed_time(g1) / K
+    print(f"# timed {K} steps in {wall:.3f}s wall ({'eager' if graphs is None else 'graph'}); eager decode p10/p50/p90 "
+          f"{np.percentile(decode_ms, 10) * 1e3:.1f}/{np.median(decode_ms) * 1e3:.1f}/{np.percentile(decode_ms, 90) * 1e3:.1f} us",
+          file=sys.stderr, flush=True)
+
     dec_avg_s = decode_ms.mean() / 1e3
     dec_gbps = by["decode"] / dec_avg_s / 1e9
     step_gbps = (by["decode"] + by["append"]) / (step_ms / 1e3) / 1e9
@@ -252,13 +274,14 @@ def main():
             "max_context": mcl, "mean_context": float(np.mean(mat.context_lens)), "pool_blocks": case.NB,
             "append_tokens_per_step": int(len(mat.step_slots)),
             "tables": "identity" if args.identity_tables else "scattered",
+            "input_sets": n_sets,
         },
         "seqs_per_s": round(B / (step_ms / 1e3), 1),
         "frac_of_hbm_peak": round(step_gbps / HBM_PEAK_GBPS, 4),
         "decode_us_p50": round(float(np.median(decode_ms)) * 1e3, 2),
         "append_us_p50": round(float(np.median(append_ms)) * 1e3, 2),
         "eager_ms_per_step": round(eager_step_ms, 5),
-        "step_launch": "eager" if graph is None else "hip_graph",
+        "step_launch": "eager" if graphs is None else "hip_graph",
         "decode_GBps_unique": round(dec_gbps, 1),
         "decode_GBps_logical": round(by["decode_logical"] / dec_avg_s / 1e9, 1),
         "kv_bytes_unique": by["kv_unique"],
@@ -268,7 +291,7 @@ def main():
     }
     traffic = measured_traffic(args.workload)
     res["roofline"] = {
-        "bound": "hbm", "kernel": "paged_attn_decode call = decode_streamk_kernel + streamk_merge_kernel",
+        "bound": "hbm", "kernel": "paged_attn_decode call = decode_piece_kernel + piece_merge_kernel",
         "achieved": round(dec_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
         "frac": round(dec_gbps / HBM_PEAK_GBPS, 4),
         "algorithmic_bytes_per_launch": by["decode"],

@@ -10,18 +10,24 @@
 // pages is the cost to keep small.  Scores are never written to memory (the
 // fused-attention property named in the section on block-level eviction).
 //
-// Work decomposition: a work item is (context split s, sequence b, KV head g),
-// numbered ((s * B) + b) * H_kv + g.  The grid covers the longest admissible
-// sequence; an item past its sequence's last split exits after one load of
-// the (cached) length.  Split-major order makes the first splits of all
-// sequences run together, so sequences that share prefix blocks read them at
-// about the same time, and KV head g of every item lands on the same XCD
-// (workgroups are dealt to the 8 XCDs round-robin), whose L2 then serves the
-// shared blocks again.
+// Matrix-core path (bf16 q; bf16 or E4M3 KV; G = H_q/H_kv <= 16; D 64/128).
 //
-// Matrix-core path (bf16 q; bf16 or E4M3 KV; G = H_q/H_kv <= 16; D 64/128):
-// one workgroup = 4 waves; a wave owns 32-token chunks of the split (chunk
-// w, w+4, ...).  Per chunk:
+// Work decomposition.  A segment is one (sequence b, KV head g); its unit of
+// work is a 32-token chunk, c_b = ceil(n_b / 32) chunks.  Every workgroup
+// reads the lengths and computes the same plan: upw = max(8, ceil(H_kv *
+// sum_b c_b / target)) chunks per piece, where target is one round of
+// resident workgroups (occupancy x CUs); segment (b, g) is cut into
+// np_b = ceil(c_b / upw) pieces of near-equal chunk counts, numbered
+// sequence-major.  Workgroup i takes piece i (a prefix scan over sequences
+// finds it); workgroups past the last piece exit.  So every resident
+// workgroup streams about the same number of bytes whatever the length mix,
+// and a batch whose segments all fit one round needs no partial results.
+// Workgroups have 8 waves when every segment fits one round whole, else 4
+// (twice as many workgroups, so one workgroup's start and end overlap
+// another's streaming on the same CU).  Inside a piece the waves take chunks
+// round-robin and merge through LDS at the end.
+//
+// Per chunk, per wave:
 //   S^T[16 tok][16 heads] = K[16 tok][D] . Q^T[D][16 heads]   two
 //     v_mfma_f32_16x16x32_bf16 chains (one per 16-token half); A = K rows
 //     straight from the pool, B = the wave's resident Q (heads >= G zero).
@@ -35,19 +41,19 @@
 // The pool layout makes every MFMA operand a 16- or 8-byte lane load: the K
 // tile is [D/X][bs][X] (16 tokens x 16 bytes contiguous per 16 lanes) and the
 // V tile is [D][bs] (4 consecutive tokens of one column per lane), so no LDS
-// staging or transposition is needed on the hot loop; LDS only merges the
-// four waves at the end.
+// staging or transposition is needed on the hot loop.
 //
-// Vector path: one wave per (sequence, split, query head), fp32 VALU; used for
-// fp32 q or KV, G > 16 or D = 256.
-//
-// Splits: a sequence with one split writes its final rows directly.  With
-// several splits each item writes its unnormalised output and (max, sum) to
-// the workspace, and split_merge (a second, small launch) combines them:
+// A piece that covers its whole segment writes the final rows; otherwise it
+// writes its unnormalised output and (max, sum) per head to the workspace,
+// and piece_merge (a second, small launch, one workgroup per segment)
+// combines the pieces:
 //     o = sum_i 2^(m_i - M) o_i / sum_i 2^(m_i - M) l_i,  M = max_i m_i.
-// (Merging inside the partition kernel by the last-arriving workgroup needs a
+// (Merging inside the piece kernel by the last-arriving workgroup needs a
 // device-scope release/acquire per workgroup; on gfx950 those are whole-L2
 // writeback/invalidate operations, which cost far more than the launch.)
+//
+// Vector path: one wave per (sequence, context split, query head), fp32 VALU,
+// fixed-size splits and split_merge; used for fp32 q or KV, G > 16 or D = 256.
 
 #include <hip/hip_runtime.h>
 
@@ -306,9 +312,9 @@ __device__ __forceinline__ void process_chunk(const Chunk<D, BS, KVT>& ch, const
 // of mixed lengths gets many segment-aligned pieces, at most upw chunks each,
 // which the hardware dispatcher balances.  Each workgroup runs a single piece,
 // which keeps register use (and so occupancy) at its single-piece minimum.
-// The 4 waves take the piece's chunks round-robin and merge through LDS; a
-// piece that is a whole segment writes its final rows, the others write
-// partials that piece_merge combines.
+// The workgroup's NW (4 or 8) waves take the piece's chunks round-robin and
+// merge through LDS; a piece that is a whole segment writes its final rows,
+// the others write partials that piece_merge combines.
 // ---------------------------------------------------------------------------
 constexpr int kMinUnits = 8;
 constexpr int kLensInRegs = 16;  // lengths a lane keeps in registers (B <= 1024 in one pass)
@@ -464,7 +470,7 @@ __global__ __launch_bounds__(64 * NW, 2) void decode_piece_kernel(DecodeArgs a, 
   f32x4 acc[D / 16];
   WaveState st;
   run_piece<D, BS, KVT, NW>(a, b, g, n, lo + w, hi, acc, st, lane);
-  // ---- merge the four waves' shares through LDS
+  // ---- merge the NW waves' shares through LDS
   const int kg = lane >> 4;
   float lt = st.l;
   lt += __shfl_xor(lt, 16, 64);

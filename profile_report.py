@@ -1,0 +1,129 @@
+#!/usr/bin/env python3
+"""Turn rocprofv3 output of bench.py runs into the summaries kept under profiles/.
+
+Reads the rocpd SQLite databases of five runs of one workload (all from the repository root):
+
+    rocprofv3 --kernel-trace --stats -T -d T -o trace -- python3 bench.py --workload W --steps 20 --warmup 5 --no-cpu-baseline
+    rocprofv3 --pmc FETCH_SIZE -T -d F -o fetch -- python3 bench.py --workload W --steps 3 --warmup 1 --no-cpu-baseline --eager
+    rocprofv3 --pmc WRITE_SIZE -T -d R -o write -- python3 bench.py --workload W --steps 3 --warmup 1 --no-cpu-baseline --eager
+    rocprofv3 --pmc FETCH_SIZE -T -d CF -o cf -- python3 bench.py --copy-calibration 1024
+    rocprofv3 --pmc WRITE_SIZE -T -d CW -o cw -- python3 bench.py --copy-calibration 1024
+
+and writes profiles/decode_<W>.md plus the workload's entry of profiles/decode_counters.json
+(the HBM bytes per decode call that bench.py reports as roofline.traffic, keyed by a hash of
+the decode kernel's code so that a changed kernel reports null until it is profiled again).
+
+    python profile_report.py W T F R CF CW
+"""
+from __future__ import annotations
+
+import glob
+import json
+import os
+import sqlite3
+import sys
+
+from bench import COUNTERS, KERNEL_SOURCE, ROOT, source_hash
+DECODE_KERNELS = ("decode_piece_kernel", "piece_merge_kernel")
+COPY_BYTES = 1 << 30
+
+TRACE_CMD = ("rocprofv3 --kernel-trace --stats -T -d <out> -o trace -- python3 bench.py --workload {w} "
+             "--steps 20 --warmup 5 --no-cpu-baseline")
+PMC_CMD = ("timeout -s KILL 150 rocprofv3 --pmc {c} -T -d <out> -o {o} -- python3 bench.py --workload {w} "
+           "--steps 3 --warmup 1 --no-cpu-baseline --eager")
+COPY_CMD = "timeout -s KILL 90 rocprofv3 --pmc {c} -T -d <out> -o {o} -- python3 bench.py --copy-calibration 1024"
+
+
+def _db(d):
+    hits = sorted(glob.glob(os.path.join(d, "**", "*_results.db"), recursive=True))
+    if not hits:
+        raise SystemExit(f"no rocpd database under {d}")
+    return sqlite3.connect(hits[0])
+
+
+def _short(name):
+    return name.split("(")[0].split("<")[0].split("::")[-1].strip()
+
+
+def trace_stats(d):
+    con = _db(d)
+    rows = con.execute("select name, total_calls, total_duration, average, percentage from top_kernels").fetchall()
+    launch = {}
+    for r in con.execute("select name, grid_x, workgroup_x, vgpr_count, accum_vgpr_count, sgpr_count, lds_size, "
+                         "scratch_size from kernels"):
+        launch.setdefault(_short(r[0]), r[1:])
+    return [(_short(n), c, t, a, p) for n, c, t, a, p in rows], launch  # durations in us
+
+
+def counter_kib(d, counter):
+    """Average value of `counter` per dispatch, per kernel (KiB for FETCH_SIZE / WRITE_SIZE)."""
+    con = _db(d)
+    out = {}
+    for name, v, n in con.execute("select kernel_name, avg(value), count(*) from counters_collection "
+                                  "where counter_name = ? group by kernel_name", (counter,)):
+        out[_short(name)] = (v, n)
+    return out
+
+
+def main(argv):
+    if len(argv) != 6:
+        raise SystemExit(__doc__)
+    w, t_dir, f_dir, r_dir, cf_dir, cw_dir = argv
+    stats, launch = trace_stats(t_dir)
+    fetch, write = counter_kib(f_dir, "FETCH_SIZE"), counter_kib(r_dir, "WRITE_SIZE")
+    cf, cw = counter_kib(cf_dir, "FETCH_SIZE")["copy_kernel"][0], counter_kib(cw_dir, "WRITE_SIZE")["copy_kernel"][0]
+    ff, wf = COPY_BYTES / (cf * 1024), COPY_BYTES / (cw * 1024)
+    sha = source_hash(KERNEL_SOURCE)
+    avg = {n: a for n, _, _, a, _ in stats}
+
+    entry = {"code_sha256_16": sha, "fetch_factor": ff, "write_factor": wf}
+    total = 0.0
+    for k in DECODE_KERNELS:
+        fb = fetch[k][0] * 1024 * ff
+        wb = write[k][0] * 1024 * wf
+        entry[k] = {"fetch_bytes": round(fb), "write_bytes": round(wb), "avg_us_trace": round(avg[k], 3)}
+        total += fb + wb
+    entry["hbm_bytes_per_launch"] = round(total)
+    try:
+        rec = json.load(open(COUNTERS))
+    except (OSError, ValueError):
+        rec = {}
+    rec[w] = entry
+    with open(COUNTERS, "w") as f:
+        json.dump(rec, f, indent=1, sort_keys=True)
+        f.write("\n")
+
+    L = [f"# paged decode on MI355X: workload `{w}`", "",
+         "Kernel trace (rocprofv3 --kernel-trace --stats), one GPU: 20 timed + 5 warm-up steps, the eager",
+         "per-call timing pass, and the bench's setup (prefill appends, a 4 GiB read-ceiling probe).", "",
+         "Command (from the repository root):", "", "    " + TRACE_CMD.format(w=w), "",
+         "| kernel | calls | total us | average us | % |", "|---|---|---|---|---|"]
+    for n, c, t, a, p in stats:
+        L.append(f"| {n} | {c} | {t:.1f} | {a:.2f} | {p:.1f} |")
+    L.append("")
+    for k in DECODE_KERNELS:
+        if k in launch:
+            g, wg, v, ag, sg, lds, scr = launch[k]
+            L.append(f"{k} launch: grid {g} threads in workgroups of {wg}; VGPR field {v}, AGPR {ag}, "
+                     f"SGPR {sg}, LDS {lds} B, scratch {scr} B.")
+    L += ["", "kv_append calls of the step are the short ones; the long ones are the setup's prefill.", "",
+          "## HBM traffic (rocprofv3 --pmc, one counter per run)", "", "Commands:", "",
+          "    " + PMC_CMD.format(c="FETCH_SIZE", o="fetch", w=w), "    " + PMC_CMD.format(c="WRITE_SIZE", o="write", w=w),
+          "    " + COPY_CMD.format(c="FETCH_SIZE", o="cf"), "    " + COPY_CMD.format(c="WRITE_SIZE", o="cw"), "",
+          f"Calibration: the library's copy kernel over 1 GiB reads FETCH_SIZE = {cf:.1f} KiB and WRITE_SIZE = "
+          f"{cw:.1f} KiB per dispatch, so bytes = FETCH_SIZE x {ff:.4f} x 1024 and WRITE_SIZE x {wf:.4f} x 1024.", "",
+          "| kernel | FETCH_SIZE KiB/dispatch | WRITE_SIZE KiB/dispatch | dispatches | fetched MB | written MB |",
+          "|---|---|---|---|---|---|"]
+    for k in DECODE_KERNELS:
+        L.append(f"| {k} | {fetch[k][0]:.1f} | {write[k][0]:.1f} | {fetch[k][1]} | "
+                 f"{entry[k]['fetch_bytes'] / 1e6:.2f} | {entry[k]['write_bytes'] / 1e6:.2f} |")
+    L += ["", f"Decode call total: {total / 1e6:.2f} MB moved beyond L2 per launch "
+          f"(kernel code sha256[:16], comments and whitespace removed: {sha}).", ""]
+    with open(os.path.join(ROOT, "profiles", f"decode_{w}.md"), "w") as f:
+        f.write("\n".join(L))
+    print(f"{w}: {total / 1e6:.2f} MB per decode call; " +
+          ", ".join(f"{k} {avg[k]:.2f} us" for k in DECODE_KERNELS))
+
+
+if __name__ == "__main__":
+    main(sys.argv[1:])
