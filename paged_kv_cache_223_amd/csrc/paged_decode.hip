@@ -141,7 +141,8 @@ template <int D, int BS, int KVT>
 struct Chunk {
   static constexpr int kKLoads = KVT == PKV_BF16 ? D / 32 : D / 64;  // 16-byte K loads per half
   u32x4 k[2][kKLoads];
-  // V operand words per output tile: bf16 -> 4 words, e4m3 -> 2 words (codes)
+  // V operand per output tile: 8 consecutive tokens of one column, as
+  // bf16 (4 words) or E4M3 codes (2 words)
   typename std::conditional<KVT == PKV_BF16, u32x4, u32x2>::type v[D / 16];
 };
 
@@ -176,24 +177,40 @@ __device__ __forceinline__ void load_chunk(Chunk<D, BS, KVT>& ch, const char* __
     for (int c = 0; c < Chunk<D, BS, KVT>::kKLoads; ++c)
       ch.k[a][c] = __builtin_nontemporal_load((const u32x4*)(base + (size_t)c * 64 * BS));
   }
-  const int n = lane & 15, qg = lane >> 4;
+  // V: lane (n, kg) holds tokens 8kg .. 8kg+7 of column n of each 16-column
+  // tile (the B operand of the PV MFMA), one 16- or 8-byte load per tile
+  const int n = lane & 15;
+  const int tv = 8 * kg;
+  const int vid = pick<NBCH>(ids, BS >= 32 ? 0 : tv / BS);
+  const char* vbase = vpool + (size_t)vid * bstride + gofs + ((size_t)n * BS + tv % BS) * S;
 #pragma unroll
-  for (int a = 0; a < 2; ++a) {
-    const int tv = 16 * a + 4 * qg;  // first of the 4 tokens this lane's V words hold
-    const int id = pick<NBCH>(ids, BS >= 32 ? 0 : tv / BS);
-    const char* base = vpool + (size_t)id * bstride + gofs + ((size_t)n * BS + tv % BS) * S;
-#pragma unroll
-    for (int t = 0; t < D / 16; ++t) {
-      const char* p = base + (size_t)t * 16 * BS * S;
-      if constexpr (KVT == PKV_BF16) {
-        u32x2 x = __builtin_nontemporal_load((const u32x2*)p);
-        ch.v[t][2 * a] = x.x;
-        ch.v[t][2 * a + 1] = x.y;
-      } else {
-        ch.v[t][a] = __builtin_nontemporal_load((const uint32_t*)p);
-      }
-    }
+  for (int t = 0; t < D / 16; ++t) {
+    const char* p = vbase + (size_t)t * 16 * BS * S;
+    if constexpr (KVT == PKV_BF16)
+      ch.v[t] = __builtin_nontemporal_load((const u32x4*)p);
+    else
+      ch.v[t] = __builtin_nontemporal_load((const u32x2*)p);
   }
+}
+
+// Regroup the P operand across lane groups.  In: lane group r (lanes 16r ..
+// 16r+15) holds, for its head, tokens 4r..4r+3 of the chunk's first half in
+// words 0,1 and of the second half in words 2,3 (the QK^T accumulator rows).
+// Out: lane group r holds tokens 8r .. 8r+7 in words 0..3, so that each
+// lane's V operand is 8 consecutive tokens of one column.  With rows R0..R3
+// of two registers X (half 0) and Y (half 1): permlane32_swap gives
+// X' = [X0 X1 Y0 Y1], Y' = [X2 X3 Y2 Y3]; permlane16_swap then gives
+// [X0 X2 Y0 Y2] (tokens 8r..8r+3) and [X1 X3 Y1 Y3] (tokens 8r+4..8r+7).
+__device__ __forceinline__ u32x4 tokens_by_eight(u32x4 v) {
+  u32x4 r;
+#pragma unroll
+  for (int w = 0; w < 2; ++w) {
+    const auto a = __builtin_amdgcn_permlane32_swap(v[w], v[w + 2], false, false);
+    const auto b = __builtin_amdgcn_permlane16_swap(a[0], a[1], false, false);
+    r[w] = b[0];
+    r[w + 2] = b[1];
+  }
+  return r;
 }
 
 struct WaveState {
@@ -266,6 +283,7 @@ __device__ __forceinline__ void process_chunk(const Chunk<D, BS, KVT>& ch, const
     lo[j] = p - __builtin_bit_cast(float, bits & 0xFFFF0000u);
   }
   st.l += psum;
+  // bf16 pairs: words 0,1 = tokens 4kg..4kg+3 of half 0, words 2,3 = the same of half 1
   u32x4 ph, pl;
 #pragma unroll
   for (int w = 0; w < 4; ++w) {
@@ -273,15 +291,15 @@ __device__ __forceinline__ void process_chunk(const Chunk<D, BS, KVT>& ch, const
     pl[w] = __builtin_amdgcn_perm(__builtin_bit_cast(uint32_t, lo[2 * w + 1]),
                                   __builtin_bit_cast(uint32_t, lo[2 * w]), 0x07060302u);
   }
-  // ---- V tail mask: k-slot j of lane group kg is token (j<4 ? 4kg+j : 16+4kg+j-4)
+  ph = tokens_by_eight(ph);
+  pl = tokens_by_eight(pl);
+  // ---- V tail mask: k-slot j of lane group kg is token 8kg + j
   u32x4 vmask = u32x4{~0u, ~0u, ~0u, ~0u};
   if (tail) {
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
-      const int j0 = 2 * w, j1 = 2 * w + 1;
-      const int t0 = cs + (j0 < 4 ? 4 * kg + j0 : 16 + 4 * kg + j0 - 4);
-      const int t1 = cs + (j1 < 4 ? 4 * kg + j1 : 16 + 4 * kg + j1 - 4);
-      vmask[w] = (t0 < n ? 0x0000FFFFu : 0u) | (t1 < n ? 0xFFFF0000u : 0u);
+      const int t0 = cs + 8 * kg + 2 * w;
+      vmask[w] = (t0 < n ? 0x0000FFFFu : 0u) | (t0 + 1 < n ? 0xFFFF0000u : 0u);
     }
   }
   // ---- O += P V
@@ -445,7 +463,7 @@ __device__ __forceinline__ void run_piece(const DecodeArgs& a, int b, int g, int
 }
 
 template <int D, int BS, int KVT, int NW>
-__global__ __launch_bounds__(64 * NW, 2) void decode_piece_kernel(DecodeArgs a, int target) {
+__global__ __launch_bounds__(64 * NW, KVT == PKV_FP8_E4M3 ? 3 : 2) void decode_piece_kernel(DecodeArgs a, int target) {
   constexpr int NT = 64 * NW;
   __shared__ float sh_acc[NW][16][D];
   __shared__ float sh_m[NW][16];
