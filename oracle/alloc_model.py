@@ -21,6 +21,16 @@ bit for bit):
   * free: logical blocks are visited last to first, refcount goes down, a block
     reaching zero is pushed, so the next pops return the freed sequence's blocks
     in their original logical order.
+
+Copy-on-write append (PA, same section: sharers point at one physical block
+and only diverge where their content differs; FG "Why it matters": cheap
+forks for beam search and branching conversations).  `append_slots_cow` is
+append_slots except where the last block is shared and partly filled: the
+growing sequence first takes a fresh block for that logical position (popped
+before any growth block), the old block loses one reference, and the pair
+(old, new) is returned so that the caller copies the block's contents before
+writing the new tokens.  The fresh block counts towards the all-or-nothing
+block need.
 """
 from __future__ import annotations
 
@@ -81,6 +91,28 @@ class AllocModel:
         slots = [blocks[p // bs] * bs + p % bs for p in range(L, L + n)]
         self.lens[seq] = L + n
         return Status.OK, slots
+
+    def append_slots_cow(self, seq, n):
+        """(status, slots, copies): copies is a list of (src_block, dst_block) pairs (0 or 1)."""
+        if seq not in self.blocks:
+            return Status.UNKNOWN_SEQ, None, None
+        if n < 0:
+            return Status.INVALID_ARG, None, None
+        blocks, L, bs = self.blocks[seq], self.lens[seq], self.bs
+        cow = n > 0 and L % bs != 0 and self.rc[blocks[-1]] > 1
+        need = _ceil_div(L + n, bs) - _ceil_div(L, bs) + (1 if cow else 0)
+        if need > len(self.stack):
+            return Status.OUT_OF_BLOCKS, None, None
+        copies = []
+        if cow:
+            old, new = blocks[-1], self.stack.pop()
+            self.rc[old] -= 1
+            self.rc[new] = 1
+            blocks[-1] = new
+            copies.append((old, new))
+        st, slots = self.append_slots(seq, n)
+        assert st == Status.OK
+        return Status.OK, slots, copies
 
     def fork(self, parent, child) -> int:
         if parent not in self.blocks:

@@ -152,3 +152,19 @@ def ref_decode(q, q_dtype, k_pool, v_pool, kv_dtype, block_tables, context_lens,
 
 __all__ = ["pool_shapes", "lanes_per_16b", "empty_pools", "to_f64", "ref_append",
            "gather_sequence", "ref_decode"]
+
+
+def ref_copy_blocks(k_pool, v_pool, pairs):
+    """Copy-on-write block copy: for each (src, dst) pair in order, physical block dst of
+    both pools becomes an exact copy of block src (every head, every token slot).
+
+    "Paged Attention and KV Cache Fragmentation", section "How PagedAttention maps an OS
+    concept onto GPU memory": sharers of a block diverge only where their content differs;
+    the copy gives the diverging sequence its own block holding the shared tokens.
+    Returns new arrays; the inputs are not modified."""
+    k, v = np.array(k_pool, copy=True), np.array(v_pool, copy=True)
+    for src, dst in pairs:
+        k[dst] = k[src]
+        v[dst] = v[src]
+    return k, v
+
