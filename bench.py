@@ -58,6 +58,9 @@ def parse():
                    help="launch the step's kernels one by one instead of replaying a captured HIP graph")
     p.add_argument("--identity-tables", action="store_true",
                    help="lay every sequence out contiguously (identity block order) instead of scattered")
+    p.add_argument("--op", default="step", choices=["step", "copy_blocks"],
+                   help="step: the decode step (default); copy_blocks: copy-on-write block copies alone")
+    p.add_argument("--pairs", type=int, default=4096, help="block pairs per copy_blocks call (--op copy_blocks)")
     p.add_argument("--sets", type=int, default=0,
                    help="independent copies of the inputs the steps rotate through (0 = enough for 1 GB of "
                         "KV, so the 256 MB last-level cache cannot hold the working set)")
@@ -137,6 +140,9 @@ def main():
             pkv.copy_(dst, src)
         torch.cuda.synchronize()
         print(json.dumps({"copy_calibration_bytes_per_launch": n, "launches": 5}), flush=True)
+        return
+    if args.op == "copy_blocks":
+        bench_copy_blocks(args, torch, pkv, dev)
         return
     t_setup = time.time()
     wname, kw = WORKLOADS[args.workload]
@@ -301,6 +307,48 @@ def main():
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(case, mat, out, args.cpu_seconds, by, B)
     print(json.dumps(res), flush=True)
+
+
+def bench_copy_blocks(args, torch, pkv, dev):
+    """Copy-on-write block copies alone: `pairs` random disjoint (src, dst) block pairs of a pool
+    shaped like the 70B layer's (H_kv 8, D 128, bs 16, bf16: 32 KiB per block and pool); GB/s
+    counts the bytes read plus the bytes written."""
+    H_kv, D, bs = 8, 128, 16
+    NB = 2 * args.pairs + 64
+    ks, vs = pkv.pool_shapes(NB, H_kv, D, bs, pkv.BF16)
+    k_pool = torch.zeros(ks, dtype=torch.bfloat16, device=dev)
+    v_pool = torch.zeros(vs, dtype=torch.bfloat16, device=dev)
+    perm = torch.from_numpy(np.random.default_rng(5).permutation(NB).astype(np.int32)).to(dev)
+    src, dst = perm[:args.pairs].contiguous(), perm[args.pairs:2 * args.pairs].contiguous()
+    # a small call takes less GPU time than its Python launch, so calls are timed from a
+    # captured graph of R back-to-back copies (per-call time = replay time / R)
+    R = 20
+    for _ in range(3):
+        pkv.copy_blocks(k_pool, v_pool, src, dst)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for _ in range(R):
+            pkv.copy_blocks(k_pool, v_pool, src, dst)
+    for _ in range(args.warmup):
+        graph.replay()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    for e0, e1 in ev:
+        e0.record()
+        graph.replay()
+        e1.record()
+    torch.cuda.synchronize()
+    ms = np.array([e0.elapsed_time(e1) for e0, e1 in ev]) / R
+    block_bytes = 2 * H_kv * D * bs * 2
+    moved = 2 * args.pairs * block_bytes  # read + write
+    avg_s = ms.mean() / 1e3
+    print(json.dumps({
+        "metric": "copy_blocks GB/s (bytes read + written)", "value": round(moved / avg_s / 1e9, 1), "unit": "GB/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(float(ms.mean()), 5),
+        "higher_is_better": True, "dtype": "bf16", "data": "synthetic (zero-filled pools, random disjoint pairs)",
+        "config": {"workload": f"{args.pairs} block copies, 70B-layer block shape (H_kv 8, D 128, bs 16)",
+                   "pairs": args.pairs, "bytes_per_pair_read": block_bytes},
+        "us_p50": round(float(np.median(ms)) * 1e3, 2),
+        "frac_of_hbm_peak": round(moved / avg_s / 1e9 / HBM_PEAK_GBPS, 4)}), flush=True)
 
 
 def cpu_baseline(case, mat, out_dev, budget_s, by, B):

@@ -10,8 +10,9 @@
  * and may be shared by several sequences (a common prefix, a fork).  The
  * attention kernel walks the table.
  *
- * Three groups of calls:
+ * Groups of calls:
  *   pkv_kv_append          scatter this step's K/V rows into their slots
+ *   pkv_copy_blocks        copy whole blocks (copy-on-write of shared blocks)
  *   pkv_paged_attn_decode  one query token per sequence attends over its paged KV
  *   pkv_alloc_* / pkv_seq_* host-side fixed-block free-list allocator
  *
@@ -99,6 +100,25 @@ int pkv_kv_append(const void* k, const void* v, int src_dtype, const int64_t* sl
                   void* stream);
 
 /*
+ * pkv_copy_blocks — for i in 0..n_pairs-1, physical block dst[i] of both pools
+ * becomes a copy of block src[i]: every head, every token slot, bit for bit.
+ * ("Paged Attention and KV Cache Fragmentation", section "How PagedAttention
+ * maps an OS concept onto GPU memory": sharers of a block diverge only where
+ * their content differs; the copy gives a diverging sequence its own block.)
+ * Use it with the pairs pkv_seq_append_slots_cow reports, before the
+ * pkv_kv_append that writes the new tokens, on the same stream.
+ *
+ *   k_pool, v_pool device, layouts above, pool_dtype
+ *   src, dst       device int32 [n_pairs]; a pair with an id outside [0, NB)
+ *                  is skipped (caller error); src == dst is a no-op.  A block
+ *                  that is the dst of one pair and the src or dst of another
+ *                  is a caller error (the pairs run concurrently).
+ *   D must be a multiple of 16 and <= 512; bs in 1..256.
+ */
+int pkv_copy_blocks(void* k_pool, void* v_pool, int pool_dtype, int32_t NB, int32_t bs, int32_t H_kv,
+                    int32_t D, const int32_t* src, const int32_t* dst, int32_t n_pairs, void* stream);
+
+/*
  * pkv_decode_workspace_bytes — size of the scratch buffer pkv_paged_attn_decode
  * needs for these sizes (0 is possible).  The same arguments must be passed to
  * the decode call.  Returns 0 and sets the last error for invalid sizes.
@@ -161,6 +181,13 @@ int pkv_paged_attn_decode(float* out, const void* q, int q_dtype, const void* k_
  *     it is all-or-nothing: on PKV_ERR_OUT_OF_BLOCKS nothing changes;
  *     if L % bs != 0, n > 0 and the last block is shared (refcount > 1)
  *     it fails with PKV_ERR_SHARED_BLOCK and nothing changes;
+ *   - append with copy-on-write (pkv_seq_append_slots_cow) handles that case
+ *     instead: the sequence first takes a fresh block for its last logical
+ *     block (popped before any growth block), the shared block's refcount
+ *     goes down by one, and the pair (shared, fresh) is reported for
+ *     pkv_copy_blocks.  The fresh block counts towards the all-or-nothing
+ *     need.  In every other case it behaves as pkv_seq_append_slots and
+ *     reports no pair;
  *   - fork: the child (a new id) gets the parent's blocks and length, and
  *     each of those blocks' refcount goes up by one;
  *   - free: the sequence's blocks are visited last to first, refcount goes
@@ -175,6 +202,9 @@ int32_t pkv_alloc_num_free(const pkv_allocator* a);
 int pkv_seq_add(pkv_allocator* a, int64_t seq); /* PKV_ERR_INVALID_ARG if seq exists */
 /* slots_out: host int64 [n] (may be NULL when n == 0) receives the new tokens' slots. */
 int pkv_seq_append_slots(pkv_allocator* a, int64_t seq, int32_t n, int64_t* slots_out);
+/* copy_src, copy_dst: host int32 [1] receive the pair, n_copies (host) its count, 0 or 1. */
+int pkv_seq_append_slots_cow(pkv_allocator* a, int64_t seq, int32_t n, int64_t* slots_out,
+                             int32_t* copy_src, int32_t* copy_dst, int32_t* n_copies);
 int pkv_seq_fork(pkv_allocator* a, int64_t parent, int64_t child);
 int pkv_seq_free(pkv_allocator* a, int64_t seq);
 int pkv_seq_len(const pkv_allocator* a, int64_t seq, int32_t* len_out);

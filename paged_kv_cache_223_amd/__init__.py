@@ -45,6 +45,7 @@ SIGNATURES = {
     "pkv_abi_version": (ctypes.c_int, []),
     "pkv_kv_append": (ctypes.c_int, [_P, _P, ctypes.c_int, _P, _I32, _P, _P, ctypes.c_int, _I32, _I32, _I32,
                                      _I32, _P, _P, _P]),
+    "pkv_copy_blocks": (ctypes.c_int, [_P, _P, ctypes.c_int, _I32, _I32, _I32, _I32, _P, _P, _I32, _P]),
     "pkv_decode_workspace_bytes": (_SZ, [_I32, _I32, _I32, _I32, _I32, _I32]),
     "pkv_paged_attn_decode": (ctypes.c_int, [_P, _P, ctypes.c_int, _P, _P, ctypes.c_int, _P, _I32, _P, _I32,
                                              _I32, _I32, _I32, _I32, _I32, _I32, ctypes.c_float, _P, _P, _P,
@@ -54,6 +55,7 @@ SIGNATURES = {
     "pkv_alloc_num_free": (_I32, [_P]),
     "pkv_seq_add": (ctypes.c_int, [_P, _I64]),
     "pkv_seq_append_slots": (ctypes.c_int, [_P, _I64, _I32, _P]),
+    "pkv_seq_append_slots_cow": (ctypes.c_int, [_P, _I64, _I32, _P, _P, _P, _P]),
     "pkv_seq_fork": (ctypes.c_int, [_P, _I64, _I64]),
     "pkv_seq_free": (ctypes.c_int, [_P, _I64]),
     "pkv_seq_len": (ctypes.c_int, [_P, _I64, _P]),
@@ -184,6 +186,19 @@ def kv_append(k, v, slot_mapping, k_pool, v_pool, k_scale=None, v_scale=None):
                              kv, NB, bs, H_kv, D, _ptr(k_scale), _ptr(v_scale), _stream()))
 
 
+def copy_blocks(k_pool, v_pool, src, dst):
+    """Block dst[i] of both pools becomes a copy of block src[i] (int32 device tensors [n])."""
+    torch = _torch()
+    _dev(k_pool, v_pool, src, dst)
+    kv, NB, H_kv, D, bs = _pool_dims(k_pool, v_pool)
+    if src.dtype != torch.int32 or dst.dtype != torch.int32 or src.dim() != 1 or src.shape != dst.shape:
+        raise ValueError("src and dst must be int32 [n] of one length")
+    if not (src.is_contiguous() and dst.is_contiguous()):
+        raise ValueError("src and dst must be contiguous")
+    _check(lib.pkv_copy_blocks(_ptr(k_pool), _ptr(v_pool), kv, NB, bs, H_kv, D, _ptr(src), _ptr(dst),
+                               src.shape[0], _stream()))
+
+
 def decode_workspace_bytes(B: int, H_q: int, H_kv: int, D: int, max_context_len: int, bs: int) -> int:
     return int(lib.pkv_decode_workspace_bytes(B, H_q, H_kv, D, max_context_len, bs))
 
@@ -266,6 +281,7 @@ class Allocator:
 
     def __init__(self, NB: int, bs: int, initial_free_order=None):
         self.NB, self.bs = int(NB), int(bs)
+        self._lib = lib  # kept for __del__, which may run after module globals are cleared
         self._h = ctypes.c_void_p()
         order = None
         if initial_free_order is not None:
@@ -278,7 +294,7 @@ class Allocator:
     def __del__(self):
         h = getattr(self, "_h", None)
         if h:
-            lib.pkv_alloc_destroy(h)
+            self._lib.pkv_alloc_destroy(h)
             self._h = None
 
     def num_free(self) -> int:
@@ -291,6 +307,17 @@ class Allocator:
         out = np.empty(max(int(n), 0), np.int64)
         st = int(lib.pkv_seq_append_slots(self._h, int(seq), int(n), out.ctypes.data if n > 0 else None))
         return st, (out if st == OK else None)
+
+    def append_slots_cow(self, seq, n: int):
+        """(status, slots, copies): copies is a list of (src_block, dst_block) pairs (0 or 1) to run
+        through copy_blocks before the new tokens are appended."""
+        out = np.empty(max(int(n), 0), np.int64)
+        src, dst, cnt = ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int32()
+        st = int(lib.pkv_seq_append_slots_cow(self._h, int(seq), int(n), out.ctypes.data if n > 0 else None,
+                                              ctypes.byref(src), ctypes.byref(dst), ctypes.byref(cnt)))
+        if st != OK:
+            return st, None, None
+        return st, out, ([(src.value, dst.value)] if cnt.value else [])
 
     def fork(self, parent, child) -> int:
         return int(lib.pkv_seq_fork(self._h, int(parent), int(child)))
@@ -315,7 +342,8 @@ class Allocator:
         return int(lib.pkv_block_refcount(self._h, int(block)))
 
 
-__all__ = ["lib", "LIB_PATH", "PkvError", "last_error", "kv_append", "paged_attn_decode", "decode_workspace_bytes",
+__all__ = ["lib", "LIB_PATH", "PkvError", "last_error", "kv_append", "copy_blocks", "paged_attn_decode",
+           "decode_workspace_bytes",
            "decode_workspace",
            "pool_shapes", "dtype_code", "stream_read", "copy_", "Allocator", "SIGNATURES",
            "F32", "BF16", "FP8_E4M3"]

@@ -8,7 +8,8 @@
 // branches, point at the same physical blocks.  "KV Cache Fragmentation"
 // field guide (defragging.ai), section "Why it matters": sharing makes forks
 // cheap.  Exact semantics (LIFO order, all-or-nothing appends, the shared
-// partial-block rule, reverse-order frees) are spelled out in pkv.h.
+// partial-block rule, copy-on-write appends, reverse-order frees) are spelled
+// out in pkv.h.
 
 #include <stdint.h>
 
@@ -79,7 +80,11 @@ int pkv_seq_add(pkv_allocator* a, int64_t seq) {
   return PKV_OK;
 }
 
-int pkv_seq_append_slots(pkv_allocator* a, int64_t seq, int32_t n, int64_t* slots_out) {
+// Shared body of the two appends.  With `cow`, a shared partly filled last
+// block is replaced by a fresh one (popped before the growth blocks) and the
+// pair (old, new) is reported; without it, that case is refused.
+static int append_impl(pkv_allocator* a, int64_t seq, int32_t n, int64_t* slots_out, bool cow,
+                       int32_t* copy_src, int32_t* copy_dst, int32_t* n_copies) {
   if (!a) return PKV_ERR_INVALID_ARG;
   auto it = a->seqs.find(seq);
   if (it == a->seqs.end()) {
@@ -96,16 +101,29 @@ int pkv_seq_append_slots(pkv_allocator* a, int64_t seq, int32_t n, int64_t* slot
     set_error("append_slots: length would exceed 2^31-1");
     return PKV_ERR_INVALID_ARG;
   }
-  if (n > 0 && L % bs != 0 && a->rc[s.blocks.back()] > 1) {
+  const bool shared_tail = n > 0 && L % bs != 0 && a->rc[s.blocks.back()] > 1;
+  if (shared_tail && !cow) {
     set_error("append_slots: sequence %lld would grow into shared block %d", (long long)seq, s.blocks.back());
     return PKV_ERR_SHARED_BLOCK;
   }
-  const int64_t need = ceil_div(L + n, bs) - ceil_div(L, bs);
+  const int64_t need = ceil_div(L + n, bs) - ceil_div(L, bs) + (shared_tail ? 1 : 0);
   if (need > (int64_t)a->stack.size()) {
     set_error("append_slots: need %lld blocks, %zu free", (long long)need, a->stack.size());
     return PKV_ERR_OUT_OF_BLOCKS;
   }
-  for (int64_t i = 0; i < need; ++i) {
+  if (cow) *n_copies = 0;
+  if (shared_tail) {
+    const int32_t old = s.blocks.back(), fresh = a->stack.back();
+    a->stack.pop_back();
+    a->rc[old] -= 1;
+    a->rc[fresh] = 1;
+    s.blocks.back() = fresh;
+    copy_src[0] = old;
+    copy_dst[0] = fresh;
+    *n_copies = 1;
+  }
+  const int64_t grow = need - (shared_tail ? 1 : 0);
+  for (int64_t i = 0; i < grow; ++i) {
     const int32_t b = a->stack.back();
     a->stack.pop_back();
     a->rc[b] = 1;
@@ -114,6 +132,19 @@ int pkv_seq_append_slots(pkv_allocator* a, int64_t seq, int32_t n, int64_t* slot
   for (int64_t p = L; p < L + n; ++p) slots_out[p - L] = (int64_t)s.blocks[p / bs] * bs + p % bs;
   s.len = L + n;
   return PKV_OK;
+}
+
+int pkv_seq_append_slots(pkv_allocator* a, int64_t seq, int32_t n, int64_t* slots_out) {
+  return append_impl(a, seq, n, slots_out, false, nullptr, nullptr, nullptr);
+}
+
+int pkv_seq_append_slots_cow(pkv_allocator* a, int64_t seq, int32_t n, int64_t* slots_out, int32_t* copy_src,
+                             int32_t* copy_dst, int32_t* n_copies) {
+  if (!copy_src || !copy_dst || !n_copies) {
+    set_error("append_slots_cow: null copy output");
+    return PKV_ERR_INVALID_ARG;
+  }
+  return append_impl(a, seq, n, slots_out, true, copy_src, copy_dst, n_copies);
 }
 
 int pkv_seq_fork(pkv_allocator* a, int64_t parent, int64_t child) {

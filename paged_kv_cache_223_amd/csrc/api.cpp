@@ -89,6 +89,43 @@ int pkv_kv_append(const void* k, const void* v, int src_dtype, const int64_t* sl
   return hip_status(launch_kv_append(a, (hipStream_t)stream), "kv_append launch");
 }
 
+int pkv_copy_blocks(void* k_pool, void* v_pool, int pool_dtype, int32_t NB, int32_t bs, int32_t H_kv, int32_t D,
+                    const int32_t* src, const int32_t* dst, int32_t n_pairs, void* stream) {
+  g_err[0] = 0;
+  if (n_pairs < 0 || NB <= 0 || bs <= 0 || bs > 256 || H_kv <= 0 || D <= 0) {
+    set_error("copy_blocks: bad sizes n_pairs=%d NB=%d bs=%d H_kv=%d D=%d", n_pairs, NB, bs, H_kv, D);
+    return PKV_ERR_INVALID_ARG;
+  }
+  if (!valid_dtype(pool_dtype)) {
+    set_error("copy_blocks: unknown dtype %d", pool_dtype);
+    return PKV_ERR_INVALID_ARG;
+  }
+  if (D % 16 != 0 || D > 512) {
+    set_error("copy_blocks: D=%d must be a multiple of 16 and <= 512", D);
+    return PKV_ERR_UNSUPPORTED;
+  }
+  if (n_pairs == 0) return PKV_OK;
+  if (!k_pool || !v_pool || !src || !dst) {
+    set_error("copy_blocks: null pointer");
+    return PKV_ERR_INVALID_ARG;
+  }
+  const int elem = pool_dtype == PKV_F32 ? 4 : pool_dtype == PKV_BF16 ? 2 : 1;
+  CopyBlocksArgs a{};
+  a.k_pool = k_pool;
+  a.v_pool = v_pool;
+  a.src = src;
+  a.dst = dst;
+  a.n_pairs = n_pairs;
+  a.NB = NB;
+  a.block_units = (long long)H_kv * D * bs * elem / 16;
+  a.tiles = (a.block_units + kCopyThreads * kCopyUnroll - 1) / (kCopyThreads * kCopyUnroll);
+  if ((long long)n_pairs * 2 * a.tiles > 0x7FFFFFFFLL) {
+    set_error("copy_blocks: too many pairs for one launch");
+    return PKV_ERR_INVALID_ARG;
+  }
+  return hip_status(launch_copy_blocks(a, (hipStream_t)stream), "copy_blocks launch");
+}
+
 size_t pkv_decode_workspace_bytes(int32_t B, int32_t H_q, int32_t H_kv, int32_t D, int32_t max_context_len,
                                   int32_t bs) {
   g_err[0] = 0;

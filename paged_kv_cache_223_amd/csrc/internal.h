@@ -113,6 +113,21 @@ struct AppendArgs {
 };
 hipError_t launch_kv_append(const AppendArgs& a, hipStream_t s);
 
+// whole-block copies of both pools (copy-on-write)
+struct CopyBlocksArgs {
+  void* k_pool;
+  void* v_pool;
+  const int32_t* src;  // device [n_pairs]
+  const int32_t* dst;  // device [n_pairs]
+  int32_t n_pairs;
+  int32_t NB;
+  long long block_units;  // 16-byte units per block of one pool (H_kv * D * bs * elem / 16)
+  long long tiles;        // copy tiles per block of one pool
+};
+constexpr int kCopyThreads = 256;
+constexpr int kCopyUnroll = 4;
+hipError_t launch_copy_blocks(const CopyBlocksArgs& a, hipStream_t s);
+
 // stream.hip
 size_t stream_read_blocks(size_t bytes);
 hipError_t launch_stream_read(const void* src, size_t bytes, float* sink, hipStream_t s);

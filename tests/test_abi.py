@@ -114,3 +114,39 @@ def test_append_rejects_bad_arguments_before_launch(kw, status):
 
 def test_append_zero_tokens_is_a_no_op():
     assert _append(T=0, k=None, v=None, slots=None) == pkv.OK
+
+
+def _copy_blocks(**kw):
+    a = dict(kp=P, vp=P, pool=pkv.BF16, NB=8, bs=16, H=2, D=128, src=P, dst=P, n=3, stream=None)
+    a.update(kw)
+    return pkv.lib.pkv_copy_blocks(a["kp"], a["vp"], a["pool"], a["NB"], a["bs"], a["H"], a["D"], a["src"],
+                                   a["dst"], a["n"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(n=-1), pkv.ERR_INVALID_ARG),
+    (dict(NB=0), pkv.ERR_INVALID_ARG),
+    (dict(bs=300), pkv.ERR_INVALID_ARG),
+    (dict(pool=5), pkv.ERR_INVALID_ARG),
+    (dict(D=40), pkv.ERR_UNSUPPORTED),
+    (dict(src=None), pkv.ERR_INVALID_ARG),
+    (dict(vp=None), pkv.ERR_INVALID_ARG),
+])
+def test_copy_blocks_rejects_bad_arguments_before_launch(kw, status):
+    assert _copy_blocks(**kw) == status
+    assert pkv.last_error()
+
+
+def test_copy_blocks_zero_pairs_is_a_no_op():
+    assert _copy_blocks(n=0, src=None, dst=None) == pkv.OK
+
+
+def test_cow_append_needs_its_copy_outputs():
+    a = pkv.Allocator(4, 4)
+    a.seq_add(0)
+    out = (ctypes.c_int64 * 2)()
+    c = ctypes.c_int32()
+    assert pkv.lib.pkv_seq_append_slots_cow(a._h, 0, 2, out, None, ctypes.byref(c), ctypes.byref(c)) == \
+        pkv.ERR_INVALID_ARG
+    assert pkv.lib.pkv_seq_append_slots_cow(a._h, 7, 2, out, ctypes.byref(c), ctypes.byref(c), ctypes.byref(c)) == \
+        pkv.ERR_UNKNOWN_SEQ

@@ -57,6 +57,54 @@ def test_random_ops_identical_to_model(seed):
     _same_state(cpp, model, live)
 
 
+@pytest.mark.parametrize("seed", range(4))
+def test_random_cow_ops_identical_to_model(seed):
+    """Beam-like scripts: many forks of partly filled sequences, copy-on-write appends mixed with
+    plain ones (which must still refuse a shared partial block), frees."""
+    rng = np.random.default_rng(300 + seed)
+    NB, bs = [96, 40, 200, 31][seed], [16, 3, 8, 1][seed]
+    cpp, model = _pair(NB, bs, rng.permutation(NB))
+    live, nid, copies_seen = [], 0, 0
+    for step in range(3000):
+        r = rng.random()
+        if r < 0.15 or not live:
+            assert cpp.seq_add(nid) == model.seq_add(nid) == 0
+            live.append(nid)
+            nid += 1
+        elif r < 0.55:
+            s = live[rng.integers(len(live))]
+            n = int(rng.integers(0, 2 * bs + 2))
+            st1, sl1, c1 = cpp.append_slots_cow(s, n)
+            st2, sl2, c2 = model.append_slots_cow(s, n)
+            assert st1 == st2
+            if st1 == 0:
+                assert list(sl1) == list(sl2) and c1 == c2
+                copies_seen += len(c1)
+        elif r < 0.65:
+            s = live[rng.integers(len(live))]
+            n = int(rng.integers(0, 2 * bs + 2))
+            st1, sl1 = cpp.append_slots(s, n)
+            st2, sl2 = model.append_slots(s, n)
+            assert st1 == st2
+            if st1 == 0:
+                assert list(sl1) == list(sl2)
+        elif r < 0.85:
+            s = live[rng.integers(len(live))]
+            assert cpp.fork(s, nid) == model.fork(s, nid) == 0
+            live.append(nid)
+            nid += 1
+        else:
+            s = live.pop(rng.integers(len(live)))
+            assert cpp.free(s) == model.free(s) == 0
+        if step % 53 == 0:
+            _same_state(cpp, model, live)
+    _same_state(cpp, model, live)
+    if bs == 1:
+        assert copies_seen == 0  # a 1-token block is never partly filled
+    else:
+        assert copies_seen >= 3
+
+
 @pytest.mark.parametrize("builder", [
     lambda: workloads.tiny_f32(),
     lambda: workloads.llama8b_bf16(),

@@ -1,0 +1,135 @@
+"""Copy-on-write on the GPU: pkv_copy_blocks is bit-exact against the oracle's block copy, and a
+beam-search script run through the product (C++ allocator with copy-on-write appends,
+copy_blocks, kv_append, decode) gives the oracle's tables, pools (bit for bit) and decode
+outputs (within the decode tolerance).
+
+"Paged Attention and KV Cache Fragmentation", section "How PagedAttention maps an OS concept
+onto GPU memory": beam-search branches point at the same physical blocks and diverge only
+where their content differs."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import paged_kv_cache_223_amd as pkv
+import workloads
+from tests.gpu_helpers import DEV, from_dev, to_dev
+from tests.oracle_cases import row_rel_err
+
+pytestmark = pytest.mark.gpu
+
+KVD = {"f32": pkv.F32, "bf16": pkv.BF16, "e4m3": pkv.FP8_E4M3}
+
+
+def _ids(pairs):
+    src = torch.tensor([p[0] for p in pairs], dtype=torch.int32, device=DEV)
+    dst = torch.tensor([p[1] for p in pairs], dtype=torch.int32, device=DEV)
+    return src, dst
+
+
+@pytest.mark.parametrize("dtype,bs,H,D", [("f32", 16, 2, 64), ("bf16", 16, 8, 128), ("bf16", 32, 4, 128),
+                                          ("e4m3", 8, 8, 128), ("e4m3", 32, 3, 64)])
+def test_copy_blocks_bit_exact(dtype, bs, H, D):
+    print(f"copy_blocks {dtype} bs={bs} H={H} D={D}", flush=True)
+    rng = np.random.default_rng(11)
+    NB = 40
+    kp, vp = oracle.empty_pools(NB, H, D, bs, dtype)
+    bits = {"f32": np.uint32, "bf16": np.uint16, "e4m3": np.uint8}[dtype]
+    kp[:] = rng.integers(0, np.iinfo(bits).max, kp.shape, dtype=bits, endpoint=True).view(kp.dtype)
+    vp[:] = rng.integers(0, np.iinfo(bits).max, vp.shape, dtype=bits, endpoint=True).view(vp.dtype)
+    perm = rng.permutation(NB)
+    pairs = [(int(perm[i]), int(perm[20 + i])) for i in range(12)]  # sources and targets disjoint
+    k_dev, v_dev = to_dev(kp, dtype), to_dev(vp, dtype)
+    src, dst = _ids(pairs + [(NB + 5, int(perm[35])), (int(perm[36]), -1), (int(perm[37]), int(perm[37]))])
+    pkv.copy_blocks(k_dev, v_dev, src, dst)  # the last three pairs are skipped / no-ops
+    torch.cuda.synchronize()
+    ek, ev = oracle.ref_copy_blocks(kp, vp, pairs)
+    assert np.array_equal(from_dev(k_dev).view(bits), ek.view(bits))
+    assert np.array_equal(from_dev(v_dev).view(bits), ev.view(bits))
+
+
+def _nan_pools(NB, H, D, bs, dtype):
+    kp, vp = oracle.empty_pools(NB, H, D, bs, dtype)
+    if dtype == "e4m3":
+        kp[:] = 0x7F
+        vp[:] = 0x7F
+    else:
+        kp[:] = 0x7FC0  # bf16 NaN
+        vp[:] = 0x7FC0
+    return kp, vp
+
+
+def _replay_oracle(sc):
+    m = oracle.AllocModel(sc.NB, sc.bs)
+    kp, vp = _nan_pools(sc.NB, sc.H_kv, sc.d, sc.bs, sc.kv_dtype)
+    outs, n_copies = [], 0
+    for op in sc.ops:
+        if op[0] == "add":
+            assert m.seq_add(op[1]) == 0
+        elif op[0] == "fork":
+            assert m.fork(op[1], op[2]) == 0
+        elif op[0] == "free":
+            assert m.free(op[1]) == 0
+        elif op[0] == "append":
+            st, slots, copies = m.append_slots_cow(op[1], len(sc.rows[op[2]][0]))
+            assert st == 0
+            n_copies += len(copies)
+            kp, vp = oracle.ref_copy_blocks(kp, vp, copies)
+            k, v = sc.rows[op[2]]
+            kp, vp = oracle.ref_append(kp, vp, k, v, "bf16", slots, sc.bs, sc.kv_dtype, sc.k_scale, sc.v_scale)
+        else:
+            sids, qi = op[1], op[2]
+            mb = max(len(m.blocks[s]) for s in sids)
+            st, tab, lens = m.block_tables(sids, mb)
+            o = oracle.ref_decode(sc.qs[qi], "bf16", kp, vp, sc.kv_dtype, tab, lens, sc.scale, sc.bs,
+                                  sc.k_scale, sc.v_scale)
+            outs.append((tab, lens, o))
+    return kp, vp, outs, n_copies
+
+
+def _replay_gpu(sc):
+    a = pkv.Allocator(sc.NB, sc.bs)
+    kp0, vp0 = _nan_pools(sc.NB, sc.H_kv, sc.d, sc.bs, sc.kv_dtype)
+    kp, vp = to_dev(kp0, sc.kv_dtype), to_dev(vp0, sc.kv_dtype)
+    ks = None if sc.k_scale is None else torch.from_numpy(sc.k_scale).to(DEV)
+    vs = None if sc.v_scale is None else torch.from_numpy(sc.v_scale).to(DEV)
+    outs = []
+    for op in sc.ops:
+        if op[0] == "add":
+            assert a.seq_add(op[1]) == 0
+        elif op[0] == "fork":
+            assert a.fork(op[1], op[2]) == 0
+        elif op[0] == "free":
+            assert a.free(op[1]) == 0
+        elif op[0] == "append":
+            k, v = sc.rows[op[2]]
+            st, slots, copies = a.append_slots_cow(op[1], len(k))
+            assert st == 0
+            if copies:
+                pkv.copy_blocks(kp, vp, *_ids(copies))
+            pkv.kv_append(to_dev(k, "bf16"), to_dev(v, "bf16"), torch.from_numpy(slots).to(DEV), kp, vp, ks, vs)
+        else:
+            sids, qi = op[1], op[2]
+            mb = max(int(np.ceil(a.seq_len(s)[1] / sc.bs)) for s in sids)
+            st, tab, lens = a.block_tables(sids, mb)
+            assert st == 0
+            out = pkv.paged_attn_decode(to_dev(sc.qs[qi], "bf16"), kp, vp, torch.from_numpy(tab).to(DEV),
+                                        torch.from_numpy(lens).to(DEV), sc.scale, int(lens.max()), ks, vs)
+            outs.append((tab, lens, out.cpu().numpy().astype(np.float64)))
+    torch.cuda.synchronize()
+    return from_dev(kp), from_dev(vp), outs
+
+
+@pytest.mark.parametrize("bs,kv_dtype", [(8, "bf16"), (16, "bf16"), (32, "bf16"), (16, "e4m3"), (32, "e4m3")])
+def test_beam_search_copy_on_write_matches_oracle(bs, kv_dtype):
+    sc = workloads.beam_search(bs=bs, kv_dtype=kv_dtype)
+    print(f"beam search {sc.name}: {len(sc.ops)} ops, NB={sc.NB}", flush=True)
+    ek, ev, eouts, n_copies = _replay_oracle(sc)
+    assert n_copies >= 6  # the script really exercises copy-on-write
+    gk, gv, gouts = _replay_gpu(sc)
+    assert np.array_equal(gk, ek) and np.array_equal(gv, ev)  # every block, every slot, bit for bit
+    bound = 2e-2 if kv_dtype == "e4m3" else 2e-3
+    for (et, el, eo), (gt, gl, go) in zip(eouts, gouts):
+        assert np.array_equal(et, gt) and np.array_equal(el, gl)
+        assert np.isfinite(go).all()
+        assert row_rel_err(go, eo) <= bound

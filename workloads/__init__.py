@@ -306,6 +306,86 @@ def custom(name, B, H_q, H_kv, d, bs, kv_dtype, q_dtype, lens, seed, fill="noise
     return case
 
 
+@dataclass
+class BeamScript:
+    """A seeded beam-search allocation script plus the rows every append writes.
+
+    ops: ("add", sid) | ("append", sid, rows_index) | ("fork", parent, child) | ("free", sid)
+         | ("decode", sids, q_index).  An append is meant to run as a copy-on-write append:
+    allocator append with copy-on-write, then the reported block copies, then the scatter of
+    rows[rows_index] into the returned slots."""
+    name: str
+    H_q: int
+    H_kv: int
+    d: int
+    bs: int
+    kv_dtype: str
+    NB: int
+    scale: float
+    ops: list
+    rows: list          # (k bf16 bits [n, H_kv, d], v bf16 bits [n, H_kv, d])
+    qs: list            # bf16 bits [len(sids), H_q, d]
+    k_scale: np.ndarray = None
+    v_scale: np.ndarray = None
+
+
+def beam_search(seed=1006, bs=16, prompts=3, width=4, steps=6, prompt_lo=17, prompt_hi=300, H_q=8, H_kv=2, d=128,
+                kv_dtype="bf16", reselect=0.35):
+    """Beam-search-shaped sharing ("KV Cache Fragmentation" field guide, section "Why it
+    matters": cheap forks for beam search; "Paged Attention and KV Cache Fragmentation",
+    section "How PagedAttention maps an OS concept onto GPU memory": branches share blocks
+    until they diverge).  Each prompt is prefilled once and forked into `width` beams; every
+    step appends one token to every beam; with probability `reselect` per prompt and step a
+    random beam is dropped and a random survivor is forked in its place, so partly filled
+    blocks keep being shared and copied on write.  All beams are decoded after every step."""
+    rng = _rng(seed, 0)
+    data = _rng(seed, 1)
+    ops, rows, qs = [], [], []
+    sid = 0
+
+    def new_rows(n):
+        k = round_bf16(data.standard_normal((n, H_kv, d), dtype=np.float32))
+        v = round_bf16(data.standard_normal((n, H_kv, d), dtype=np.float32))
+        rows.append((k, v))
+        return len(rows) - 1
+
+    beams = []
+    for _ in range(prompts):
+        n = int(rng.integers(prompt_lo, prompt_hi + 1))
+        ops.append(("add", sid))
+        ops.append(("append", sid, new_rows(n)))
+        group = [sid]
+        sid += 1
+        for _ in range(width - 1):
+            ops.append(("fork", group[0], sid))
+            group.append(sid)
+            sid += 1
+        beams.append(group)
+    for _ in range(steps):
+        for group in beams:
+            for b in group:
+                ops.append(("append", b, new_rows(1)))
+            if rng.random() < reselect and len(group) > 1:
+                drop = group.pop(int(rng.integers(len(group))))
+                ops.append(("free", drop))
+                parent = group[int(rng.integers(len(group)))]
+                ops.append(("fork", parent, sid))
+                group.append(sid)
+                sid += 1
+        live = [b for g in beams for b in g]
+        qs.append(round_bf16(data.standard_normal((len(live), H_q, d), dtype=np.float32)))
+        ops.append(("decode", live, len(qs) - 1))
+    NB = prompts * width * (-(-(prompt_hi + steps) // bs) + 2)
+    script = BeamScript(f"beam_search_bs{bs}_{kv_dtype}", H_q, H_kv, d, bs, kv_dtype, NB,
+                        float(np.float32(1.0 / math.sqrt(d))), ops, rows, qs)
+    if kv_dtype == "e4m3":
+        amax_k = np.max([np.abs(bf16_bits_as_f32(k)).max(axis=(0, 2)) for k, _ in rows], axis=0)
+        amax_v = np.max([np.abs(bf16_bits_as_f32(v)).max(axis=(0, 2)) for _, v in rows], axis=0)
+        script.k_scale = (np.maximum(amax_k, np.float32(1e-3)) / np.float32(448.0)).astype(np.float32)
+        script.v_scale = (np.maximum(amax_v, np.float32(1e-3)) / np.float32(448.0)).astype(np.float32)
+    return script
+
+
 BUILDERS = {
     "tiny_f32": tiny_f32,
     "llama8b_bf16": llama8b_bf16,
