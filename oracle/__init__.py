@@ -8,8 +8,8 @@ with it; the two meet only in the seeded input generators of `workloads`.
 
 Modules
   formats     bf16 and OCP FP8 E4M3FN decoding/encoding from the formats' definitions
-  paged       the pool layout, the slot scatter (kv_append), the copy-on-write block copy and
-              gather-then-attend decode
+  paged       the pool layout, the slot scatter (kv_append), the copy-on-write block copy, the
+              swap gather/scatter of whole blocks and gather-then-attend decode
   brute       a second, pure-Python decode for tiny cases (no max subtraction, fsum)
   alloc_model the fixed-block free-list allocator with refcounted shared blocks
   footprint   KV byte arithmetic and allocation-waste accounting
@@ -20,7 +20,8 @@ test modules named test_oracle_*); none is "parity unpinned".
 from .formats import (bf16_bits_to_f64, e4m3_decode_table, e4m3_decode, e4m3_encode,
                       E4M3_MAX)
 from .paged import (pool_shapes, lanes_per_16b, ref_append, ref_decode, gather_sequence,
-                    empty_pools, ref_copy_blocks)
+                    empty_pools, ref_copy_blocks, ref_gather_blocks,
+                    ref_scatter_blocks)
 from .brute import brute_decode
 from .alloc_model import AllocModel, Status
 from .footprint import (bytes_per_token, request_bytes, memory_bill, kv_bytes_logical,
@@ -29,7 +30,7 @@ from .footprint import (bytes_per_token, request_bytes, memory_bill, kv_bytes_lo
 __all__ = [
     "bf16_bits_to_f64", "e4m3_decode_table", "e4m3_decode", "e4m3_encode", "E4M3_MAX",
     "pool_shapes", "lanes_per_16b", "ref_append", "ref_decode", "gather_sequence", "empty_pools",
-    "ref_copy_blocks",
+    "ref_copy_blocks", "ref_gather_blocks", "ref_scatter_blocks",
     "brute_decode", "AllocModel", "Status",
     "bytes_per_token", "request_bytes", "memory_bill", "kv_bytes_logical", "kv_bytes_unique",
     "paged_waste", "contiguous_waste",

@@ -31,6 +31,15 @@ before any growth block), the old block loses one reference, and the pair
 (old, new) is returned so that the caller copies the block's contents before
 writing the new tokens.  The fresh block counts towards the all-or-nothing
 block need.
+
+Swap (PA, section "Offloading paged KV blocks to CPU DRAM and NVMe": blocks of
+a sequence that is not running move to host memory and come back later).
+`swap_out` returns the sequence's blocks in logical order (the caller saves
+their contents) and releases them as `free` does, but keeps the sequence and
+its length; a swapped-out sequence holds no blocks and cannot grow, fork or
+appear in a block table.  `swap_in` takes ceil(len / bs) fresh blocks,
+all-or-nothing, popped in logical order, and returns them (the caller restores
+the contents into them).
 """
 from __future__ import annotations
 
@@ -62,6 +71,7 @@ class AllocModel:
         self.rc = [0] * NB
         self.blocks = {}
         self.lens = {}
+        self.swapped = set()
 
     def num_free(self) -> int:
         return len(self.stack)
@@ -76,7 +86,7 @@ class AllocModel:
     def append_slots(self, seq, n):
         if seq not in self.blocks:
             return Status.UNKNOWN_SEQ, None
-        if n < 0:
+        if n < 0 or seq in self.swapped:
             return Status.INVALID_ARG, None
         blocks, L, bs = self.blocks[seq], self.lens[seq], self.bs
         if n > 0 and L % bs != 0 and self.rc[blocks[-1]] > 1:
@@ -96,7 +106,7 @@ class AllocModel:
         """(status, slots, copies): copies is a list of (src_block, dst_block) pairs (0 or 1)."""
         if seq not in self.blocks:
             return Status.UNKNOWN_SEQ, None, None
-        if n < 0:
+        if n < 0 or seq in self.swapped:
             return Status.INVALID_ARG, None, None
         blocks, L, bs = self.blocks[seq], self.lens[seq], self.bs
         cow = n > 0 and L % bs != 0 and self.rc[blocks[-1]] > 1
@@ -117,7 +127,7 @@ class AllocModel:
     def fork(self, parent, child) -> int:
         if parent not in self.blocks:
             return Status.UNKNOWN_SEQ
-        if child in self.blocks:
+        if child in self.blocks or parent in self.swapped:
             return Status.INVALID_ARG
         self.blocks[child] = list(self.blocks[parent])
         self.lens[child] = self.lens[parent]
@@ -134,7 +144,41 @@ class AllocModel:
                 self.stack.append(blk)
         del self.blocks[seq]
         del self.lens[seq]
+        self.swapped.discard(seq)
         return Status.OK
+
+    def swap_out(self, seq):
+        """(status, blocks): the sequence's blocks in logical order, then released."""
+        if seq not in self.blocks:
+            return Status.UNKNOWN_SEQ, None
+        if seq in self.swapped:
+            return Status.INVALID_ARG, None
+        blocks = list(self.blocks[seq])
+        for blk in reversed(blocks):
+            self.rc[blk] -= 1
+            if self.rc[blk] == 0:
+                self.stack.append(blk)
+        self.blocks[seq] = []
+        self.swapped.add(seq)
+        return Status.OK, blocks
+
+    def swap_in(self, seq):
+        """(status, blocks): fresh blocks for the whole sequence, in logical order."""
+        if seq not in self.blocks:
+            return Status.UNKNOWN_SEQ, None
+        if seq not in self.swapped:
+            return Status.INVALID_ARG, None
+        need = _ceil_div(self.lens[seq], self.bs)
+        if need > len(self.stack):
+            return Status.OUT_OF_BLOCKS, None
+        blocks = []
+        for _ in range(need):
+            blk = self.stack.pop()
+            self.rc[blk] = 1
+            blocks.append(blk)
+        self.blocks[seq] = blocks
+        self.swapped.discard(seq)
+        return Status.OK, list(blocks)
 
     def seq_len(self, seq):
         if seq not in self.blocks:
@@ -148,6 +192,8 @@ class AllocModel:
         for i, s in enumerate(seqs):
             if s not in self.blocks:
                 return Status.UNKNOWN_SEQ, None, None
+            if s in self.swapped:
+                return Status.INVALID_ARG, None, None
             blocks = self.blocks[s]
             if len(blocks) > max_blocks:
                 return Status.INVALID_ARG, None, None

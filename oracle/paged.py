@@ -168,3 +168,29 @@ def ref_copy_blocks(k_pool, v_pool, pairs):
         v[dst] = v[src]
     return k, v
 
+
+def ref_gather_blocks(k_pool, v_pool, blocks):
+    """Swap-out staging: record i of the result holds physical block blocks[i] as raw bytes,
+    its K tile of every head followed by its V tile of every head ([n, 2, block bytes], uint8).
+
+    "Paged Attention and KV Cache Fragmentation", section "Offloading paged KV blocks to CPU
+    DRAM and NVMe": blocks move between HBM and host memory, and the scattered paged layout
+    turns that into many small transfers; gathering the blocks into one contiguous buffer
+    makes it one large transfer."""
+    ids = np.asarray(blocks, np.int64)
+    nbytes = k_pool[0].nbytes  # one block of one pool (K and V blocks have the same size)
+    kb = np.ascontiguousarray(k_pool[ids]).view(np.uint8).reshape(len(ids), nbytes)
+    vb = np.ascontiguousarray(v_pool[ids]).view(np.uint8).reshape(len(ids), nbytes)
+    return np.stack([kb, vb], axis=1)
+
+
+def ref_scatter_blocks(k_pool, v_pool, blocks, staging):
+    """Swap-in: physical block blocks[i] of both pools takes the bytes of record i of a staging
+    buffer laid out as ref_gather_blocks makes it.  Returns new pools; inputs unchanged."""
+    k, v = np.array(k_pool, copy=True), np.array(v_pool, copy=True)
+    st = np.asarray(staging, np.uint8)
+    for i, b in enumerate(np.asarray(blocks, np.int64)):
+        k[b] = st[i, 0].view(k.dtype).reshape(k.shape[1:])
+        v[b] = st[i, 1].view(v.dtype).reshape(v.shape[1:])
+    return k, v
+

@@ -16,9 +16,10 @@ def _check_invariants(m: AllocModel):
     live = {b for b in range(m.NB) if m.rc[b] > 0}
     assert m.num_free() + len(live) == m.NB
     assert len(set(m.stack)) == len(m.stack) and not (set(m.stack) & live)
-    assert sum(_ceil(m.lens[s], m.bs) for s in m.blocks) == sum(m.rc)
+    swapped = getattr(m, "swapped", set())  # swapped-out sequences keep their length, hold no blocks
+    assert sum(_ceil(m.lens[s], m.bs) for s in m.blocks if s not in swapped) == sum(m.rc)
     for s, blocks in m.blocks.items():
-        assert len(blocks) == _ceil(m.lens[s], m.bs)
+        assert len(blocks) == (0 if s in swapped else _ceil(m.lens[s], m.bs))
     # refcount = number of sequences holding the block
     held = {}
     for blocks in m.blocks.values():
