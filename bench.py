@@ -58,8 +58,10 @@ def parse():
                    help="launch the step's kernels one by one instead of replaying a captured HIP graph")
     p.add_argument("--identity-tables", action="store_true",
                    help="lay every sequence out contiguously (identity block order) instead of scattered")
-    p.add_argument("--op", default="step", choices=["step", "copy_blocks"],
-                   help="step: the decode step (default); copy_blocks: copy-on-write block copies alone")
+    p.add_argument("--op", default="step", choices=["step", "copy_blocks", "swap"],
+                   help="step: the decode step (default); copy_blocks: copy-on-write block copies alone; "
+                        "swap: swap-out / swap-in of scattered blocks to and from pinned host memory")
+    p.add_argument("--blocks", type=int, default=4096, help="blocks moved per swap call (--op swap)")
     p.add_argument("--pairs", type=int, default=4096, help="block pairs per copy_blocks call (--op copy_blocks)")
     p.add_argument("--sets", type=int, default=0,
                    help="independent copies of the inputs the steps rotate through (0 = enough for 1 GB of "
@@ -143,6 +145,9 @@ def main():
         return
     if args.op == "copy_blocks":
         bench_copy_blocks(args, torch, pkv, dev)
+        return
+    if args.op == "swap":
+        bench_swap(args, torch, pkv, dev)
         return
     t_setup = time.time()
     wname, kw = WORKLOADS[args.workload]
@@ -349,6 +354,74 @@ def bench_copy_blocks(args, torch, pkv, dev):
                    "pairs": args.pairs, "bytes_per_pair_read": block_bytes},
         "us_p50": round(float(np.median(ms)) * 1e3, 2),
         "frac_of_hbm_peak": round(moved / avg_s / 1e9 / HBM_PEAK_GBPS, 4)}), flush=True)
+
+
+def bench_swap(args, torch, pkv, dev):
+    """Swap-out / swap-in of `blocks` scattered blocks of a pool shaped like the 70B layer's
+    (H_kv 8, D 128, bs 16, bf16: a 64 KiB K+V record per block), five ways:
+      gather_device   gather into a device staging buffer (HBM to HBM)
+      gather_pinned   gather straight into pinned host memory (the kernel writes over the link)
+      gather_memcpy   gather into device staging, then one DMA copy to pinned host memory
+      per_block_dma   the naive swap-out: one DMA copy per K and per V block (2 x blocks copies)
+      scatter_pinned  swap-in: scatter straight from pinned host memory into the blocks
+    GB/s counts the record bytes moved once (blocks x 64 KiB)."""
+    H_kv, D, bs = 8, 128, 16
+    n = args.blocks
+    NB = 2 * n + 64
+    ks, vs = pkv.pool_shapes(NB, H_kv, D, bs, pkv.BF16)
+    k_pool = torch.randn(ks, device=dev).to(torch.bfloat16)
+    v_pool = torch.randn(vs, device=dev).to(torch.bfloat16)
+    perm = np.random.default_rng(9).permutation(NB).astype(np.int32)
+    ids = torch.from_numpy(perm[:n].copy()).to(dev)
+    rec = pkv.lib.pkv_block_record_bytes(pkv.BF16, bs, H_kv, D)
+    st_dev = torch.empty((n, 2, rec // 2), dtype=torch.uint8, device=dev)
+    st_host = torch.empty((n, 2, rec // 2), dtype=torch.uint8, pin_memory=True)
+    host_k = torch.empty((n,) + tuple(ks[1:]), dtype=torch.bfloat16, pin_memory=True)
+    host_v = torch.empty((n,) + tuple(vs[1:]), dtype=torch.bfloat16, pin_memory=True)
+    ids_host = perm[:n].tolist()
+
+    def per_block_dma():
+        for i, b in enumerate(ids_host):
+            host_k[i].copy_(k_pool[b], non_blocking=True)
+            host_v[i].copy_(v_pool[b], non_blocking=True)
+
+    ways = {
+        "gather_device": lambda: pkv.gather_blocks(k_pool, v_pool, ids, out=st_dev),
+        "gather_pinned": lambda: pkv.gather_blocks(k_pool, v_pool, ids, out=st_host),
+        "gather_memcpy": lambda: (pkv.gather_blocks(k_pool, v_pool, ids, out=st_dev),
+                                  st_host.copy_(st_dev, non_blocking=True)),
+        "per_block_dma": per_block_dma,
+        "scatter_pinned": lambda: pkv.scatter_blocks(k_pool, v_pool, ids, st_host),
+    }
+    res = {}
+    for name, fn in ways.items():
+        reps = 3 if name == "per_block_dma" else max(5, args.steps // 10)
+        fn()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        wall = (time.perf_counter() - t0) / reps
+        gpu = e0.elapsed_time(e1) / 1e3 / reps
+        t = max(wall, gpu)  # the naive path is bound by the host issuing copies
+        res[name] = {"ms": round(t * 1e3, 3), "GBps": round(n * rec / t / 1e9, 2)}
+    # the pinned gather must hold what the device gather holds
+    pkv.gather_blocks(k_pool, v_pool, ids, out=st_dev)
+    pkv.gather_blocks(k_pool, v_pool, ids, out=st_host)
+    torch.cuda.synchronize()
+    same = bool(torch.equal(st_dev.cpu(), st_host))
+    print(json.dumps({
+        "metric": "swap-out GB/s (scattered blocks gathered into pinned host memory)",
+        "value": res["gather_pinned"]["GBps"], "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": 1, "ms_per_step": res["gather_pinned"]["ms"], "higher_is_better": True, "dtype": "bf16",
+        "data": "synthetic (random pool, random distinct blocks)",
+        "config": {"workload": f"{n} scattered blocks, 70B-layer block shape (H_kv 8, D 128, bs 16)",
+                   "blocks": n, "record_bytes": rec},
+        "ways": res, "pinned_equals_device_gather": same}), flush=True)
 
 
 def cpu_baseline(case, mat, out_dev, budget_s, by, B):

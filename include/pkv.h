@@ -13,6 +13,8 @@
  * Groups of calls:
  *   pkv_kv_append          scatter this step's K/V rows into their slots
  *   pkv_copy_blocks        copy whole blocks (copy-on-write of shared blocks)
+ *   pkv_gather_blocks / pkv_scatter_blocks  pack blocks into / unpack from a
+ *                          contiguous staging buffer (swap-out / swap-in)
  *   pkv_paged_attn_decode  one query token per sequence attends over its paged KV
  *   pkv_alloc_* / pkv_seq_* host-side fixed-block free-list allocator
  *
@@ -119,6 +121,31 @@ int pkv_copy_blocks(void* k_pool, void* v_pool, int pool_dtype, int32_t NB, int3
                     int32_t D, const int32_t* src, const int32_t* dst, int32_t n_pairs, void* stream);
 
 /*
+ * Swap staging ("Paged Attention and KV Cache Fragmentation", section
+ * "Offloading paged KV blocks to CPU DRAM and NVMe": blocks move between HBM
+ * and host memory, and the paged layout scatters them into many small
+ * transfers).  A staging buffer holds n records of
+ * pkv_block_record_bytes(...) bytes; record i is block blocks[i]'s K block
+ * (every head) followed by its V block, raw bytes in pool layout.
+ *
+ * pkv_gather_blocks: record i <- block blocks[i].  pkv_scatter_blocks: block
+ * blocks[i] <- record i.  `staging` is device memory (then one
+ * hipMemcpyAsync moves it to or from the host) or pinned, mapped host memory
+ * (hipHostMalloc; the kernel reads or writes it directly); 16-byte aligned,
+ * owned by the caller.  Pageable host memory is refused (PKV_ERR_INVALID_ARG),
+ * checked with hipPointerGetAttributes before the launch.  blocks: device int32 [n]; an id outside [0, NB) skips
+ * its record (caller error).  Repeated ids in one scatter are a caller error.
+ * Use with pkv_seq_swap_out / pkv_seq_swap_in.  D must be a multiple of 16 and
+ * <= 512; bs in 1..256.  pkv_block_record_bytes returns 0 for bad arguments.
+ */
+size_t pkv_block_record_bytes(int pool_dtype, int32_t bs, int32_t H_kv, int32_t D);
+int pkv_gather_blocks(const void* k_pool, const void* v_pool, int pool_dtype, int32_t NB, int32_t bs,
+                      int32_t H_kv, int32_t D, const int32_t* blocks, int32_t n, void* staging,
+                      void* stream);
+int pkv_scatter_blocks(void* k_pool, void* v_pool, int pool_dtype, int32_t NB, int32_t bs, int32_t H_kv,
+                       int32_t D, const int32_t* blocks, int32_t n, const void* staging, void* stream);
+
+/*
  * pkv_decode_workspace_bytes — size of the scratch buffer pkv_paged_attn_decode
  * needs for these sizes (0 is possible).  The same arguments must be passed to
  * the decode call.  Returns 0 and sets the last error for invalid sizes.
@@ -191,7 +218,16 @@ int pkv_paged_attn_decode(float* out, const void* q, int q_dtype, const void* k_
  *   - fork: the child (a new id) gets the parent's blocks and length, and
  *     each of those blocks' refcount goes up by one;
  *   - free: the sequence's blocks are visited last to first, refcount goes
- *     down, blocks reaching zero are pushed on the free list.
+ *     down, blocks reaching zero are pushed on the free list;
+ *   - swap-out: the sequence's blocks are returned in logical order (save
+ *     their contents with pkv_gather_blocks first, or before any later
+ *     append or swap-in can reuse them) and released as by free, but the
+ *     sequence and its length stay.  A swapped-out sequence holds no blocks
+ *     and cannot grow, fork or appear in pkv_block_tables (INVALID_ARG);
+ *     free forgets it;
+ *   - swap-in: ceil(len/bs) fresh blocks, all-or-nothing (OUT_OF_BLOCKS
+ *     changes nothing), popped in logical order and returned; restore the
+ *     contents with pkv_scatter_blocks.
  * -------------------------------------------------------------------------*/
 typedef struct pkv_allocator pkv_allocator;
 
@@ -207,6 +243,13 @@ int pkv_seq_append_slots_cow(pkv_allocator* a, int64_t seq, int32_t n, int64_t* 
                              int32_t* copy_src, int32_t* copy_dst, int32_t* n_copies);
 int pkv_seq_fork(pkv_allocator* a, int64_t parent, int64_t child);
 int pkv_seq_free(pkv_allocator* a, int64_t seq);
+/* blocks_out: host int32 [max_blocks]; *n_out (host) = blocks written.  INVALID_ARG if the
+ * sequence is already swapped out (swap_out) / not swapped out (swap_in) or needs more than
+ * max_blocks entries. */
+int pkv_seq_swap_out(pkv_allocator* a, int64_t seq, int32_t* blocks_out, int32_t max_blocks,
+                     int32_t* n_out);
+int pkv_seq_swap_in(pkv_allocator* a, int64_t seq, int32_t* blocks_out, int32_t max_blocks,
+                    int32_t* n_out);
 int pkv_seq_len(const pkv_allocator* a, int64_t seq, int32_t* len_out);
 /* table_out: host int32 [n][max_blocks], padded with -1; lens_out: host int32 [n].
  * PKV_ERR_INVALID_ARG if a sequence holds more than max_blocks blocks. */

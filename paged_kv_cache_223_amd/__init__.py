@@ -46,6 +46,9 @@ SIGNATURES = {
     "pkv_kv_append": (ctypes.c_int, [_P, _P, ctypes.c_int, _P, _I32, _P, _P, ctypes.c_int, _I32, _I32, _I32,
                                      _I32, _P, _P, _P]),
     "pkv_copy_blocks": (ctypes.c_int, [_P, _P, ctypes.c_int, _I32, _I32, _I32, _I32, _P, _P, _I32, _P]),
+    "pkv_block_record_bytes": (_SZ, [ctypes.c_int, _I32, _I32, _I32]),
+    "pkv_gather_blocks": (ctypes.c_int, [_P, _P, ctypes.c_int, _I32, _I32, _I32, _I32, _P, _I32, _P, _P]),
+    "pkv_scatter_blocks": (ctypes.c_int, [_P, _P, ctypes.c_int, _I32, _I32, _I32, _I32, _P, _I32, _P, _P]),
     "pkv_decode_workspace_bytes": (_SZ, [_I32, _I32, _I32, _I32, _I32, _I32]),
     "pkv_paged_attn_decode": (ctypes.c_int, [_P, _P, ctypes.c_int, _P, _P, ctypes.c_int, _P, _I32, _P, _I32,
                                              _I32, _I32, _I32, _I32, _I32, _I32, ctypes.c_float, _P, _P, _P,
@@ -58,6 +61,8 @@ SIGNATURES = {
     "pkv_seq_append_slots_cow": (ctypes.c_int, [_P, _I64, _I32, _P, _P, _P, _P]),
     "pkv_seq_fork": (ctypes.c_int, [_P, _I64, _I64]),
     "pkv_seq_free": (ctypes.c_int, [_P, _I64]),
+    "pkv_seq_swap_out": (ctypes.c_int, [_P, _I64, _P, _I32, _P]),
+    "pkv_seq_swap_in": (ctypes.c_int, [_P, _I64, _P, _I32, _P]),
     "pkv_seq_len": (ctypes.c_int, [_P, _I64, _P]),
     "pkv_block_tables": (ctypes.c_int, [_P, _P, _I32, _I32, _P, _P]),
     "pkv_block_refcount": (_I32, [_P, _I32]),
@@ -199,6 +204,48 @@ def copy_blocks(k_pool, v_pool, src, dst):
                                src.shape[0], _stream()))
 
 
+def _staging_ok(t):
+    return t.is_cuda or t.is_pinned()
+
+
+def gather_blocks(k_pool, v_pool, blocks, out=None, pinned=False):
+    """Pack blocks[i] (int32 device tensor [n]) of both pools into record i of a staging buffer
+    (uint8 [n, 2, block bytes]: K block then V block).  `out` may be a device tensor or a pinned
+    host tensor (written directly by the kernel); without it one is allocated, pinned host memory
+    if `pinned`, else on the pools' device."""
+    torch = _torch()
+    _dev(k_pool, v_pool, blocks)
+    kv, NB, H_kv, D, bs = _pool_dims(k_pool, v_pool)
+    if blocks.dtype != torch.int32 or blocks.dim() != 1 or not blocks.is_contiguous():
+        raise ValueError("blocks must be a contiguous int32 [n] tensor")
+    n, rec = blocks.shape[0], int(lib.pkv_block_record_bytes(kv, bs, H_kv, D))
+    if out is None:
+        out = (torch.empty((n, 2, rec // 2), dtype=torch.uint8, pin_memory=True) if pinned
+               else torch.empty((n, 2, rec // 2), dtype=torch.uint8, device=k_pool.device))
+    if out.dtype != torch.uint8 or tuple(out.shape) != (n, 2, rec // 2) or not out.is_contiguous() \
+            or not _staging_ok(out):
+        raise ValueError(f"staging must be a contiguous uint8 [{n}, 2, {rec // 2}] device or pinned tensor")
+    _check(lib.pkv_gather_blocks(_ptr(k_pool), _ptr(v_pool), kv, NB, bs, H_kv, D, _ptr(blocks), n, _ptr(out),
+                                 _stream()))
+    return out
+
+
+def scatter_blocks(k_pool, v_pool, blocks, staging):
+    """Unpack record i of `staging` (as gather_blocks makes it; device or pinned host) into block
+    blocks[i] (int32 device tensor [n]) of both pools."""
+    torch = _torch()
+    _dev(k_pool, v_pool, blocks)
+    kv, NB, H_kv, D, bs = _pool_dims(k_pool, v_pool)
+    if blocks.dtype != torch.int32 or blocks.dim() != 1 or not blocks.is_contiguous():
+        raise ValueError("blocks must be a contiguous int32 [n] tensor")
+    n, rec = blocks.shape[0], int(lib.pkv_block_record_bytes(kv, bs, H_kv, D))
+    if staging.dtype != torch.uint8 or tuple(staging.shape) != (n, 2, rec // 2) or not staging.is_contiguous() \
+            or not _staging_ok(staging):
+        raise ValueError(f"staging must be a contiguous uint8 [{n}, 2, {rec // 2}] device or pinned tensor")
+    _check(lib.pkv_scatter_blocks(_ptr(k_pool), _ptr(v_pool), kv, NB, bs, H_kv, D, _ptr(blocks), n,
+                                  _ptr(staging), _stream()))
+
+
 def decode_workspace_bytes(B: int, H_q: int, H_kv: int, D: int, max_context_len: int, bs: int) -> int:
     return int(lib.pkv_decode_workspace_bytes(B, H_q, H_kv, D, max_context_len, bs))
 
@@ -325,6 +372,24 @@ class Allocator:
     def free(self, seq) -> int:
         return int(lib.pkv_seq_free(self._h, int(seq)))
 
+    def swap_out(self, seq):
+        """(status, blocks): the sequence's blocks in logical order, now released."""
+        return self._swap(lib.pkv_seq_swap_out, seq)
+
+    def swap_in(self, seq):
+        """(status, blocks): fresh blocks for the swapped-out sequence, in logical order."""
+        return self._swap(lib.pkv_seq_swap_in, seq)
+
+    def _swap(self, fn, seq):
+        st, n = self.seq_len(seq)
+        if st != OK:
+            return st, None
+        cap = max(-(-n // self.bs), 1)
+        out = np.empty(cap, np.int32)
+        cnt = ctypes.c_int32()
+        st = int(fn(self._h, int(seq), out.ctypes.data, cap, ctypes.byref(cnt)))
+        return st, (out[:cnt.value].copy() if st == OK else None)
+
     def seq_len(self, seq):
         n = ctypes.c_int32()
         st = int(lib.pkv_seq_len(self._h, int(seq), ctypes.byref(n)))
@@ -342,7 +407,8 @@ class Allocator:
         return int(lib.pkv_block_refcount(self._h, int(block)))
 
 
-__all__ = ["lib", "LIB_PATH", "PkvError", "last_error", "kv_append", "copy_blocks", "paged_attn_decode",
+__all__ = ["lib", "LIB_PATH", "PkvError", "last_error", "kv_append", "copy_blocks", "gather_blocks",
+           "scatter_blocks", "paged_attn_decode",
            "decode_workspace_bytes",
            "decode_workspace",
            "pool_shapes", "dtype_code", "stream_read", "copy_", "Allocator", "SIGNATURES",

@@ -7,9 +7,11 @@
 // them back when it finishes; sequences with a common prefix, or beam-search
 // branches, point at the same physical blocks.  "KV Cache Fragmentation"
 // field guide (defragging.ai), section "Why it matters": sharing makes forks
-// cheap.  Exact semantics (LIFO order, all-or-nothing appends, the shared
-// partial-block rule, copy-on-write appends, reverse-order frees) are spelled
-// out in pkv.h.
+// cheap.  Section "Offloading paged KV blocks to CPU DRAM and NVMe": blocks of
+// a sequence that is not running move to host memory and come back later
+// (swap-out / swap-in).  Exact semantics (LIFO order, all-or-nothing appends,
+// the shared partial-block rule, copy-on-write appends, reverse-order frees,
+// swaps) are spelled out in pkv.h.
 
 #include <stdint.h>
 
@@ -26,6 +28,7 @@ struct pkv_allocator {
   struct Seq {
     std::vector<int32_t> blocks;
     int64_t len = 0;
+    bool swapped = false;  // swapped out: keeps its length, holds no blocks
   };
   std::unordered_map<int64_t, Seq> seqs;
 };
@@ -33,6 +36,12 @@ struct pkv_allocator {
 using pkv::set_error;
 
 static int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// release a sequence's blocks last to first (a block reaching refcount 0 goes on the free list)
+static void release_blocks(pkv_allocator* a, const std::vector<int32_t>& blocks) {
+  for (auto r = blocks.rbegin(); r != blocks.rend(); ++r)
+    if (--a->rc[*r] == 0) a->stack.push_back(*r);
+}
 
 extern "C" {
 
@@ -96,6 +105,10 @@ static int append_impl(pkv_allocator* a, int64_t seq, int32_t n, int64_t* slots_
     return PKV_ERR_INVALID_ARG;
   }
   auto& s = it->second;
+  if (s.swapped) {
+    set_error("append_slots: sequence %lld is swapped out", (long long)seq);
+    return PKV_ERR_INVALID_ARG;
+  }
   const int64_t L = s.len, bs = a->bs;
   if (L + n > (int64_t)0x7FFFFFFF) {
     set_error("append_slots: length would exceed 2^31-1");
@@ -158,6 +171,10 @@ int pkv_seq_fork(pkv_allocator* a, int64_t parent, int64_t child) {
     set_error("fork: child %lld already exists", (long long)child);
     return PKV_ERR_INVALID_ARG;
   }
+  if (it->second.swapped) {
+    set_error("fork: parent %lld is swapped out", (long long)parent);
+    return PKV_ERR_INVALID_ARG;
+  }
   pkv_allocator::Seq c = it->second;  // copy before emplace (rehash may move it)
   for (int32_t b : c.blocks) a->rc[b] += 1;
   a->seqs.emplace(child, std::move(c));
@@ -171,10 +188,65 @@ int pkv_seq_free(pkv_allocator* a, int64_t seq) {
     set_error("free: unknown sequence %lld", (long long)seq);
     return PKV_ERR_UNKNOWN_SEQ;
   }
-  const auto& blocks = it->second.blocks;
-  for (auto r = blocks.rbegin(); r != blocks.rend(); ++r)
-    if (--a->rc[*r] == 0) a->stack.push_back(*r);
+  release_blocks(a, it->second.blocks);
   a->seqs.erase(it);
+  return PKV_OK;
+}
+
+int pkv_seq_swap_out(pkv_allocator* a, int64_t seq, int32_t* blocks_out, int32_t max_blocks, int32_t* n_out) {
+  if (!a || !n_out || max_blocks < 0 || (max_blocks > 0 && !blocks_out)) {
+    set_error("swap_out: bad arguments");
+    return PKV_ERR_INVALID_ARG;
+  }
+  auto it = a->seqs.find(seq);
+  if (it == a->seqs.end()) {
+    set_error("swap_out: unknown sequence %lld", (long long)seq);
+    return PKV_ERR_UNKNOWN_SEQ;
+  }
+  auto& s = it->second;
+  if (s.swapped || (int64_t)s.blocks.size() > max_blocks) {
+    set_error("swap_out: sequence %lld is swapped out already or holds more than %d blocks", (long long)seq,
+              max_blocks);
+    return PKV_ERR_INVALID_ARG;
+  }
+  for (size_t j = 0; j < s.blocks.size(); ++j) blocks_out[j] = s.blocks[j];
+  *n_out = (int32_t)s.blocks.size();
+  release_blocks(a, s.blocks);
+  s.blocks.clear();
+  s.swapped = true;
+  return PKV_OK;
+}
+
+int pkv_seq_swap_in(pkv_allocator* a, int64_t seq, int32_t* blocks_out, int32_t max_blocks, int32_t* n_out) {
+  if (!a || !n_out || max_blocks < 0 || (max_blocks > 0 && !blocks_out)) {
+    set_error("swap_in: bad arguments");
+    return PKV_ERR_INVALID_ARG;
+  }
+  auto it = a->seqs.find(seq);
+  if (it == a->seqs.end()) {
+    set_error("swap_in: unknown sequence %lld", (long long)seq);
+    return PKV_ERR_UNKNOWN_SEQ;
+  }
+  auto& s = it->second;
+  const int64_t need = ceil_div(s.len, a->bs);
+  if (!s.swapped || need > max_blocks) {
+    set_error("swap_in: sequence %lld is not swapped out or needs more than %d blocks", (long long)seq,
+              max_blocks);
+    return PKV_ERR_INVALID_ARG;
+  }
+  if (need > (int64_t)a->stack.size()) {
+    set_error("swap_in: need %lld blocks, %zu free", (long long)need, a->stack.size());
+    return PKV_ERR_OUT_OF_BLOCKS;
+  }
+  for (int64_t j = 0; j < need; ++j) {
+    const int32_t b = a->stack.back();
+    a->stack.pop_back();
+    a->rc[b] = 1;
+    s.blocks.push_back(b);
+    blocks_out[j] = b;
+  }
+  *n_out = (int32_t)need;
+  s.swapped = false;
   return PKV_OK;
 }
 
@@ -200,6 +272,10 @@ int pkv_block_tables(const pkv_allocator* a, const int64_t* seqs, int32_t n, int
     if (it == a->seqs.end()) {
       set_error("block_tables: unknown sequence %lld", (long long)seqs[i]);
       return PKV_ERR_UNKNOWN_SEQ;
+    }
+    if (it->second.swapped) {
+      set_error("block_tables: sequence %lld is swapped out", (long long)seqs[i]);
+      return PKV_ERR_INVALID_ARG;
     }
     if ((int64_t)it->second.blocks.size() > max_blocks) {
       set_error("block_tables: sequence %lld holds %zu blocks > max_blocks %d", (long long)seqs[i],

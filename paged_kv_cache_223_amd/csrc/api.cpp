@@ -89,41 +89,117 @@ int pkv_kv_append(const void* k, const void* v, int src_dtype, const int64_t* sl
   return hip_status(launch_kv_append(a, (hipStream_t)stream), "kv_append launch");
 }
 
-int pkv_copy_blocks(void* k_pool, void* v_pool, int pool_dtype, int32_t NB, int32_t bs, int32_t H_kv, int32_t D,
-                    const int32_t* src, const int32_t* dst, int32_t n_pairs, void* stream) {
-  g_err[0] = 0;
-  if (n_pairs < 0 || NB <= 0 || bs <= 0 || bs > 256 || H_kv <= 0 || D <= 0) {
-    set_error("copy_blocks: bad sizes n_pairs=%d NB=%d bs=%d H_kv=%d D=%d", n_pairs, NB, bs, H_kv, D);
+// shared validation of the block moves; fills `a` (without the index arrays)
+static int block_move_args(const char* what, void* k_pool, void* v_pool, int pool_dtype, int32_t NB, int32_t bs,
+                           int32_t H_kv, int32_t D, int32_t n, CopyBlocksArgs& a) {
+  if (n < 0 || NB <= 0 || bs <= 0 || bs > 256 || H_kv <= 0 || D <= 0) {
+    set_error("%s: bad sizes n=%d NB=%d bs=%d H_kv=%d D=%d", what, n, NB, bs, H_kv, D);
     return PKV_ERR_INVALID_ARG;
   }
   if (!valid_dtype(pool_dtype)) {
-    set_error("copy_blocks: unknown dtype %d", pool_dtype);
+    set_error("%s: unknown dtype %d", what, pool_dtype);
     return PKV_ERR_INVALID_ARG;
   }
   if (D % 16 != 0 || D > 512) {
-    set_error("copy_blocks: D=%d must be a multiple of 16 and <= 512", D);
+    set_error("%s: D=%d must be a multiple of 16 and <= 512", what, D);
     return PKV_ERR_UNSUPPORTED;
   }
-  if (n_pairs == 0) return PKV_OK;
-  if (!k_pool || !v_pool || !src || !dst) {
-    set_error("copy_blocks: null pointer");
+  if (n > 0 && (!k_pool || !v_pool)) {
+    set_error("%s: null pool", what);
     return PKV_ERR_INVALID_ARG;
   }
   const int elem = pool_dtype == PKV_F32 ? 4 : pool_dtype == PKV_BF16 ? 2 : 1;
-  CopyBlocksArgs a{};
+  a = CopyBlocksArgs{};
   a.k_pool = k_pool;
   a.v_pool = v_pool;
-  a.src = src;
-  a.dst = dst;
-  a.n_pairs = n_pairs;
+  a.n_pairs = n;
   a.NB = NB;
   a.block_units = (long long)H_kv * D * bs * elem / 16;
   a.tiles = (a.block_units + kCopyThreads * kCopyUnroll - 1) / (kCopyThreads * kCopyUnroll);
-  if ((long long)n_pairs * 2 * a.tiles > 0x7FFFFFFFLL) {
-    set_error("copy_blocks: too many pairs for one launch");
+  if ((long long)n * 2 * a.tiles > 0x7FFFFFFFLL) {
+    set_error("%s: too many blocks for one launch", what);
     return PKV_ERR_INVALID_ARG;
   }
-  return hip_status(launch_copy_blocks(a, (hipStream_t)stream), "copy_blocks launch");
+  return PKV_OK;
+}
+
+int pkv_copy_blocks(void* k_pool, void* v_pool, int pool_dtype, int32_t NB, int32_t bs, int32_t H_kv, int32_t D,
+                    const int32_t* src, const int32_t* dst, int32_t n_pairs, void* stream) {
+  g_err[0] = 0;
+  CopyBlocksArgs a;
+  const int st = block_move_args("copy_blocks", k_pool, v_pool, pool_dtype, NB, bs, H_kv, D, n_pairs, a);
+  if (st != PKV_OK || n_pairs == 0) return st;
+  if (!src || !dst) {
+    set_error("copy_blocks: null pointer");
+    return PKV_ERR_INVALID_ARG;
+  }
+  a.src = src;
+  a.dst = dst;
+  return hip_status(launch_block_move(a, kMovePairs, (hipStream_t)stream), "copy_blocks launch");
+}
+
+// Device address of a staging buffer: device memory as is, pinned host memory through its
+// mapping.  Pageable (unregistered) host memory is refused: a kernel must never touch it.
+static int staging_device_ptr(const char* what, const void* p, void** dev_ptr) {
+  hipPointerAttribute_t attr{};
+  const hipError_t e = hipPointerGetAttributes(&attr, p);
+  if (e != hipSuccess || attr.type == hipMemoryTypeUnregistered) {
+    (void)hipGetLastError();
+    set_error("%s: staging %p is neither device memory nor pinned host memory", what, p);
+    return PKV_ERR_INVALID_ARG;
+  }
+  if (attr.type == hipMemoryTypeHost) {
+    if (!attr.devicePointer) {
+      set_error("%s: pinned staging %p has no device mapping", what, p);
+      return PKV_ERR_INVALID_ARG;
+    }
+    *dev_ptr = (char*)attr.devicePointer + ((const char*)p - (const char*)attr.hostPointer);
+  } else {
+    *dev_ptr = (void*)p;
+  }
+  return PKV_OK;
+}
+
+size_t pkv_block_record_bytes(int pool_dtype, int32_t bs, int32_t H_kv, int32_t D) {
+  g_err[0] = 0;
+  if (!valid_dtype(pool_dtype) || bs <= 0 || H_kv <= 0 || D <= 0) {
+    set_error("block_record_bytes: bad arguments");
+    return 0;
+  }
+  const size_t elem = pool_dtype == PKV_F32 ? 4 : pool_dtype == PKV_BF16 ? 2 : 1;
+  return 2 * (size_t)H_kv * D * bs * elem;
+}
+
+int pkv_gather_blocks(const void* k_pool, const void* v_pool, int pool_dtype, int32_t NB, int32_t bs, int32_t H_kv,
+                      int32_t D, const int32_t* blocks, int32_t n, void* staging, void* stream) {
+  g_err[0] = 0;
+  CopyBlocksArgs a;
+  const int st = block_move_args("gather_blocks", (void*)k_pool, (void*)v_pool, pool_dtype, NB, bs, H_kv, D, n, a);
+  if (st != PKV_OK || n == 0) return st;
+  if (!blocks || !staging || ((uintptr_t)staging & 15u)) {
+    set_error("gather_blocks: null pointer or staging not 16-byte aligned");
+    return PKV_ERR_INVALID_ARG;
+  }
+  a.src = blocks;
+  const int ps = staging_device_ptr("gather_blocks", staging, &a.staging);
+  if (ps != PKV_OK) return ps;
+  return hip_status(launch_block_move(a, kMoveGather, (hipStream_t)stream), "gather_blocks launch");
+}
+
+int pkv_scatter_blocks(void* k_pool, void* v_pool, int pool_dtype, int32_t NB, int32_t bs, int32_t H_kv, int32_t D,
+                       const int32_t* blocks, int32_t n, const void* staging, void* stream) {
+  g_err[0] = 0;
+  CopyBlocksArgs a;
+  const int st = block_move_args("scatter_blocks", k_pool, v_pool, pool_dtype, NB, bs, H_kv, D, n, a);
+  if (st != PKV_OK || n == 0) return st;
+  if (!blocks || !staging || ((uintptr_t)staging & 15u)) {
+    set_error("scatter_blocks: null pointer or staging not 16-byte aligned");
+    return PKV_ERR_INVALID_ARG;
+  }
+  a.dst = blocks;
+  const int ps = staging_device_ptr("scatter_blocks", staging, &a.staging);
+  if (ps != PKV_OK) return ps;
+  return hip_status(launch_block_move(a, kMoveScatter, (hipStream_t)stream), "scatter_blocks launch");
 }
 
 size_t pkv_decode_workspace_bytes(int32_t B, int32_t H_q, int32_t H_kv, int32_t D, int32_t max_context_len,

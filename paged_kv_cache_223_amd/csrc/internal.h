@@ -113,12 +113,15 @@ struct AppendArgs {
 };
 hipError_t launch_kv_append(const AppendArgs& a, hipStream_t s);
 
-// whole-block copies of both pools (copy-on-write)
+// whole-block moves of both pools: pool -> pool (copy-on-write pairs),
+// pool -> staging records (swap-out gather), staging -> pool (swap-in scatter)
+enum BlockMove { kMovePairs = 0, kMoveGather = 1, kMoveScatter = 2 };
 struct CopyBlocksArgs {
   void* k_pool;
   void* v_pool;
-  const int32_t* src;  // device [n_pairs]
-  const int32_t* dst;  // device [n_pairs]
+  const int32_t* src;  // device [n_pairs]: source blocks (pairs, gather)
+  const int32_t* dst;  // device [n_pairs]: target blocks (pairs, scatter)
+  void* staging;       // gather / scatter: [n_pairs][2 (K, V)][block bytes], device or mapped host memory
   int32_t n_pairs;
   int32_t NB;
   long long block_units;  // 16-byte units per block of one pool (H_kv * D * bs * elem / 16)
@@ -126,7 +129,7 @@ struct CopyBlocksArgs {
 };
 constexpr int kCopyThreads = 256;
 constexpr int kCopyUnroll = 4;
-hipError_t launch_copy_blocks(const CopyBlocksArgs& a, hipStream_t s);
+hipError_t launch_block_move(const CopyBlocksArgs& a, BlockMove mode, hipStream_t s);
 
 // stream.hip
 size_t stream_read_blocks(size_t bytes);

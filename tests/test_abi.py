@@ -150,3 +150,47 @@ def test_cow_append_needs_its_copy_outputs():
         pkv.ERR_INVALID_ARG
     assert pkv.lib.pkv_seq_append_slots_cow(a._h, 7, 2, out, ctypes.byref(c), ctypes.byref(c), ctypes.byref(c)) == \
         pkv.ERR_UNKNOWN_SEQ
+
+
+def _move(fn, **kw):
+    a = dict(kp=P, vp=P, pool=pkv.BF16, NB=8, bs=16, H=2, D=128, blocks=P, n=3, staging=P, stream=None)
+    a.update(kw)
+    return fn(a["kp"], a["vp"], a["pool"], a["NB"], a["bs"], a["H"], a["D"], a["blocks"], a["n"], a["staging"],
+              a["stream"])
+
+
+@pytest.mark.parametrize("which", ["pkv_gather_blocks", "pkv_scatter_blocks"])
+@pytest.mark.parametrize("kw,status", [
+    (dict(n=-1), pkv.ERR_INVALID_ARG),
+    (dict(bs=0), pkv.ERR_INVALID_ARG),
+    (dict(pool=9), pkv.ERR_INVALID_ARG),
+    (dict(D=24), pkv.ERR_UNSUPPORTED),
+    (dict(blocks=None), pkv.ERR_INVALID_ARG),
+    (dict(staging=None), pkv.ERR_INVALID_ARG),
+    (dict(staging=ctypes.c_void_p(0x1008)), pkv.ERR_INVALID_ARG),  # not 16-byte aligned
+    (dict(kp=None), pkv.ERR_INVALID_ARG),
+])
+def test_block_moves_reject_bad_arguments_before_launch(which, kw, status):
+    assert _move(getattr(pkv.lib, which), **kw) == status
+    assert pkv.last_error()
+
+
+def test_block_moves_zero_blocks_are_no_ops_and_record_size():
+    assert _move(pkv.lib.pkv_gather_blocks, n=0, blocks=None, staging=None) == pkv.OK
+    assert _move(pkv.lib.pkv_scatter_blocks, n=0, blocks=None, staging=None) == pkv.OK
+    assert pkv.lib.pkv_block_record_bytes(pkv.BF16, 16, 8, 128) == 2 * 8 * 128 * 16 * 2
+    assert pkv.lib.pkv_block_record_bytes(pkv.FP8_E4M3, 32, 8, 128) == 2 * 8 * 128 * 32
+    assert pkv.lib.pkv_block_record_bytes(pkv.BF16, 0, 8, 128) == 0
+
+
+def test_swap_calls_check_their_outputs():
+    a = pkv.Allocator(8, 4)
+    a.seq_add(0)
+    a.append_slots(0, 9)  # 3 blocks
+    n = ctypes.c_int32()
+    buf = (ctypes.c_int32 * 2)()
+    assert pkv.lib.pkv_seq_swap_out(a._h, 0, buf, 2, ctypes.byref(n)) == pkv.ERR_INVALID_ARG  # too small
+    assert a.seq_len(0) == (pkv.OK, 9) and a.num_free() == 5  # nothing changed
+    assert pkv.lib.pkv_seq_swap_out(a._h, 0, buf, 2, None) == pkv.ERR_INVALID_ARG
+    assert pkv.lib.pkv_seq_swap_in(a._h, 5, buf, 2, ctypes.byref(n)) == pkv.ERR_UNKNOWN_SEQ
+

@@ -105,6 +105,65 @@ def test_random_cow_ops_identical_to_model(seed):
         assert copies_seen >= 3
 
 
+@pytest.mark.parametrize("seed", range(4))
+def test_random_swap_ops_identical_to_model(seed):
+    """Scripts with swap-out / swap-in mixed into copy-on-write appends, forks and frees; every
+    call on a swapped-out sequence that must be refused is tried too."""
+    rng = np.random.default_rng(700 + seed)
+    NB, bs = [64, 30, 128, 23][seed], [16, 4, 8, 1][seed]
+    cpp, model = _pair(NB, bs, rng.permutation(NB))
+    live, swapped, nid, swaps = [], set(), 0, 0
+    for step in range(3000):
+        r = rng.random()
+        resident = [s for s in live if s not in swapped]
+        if r < 0.12 or not live:
+            assert cpp.seq_add(nid) == model.seq_add(nid) == 0
+            live.append(nid)
+            nid += 1
+        elif r < 0.45 and resident:
+            s = resident[rng.integers(len(resident))]
+            n = int(rng.integers(0, 2 * bs + 2))
+            st1, sl1, c1 = cpp.append_slots_cow(s, n)
+            st2, sl2, c2 = model.append_slots_cow(s, n)
+            assert st1 == st2
+            if st1 == 0:
+                assert list(sl1) == list(sl2) and c1 == c2
+        elif r < 0.55 and resident:
+            s = resident[rng.integers(len(resident))]
+            assert cpp.fork(s, nid) == model.fork(s, nid) == 0
+            live.append(nid)
+            nid += 1
+        elif r < 0.67 and resident:
+            s = resident[rng.integers(len(resident))]
+            st1, b1 = cpp.swap_out(s)
+            st2, b2 = model.swap_out(s)
+            assert st1 == st2 == 0 and list(b1) == list(b2)
+            swapped.add(s)
+            swaps += 1
+        elif r < 0.8 and swapped:
+            s = sorted(swapped)[rng.integers(len(swapped))]
+            # refused while swapped out
+            assert cpp.append_slots(s, 1)[0] == model.append_slots(s, 1)[0] == pkv.ERR_INVALID_ARG
+            assert cpp.fork(s, nid) == model.fork(s, nid) == pkv.ERR_INVALID_ARG
+            assert cpp.swap_out(s)[0] == model.swap_out(s)[0] == pkv.ERR_INVALID_ARG
+            assert cpp.block_tables([s], 1 << 12)[0] == pkv.ERR_INVALID_ARG
+            st1, b1 = cpp.swap_in(s)
+            st2, b2 = model.swap_in(s)
+            assert st1 == st2
+            if st1 == 0:
+                assert list(b1) == list(b2)
+                swapped.discard(s)
+        else:
+            s = live.pop(rng.integers(len(live)))
+            swapped.discard(s)
+            assert cpp.free(s) == model.free(s) == 0
+        if step % 61 == 0:
+            _same_state(cpp, model, [s for s in live if s not in swapped])
+            for s in live:
+                assert cpp.seq_len(s) == model.seq_len(s)
+    assert swaps >= 50
+
+
 @pytest.mark.parametrize("builder", [
     lambda: workloads.tiny_f32(),
     lambda: workloads.llama8b_bf16(),

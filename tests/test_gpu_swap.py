@@ -1,0 +1,137 @@
+"""Swap-out / swap-in on the GPU: pkv_gather_blocks and pkv_scatter_blocks are bit-exact against
+the oracle's gather / scatter, with the staging buffer in device memory or in pinned host memory
+written and read directly by the kernels; and sequences swapped out to pinned host memory, whose
+blocks are then reused by other sequences, decode after swap-in exactly as before (bit for bit:
+the decode's reduction order follows logical blocks, not physical placement).
+
+"Paged Attention and KV Cache Fragmentation", section "Offloading paged KV blocks to CPU DRAM
+and NVMe"."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import paged_kv_cache_223_amd as pkv
+import workloads
+from tests.gpu_helpers import DEV, from_dev, to_dev
+from tests.oracle_cases import row_rel_err
+
+pytestmark = pytest.mark.gpu
+
+BITS = {"f32": np.uint32, "bf16": np.uint16, "e4m3": np.uint8}
+
+
+def _random_pools(rng, NB, H, D, bs, dtype):
+    kp, vp = oracle.empty_pools(NB, H, D, bs, dtype)
+    b = BITS[dtype]
+    kp[:] = rng.integers(0, np.iinfo(b).max, kp.shape, dtype=b, endpoint=True).view(kp.dtype)
+    vp[:] = rng.integers(0, np.iinfo(b).max, vp.shape, dtype=b, endpoint=True).view(vp.dtype)
+    return kp, vp
+
+
+@pytest.mark.parametrize("where", ["device", "pinned"])
+@pytest.mark.parametrize("dtype,bs,H,D", [("f32", 8, 2, 64), ("bf16", 16, 8, 128), ("e4m3", 32, 4, 128)])
+def test_gather_blocks_bit_exact(where, dtype, bs, H, D):
+    print(f"gather {dtype} bs={bs} H={H} D={D} into {where}", flush=True)
+    rng = np.random.default_rng(21)
+    NB = 48
+    kp, vp = _random_pools(rng, NB, H, D, bs, dtype)
+    blocks = [int(x) for x in rng.integers(0, NB, 20)] + [NB + 3]  # repeats allowed; last id is skipped
+    kd, vd = to_dev(kp, dtype), to_dev(vp, dtype)
+    ids = torch.tensor(blocks, dtype=torch.int32, device=DEV)
+    rec = pkv.lib.pkv_block_record_bytes(pkv.dtype_code(kd), bs, H, D)
+    out = torch.full((len(blocks), 2, rec // 2), 0xAB, dtype=torch.uint8,
+                     **({"device": DEV} if where == "device" else {"pin_memory": True}))
+    pkv.gather_blocks(kd, vd, ids, out=out)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    assert np.array_equal(got[:-1], oracle.ref_gather_blocks(kp, vp, blocks[:-1]))
+    assert (got[-1] == 0xAB).all()  # the out-of-range id left its record alone
+
+
+@pytest.mark.parametrize("where", ["device", "pinned"])
+@pytest.mark.parametrize("dtype,bs,H,D", [("f32", 8, 2, 64), ("bf16", 16, 8, 128), ("e4m3", 32, 4, 128)])
+def test_scatter_blocks_bit_exact(where, dtype, bs, H, D):
+    print(f"scatter {dtype} bs={bs} H={H} D={D} from {where}", flush=True)
+    rng = np.random.default_rng(22)
+    NB = 48
+    kp, vp = _random_pools(rng, NB, H, D, bs, dtype)
+    blocks = [int(x) for x in rng.permutation(NB)[:17]]
+    rec = pkv.lib.pkv_block_record_bytes(pkv.dtype_code(to_dev(kp[:1], dtype)), bs, H, D)
+    staging = rng.integers(0, 256, (len(blocks), 2, rec // 2), dtype=np.uint8)
+    st_t = torch.from_numpy(staging)
+    st_t = st_t.to(DEV) if where == "device" else st_t.pin_memory()
+    kd, vd = to_dev(kp, dtype), to_dev(vp, dtype)
+    pkv.scatter_blocks(kd, vd, torch.tensor(blocks, dtype=torch.int32, device=DEV), st_t)
+    torch.cuda.synchronize()
+    ek, ev = oracle.ref_scatter_blocks(kp, vp, blocks, staging)
+    assert np.array_equal(from_dev(kd).view(BITS[dtype]), ek.view(BITS[dtype]))
+    assert np.array_equal(from_dev(vd).view(BITS[dtype]), ev.view(BITS[dtype]))
+
+
+def test_pageable_staging_is_refused():
+    kd = torch.zeros(pkv.pool_shapes(4, 1, 64, 8, pkv.BF16)[0], dtype=torch.bfloat16, device=DEV)
+    vd = torch.zeros(pkv.pool_shapes(4, 1, 64, 8, pkv.BF16)[1], dtype=torch.bfloat16, device=DEV)
+    ids = torch.tensor([1], dtype=torch.int32, device=DEV)
+    pageable = np.zeros(2 * 64 * 8 * 2 + 64, np.uint8)
+    p = (pageable.ctypes.data + 15) // 16 * 16
+    st = pkv.lib.pkv_gather_blocks(pkv._ptr(kd), pkv._ptr(vd), pkv.BF16, 4, 8, 1, 64, pkv._ptr(ids), 1, p, None)
+    assert st == pkv.ERR_INVALID_ARG and "pinned" in pkv.last_error()
+
+
+@pytest.mark.parametrize("kv_dtype,bs", [("bf16", 16), ("e4m3", 32)])
+def test_swap_out_reuse_swap_in_decodes_as_before(kv_dtype, bs):
+    print(f"swap round trip {kv_dtype} bs={bs}", flush=True)
+    lens = [300, 1, 57, 1000, 64, 777]
+    case = workloads.custom(f"swap_{kv_dtype}", 6, 16, 2, 128, bs, kv_dtype, "bf16", lens, 4242,
+                            NB=sum(-(-n // bs) for n in lens) + 40)
+    a = pkv.Allocator(case.NB, bs, case.initial_free_order)
+    mat = workloads.materialize(case, a)
+    kvd = {"bf16": pkv.BF16, "e4m3": pkv.FP8_E4M3}[kv_dtype]
+    ks, vs = pkv.pool_shapes(case.NB, 2, 128, bs, kvd)
+    fill = dict(dtype=torch.uint8) if kv_dtype == "e4m3" else dict(dtype=torch.bfloat16)
+    kp = torch.full(ks, 0x7F if kv_dtype == "e4m3" else float("nan"), device=DEV, **fill)
+    vp = torch.full(vs, 0x7F if kv_dtype == "e4m3" else float("nan"), device=DEV, **fill)
+    k_s = None if case.k_scale is None else torch.from_numpy(case.k_scale).to(DEV)
+    v_s = None if case.v_scale is None else torch.from_numpy(case.v_scale).to(DEV)
+    pkv.kv_append(to_dev(mat.k_src, "bf16"), to_dev(mat.v_src, "bf16"), torch.from_numpy(mat.slots).to(DEV),
+                  kp, vp, k_s, v_s)
+    seqs = list(range(6))
+    q = to_dev(case.q, "bf16")
+
+    def run():
+        mb = max(-(-n // bs) for n in lens)
+        st, tab, ln = a.block_tables(seqs, mb)
+        assert st == 0
+        out = pkv.paged_attn_decode(q, kp, vp, torch.from_numpy(tab).to(DEV), torch.from_numpy(ln).to(DEV),
+                                    float(case.scale), max(lens), k_s, v_s)
+        torch.cuda.synchronize()
+        return out.cpu().numpy(), tab
+
+    before, tab_before = run()
+    # swap out three sequences to pinned host memory, then let a newcomer take (and overwrite) the blocks
+    saved = {}
+    for s in (0, 3, 4):
+        st, blocks = a.swap_out(s)
+        assert st == 0
+        saved[s] = pkv.gather_blocks(kp, vp, torch.from_numpy(blocks).to(DEV), pinned=True)
+    torch.cuda.synchronize()
+    a.seq_add(99)
+    free = a.num_free()
+    st, slots = a.append_slots(99, free * bs)
+    assert st == 0
+    junk = torch.randn((free * bs, 2, 128), device=DEV).to(torch.bfloat16)
+    pkv.kv_append(junk, junk, torch.from_numpy(slots).to(DEV), kp, vp, k_s, v_s)
+    a.free(99)
+    for s in (4, 0, 3):  # back in another order, into other blocks
+        st, blocks = a.swap_in(s)
+        assert st == 0
+        pkv.scatter_blocks(kp, vp, torch.from_numpy(blocks).to(DEV), saved[s])
+    after, tab_after = run()
+    assert not np.array_equal(tab_before, tab_after)  # the sequences really moved
+    assert np.array_equal(before.view(np.uint32), after.view(np.uint32))
+    ek, ev = oracle.ref_append(*oracle.empty_pools(case.NB, 2, 128, bs, kv_dtype), mat.k_src, mat.v_src, "bf16",
+                               mat.slots, bs, kv_dtype, case.k_scale, case.v_scale)
+    ref = oracle.ref_decode(case.q, "bf16", ek, ev, kv_dtype, mat.block_tables, mat.context_lens, case.scale, bs,
+                            case.k_scale, case.v_scale)
+    assert row_rel_err(after, ref) <= (2e-2 if kv_dtype == "e4m3" else 2e-3)
