@@ -40,6 +40,18 @@ its length; a swapped-out sequence holds no blocks and cannot grow, fork or
 appear in a block table.  `swap_in` takes ceil(len / bs) fresh blocks,
 all-or-nothing, popped in logical order, and returns them (the caller restores
 the contents into them).
+
+Whole-block eviction (PA, section "A fragmentation problem that paging itself
+creates: block-level eviction mismatch": evicting whole blocks keeps the paged
+structure that token-level eviction breaks; StreamingLLM keeps a few sink
+tokens at the start plus a window of recent tokens).  `evict_blocks` removes
+full logical blocks [first, first + count) from a sequence: the table closes
+the gap, the length drops by count * bs, the blocks are released as by free.
+`streaming_evict(seq, S, W)` evicts the whole blocks strictly between the
+blocks holding the first S tokens and the block holding token len - W, and
+returns the sink length and window start the decode must use in the
+compacted positions, so that it attends exactly the first S and the last W
+tokens of the sequence as it was before the eviction.
 """
 from __future__ import annotations
 
@@ -179,6 +191,39 @@ class AllocModel:
         self.blocks[seq] = blocks
         self.swapped.discard(seq)
         return Status.OK, list(blocks)
+
+    def _release(self, blocks):
+        for blk in reversed(blocks):
+            self.rc[blk] -= 1
+            if self.rc[blk] == 0:
+                self.stack.append(blk)
+
+    def evict_blocks(self, seq, first, count) -> int:
+        if seq not in self.blocks:
+            return Status.UNKNOWN_SEQ
+        full = self.lens[seq] // self.bs
+        if seq in self.swapped or first < 0 or count < 0 or first + count > full:
+            return Status.INVALID_ARG
+        blocks = self.blocks[seq]
+        self._release(blocks[first:first + count])
+        self.blocks[seq] = blocks[:first] + blocks[first + count:]
+        self.lens[seq] -= count * self.bs
+        return Status.OK
+
+    def streaming_evict(self, seq, sink_tokens, window_tokens):
+        """(status, sink_len, window_start, evicted_blocks)."""
+        if seq not in self.blocks:
+            return Status.UNKNOWN_SEQ, None, None, None
+        if seq in self.swapped or sink_tokens < 0 or window_tokens < 0:
+            return Status.INVALID_ARG, None, None, None
+        L, bs = self.lens[seq], self.bs
+        if L <= sink_tokens + window_tokens:
+            return Status.OK, 0, 0, 0  # everything is kept and attended
+        first = _ceil_div(sink_tokens, bs)
+        count = max((L - window_tokens) // bs - first, 0)
+        st = self.evict_blocks(seq, first, count)
+        assert st == Status.OK
+        return Status.OK, sink_tokens, L - window_tokens - count * bs, count
 
     def seq_len(self, seq):
         if seq not in self.blocks:

@@ -29,7 +29,7 @@ def _scalar_decoder(dtype):
 
 
 def brute_decode(q, q_dtype, k_pool, v_pool, kv_dtype, block_tables, context_lens, scale, bs,
-                 k_scale=None, v_scale=None):
+                 k_scale=None, v_scale=None, sink_lens=None, window_starts=None):
     qd = _scalar_decoder(q_dtype)
     kd = _scalar_decoder(kv_dtype)
     q = np.asarray(q)
@@ -43,6 +43,8 @@ def brute_decode(q, q_dtype, k_pool, v_pool, kv_dtype, block_tables, context_len
     out = [[[0.0] * d for _ in range(H_q)] for _ in range(B)]
     for b in range(B):
         n = int(context_lens[b])
+        sink = 0 if sink_lens is None else int(sink_lens[b])
+        wst = 0 if window_starts is None else int(window_starts[b])
         for h in range(H_q):
             g = h // G
             ks = float(np.float32(k_scale[g])) if kv_dtype == "e4m3" else 1.0
@@ -50,6 +52,8 @@ def brute_decode(q, q_dtype, k_pool, v_pool, kv_dtype, block_tables, context_len
             qv = [qd(q[b, h, i]) for i in range(d)]
             weights, vrows = [], []
             for t in range(n):
+                if sink <= t < wst:  # dropped by the sink + window rule
+                    continue
                 blk = int(block_tables[b][t // bs])
                 assert 0 <= blk < NB
                 off = t % bs
@@ -63,7 +67,7 @@ def brute_decode(q, q_dtype, k_pool, v_pool, kv_dtype, block_tables, context_len
                 s = sc * math.fsum(a * c for a, c in zip(qv, krow))
                 weights.append(math.exp(s))
                 vrows.append(vrow)
-            if n:
+            if weights:
                 den = math.fsum(weights)
                 out[b][h] = [math.fsum(w * vr[i] for w, vr in zip(weights, vrows)) / den
                              for i in range(d)]

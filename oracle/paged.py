@@ -119,16 +119,28 @@ def gather_sequence(k_pool, v_pool, kv_dtype, table_row, n, bs, k_scale=None, v_
     return K, V
 
 
+def attended(n, sink_len=0, window_start=0):
+    """Logical positions a decode attends: t < n with t < sink_len or t >= window_start.
+
+    "Paged Attention and KV Cache Fragmentation", section "A fragmentation problem that paging
+    itself creates: block-level eviction mismatch": StreamingLLM keeps a few attention-sink tokens
+    at the start plus a window of recent tokens and drops the rest.  With sink_len = 0 the window
+    start is a plain per-sequence start offset; with window_start <= sink_len nothing is dropped."""
+    t = np.arange(n)
+    return (t < sink_len) | (t >= window_start)
+
+
 def ref_decode(q, q_dtype, k_pool, v_pool, kv_dtype, block_tables, context_lens, scale, bs,
-               k_scale=None, v_scale=None, rows=None):
+               k_scale=None, v_scale=None, rows=None, sink_lens=None, window_starts=None):
     """Paged decode attention, gather-then-attend, fp64.
 
     q [B, H_q, d] (fp32 values or bf16 bits); returns fp64 [B, H_q, d].
     For sequence b with n = context_lens[b] > 0 and query head h (KV head g = h // G):
-        s_t = scale * <q[b,h], K_b[g, t]>,  t < n
+        s_t = scale * <q[b,h], K_b[g, t]>,  t in A_b
         o[b,h] = sum_t exp(s_t - max s) V_b[g, t] / sum_t exp(s_t - max s)
-    n = 0 gives a zero row.  `rows` optionally restricts the work to some batch entries
-    (other rows are left zero).
+    where A_b = attended(n, sink_lens[b], window_starts[b]) (all t < n when both are None).
+    An empty A_b (n = 0 among others) gives a zero row.  `rows` optionally restricts the work
+    to some batch entries (other rows are left zero).
     """
     q64 = to_f64(q, q_dtype)
     B, H_q, d = q64.shape
@@ -139,9 +151,12 @@ def ref_decode(q, q_dtype, k_pool, v_pool, kv_dtype, block_tables, context_lens,
     out = np.zeros((B, H_q, d), np.float64)
     for b in (range(B) if rows is None else rows):
         n = int(context_lens[b])
-        if n == 0:
+        keep = attended(n, 0 if sink_lens is None else int(sink_lens[b]),
+                        0 if window_starts is None else int(window_starts[b]))
+        if not keep.any():
             continue
         K, V = gather_sequence(k_pool, v_pool, kv_dtype, block_tables[b], n, bs, k_scale, v_scale)
+        K, V = K[:, keep], V[:, keep]
         for h in range(H_q):
             g = h // G
             s = s64 * (K[g] @ q64[b, h])
@@ -151,7 +166,7 @@ def ref_decode(q, q_dtype, k_pool, v_pool, kv_dtype, block_tables, context_lens,
 
 
 __all__ = ["pool_shapes", "lanes_per_16b", "empty_pools", "to_f64", "ref_append",
-           "gather_sequence", "ref_decode"]
+           "gather_sequence", "ref_decode", "attended"]
 
 
 def ref_copy_blocks(k_pool, v_pool, pairs):
