@@ -16,6 +16,8 @@
  *   pkv_gather_blocks / pkv_scatter_blocks  pack blocks into / unpack from a
  *                          contiguous staging buffer (swap-out / swap-in)
  *   pkv_paged_attn_decode  one query token per sequence attends over its paged KV
+ *   pkv_paged_attn_decode_window  the same, attending only sink tokens and a
+ *                          recent window (StreamingLLM; with pkv_seq_streaming_evict)
  *   pkv_alloc_* / pkv_seq_* host-side fixed-block free-list allocator
  *
  * ---------------------------------------------------------------------------
@@ -192,6 +194,33 @@ int pkv_paged_attn_decode(float* out, const void* q, int q_dtype, const void* k_
                           const float* v_scale, void* workspace, size_t workspace_bytes,
                           void* stream);
 
+/*
+ * pkv_paged_attn_decode_window — pkv_paged_attn_decode over part of each
+ * sequence: sequence b attends the positions t < n with t < sink_lens[b] or
+ * t >= window_starts[b] (positions in its current table).  A row that attends
+ * nothing is zero.  ("Paged Attention and KV Cache Fragmentation", section
+ * "A fragmentation problem that paging itself creates: block-level eviction
+ * mismatch": StreamingLLM keeps a few attention-sink tokens at the start and
+ * a window of recent tokens.)
+ *
+ *   sink_lens, window_starts  device int32 [B], each may be NULL (= 0 for
+ *                  every sequence); a negative sink length counts as 0.  With
+ *                  sink_lens NULL, window_starts is a per-sequence start
+ *                  offset.  Both NULL: identical to pkv_paged_attn_decode.
+ * The positions between the two ranges are read from the table like any
+ * other (their blocks must be valid) but weigh nothing, NaN included; evict
+ * their whole blocks (pkv_seq_streaming_evict) so that they are not read.
+ * Other arguments, workspace included, as pkv_paged_attn_decode.
+ */
+int pkv_paged_attn_decode_window(float* out, const void* q, int q_dtype, const void* k_pool,
+                                 const void* v_pool, int kv_dtype, const int32_t* block_tables,
+                                 int32_t max_blocks_per_seq, const int32_t* context_lens,
+                                 int32_t max_context_len, const int32_t* sink_lens,
+                                 const int32_t* window_starts, int32_t B, int32_t H_q, int32_t H_kv,
+                                 int32_t D, int32_t NB, int32_t bs, float scale, const float* k_scale,
+                                 const float* v_scale, void* workspace, size_t workspace_bytes,
+                                 void* stream);
+
 /* ---------------------------------------------------------------------------
  * Host allocator: fixed-size blocks, LIFO free list, per-block refcounts.
  * ("Paged Attention and KV Cache Fragmentation", section "How PagedAttention
@@ -227,7 +256,16 @@ int pkv_paged_attn_decode(float* out, const void* q, int q_dtype, const void* k_
  *     free forgets it;
  *   - swap-in: ceil(len/bs) fresh blocks, all-or-nothing (OUT_OF_BLOCKS
  *     changes nothing), popped in logical order and returned; restore the
- *     contents with pkv_scatter_blocks.
+ *     contents with pkv_scatter_blocks;
+ *   - evict_blocks(first, count): full logical blocks [first, first+count)
+ *     leave the sequence; its table closes the gap, its length drops by
+ *     count*bs, the blocks are released last to first as by free.  A range
+ *     that is not made of full blocks of a resident sequence: INVALID_ARG;
+ *   - streaming_evict(S, W): if len <= S + W nothing changes and the decode
+ *     attends everything (sink_len = window_start = 0).  Otherwise it evicts
+ *     blocks [ceil(S/bs), (len-W)/bs) (none if empty) and returns sink_len = S
+ *     and window_start = len - W - evicted*bs: with these, the decode attends
+ *     exactly the first S and the last W tokens the sequence had before.
  * -------------------------------------------------------------------------*/
 typedef struct pkv_allocator pkv_allocator;
 
@@ -250,6 +288,10 @@ int pkv_seq_swap_out(pkv_allocator* a, int64_t seq, int32_t* blocks_out, int32_t
                      int32_t* n_out);
 int pkv_seq_swap_in(pkv_allocator* a, int64_t seq, int32_t* blocks_out, int32_t max_blocks,
                     int32_t* n_out);
+int pkv_seq_evict_blocks(pkv_allocator* a, int64_t seq, int32_t first, int32_t count);
+/* outputs: host int32 scalars */
+int pkv_seq_streaming_evict(pkv_allocator* a, int64_t seq, int32_t sink_tokens, int32_t window_tokens,
+                            int32_t* sink_len_out, int32_t* window_start_out, int32_t* evicted_out);
 int pkv_seq_len(const pkv_allocator* a, int64_t seq, int32_t* len_out);
 /* table_out: host int32 [n][max_blocks], padded with -1; lens_out: host int32 [n].
  * PKV_ERR_INVALID_ARG if a sequence holds more than max_blocks blocks. */

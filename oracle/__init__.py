@@ -21,7 +21,7 @@ from .formats import (bf16_bits_to_f64, e4m3_decode_table, e4m3_decode, e4m3_enc
                       E4M3_MAX)
 from .paged import (pool_shapes, lanes_per_16b, ref_append, ref_decode, gather_sequence,
                     empty_pools, ref_copy_blocks, ref_gather_blocks,
-                    ref_scatter_blocks)
+                    ref_scatter_blocks, attended)
 from .brute import brute_decode
 from .alloc_model import AllocModel, Status
 from .footprint import (bytes_per_token, request_bytes, memory_bill, kv_bytes_logical,
@@ -30,7 +30,7 @@ from .footprint import (bytes_per_token, request_bytes, memory_bill, kv_bytes_lo
 __all__ = [
     "bf16_bits_to_f64", "e4m3_decode_table", "e4m3_decode", "e4m3_encode", "E4M3_MAX",
     "pool_shapes", "lanes_per_16b", "ref_append", "ref_decode", "gather_sequence", "empty_pools",
-    "ref_copy_blocks", "ref_gather_blocks", "ref_scatter_blocks",
+    "ref_copy_blocks", "ref_gather_blocks", "ref_scatter_blocks", "attended",
     "brute_decode", "AllocModel", "Status",
     "bytes_per_token", "request_bytes", "memory_bill", "kv_bytes_logical", "kv_bytes_unique",
     "paged_waste", "contiguous_waste",

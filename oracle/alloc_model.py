@@ -221,8 +221,9 @@ class AllocModel:
             return Status.OK, 0, 0, 0  # everything is kept and attended
         first = _ceil_div(sink_tokens, bs)
         count = max((L - window_tokens) // bs - first, 0)
-        st = self.evict_blocks(seq, first, count)
-        assert st == Status.OK
+        if count:  # the blocks strictly between the sink blocks and the window's first block
+            st = self.evict_blocks(seq, first, count)
+            assert st == Status.OK
         return Status.OK, sink_tokens, L - window_tokens - count * bs, count
 
     def seq_len(self, seq):

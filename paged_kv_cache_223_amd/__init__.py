@@ -53,6 +53,9 @@ SIGNATURES = {
     "pkv_paged_attn_decode": (ctypes.c_int, [_P, _P, ctypes.c_int, _P, _P, ctypes.c_int, _P, _I32, _P, _I32,
                                              _I32, _I32, _I32, _I32, _I32, _I32, ctypes.c_float, _P, _P, _P,
                                              _SZ, _P]),
+    "pkv_paged_attn_decode_window": (ctypes.c_int, [_P, _P, ctypes.c_int, _P, _P, ctypes.c_int, _P, _I32, _P,
+                                                    _I32, _P, _P, _I32, _I32, _I32, _I32, _I32, _I32,
+                                                    ctypes.c_float, _P, _P, _P, _SZ, _P]),
     "pkv_alloc_create": (ctypes.c_int, [_I32, _I32, _P, ctypes.POINTER(_P)]),
     "pkv_alloc_destroy": (None, [_P]),
     "pkv_alloc_num_free": (_I32, [_P]),
@@ -63,6 +66,8 @@ SIGNATURES = {
     "pkv_seq_free": (ctypes.c_int, [_P, _I64]),
     "pkv_seq_swap_out": (ctypes.c_int, [_P, _I64, _P, _I32, _P]),
     "pkv_seq_swap_in": (ctypes.c_int, [_P, _I64, _P, _I32, _P]),
+    "pkv_seq_evict_blocks": (ctypes.c_int, [_P, _I64, _I32, _I32]),
+    "pkv_seq_streaming_evict": (ctypes.c_int, [_P, _I64, _I32, _I32, _P, _P, _P]),
     "pkv_seq_len": (ctypes.c_int, [_P, _I64, _P]),
     "pkv_block_tables": (ctypes.c_int, [_P, _P, _I32, _I32, _P, _P]),
     "pkv_block_refcount": (_I32, [_P, _I32]),
@@ -270,18 +275,21 @@ def _cached_workspace(device, need: int):
 
 
 def paged_attn_decode(q, k_pool, v_pool, block_tables, context_lens, scale: float, max_context_len: int,
-                      k_scale=None, v_scale=None, out=None, workspace=None):
-    """Decode attention of one query token per sequence over its paged KV; fp32 [B, H_q, D]."""
+                      k_scale=None, v_scale=None, out=None, workspace=None, sink_lens=None, window_starts=None):
+    """Decode attention of one query token per sequence over its paged KV; fp32 [B, H_q, D].
+    With sink_lens and/or window_starts (int32 [B]) sequence b attends only t < sink_lens[b] or
+    t >= window_starts[b] (pkv_paged_attn_decode_window)."""
     torch = _torch()
-    _dev(q, k_pool, v_pool, block_tables, context_lens, k_scale, v_scale, out, workspace)
+    _dev(q, k_pool, v_pool, block_tables, context_lens, k_scale, v_scale, out, workspace, sink_lens, window_starts)
     kv, NB, H_kv, D, bs = _pool_dims(k_pool, v_pool)
     if q.dim() != 3 or q.shape[2] != D:
         raise ValueError("q must be [B, H_q, D]")
     B, H_q, _ = q.shape
     if block_tables.dtype != torch.int32 or block_tables.dim() != 2 or block_tables.shape[0] != B:
         raise ValueError("block_tables must be int32 [B, max_blocks]")
-    if context_lens.dtype != torch.int32 or context_lens.shape != (B,):
-        raise ValueError("context_lens must be int32 [B]")
+    for t in (context_lens, sink_lens, window_starts):
+        if t is not None and (t.dtype != torch.int32 or t.shape != (B,)):
+            raise ValueError("context_lens, sink_lens and window_starts must be int32 [B]")
     if out is None:
         out = torch.empty((B, H_q, D), dtype=torch.float32, device=q.device)
     elif out.dtype != torch.float32 or tuple(out.shape) != (B, H_q, D):
@@ -290,10 +298,17 @@ def paged_attn_decode(q, k_pool, v_pool, block_tables, context_lens, scale: floa
     if workspace is None and need:
         workspace = _cached_workspace(q.device, need)
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
-    _check(lib.pkv_paged_attn_decode(
-        _ptr(out), _ptr(q), dtype_code(q), _ptr(k_pool), _ptr(v_pool), kv, _ptr(block_tables),
-        block_tables.shape[1], _ptr(context_lens), int(max_context_len), B, H_q, H_kv, D, NB, bs,
-        float(scale), _ptr(k_scale), _ptr(v_scale), _ptr(workspace), ws_bytes, _stream()))
+    if sink_lens is None and window_starts is None:
+        _check(lib.pkv_paged_attn_decode(
+            _ptr(out), _ptr(q), dtype_code(q), _ptr(k_pool), _ptr(v_pool), kv, _ptr(block_tables),
+            block_tables.shape[1], _ptr(context_lens), int(max_context_len), B, H_q, H_kv, D, NB, bs,
+            float(scale), _ptr(k_scale), _ptr(v_scale), _ptr(workspace), ws_bytes, _stream()))
+    else:
+        _check(lib.pkv_paged_attn_decode_window(
+            _ptr(out), _ptr(q), dtype_code(q), _ptr(k_pool), _ptr(v_pool), kv, _ptr(block_tables),
+            block_tables.shape[1], _ptr(context_lens), int(max_context_len), _ptr(sink_lens), _ptr(window_starts),
+            B, H_q, H_kv, D, NB, bs, float(scale), _ptr(k_scale), _ptr(v_scale), _ptr(workspace), ws_bytes,
+            _stream()))
     return out
 
 
@@ -389,6 +404,16 @@ class Allocator:
         cnt = ctypes.c_int32()
         st = int(fn(self._h, int(seq), out.ctypes.data, cap, ctypes.byref(cnt)))
         return st, (out[:cnt.value].copy() if st == OK else None)
+
+    def evict_blocks(self, seq, first: int, count: int) -> int:
+        return int(lib.pkv_seq_evict_blocks(self._h, int(seq), int(first), int(count)))
+
+    def streaming_evict(self, seq, sink_tokens: int, window_tokens: int):
+        """(status, sink_len, window_start, evicted_blocks) for paged_attn_decode's masks."""
+        sl, ws, ev = ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int32()
+        st = int(lib.pkv_seq_streaming_evict(self._h, int(seq), int(sink_tokens), int(window_tokens),
+                                             ctypes.byref(sl), ctypes.byref(ws), ctypes.byref(ev)))
+        return (st, sl.value, ws.value, ev.value) if st == OK else (st, None, None, None)
 
     def seq_len(self, seq):
         n = ctypes.c_int32()

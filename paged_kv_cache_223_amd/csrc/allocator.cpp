@@ -9,9 +9,12 @@
 // field guide (defragging.ai), section "Why it matters": sharing makes forks
 // cheap.  Section "Offloading paged KV blocks to CPU DRAM and NVMe": blocks of
 // a sequence that is not running move to host memory and come back later
-// (swap-out / swap-in).  Exact semantics (LIFO order, all-or-nothing appends,
-// the shared partial-block rule, copy-on-write appends, reverse-order frees,
-// swaps) are spelled out in pkv.h.
+// (swap-out / swap-in).  Section "A fragmentation problem that paging itself
+// creates: block-level eviction mismatch": eviction of whole blocks keeps the
+// paged structure; StreamingLLM keeps sink tokens plus a recent window.  Exact
+// semantics (LIFO order, all-or-nothing appends, the shared partial-block rule,
+// copy-on-write appends, reverse-order frees, swaps, block eviction) are
+// spelled out in pkv.h.
 
 #include <stdint.h>
 
@@ -247,6 +250,62 @@ int pkv_seq_swap_in(pkv_allocator* a, int64_t seq, int32_t* blocks_out, int32_t 
   }
   *n_out = (int32_t)need;
   s.swapped = false;
+  return PKV_OK;
+}
+
+int pkv_seq_evict_blocks(pkv_allocator* a, int64_t seq, int32_t first, int32_t count) {
+  if (!a) return PKV_ERR_INVALID_ARG;
+  auto it = a->seqs.find(seq);
+  if (it == a->seqs.end()) {
+    set_error("evict_blocks: unknown sequence %lld", (long long)seq);
+    return PKV_ERR_UNKNOWN_SEQ;
+  }
+  auto& s = it->second;
+  const int64_t full = s.len / a->bs;
+  if (s.swapped || first < 0 || count < 0 || (int64_t)first + count > full) {
+    set_error("evict_blocks: blocks [%d, %d) are not full blocks of resident sequence %lld", first,
+              first + count, (long long)seq);
+    return PKV_ERR_INVALID_ARG;
+  }
+  const std::vector<int32_t> gone(s.blocks.begin() + first, s.blocks.begin() + first + count);
+  release_blocks(a, gone);
+  s.blocks.erase(s.blocks.begin() + first, s.blocks.begin() + first + count);
+  s.len -= (int64_t)count * a->bs;
+  return PKV_OK;
+}
+
+int pkv_seq_streaming_evict(pkv_allocator* a, int64_t seq, int32_t sink_tokens, int32_t window_tokens,
+                            int32_t* sink_len_out, int32_t* window_start_out, int32_t* evicted_out) {
+  if (!a || !sink_len_out || !window_start_out || !evicted_out || sink_tokens < 0 || window_tokens < 0) {
+    set_error("streaming_evict: bad arguments");
+    return PKV_ERR_INVALID_ARG;
+  }
+  auto it = a->seqs.find(seq);
+  if (it == a->seqs.end()) {
+    set_error("streaming_evict: unknown sequence %lld", (long long)seq);
+    return PKV_ERR_UNKNOWN_SEQ;
+  }
+  if (it->second.swapped) {
+    set_error("streaming_evict: sequence %lld is swapped out", (long long)seq);
+    return PKV_ERR_INVALID_ARG;
+  }
+  const int64_t L = it->second.len, bs = a->bs;
+  if (L <= (int64_t)sink_tokens + window_tokens) {  // everything is kept and attended
+    *sink_len_out = 0;
+    *window_start_out = 0;
+    *evicted_out = 0;
+    return PKV_OK;
+  }
+  const int64_t first = ceil_div(sink_tokens, bs);
+  int64_t count = (L - window_tokens) / bs - first;
+  if (count < 0) count = 0;
+  if (count > 0) {  // the blocks strictly between the sink blocks and the window's first block
+    const int st = pkv_seq_evict_blocks(a, seq, (int32_t)first, (int32_t)count);
+    if (st != PKV_OK) return st;
+  }
+  *sink_len_out = sink_tokens;
+  *window_start_out = (int32_t)(L - window_tokens - count * bs);
+  *evicted_out = (int32_t)count;
   return PKV_OK;
 }
 

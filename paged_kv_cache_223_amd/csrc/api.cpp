@@ -212,12 +212,12 @@ size_t pkv_decode_workspace_bytes(int32_t B, int32_t H_q, int32_t H_kv, int32_t 
   return workspace_bytes_for(B, H_q, H_kv, D, plan_splits(B, H_kv, max_context_len), current_num_cus());
 }
 
-int pkv_paged_attn_decode(float* out, const void* q, int q_dtype, const void* k_pool, const void* v_pool,
-                          int kv_dtype, const int32_t* block_tables, int32_t max_blocks_per_seq,
-                          const int32_t* context_lens, int32_t max_context_len, int32_t B, int32_t H_q, int32_t H_kv,
-                          int32_t D, int32_t NB, int32_t bs, float scale, const float* k_scale,
-                          const float* v_scale, void* workspace, size_t workspace_bytes, void* stream) {
-  g_err[0] = 0;
+static int decode_impl(float* out, const void* q, int q_dtype, const void* k_pool, const void* v_pool, int kv_dtype,
+                       const int32_t* block_tables, int32_t max_blocks_per_seq, const int32_t* context_lens,
+                       int32_t max_context_len, const int32_t* sink_lens, const int32_t* window_starts, int32_t B,
+                       int32_t H_q, int32_t H_kv, int32_t D, int32_t NB, int32_t bs, float scale,
+                       const float* k_scale, const float* v_scale, void* workspace, size_t workspace_bytes,
+                       void* stream) {
   if (B < 0 || H_q <= 0 || H_kv <= 0 || NB <= 0 || max_blocks_per_seq <= 0 || max_context_len < 0) {
     set_error("decode: bad sizes B=%d H_q=%d H_kv=%d NB=%d max_blocks=%d max_context_len=%d", B, H_q, H_kv, NB,
               max_blocks_per_seq, max_context_len);
@@ -271,6 +271,8 @@ int pkv_paged_attn_decode(float* out, const void* q, int q_dtype, const void* k_
   a.v_pool = v_pool;
   a.block_tables = block_tables;
   a.context_lens = context_lens;
+  a.sink_lens = sink_lens;
+  a.window_starts = window_starts;
   a.k_scale = k_scale;
   a.v_scale = v_scale;
   if (need > 0) {
@@ -299,6 +301,29 @@ int pkv_paged_attn_decode(float* out, const void* q, int q_dtype, const void* k_
   const int st = hip_status(launch_decode_vector(a, s), "decode launch");
   if (st != PKV_OK || plan.max_splits <= 1) return st;
   return hip_status(launch_split_merge(a, s), "split merge launch");
+}
+
+int pkv_paged_attn_decode(float* out, const void* q, int q_dtype, const void* k_pool, const void* v_pool,
+                          int kv_dtype, const int32_t* block_tables, int32_t max_blocks_per_seq,
+                          const int32_t* context_lens, int32_t max_context_len, int32_t B, int32_t H_q, int32_t H_kv,
+                          int32_t D, int32_t NB, int32_t bs, float scale, const float* k_scale,
+                          const float* v_scale, void* workspace, size_t workspace_bytes, void* stream) {
+  g_err[0] = 0;
+  return decode_impl(out, q, q_dtype, k_pool, v_pool, kv_dtype, block_tables, max_blocks_per_seq, context_lens,
+                     max_context_len, nullptr, nullptr, B, H_q, H_kv, D, NB, bs, scale, k_scale, v_scale, workspace,
+                     workspace_bytes, stream);
+}
+
+int pkv_paged_attn_decode_window(float* out, const void* q, int q_dtype, const void* k_pool, const void* v_pool,
+                                 int kv_dtype, const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                 const int32_t* context_lens, int32_t max_context_len, const int32_t* sink_lens,
+                                 const int32_t* window_starts, int32_t B, int32_t H_q, int32_t H_kv, int32_t D,
+                                 int32_t NB, int32_t bs, float scale, const float* k_scale, const float* v_scale,
+                                 void* workspace, size_t workspace_bytes, void* stream) {
+  g_err[0] = 0;
+  return decode_impl(out, q, q_dtype, k_pool, v_pool, kv_dtype, block_tables, max_blocks_per_seq, context_lens,
+                     max_context_len, sink_lens, window_starts, B, H_q, H_kv, D, NB, bs, scale, k_scale, v_scale,
+                     workspace, workspace_bytes, stream);
 }
 
 size_t pkv_stream_read_sink_floats(size_t bytes) { return stream_read_blocks(bytes); }

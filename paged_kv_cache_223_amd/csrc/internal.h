@@ -78,6 +78,8 @@ struct DecodeArgs {
   const void* v_pool;
   const int32_t* block_tables;
   const int32_t* context_lens;
+  const int32_t* sink_lens;      // optional [B]: attend t < sink_lens[b] ...
+  const int32_t* window_starts;  // optional [B]: ... or t >= window_starts[b] (both null: every t < n)
   const float* k_scale;
   const float* v_scale;
   float* ws_o;   // [B][H_q][max_splits][D] split partial outputs (unnormalised)

@@ -213,6 +213,16 @@ __device__ __forceinline__ u32x4 tokens_by_eight(u32x4 v) {
   return r;
 }
 
+// The hole [lo, hi) of logical positions sequence b does not attend: without
+// masks it is empty; with them, t < n is attended iff t < sink or t >= window.
+__device__ __forceinline__ void seq_hole(const DecodeArgs& a, int b, int& lo, int& hi) {
+  lo = 0;
+  hi = 0;
+  if (a.sink_lens) lo = max(a.sink_lens[b], 0);
+  if (a.window_starts) hi = a.window_starts[b];
+  hi = max(hi, lo);
+}
+
 struct WaveState {
   float m;  // running max of head (lane & 15), log2 units, same in the head's 4 lanes
   float l;  // this lane's share of the running sum
@@ -221,10 +231,11 @@ struct WaveState {
 template <int D, int BS, int KVT>
 __device__ __forceinline__ void process_chunk(const Chunk<D, BS, KVT>& ch, const u32x4 (&qop)[D / 32],
                                               f32x4 (&acc)[D / 16], WaveState& st, int chunk, int n,
-                                              float sl, int lane) {
+                                              int hlo, int hhi, float sl, int lane) {
   const int cs = chunk * 32;
   const int kg = lane >> 4;
-  const bool tail = cs + 32 > n;  // wave-uniform
+  // wave-uniform: the chunk holds a token past n or inside the hole [hlo, hhi)
+  const bool tail = cs + 32 > n || (cs < hhi && cs + 32 > hlo);
   // ---- S^T = K Q^T for the two 16-token halves
   f32x4 s[2];
 #pragma unroll
@@ -248,7 +259,10 @@ __device__ __forceinline__ void process_chunk(const Chunk<D, BS, KVT>& ch, const
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       float v = s[a][i] * sl;
-      if (tail) v = (cs + 16 * a + 4 * kg + i < n) ? v : -INFINITY;
+      if (tail) {
+        const int t = cs + 16 * a + 4 * kg + i;
+        v = (t < n && (t < hlo || t >= hhi)) ? v : -INFINITY;
+      }
       x[4 * a + i] = v;
     }
   // ---- chunk max per head: 8 values in the lane, then the head's 4 lanes
@@ -273,10 +287,16 @@ __device__ __forceinline__ void process_chunk(const Chunk<D, BS, KVT>& ch, const
   // ---- P = exp2(x - m): keep fp32 sum, split into bf16 hi + lo for the MFMA
   uint32_t hb[8];
   float lo[8];
+  float pj[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) pj[j] = exp2_fast(x[j] - st.m);
+  if (tail)  // a masked token weighs 0, also while no token has been seen (m = -inf)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) pj[j] = x[j] == -INFINITY ? 0.f : pj[j];
   float psum = 0.f;
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
-    const float p = exp2_fast(x[j] - st.m);
+    const float p = pj[j];
     psum += p;
     const uint32_t bits = __builtin_bit_cast(uint32_t, p);
     hb[j] = bits;
@@ -298,8 +318,9 @@ __device__ __forceinline__ void process_chunk(const Chunk<D, BS, KVT>& ch, const
   if (tail) {
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
-      const int t0 = cs + 8 * kg + 2 * w;
-      vmask[w] = (t0 < n ? 0x0000FFFFu : 0u) | (t0 + 1 < n ? 0xFFFF0000u : 0u);
+      const int t0 = cs + 8 * kg + 2 * w, t1 = t0 + 1;
+      const bool ok0 = t0 < n && (t0 < hlo || t0 >= hhi), ok1 = t1 < n && (t1 < hlo || t1 >= hhi);
+      vmask[w] = (ok0 ? 0x0000FFFFu : 0u) | (ok1 ? 0xFFFF0000u : 0u);
     }
   }
   // ---- O += P V
@@ -416,8 +437,8 @@ __device__ int plan_piece(const DecodeArgs& a, int target, int item, int lane, P
 // The wave's share of one piece: chunks first, first + NW, ... below c_end of
 // segment (b, g), with the next chunk's loads in flight while one is computed.
 template <int D, int BS, int KVT, int NW>
-__device__ __forceinline__ void run_piece(const DecodeArgs& a, int b, int g, int n, int first, int c_end,
-                                          f32x4 (&acc)[D / 16], WaveState& st, int lane) {
+__device__ __forceinline__ void run_piece(const DecodeArgs& a, int b, int g, int n, int hlo, int hhi, int first,
+                                          int c_end, f32x4 (&acc)[D / 16], WaveState& st, int lane) {
   const int G = a.G;
   const int last_blk = (n + BS - 1) / BS - 1;
   const int32_t* tab = a.block_tables + (size_t)b * a.max_blocks;
@@ -448,17 +469,17 @@ __device__ __forceinline__ void run_piece(const DecodeArgs& a, int b, int g, int
   int k = 0;
   for (; k + 2 < cnt; k += 2) {
     load_chunk(Bf, kpool, vpool, tab, c + NW, last_blk, a.NB, a.H_kv, g, lane);
-    process_chunk(A, qop, acc, st, c, n, sl, lane);
+    process_chunk(A, qop, acc, st, c, n, hlo, hhi, sl, lane);
     load_chunk(A, kpool, vpool, tab, c + 2 * NW, last_blk, a.NB, a.H_kv, g, lane);
-    process_chunk(Bf, qop, acc, st, c + NW, n, sl, lane);
+    process_chunk(Bf, qop, acc, st, c + NW, n, hlo, hhi, sl, lane);
     c += 2 * NW;
   }
   if (k + 1 < cnt) {
     load_chunk(Bf, kpool, vpool, tab, c + NW, last_blk, a.NB, a.H_kv, g, lane);
-    process_chunk(A, qop, acc, st, c, n, sl, lane);
-    process_chunk(Bf, qop, acc, st, c + NW, n, sl, lane);
+    process_chunk(A, qop, acc, st, c, n, hlo, hhi, sl, lane);
+    process_chunk(Bf, qop, acc, st, c + NW, n, hlo, hhi, sl, lane);
   } else {
-    process_chunk(A, qop, acc, st, c, n, sl, lane);
+    process_chunk(A, qop, acc, st, c, n, hlo, hhi, sl, lane);
   }
 }
 
@@ -485,9 +506,13 @@ __global__ __launch_bounds__(64 * NW, KVT == PKV_FP8_E4M3 ? 3 : 2) void decode_p
   const int b = pp.b, g = uniform(pp.g), np = uniform(pp.np);
   const int lo = uniform(pp.lo), hi = uniform(pp.hi);
   const int n = uniform(seq_len(a.context_lens, b, cap));
+  int hlo, hhi;
+  seq_hole(a, b, hlo, hhi);
+  hlo = uniform(hlo);
+  hhi = uniform(hhi);
   f32x4 acc[D / 16];
   WaveState st;
-  run_piece<D, BS, KVT, NW>(a, b, g, n, lo + w, hi, acc, st, lane);
+  run_piece<D, BS, KVT, NW>(a, b, g, n, hlo, hhi, lo + w, hi, acc, st, lane);
   // ---- merge the NW waves' shares through LDS
   const int kg = lane >> 4;
   float lt = st.l;
@@ -512,14 +537,14 @@ __global__ __launch_bounds__(64 * NW, KVT == PKV_FP8_E4M3 ? 3 : 2) void decode_p
     for (int i = 1; i < NW; ++i) M = fmaxf(M, sh_m[i][hh]);
     float L = 0.f, O = 0.f;
 #pragma unroll
-    for (int i = 0; i < NW; ++i) {
-      const float wt = exp2_fast(sh_m[i][hh] - M);
+    for (int i = 0; i < NW; ++i) {  // a wave that attended nothing (m = -inf) weighs 0
+      const float wt = sh_m[i][hh] == -INFINITY ? 0.f : exp2_fast(sh_m[i][hh] - M);
       L += wt * sh_l[i][hh];
       O += wt * sh_acc[i][hh][col];
     }
     O *= vs;
     if (np == 1) {
-      a.out[orow + e] = O / L;
+      a.out[orow + e] = L > 0.f ? O / L : 0.f;  // nothing attended: zero row
     } else {
       a.ws_o[(prow + hh) * D + col] = O;
       if (col == 0) {
@@ -567,6 +592,7 @@ __global__ __launch_bounds__(256) void piece_merge_kernel(DecodeArgs a, int targ
       for (int p = p0; p < np; p += 16) {
         const size_t r = (size_t)(first + p) * 16 + h;
         const float mp = a.ws_ml[2 * r], lp = a.ws_ml[2 * r + 1];
+        if (mp == -INFINITY) continue;  // a piece that attended nothing
         const float mn = fmaxf(m, mp);
         l = (m == -INFINITY ? 0.f : l * exp2_fast(m - mn)) + lp * exp2_fast(mp - mn);
         m = mn;
@@ -582,8 +608,9 @@ __global__ __launch_bounds__(256) void piece_merge_kernel(DecodeArgs a, int targ
     float L = 0.f;
     for (int i = 0; i < 16; ++i)
       if (sh_red[i][tid][0] != -INFINITY) L += sh_red[i][tid][1] * exp2_fast(sh_red[i][tid][0] - M);
-    sh_M[tid] = M;
-    sh_iL[tid] = 1.f / L;
+    // nothing attended in any piece: zero row (every piece weight exp2(-inf - 0) is 0)
+    sh_M[tid] = M == -INFINITY ? 0.f : M;
+    sh_iL[tid] = L > 0.f ? 1.f / L : 0.f;
   }
   __syncthreads();
   // ---- outputs: each thread owns (head, column) elements and sums their pieces
@@ -648,6 +675,8 @@ __global__ __launch_bounds__(64) void decode_vector_kernel(DecodeArgs a) {
   const int X = 16 / elem_bytes_dev(kvt);
   const int t_begin = split * a.split_tokens;
   const int t_end = min(n, t_begin + a.split_tokens);
+  int hlo, hhi;
+  seq_hole(a, b, hlo, hhi);
   const int last_blk = (n + bs - 1) / bs - 1;
   const int32_t* tab = a.block_tables + (size_t)b * a.max_blocks;
   for (int d = lane; d < D; d += 64) sh_q[d] = load_elem(a.q, orow + d, a.q_dtype);
@@ -663,7 +692,7 @@ __global__ __launch_bounds__(64) void decode_vector_kernel(DecodeArgs a) {
   for (int k = 0; k < KD; ++k) acc[k] = 0.f;
   for (int t0 = t_begin; t0 < t_end; t0 += 64) {
     const int tok = t0 + lane;
-    const bool valid = tok < t_end;
+    const bool valid = tok < t_end && (tok < hlo || tok >= hhi);
     float s = -INFINITY;
     int blk = 0, off = 0;
     if (valid) {
@@ -678,19 +707,20 @@ __global__ __launch_bounds__(64) void decode_vector_kernel(DecodeArgs a) {
     float tm = s;
     for (int o = 32; o; o >>= 1) tm = fmaxf(tm, __shfl_xor(tm, o, 64));
     const float mn = fmaxf(m, tm);
-    const float alpha = exp2_fast(m - mn);
+    const float alpha = mn == -INFINITY ? 1.f : exp2_fast(m - mn);  // nothing attended yet: no rescale
     const float p = valid ? exp2_fast(s - mn) : 0.f;
     float ps = p;
     for (int o = 32; o; o >>= 1) ps += __shfl_xor(ps, o, 64);
     l = l * alpha + ps;
     sh_p[lane] = p;
-    sh_blk[lane] = blk;
+    sh_blk[lane] = valid ? blk : -1;  // masked tokens are skipped, so their V is never read
     sh_off[lane] = off;
     __syncthreads();
 #pragma unroll
     for (int k = 0; k < KD; ++k) acc[k] *= alpha;
     const int cnt = min(64, t_end - t0);
     for (int tt = 0; tt < cnt; ++tt) {
+      if (sh_blk[tt] < 0) continue;
       const float pp = sh_p[tt];
       const size_t tile = ((size_t)sh_blk[tt] * a.H_kv + g) * (size_t)D * bs;
 #pragma unroll
@@ -704,7 +734,7 @@ __global__ __launch_bounds__(64) void decode_vector_kernel(DecodeArgs a) {
   for (int k = 0; k < KD; ++k) {
     const int d = lane + 64 * k;
     if (nsplit == 1) {
-      a.out[orow + d] = acc[k] * vs / l;
+      a.out[orow + d] = l > 0.f ? acc[k] * vs / l : 0.f;  // nothing attended: zero row
     } else {
       const size_t pr = ((size_t)b * a.H_q + hq) * a.max_splits + split;
       a.ws_o[pr * D + d] = acc[k] * vs;
@@ -735,9 +765,10 @@ __global__ __launch_bounds__(256) void split_merge_kernel(DecodeArgs a) {
       float M = -INFINITY;
       for (int i = 0; i < nsplit; ++i) M = fmaxf(M, ml[2 * i]);
       float L = 0.f;
-      for (int i = 0; i < nsplit; ++i) L += exp2_fast(ml[2 * i] - M) * ml[2 * i + 1];
-      sh_M[tid] = M;
-      sh_iL[tid] = 1.f / L;
+      for (int i = 0; i < nsplit; ++i)
+        if (ml[2 * i] != -INFINITY) L += exp2_fast(ml[2 * i] - M) * ml[2 * i + 1];
+      sh_M[tid] = M == -INFINITY ? 0.f : M;  // nothing attended: zero row
+      sh_iL[tid] = L > 0.f ? 1.f / L : 0.f;
     }
     __syncthreads();
     for (int e = tid; e < nh * D; e += 256) {

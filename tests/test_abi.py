@@ -82,6 +82,32 @@ def test_decode_empty_batch_is_a_no_op():
     assert _decode(B=0) == pkv.OK
 
 
+def _decode_window(**kw):
+    a = dict(out=P, q=P, q_dtype=pkv.BF16, k=P, v=P, kv=pkv.BF16, tab=P, mb=4, lens=P, mcl=64, sinks=P, wins=P, B=2,
+             H_q=8, H_kv=2, D=128, NB=16, bs=16, scale=0.1, ks=None, vs=None, ws=None, wsb=0, stream=None)
+    a.update(kw)
+    return pkv.lib.pkv_paged_attn_decode_window(
+        a["out"], a["q"], a["q_dtype"], a["k"], a["v"], a["kv"], a["tab"], a["mb"], a["lens"], a["mcl"], a["sinks"],
+        a["wins"], a["B"], a["H_q"], a["H_kv"], a["D"], a["NB"], a["bs"], a["scale"], a["ks"], a["vs"], a["ws"],
+        a["wsb"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(H_q=6, H_kv=4), pkv.ERR_INVALID_ARG),
+    (dict(D=96), pkv.ERR_UNSUPPORTED),
+    (dict(bs=12), pkv.ERR_UNSUPPORTED),
+    (dict(out=None), pkv.ERR_INVALID_ARG),
+    (dict(), pkv.ERR_INVALID_ARG),  # needs a workspace, none given
+])
+def test_decode_window_rejects_bad_arguments_before_launch(kw, status):
+    assert _decode_window(**kw) == status
+    assert _decode_window(sinks=None, wins=None, **kw) == status
+
+
+def test_decode_window_empty_batch_is_a_no_op():
+    assert _decode_window(B=0) == pkv.OK
+
+
 def test_workspace_size_covers_both_paths():
     small = pkv.decode_workspace_bytes(4, 64, 8, 128, 200, 16)
     assert small > 0 and small % 4 == 0  # the matrix-core path always keeps its partial slots

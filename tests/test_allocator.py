@@ -164,6 +164,53 @@ def test_random_swap_ops_identical_to_model(seed):
     assert swaps >= 50
 
 
+@pytest.mark.parametrize("seed", range(4))
+def test_random_eviction_ops_identical_to_model(seed):
+    """Streaming evictions and explicit block evictions (valid and invalid ranges) mixed into
+    appends, forks and frees."""
+    rng = np.random.default_rng(900 + seed)
+    NB, bs = [80, 31, 150, 40][seed], [16, 4, 8, 1][seed]
+    cpp, model = _pair(NB, bs, rng.permutation(NB))
+    live, nid, evicted = [], 0, 0
+    for step in range(3000):
+        r = rng.random()
+        if r < 0.12 or not live:
+            assert cpp.seq_add(nid) == model.seq_add(nid) == 0
+            live.append(nid)
+            nid += 1
+        elif r < 0.5:
+            s = live[rng.integers(len(live))]
+            n = int(rng.integers(0, 3 * bs + 2))
+            st1, sl1, c1 = cpp.append_slots_cow(s, n)
+            st2, sl2, c2 = model.append_slots_cow(s, n)
+            assert st1 == st2 and (st1 != 0 or (list(sl1) == list(sl2) and c1 == c2))
+        elif r < 0.6:
+            s = live[rng.integers(len(live))]
+            assert cpp.fork(s, nid) == model.fork(s, nid) == 0
+            live.append(nid)
+            nid += 1
+        elif r < 0.72:
+            s = live[rng.integers(len(live))]
+            S, W = int(rng.integers(0, 3 * bs)), int(rng.integers(0, 6 * bs))
+            got = cpp.streaming_evict(s, S, W)
+            want = model.streaming_evict(s, S, W)
+            assert got == tuple(int(x) for x in want)
+            evicted += got[3] or 0
+        elif r < 0.8:
+            s = live[rng.integers(len(live))]
+            full = model.lens[s] // bs
+            first, count = int(rng.integers(-1, full + 2)), int(rng.integers(-1, 3))
+            assert cpp.evict_blocks(s, first, count) == model.evict_blocks(s, first, count)
+        else:
+            s = live.pop(rng.integers(len(live)))
+            assert cpp.free(s) == model.free(s) == 0
+        if step % 67 == 0:
+            _same_state(cpp, model, live)
+            for s in live:
+                assert cpp.seq_len(s) == model.seq_len(s)
+    assert evicted >= 20
+
+
 @pytest.mark.parametrize("builder", [
     lambda: workloads.tiny_f32(),
     lambda: workloads.llama8b_bf16(),

@@ -39,6 +39,11 @@ def test_worked_example_streaming_evict():
     m.append_slots(2, 10)  # blocks 1, 2, 6
     assert m.streaming_evict(2, 0, 5) == (Status.OK, 0, 1, 1)
     assert m.lens[2] == 6
+    # the sinks end inside the only (partial) block: nothing to evict, the rest is masked
+    m.seq_add(3)
+    m.append_slots(3, 3)
+    assert m.streaming_evict(3, 2, 0) == (Status.OK, 2, 3, 0)
+    assert list(np.nonzero(attended(3, 2, 3))[0]) == [0, 1]
     _check_invariants(m)
 
 
