@@ -165,8 +165,45 @@ def ref_decode(q, q_dtype, k_pool, v_pool, kv_dtype, block_tables, context_lens,
     return out
 
 
+def ref_prefill(q, q_dtype, k_pool, v_pool, kv_dtype, block_tables, context_lens, query_start, scale, bs,
+                k_scale=None, v_scale=None, seqs=None):
+    """Paged prefill (chunked multi-query attention) over the same pools, fp64.
+
+    The last C_b = query_start[b+1] - query_start[b] tokens of sequence b (n_b = context_lens[b]
+    tokens, their K/V already appended) are its queries, packed in q [T, H_q, d] at rows
+    query_start[b] ... query_start[b+1]-1.  Query i sits at position p = n_b - C_b + i and attends
+    causally: s_t = scale * <q_i, K_b[g, t]> for t <= p, o_i = softmax(s) V_b[g, :p+1].
+    Returns fp64 [T, H_q, d].  `seqs` optionally restricts the work (other rows stay zero).
+
+    "Paged Attention and KV Cache Fragmentation", section "How PagedAttention maps an OS concept
+    onto GPU memory": a sequence's blocks are taken as it grows; the prompt (or each chunk of
+    it) is written into them and attends over everything before it through the same table."""
+    q64 = to_f64(q, q_dtype)
+    T, H_q, d = q64.shape
+    H_kv = k_pool.shape[1]
+    G = H_q // H_kv
+    assert G * H_kv == H_q
+    s64 = float(np.float32(scale))
+    qs = np.asarray(query_start, np.int64)
+    out = np.zeros((T, H_q, d), np.float64)
+    for b in (range(len(qs) - 1) if seqs is None else seqs):
+        n, r0, C = int(context_lens[b]), int(qs[b]), int(qs[b + 1] - qs[b])
+        assert 0 <= C <= n
+        if C == 0:
+            continue
+        K, V = gather_sequence(k_pool, v_pool, kv_dtype, block_tables[b], n, bs, k_scale, v_scale)
+        for i in range(C):
+            p = n - C + i
+            for h in range(H_q):
+                g = h // G
+                s = s64 * (K[g, :p + 1] @ q64[r0 + i, h])
+                w = np.exp(s - s.max())
+                out[r0 + i, h] = (w @ V[g, :p + 1]) / w.sum()
+    return out
+
+
 __all__ = ["pool_shapes", "lanes_per_16b", "empty_pools", "to_f64", "ref_append",
-           "gather_sequence", "ref_decode", "attended"]
+           "gather_sequence", "ref_decode", "attended", "ref_prefill"]
 
 
 def ref_copy_blocks(k_pool, v_pool, pairs):
