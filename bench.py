@@ -58,9 +58,13 @@ def parse():
                    help="launch the step's kernels one by one instead of replaying a captured HIP graph")
     p.add_argument("--identity-tables", action="store_true",
                    help="lay every sequence out contiguously (identity block order) instead of scattered")
-    p.add_argument("--op", default="step", choices=["step", "copy_blocks", "swap"],
+    p.add_argument("--op", default="step", choices=["step", "copy_blocks", "swap", "prefill"],
                    help="step: the decode step (default); copy_blocks: copy-on-write block copies alone; "
-                        "swap: swap-out / swap-in of scattered blocks to and from pinned host memory")
+                        "swap: swap-out / swap-in of scattered blocks to and from pinned host memory; "
+                        "prefill: causal chunked prefill over the paged pools")
+    p.add_argument("--prior", type=int, default=2048, help="earlier tokens per sequence (--op prefill)")
+    p.add_argument("--chunk", type=int, default=2048, help="new tokens per sequence (--op prefill)")
+    p.add_argument("--seqs", type=int, default=4, help="sequences (--op prefill)")
     p.add_argument("--blocks", type=int, default=4096, help="blocks moved per swap call (--op swap)")
     p.add_argument("--pairs", type=int, default=4096, help="block pairs per copy_blocks call (--op copy_blocks)")
     p.add_argument("--sets", type=int, default=0,
@@ -148,6 +152,9 @@ def main():
         return
     if args.op == "swap":
         bench_swap(args, torch, pkv, dev)
+        return
+    if args.op == "prefill":
+        bench_prefill(args, torch, pkv, dev)
         return
     t_setup = time.time()
     wname, kw = WORKLOADS[args.workload]
@@ -422,6 +429,66 @@ def bench_swap(args, torch, pkv, dev):
         "config": {"workload": f"{n} scattered blocks, 70B-layer block shape (H_kv 8, D 128, bs 16)",
                    "blocks": n, "record_bytes": rec},
         "ways": res, "pinned_equals_device_gather": same}), flush=True)
+
+
+def bench_prefill(args, torch, pkv, dev):
+    """Causal chunked prefill on the 70B layer shape (H_q 64, H_kv 8, D 128, bf16, bs 16): `seqs`
+    sequences, each with `prior` earlier tokens and a `chunk` of new ones (appended before the
+    timed region).  FLOPs count the two products over the causal range only:
+    4 * H_q * D * sum over queries of (position + 1)."""
+    H_q, H_kv, D, bs = 64, 8, 128, 16
+    B, prior, C = args.seqs, args.prior, args.chunk
+    n = prior + C
+    nb = -(-n // bs)
+    NB = B * nb + 16
+    rng = np.random.default_rng(17)
+    alloc = pkv.Allocator(NB, bs, rng.permutation(NB).astype(np.int32))
+    slots = []
+    for b in range(B):
+        alloc.seq_add(b)
+        slots.append(alloc.append_slots(b, n)[1])
+    st, tab, lens = alloc.block_tables(list(range(B)), nb)
+    ks, vs = pkv.pool_shapes(NB, H_kv, D, bs, pkv.BF16)
+    k_pool = torch.empty(ks, dtype=torch.bfloat16, device=dev)
+    v_pool = torch.empty(vs, dtype=torch.bfloat16, device=dev)
+    kv = torch.randn((B * n, 2, H_kv, D), device=dev).to(torch.bfloat16)
+    pkv.kv_append(kv[:, 0].contiguous(), kv[:, 1].contiguous(), torch.from_numpy(np.concatenate(slots)).to(dev),
+                  k_pool, v_pool)
+    del kv
+    q = torch.randn((B * C, H_q, D), device=dev).to(torch.bfloat16)
+    qs = torch.arange(0, B * C + 1, C, dtype=torch.int32, device=dev)
+    tab_d, lens_d = torch.from_numpy(tab).to(dev), torch.from_numpy(lens).to(dev)
+    out = torch.empty((B * C, H_q, D), dtype=torch.float32, device=dev)
+    scale = 1 / np.sqrt(D)
+
+    def call():
+        pkv.paged_prefill(q, k_pool, v_pool, tab_d, lens_d, qs, scale, C, out=out)
+
+    for _ in range(args.warmup):
+        call()
+    torch.cuda.synchronize()
+    K = max(args.steps // 10, 5)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
+    for e0, e1 in ev:
+        e0.record()
+        call()
+        e1.record()
+    torch.cuda.synchronize()
+    ms = np.array([e0.elapsed_time(e1) for e0, e1 in ev])
+    flops = 4.0 * H_q * D * B * sum(p + 1 for p in range(prior, n))
+    kv_bytes = B * n * H_kv * D * 2 * 2
+    avg_s = ms.mean() / 1e3
+    tf = flops / avg_s / 1e12
+    print(json.dumps({
+        "metric": "paged prefill TFLOP/s (causal, bf16 MFMA)", "value": round(tf, 1), "unit": "TFLOP/s",
+        "n_gpus": 1, "steps": K, "warmup": args.warmup, "ms_per_step": round(float(ms.mean()), 4),
+        "higher_is_better": True, "dtype": "bf16", "data": "synthetic (N(0,1) K/V/q, allocator-scattered tables)",
+        "config": {"workload": f"{B} sequences x ({prior} earlier + {C} new tokens), 70B layer shape "
+                               f"(H_q 64, H_kv 8, D 128, bs 16)", "seqs": B, "prior": prior, "chunk": C},
+        "us_p50": round(float(np.median(ms)) * 1e3, 1), "flops_per_call": flops,
+        "roofline": {"bound": "mfma", "achieved": round(tf, 1), "peak": 2500.0, "unit": "TFLOP/s",
+                     "frac": round(tf / 2500.0, 4), "traffic": None},
+        "kv_bytes": kv_bytes, "kv_GBps": round(kv_bytes / avg_s / 1e9, 1)}), flush=True)
 
 
 def cpu_baseline(case, mat, out_dev, budget_s, by, B):

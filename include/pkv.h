@@ -18,6 +18,8 @@
  *   pkv_paged_attn_decode  one query token per sequence attends over its paged KV
  *   pkv_paged_attn_decode_window  the same, attending only sink tokens and a
  *                          recent window (StreamingLLM; with pkv_seq_streaming_evict)
+ *   pkv_paged_prefill      causal attention of a chunk of new tokens per sequence
+ *                          (prompt or chunked prefill) over the same pools
  *   pkv_alloc_* / pkv_seq_* host-side fixed-block free-list allocator
  *
  * ---------------------------------------------------------------------------
@@ -220,6 +222,34 @@ int pkv_paged_attn_decode_window(float* out, const void* q, int q_dtype, const v
                                  int32_t D, int32_t NB, int32_t bs, float scale, const float* k_scale,
                                  const float* v_scale, void* workspace, size_t workspace_bytes,
                                  void* stream);
+
+/*
+ * pkv_paged_prefill — causal chunked prefill over the paged pools.  The last
+ * C_b = query_start[b+1] - query_start[b] tokens of sequence b (whose K/V are
+ * already appended, so context_lens[b] = n_b counts them) are its queries:
+ * query i, at row query_start[b] + i of q and out, sits at position
+ * p = n_b - C_b + i and attends positions 0..p:
+ *     out[r][h] = sum_{t<=p} softmax_t(scale * <q[r][h], K_b[g][t]>) V_b[g][t]
+ * ("Paged Attention and KV Cache Fragmentation", section "How PagedAttention
+ * maps an OS concept onto GPU memory": a prompt is written into the blocks a
+ * sequence takes as it grows and attends over them through its table.)
+ *
+ *   out            device fp32 [T][H_q][D]; rows of no sequence are not written
+ *   q              device bf16 [T][H_q][D]
+ *   query_start    device int32 [B+1], non-decreasing, query_start[B] <= T
+ *   max_query_len  host hint >= max C_b (sizes the launch); queries past it
+ *                  are not computed
+ *   others         as pkv_paged_attn_decode
+ * Requires bf16 q, bf16 or E4M3 KV, D in {64, 128}, bs in {8, 16, 32} and
+ * G = H_q / H_kv in {1, 2, 4, 8, 16} (else PKV_ERR_UNSUPPORTED).  No workspace.
+ * Device contents are clamped as for the decode; a sequence whose rows leave
+ * [0, T) is skipped, and one with C_b > n_b gets zero rows (caller errors).
+ */
+int pkv_paged_prefill(float* out, const void* q, int q_dtype, const void* k_pool, const void* v_pool,
+                      int kv_dtype, const int32_t* block_tables, int32_t max_blocks_per_seq,
+                      const int32_t* context_lens, const int32_t* query_start, int32_t max_query_len,
+                      int32_t B, int32_t T, int32_t H_q, int32_t H_kv, int32_t D, int32_t NB, int32_t bs,
+                      float scale, const float* k_scale, const float* v_scale, void* stream);
 
 /* ---------------------------------------------------------------------------
  * Host allocator: fixed-size blocks, LIFO free list, per-block refcounts.

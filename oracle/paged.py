@@ -166,14 +166,15 @@ def ref_decode(q, q_dtype, k_pool, v_pool, kv_dtype, block_tables, context_lens,
 
 
 def ref_prefill(q, q_dtype, k_pool, v_pool, kv_dtype, block_tables, context_lens, query_start, scale, bs,
-                k_scale=None, v_scale=None, seqs=None):
+                k_scale=None, v_scale=None, seqs=None, rows=None):
     """Paged prefill (chunked multi-query attention) over the same pools, fp64.
 
     The last C_b = query_start[b+1] - query_start[b] tokens of sequence b (n_b = context_lens[b]
     tokens, their K/V already appended) are its queries, packed in q [T, H_q, d] at rows
     query_start[b] ... query_start[b+1]-1.  Query i sits at position p = n_b - C_b + i and attends
     causally: s_t = scale * <q_i, K_b[g, t]> for t <= p, o_i = softmax(s) V_b[g, :p+1].
-    Returns fp64 [T, H_q, d].  `seqs` optionally restricts the work (other rows stay zero).
+    Returns fp64 [T, H_q, d].  `seqs` (sequences) or `rows` (packed query rows) optionally restrict
+    the work; other rows stay zero.
 
     "Paged Attention and KV Cache Fragmentation", section "How PagedAttention maps an OS concept
     onto GPU memory": a sequence's blocks are taken as it grows; the prompt (or each chunk of
@@ -191,8 +192,11 @@ def ref_prefill(q, q_dtype, k_pool, v_pool, kv_dtype, block_tables, context_lens
         assert 0 <= C <= n
         if C == 0:
             continue
+        wanted = [i for i in range(C) if rows is None or r0 + i in rows]
+        if not wanted:
+            continue
         K, V = gather_sequence(k_pool, v_pool, kv_dtype, block_tables[b], n, bs, k_scale, v_scale)
-        for i in range(C):
+        for i in wanted:
             p = n - C + i
             for h in range(H_q):
                 g = h // G

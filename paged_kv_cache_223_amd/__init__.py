@@ -56,6 +56,8 @@ SIGNATURES = {
     "pkv_paged_attn_decode_window": (ctypes.c_int, [_P, _P, ctypes.c_int, _P, _P, ctypes.c_int, _P, _I32, _P,
                                                     _I32, _P, _P, _I32, _I32, _I32, _I32, _I32, _I32,
                                                     ctypes.c_float, _P, _P, _P, _SZ, _P]),
+    "pkv_paged_prefill": (ctypes.c_int, [_P, _P, ctypes.c_int, _P, _P, ctypes.c_int, _P, _I32, _P, _P, _I32, _I32,
+                                         _I32, _I32, _I32, _I32, _I32, _I32, ctypes.c_float, _P, _P, _P]),
     "pkv_alloc_create": (ctypes.c_int, [_I32, _I32, _P, ctypes.POINTER(_P)]),
     "pkv_alloc_destroy": (None, [_P]),
     "pkv_alloc_num_free": (_I32, [_P]),
@@ -312,6 +314,34 @@ def paged_attn_decode(q, k_pool, v_pool, block_tables, context_lens, scale: floa
     return out
 
 
+def paged_prefill(q, k_pool, v_pool, block_tables, context_lens, query_start, scale: float, max_query_len: int,
+                  k_scale=None, v_scale=None, out=None):
+    """Causal prefill of the last C_b tokens of each sequence (K/V already appended); q bf16 [T, H_q, D]
+    packed by query_start (int32 [B+1]); returns fp32 [T, H_q, D]."""
+    torch = _torch()
+    _dev(q, k_pool, v_pool, block_tables, context_lens, query_start, k_scale, v_scale, out)
+    kv, NB, H_kv, D, bs = _pool_dims(k_pool, v_pool)
+    if q.dim() != 3 or q.shape[2] != D:
+        raise ValueError("q must be [T, H_q, D]")
+    T, H_q, _ = q.shape
+    B = block_tables.shape[0]
+    if block_tables.dtype != torch.int32 or block_tables.dim() != 2:
+        raise ValueError("block_tables must be int32 [B, max_blocks]")
+    if context_lens.dtype != torch.int32 or context_lens.shape != (B,):
+        raise ValueError("context_lens must be int32 [B]")
+    if query_start.dtype != torch.int32 or query_start.shape != (B + 1,):
+        raise ValueError("query_start must be int32 [B + 1]")
+    if out is None:
+        out = torch.empty((T, H_q, D), dtype=torch.float32, device=q.device)
+    elif out.dtype != torch.float32 or tuple(out.shape) != (T, H_q, D):
+        raise ValueError("out must be fp32 [T, H_q, D]")
+    _check(lib.pkv_paged_prefill(_ptr(out), _ptr(q), dtype_code(q), _ptr(k_pool), _ptr(v_pool), kv,
+                                 _ptr(block_tables), block_tables.shape[1], _ptr(context_lens), _ptr(query_start),
+                                 int(max_query_len), B, T, H_q, H_kv, D, NB, bs, float(scale), _ptr(k_scale),
+                                 _ptr(v_scale), _stream()))
+    return out
+
+
 def stream_read(src, sink=None):
     """Read all of `src` (bytes multiple of 16) once; returns the per-workgroup sink."""
     torch = _torch()
@@ -433,7 +463,7 @@ class Allocator:
 
 
 __all__ = ["lib", "LIB_PATH", "PkvError", "last_error", "kv_append", "copy_blocks", "gather_blocks",
-           "scatter_blocks", "paged_attn_decode",
+           "scatter_blocks", "paged_attn_decode", "paged_prefill",
            "decode_workspace_bytes",
            "decode_workspace",
            "pool_shapes", "dtype_code", "stream_read", "copy_", "Allocator", "SIGNATURES",

@@ -326,6 +326,76 @@ int pkv_paged_attn_decode_window(float* out, const void* q, int q_dtype, const v
                      workspace, workspace_bytes, stream);
 }
 
+int pkv_paged_prefill(float* out, const void* q, int q_dtype, const void* k_pool, const void* v_pool, int kv_dtype,
+                      const int32_t* block_tables, int32_t max_blocks_per_seq, const int32_t* context_lens,
+                      const int32_t* query_start, int32_t max_query_len, int32_t B, int32_t T, int32_t H_q,
+                      int32_t H_kv, int32_t D, int32_t NB, int32_t bs, float scale, const float* k_scale,
+                      const float* v_scale, void* stream) {
+  g_err[0] = 0;
+  if (B < 0 || T < 0 || H_q <= 0 || H_kv <= 0 || NB <= 0 || max_blocks_per_seq <= 0 || max_query_len < 0) {
+    set_error("prefill: bad sizes B=%d T=%d H_q=%d H_kv=%d NB=%d max_blocks=%d max_query_len=%d", B, T, H_q, H_kv,
+              NB, max_blocks_per_seq, max_query_len);
+    return PKV_ERR_INVALID_ARG;
+  }
+  if (H_q % H_kv != 0) {
+    set_error("prefill: H_q=%d is not a multiple of H_kv=%d", H_q, H_kv);
+    return PKV_ERR_INVALID_ARG;
+  }
+  const int G = H_q / H_kv;
+  if (!(D == 64 || D == 128) || !(bs == 8 || bs == 16 || bs == 32) || 16 % G != 0 || q_dtype != PKV_BF16 ||
+      !(kv_dtype == PKV_BF16 || kv_dtype == PKV_FP8_E4M3)) {
+    set_error("prefill: unsupported D=%d bs=%d G=%d q=%d kv=%d (D 64/128, bs 8/16/32, G in {1,2,4,8,16}, bf16 q, "
+              "bf16/E4M3 KV)", D, bs, G, q_dtype, kv_dtype);
+    return PKV_ERR_UNSUPPORTED;
+  }
+  if (!std::isfinite(scale)) {
+    set_error("prefill: scale is not finite");
+    return PKV_ERR_INVALID_ARG;
+  }
+  if (B == 0 || T == 0 || max_query_len == 0) return PKV_OK;
+  if (!out || !q || !k_pool || !v_pool || !block_tables || !context_lens || !query_start) {
+    set_error("prefill: null pointer");
+    return PKV_ERR_INVALID_ARG;
+  }
+  if (kv_dtype == PKV_FP8_E4M3 && (!k_scale || !v_scale)) {
+    set_error("prefill: E4M3 KV needs k_scale and v_scale");
+    return PKV_ERR_INVALID_ARG;
+  }
+  const int wg_tok = prefill_wg_tokens(G);
+  const long long groups = ((long long)max_query_len + wg_tok - 1) / wg_tok;
+  const long long items = (long long)B * H_kv * groups;
+  if (items > 0x7FFFFFF0LL) {
+    set_error("prefill: launch too large (%lld work items)", items);
+    return PKV_ERR_INVALID_ARG;
+  }
+  PrefillArgs a{};
+  a.out = out;
+  a.q = q;
+  a.k_pool = k_pool;
+  a.v_pool = v_pool;
+  a.block_tables = block_tables;
+  a.context_lens = context_lens;
+  a.query_start = query_start;
+  a.k_scale = k_scale;
+  a.v_scale = v_scale;
+  a.B = B;
+  a.T = T;
+  a.H_q = H_q;
+  a.H_kv = H_kv;
+  a.G = G;
+  a.D = D;
+  a.NB = NB;
+  a.bs = bs;
+  a.max_blocks = max_blocks_per_seq;
+  const long long cap = (long long)max_blocks_per_seq * bs;
+  a.len_cap = (int)(cap < 0x7FFFFFFF ? cap : 0x7FFFFFFF);
+  a.scale_log2 = scale * 1.4426950408889634f;
+  a.kv_dtype = kv_dtype;
+  a.items = (int)items;
+  a.groups_per_seq = (int)groups;
+  return hip_status(launch_prefill(a, (hipStream_t)stream), "prefill launch");
+}
+
 size_t pkv_stream_read_sink_floats(size_t bytes) { return stream_read_blocks(bytes); }
 
 int pkv_stream_read(const void* src, size_t bytes, float* sink, void* stream) {

@@ -115,6 +115,26 @@ struct AppendArgs {
 };
 hipError_t launch_kv_append(const AppendArgs& a, hipStream_t s);
 
+// paged prefill (causal chunked multi-query attention)
+struct PrefillArgs {
+  float* out;                  // [T][H_q][D]
+  const void* q;               // [T][H_q][D] bf16
+  const void* k_pool;
+  const void* v_pool;
+  const int32_t* block_tables;  // [B][max_blocks]
+  const int32_t* context_lens;  // [B]
+  const int32_t* query_start;   // [B + 1]
+  const float* k_scale;
+  const float* v_scale;
+  int B, T, H_q, H_kv, G, D, NB, bs, max_blocks, len_cap;
+  float scale_log2;
+  int kv_dtype;
+  int items;           // B * H_kv * groups_per_seq work items
+  int groups_per_seq;  // tile groups that cover the longest chunk
+};
+int prefill_wg_tokens(int G);  // query tokens one workgroup covers
+hipError_t launch_prefill(const PrefillArgs& a, hipStream_t s);
+
 // whole-block moves of both pools: pool -> pool (copy-on-write pairs),
 // pool -> staging records (swap-out gather), staging -> pool (swap-in scatter)
 enum BlockMove { kMovePairs = 0, kMoveGather = 1, kMoveScatter = 2 };

@@ -1,0 +1,313 @@
+// Paged prefill (chunked multi-query attention) for gfx950 (CDNA4).
+//
+// Method: "Paged Attention and KV Cache Fragmentation" (inferenceengineering.co),
+// section "How PagedAttention maps an OS concept onto GPU memory": a sequence
+// takes blocks as it grows; a prompt, or each chunk of it, is appended into
+// them and then attends, causally, over everything before it through the
+// same block table the decode walks.  Query i of the C_b new tokens of
+// sequence b sits at position p = n_b - C_b + i and attends positions 0..p.
+//
+// Tiles.  An MFMA column tile is 16 (query token, head) pairs of one KV head g:
+// 16 / G consecutive query tokens times the G query heads that share g.  The
+// QK^T and PV steps are the decode's (S^T = K Q^T, P split into bf16 hi + lo,
+// P regrouped across lane groups, O += P V); only the mask differs: column
+// (token at p, head) keeps key t iff t <= p.
+//
+// Workgroups.  NW waves, one column tile each, cover NW * 16 / G consecutive
+// query tokens of one (sequence, KV head).  They share every 32-token K/V
+// chunk through LDS: the workgroup copies the chunk's pool tiles (bytes as in
+// the pool) into one LDS buffer while the waves compute the previous chunk from
+// the other, with the chunk after that already loading into registers, so
+// each chunk crosses the L2 once per workgroup, not once per wave.  Work
+// items are dealt to the 8 XCDs so that the workgroups of one (sequence, KV
+// head) share one XCD's L2, and the latest (longest) tiles of a sequence are
+// dispatched first.
+
+#include <hip/hip_runtime.h>
+
+#include <math.h>
+
+#include <type_traits>
+
+#include "internal.h"
+#include "tile_ops.h"
+
+namespace pkv {
+namespace {
+
+constexpr int kStages = 2;  // the chunk being computed and the one being filled
+
+template <int D, int BS, int KVT>
+struct Stage {
+  static constexpr int S = KvTraits<KVT>::kBytes;
+  static constexpr int NBCH = BS >= 32 ? 1 : 32 / BS;  // blocks of one 32-token chunk
+  static constexpr int kTile = D * BS * S;             // one block's tile of one head (K or V)
+  static constexpr int kBytes = 2 * NBCH * kTile;      // the chunk in LDS: K tiles, then V tiles
+  static constexpr int kUnits = kBytes / 16;
+};
+
+// Copy one chunk's tiles (global -> registers); the workgroup's threads take
+// 16-byte units round-robin.  Blocks past the sequence's last block read the
+// last block again (masked later), so every access stays inside the pool.
+template <int D, int BS, int KVT, int NT>
+struct Stager {
+  using St = Stage<D, BS, KVT>;
+  static constexpr int kPer = (St::kUnits + NT - 1) / NT;
+  u32x4 r[kPer];
+
+  __device__ __forceinline__ void load(const char* __restrict__ kpool, const char* __restrict__ vpool,
+                                       const int32_t* __restrict__ tab, int chunk, int last_blk, int NB,
+                                       int H_kv, int g, int tid) {
+    constexpr int tileU = St::kTile / 16;
+    const size_t bstride = (size_t)H_kv * St::kTile;
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) {
+      const int u = tid + k * NT;
+      if (St::kUnits % NT == 0 || u < St::kUnits) {
+        const int part = u / (St::NBCH * tileU);  // 0 = K, 1 = V
+        const int w = u % (St::NBCH * tileU);
+        const int i = w / tileU;
+        const int id = block_id(tab, chunk * 32 / BS + i, last_blk, NB);
+        const char* src = (part == 0 ? kpool : vpool) + (size_t)id * bstride + (size_t)g * St::kTile +
+                          (size_t)(w % tileU) * 16;
+        r[k] = *(const u32x4*)src;
+      }
+    }
+  }
+
+  __device__ __forceinline__ void store(char* lds, int tid) const {
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) {
+      const int u = tid + k * NT;
+      if (St::kUnits % NT == 0 || u < St::kUnits) *(u32x4*)(lds + (size_t)u * 16) = r[k];
+    }
+  }
+};
+
+// one wave's QK^T, causal softmax and PV over one staged chunk
+template <int D, int BS, int KVT>
+__device__ __forceinline__ void prefill_chunk(const char* lds, const u32x4 (&qop)[D / 32], f32x4 (&acc)[D / 16],
+                                              float& m, float& l, int chunk, int n, int p_lane, int p_min,
+                                              float sl, int lane) {
+  using St = Stage<D, BS, KVT>;
+  constexpr int S = St::S;
+  const int cs = chunk * 32;
+  const int mrow = lane & 15, kg = lane >> 4;
+  const char* kl = lds;
+  const char* vl = lds + St::NBCH * St::kTile;
+  // wave-uniform: some key of the chunk lies past the earliest query position of the wave
+  const bool diag = cs + 31 > p_min;
+  // ---- S^T = K Q^T for the two 16-token halves
+  f32x4 s[2];
+#pragma unroll
+  for (int a = 0; a < 2; ++a) {
+    const int tk = 16 * a + mrow;
+    const char* kb = kl + (BS >= 32 ? 0 : (tk / BS) * St::kTile) + (size_t)(kg * BS + tk % BS) * 16;
+    s[a] = f32x4{0.f, 0.f, 0.f, 0.f};
+    if constexpr (KVT == PKV_BF16) {
+#pragma unroll
+      for (int c = 0; c < D / 32; ++c) s[a] = mfma16x16x32(*(const u32x4*)(kb + (size_t)c * 64 * BS), qop[c], s[a]);
+    } else {
+#pragma unroll
+      for (int u = 0; u < D / 64; ++u) {
+        const u32x4 w = *(const u32x4*)(kb + (size_t)u * 64 * BS);
+        s[a] = mfma16x16x32(e4m3x8_to_bf16x8(w.x, w.y), qop[2 * u], s[a]);
+        s[a] = mfma16x16x32(e4m3x8_to_bf16x8(w.z, w.w), qop[2 * u + 1], s[a]);
+      }
+    }
+  }
+  float x[8];
+#pragma unroll
+  for (int a = 0; a < 2; ++a)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      float v = s[a][i] * sl;
+      if (diag) v = (cs + 16 * a + 4 * kg + i <= p_lane) ? v : -INFINITY;
+      x[4 * a + i] = v;
+    }
+  float cm = x[0];
+#pragma unroll
+  for (int j = 1; j < 8; ++j) cm = fmaxf(cm, x[j]);
+  cm = fmaxf(cm, __shfl_xor(cm, 16, 64));
+  cm = fmaxf(cm, __shfl_xor(cm, 32, 64));
+  const bool need = cm > m + kRescaleLog2;
+  if (__ballot(need)) {
+    const float mu = need ? cm : m;
+    const float alpha = exp2_fast(m - mu);
+    l *= alpha;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float ai = __shfl(alpha, 4 * kg + i, 64);
+#pragma unroll
+      for (int t = 0; t < D / 16; ++t) acc[t][i] *= ai;
+    }
+    m = mu;
+  }
+  uint32_t hb[8];
+  float lo[8];
+  float psum = 0.f;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const float p = exp2_fast(x[j] - m);  // key 0 is in every column's range, so m is finite here
+    psum += p;
+    const uint32_t bits = __builtin_bit_cast(uint32_t, p);
+    hb[j] = bits;
+    lo[j] = p - __builtin_bit_cast(float, bits & 0xFFFF0000u);
+  }
+  l += psum;
+  u32x4 ph, pl;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    ph[w] = __builtin_amdgcn_perm(hb[2 * w + 1], hb[2 * w], 0x07060302u);
+    pl[w] = __builtin_amdgcn_perm(__builtin_bit_cast(uint32_t, lo[2 * w + 1]),
+                                  __builtin_bit_cast(uint32_t, lo[2 * w]), 0x07060302u);
+  }
+  ph = tokens_by_eight(ph);
+  pl = tokens_by_eight(pl);
+  // V rows past the sequence end may hold anything: zero-select them (their weights are 0)
+  const bool tail = cs + 32 > n;
+  u32x4 vmask = u32x4{~0u, ~0u, ~0u, ~0u};
+  if (tail) {
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const int t0 = cs + 8 * kg + 2 * w;
+      vmask[w] = (t0 < n ? 0x0000FFFFu : 0u) | (t0 + 1 < n ? 0xFFFF0000u : 0u);
+    }
+  }
+  const int tv = 8 * kg;
+  const char* vb = vl + (BS >= 32 ? 0 : (tv / BS) * St::kTile) + ((size_t)mrow * BS + tv % BS) * S;
+#pragma unroll
+  for (int t = 0; t < D / 16; ++t) {
+    u32x4 vop;
+    if constexpr (KVT == PKV_BF16) {
+      vop = *(const u32x4*)(vb + (size_t)t * 16 * BS * S);
+    } else {
+      const u32x2 w = *(const u32x2*)(vb + (size_t)t * 16 * BS * S);
+      vop = e4m3x8_to_bf16x8(w.x, w.y);
+    }
+    if (tail) vop &= vmask;
+    acc[t] = mfma16x16x32(ph, vop, acc[t]);
+    acc[t] = mfma16x16x32(pl, vop, acc[t]);
+  }
+}
+
+template <int D, int BS, int KVT, int NW>
+__global__ __launch_bounds__(64 * NW, 2) void prefill_kernel(PrefillArgs a) {
+  using St = Stage<D, BS, KVT>;
+  constexpr int NT = 64 * NW;
+  __shared__ __align__(16) char sh_stage[kStages][St::kBytes];
+  const int tid = threadIdx.x, lane = tid & 63, w = uniform(tid >> 6);
+  const int G = a.G;
+  const int tok_per_tile = 16 / G;
+  const int tok_per_wg = NW * tok_per_tile;
+  // ---- work item: XCD-aware deal of (sequence, KV head, tile group), latest tile group first
+  const int items = a.items;
+  const int per_xcd = (items + 7) / 8;
+  const int item = (blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
+  if (item >= items) return;
+  const int groups = a.groups_per_seq;  // tile groups of the longest chunk
+  const int seg = item / groups;        // (b, g) in sequence-major order
+  const int b = seg / a.H_kv, g = seg % a.H_kv;
+  const int q0 = a.query_start[b], C = a.query_start[b + 1] - q0;
+  // rows outside the T query rows the host declared are never touched (caller error)
+  if (q0 < 0 || C <= 0 || q0 + C > a.T) return;
+  const int grp = groups - 1 - item % groups;  // latest first
+  const int tok0 = grp * tok_per_wg;
+  if (tok0 >= C) return;
+  const int n = uniform(min(max(a.context_lens[b], 0), a.len_cap));
+  if (n < C) {  // caller error (the chunk is longer than the sequence): zero rows, nothing read
+    for (int e = tid; e < min(tok_per_wg, C - tok0) * G * D; e += NT) {
+      const int r = e / (G * D);
+      a.out[((size_t)(q0 + tok0 + r) * a.H_q + g * G) * D + e % (G * D)] = 0.f;
+    }
+    return;
+  }
+  const int last_blk = (n + BS - 1) / BS - 1;
+  const int32_t* tab = a.block_tables + (size_t)b * a.max_blocks;
+  // this workgroup's queries: positions n - C + tok0 .. ; its last chunk covers the latest one
+  const int p_wg_max = n - C + min(C, tok0 + tok_per_wg) - 1;
+  const int nch = p_wg_max / 32 + 1;
+  // ---- this wave's column tile: columns c = (token tok0 + w * tok_per_tile + c / G, head c % G)
+  const int col = lane & 15, kgq = lane >> 4;
+  const int wtok0 = tok0 + w * tok_per_tile;
+  const int qtok = wtok0 + col / G;  // chunk-relative token of this lane's column
+  const bool qvalid = qtok < C;
+  const int p_lane = n - C + (qvalid ? qtok : min(wtok0, C - 1));  // never past the sequence
+  const int p_min = uniform(n - C + min(wtok0, C - 1));
+  u32x4 qop[D / 32];
+  {
+    const uint16_t* qrow = (const uint16_t*)a.q + ((size_t)(q0 + (qvalid ? qtok : 0)) * a.H_q + g * G + col % G) * D;
+#pragma unroll
+    for (int c = 0; c < D / 32; ++c) {
+      u32x4 v = u32x4{0u, 0u, 0u, 0u};
+      if (qvalid) v = *(const u32x4*)(qrow + qk_dofs<KVT>(c, kgq));
+      qop[c] = v;
+    }
+  }
+  float sl = a.scale_log2;
+  if constexpr (KVT == PKV_FP8_E4M3) sl *= a.k_scale[g];
+  f32x4 acc[D / 16];
+#pragma unroll
+  for (int t = 0; t < D / 16; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m = -INFINITY, l = 0.f;
+  // ---- pipeline: chunk c computed from LDS while chunks c+1 (registers) and c+2 (loads) are in flight
+  const char* kpool = (const char*)a.k_pool;
+  const char* vpool = (const char*)a.v_pool;
+  Stager<D, BS, KVT, NT> A, Bx;
+  A.load(kpool, vpool, tab, 0, last_blk, a.NB, a.H_kv, g, tid);
+  A.store(sh_stage[0], tid);
+  if (nch > 1) A.load(kpool, vpool, tab, 1, last_blk, a.NB, a.H_kv, g, tid);
+  __syncthreads();
+  for (int c = 0; c < nch; ++c) {
+    if (c + 2 < nch) Bx.load(kpool, vpool, tab, c + 2, last_blk, a.NB, a.H_kv, g, tid);
+    prefill_chunk<D, BS, KVT>(sh_stage[c % kStages], qop, acc, m, l, c, n, p_lane, p_min, sl, lane);
+    if (c + 1 < nch) A.store(sh_stage[(c + 1) % kStages], tid);
+    __syncthreads();
+    A = Bx;
+  }
+  // ---- normalise and write this wave's rows (row r = column r of the tile)
+  float lt = l;
+  lt += __shfl_xor(lt, 16, 64);
+  lt += __shfl_xor(lt, 32, 64);
+  const float vs = KVT == PKV_FP8_E4M3 ? a.v_scale[g] : 1.f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int r = 4 * kgq + i;
+    const float lr = __shfl(lt, r, 64);
+    const int rt = wtok0 + r / G;
+    if (rt < C) {
+      float* orow = a.out + ((size_t)(q0 + rt) * a.H_q + g * G + r % G) * D;
+#pragma unroll
+      for (int t = 0; t < D / 16; ++t) orow[16 * t + col] = acc[t][i] * vs / lr;
+    }
+  }
+}
+
+template <int D, int BS, int KVT>
+hipError_t launch_prefill_t(const PrefillArgs& a, hipStream_t s) {
+  constexpr int NW = 8;
+  hipLaunchKernelGGL((prefill_kernel<D, BS, KVT, NW>), dim3((unsigned)((a.items + 7) / 8 * 8)), dim3(64 * NW), 0,
+                     s, a);
+  return hipGetLastError();
+}
+
+template <int D, int KVT>
+hipError_t launch_prefill_bs(const PrefillArgs& a, hipStream_t s) {
+  switch (a.bs) {
+    case 8: return launch_prefill_t<D, 8, KVT>(a, s);
+    case 16: return launch_prefill_t<D, 16, KVT>(a, s);
+    default: return launch_prefill_t<D, 32, KVT>(a, s);
+  }
+}
+
+}  // namespace
+
+int prefill_wg_tokens(int G) { return 8 * (16 / G); }
+
+hipError_t launch_prefill(const PrefillArgs& a, hipStream_t s) {
+  if (a.kv_dtype == PKV_BF16)
+    return a.D == 64 ? launch_prefill_bs<64, PKV_BF16>(a, s) : launch_prefill_bs<128, PKV_BF16>(a, s);
+  return a.D == 64 ? launch_prefill_bs<64, PKV_FP8_E4M3>(a, s) : launch_prefill_bs<128, PKV_FP8_E4M3>(a, s);
+}
+
+}  // namespace pkv

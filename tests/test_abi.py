@@ -220,3 +220,35 @@ def test_swap_calls_check_their_outputs():
     assert pkv.lib.pkv_seq_swap_out(a._h, 0, buf, 2, None) == pkv.ERR_INVALID_ARG
     assert pkv.lib.pkv_seq_swap_in(a._h, 5, buf, 2, ctypes.byref(n)) == pkv.ERR_UNKNOWN_SEQ
 
+
+def _prefill(**kw):
+    a = dict(out=P, q=P, q_dtype=pkv.BF16, k=P, v=P, kv=pkv.BF16, tab=P, mb=4, lens=P, qs=P, mq=64, B=2, T=100,
+             H_q=8, H_kv=2, D=128, NB=16, bs=16, scale=0.1, ks=None, vs=None, stream=None)
+    a.update(kw)
+    return pkv.lib.pkv_paged_prefill(a["out"], a["q"], a["q_dtype"], a["k"], a["v"], a["kv"], a["tab"], a["mb"],
+                                     a["lens"], a["qs"], a["mq"], a["B"], a["T"], a["H_q"], a["H_kv"], a["D"],
+                                     a["NB"], a["bs"], a["scale"], a["ks"], a["vs"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(H_q=6, H_kv=4), pkv.ERR_INVALID_ARG),
+    (dict(H_q=6, H_kv=2), pkv.ERR_UNSUPPORTED),   # G = 3 does not divide 16
+    (dict(D=256), pkv.ERR_UNSUPPORTED),
+    (dict(bs=4), pkv.ERR_UNSUPPORTED),
+    (dict(q_dtype=pkv.F32), pkv.ERR_UNSUPPORTED),
+    (dict(kv=pkv.F32), pkv.ERR_UNSUPPORTED),
+    (dict(T=-1), pkv.ERR_INVALID_ARG),
+    (dict(mq=-2), pkv.ERR_INVALID_ARG),
+    (dict(scale=float("inf")), pkv.ERR_INVALID_ARG),
+    (dict(qs=None), pkv.ERR_INVALID_ARG),
+    (dict(kv=pkv.FP8_E4M3), pkv.ERR_INVALID_ARG),  # scales missing
+])
+def test_prefill_rejects_bad_arguments_before_launch(kw, status):
+    assert _prefill(**kw) == status
+    assert pkv.last_error()
+
+
+def test_prefill_empty_is_a_no_op():
+    assert _prefill(B=0) == pkv.OK
+    assert _prefill(T=0) == pkv.OK
+
