@@ -13,8 +13,9 @@
 // P regrouped across lane groups, O += P V); only the mask differs: column
 // (token at p, head) keeps key t iff t <= p.
 //
-// Workgroups.  NW waves, one column tile each, cover NW * 16 / G consecutive
-// query tokens of one (sequence, KV head).  They share every 32-token K/V
+// Workgroups.  NW waves with R column tiles each cover NW * R * 16 / G
+// consecutive query tokens of one (sequence, KV head); every K and V operand
+// a wave reads from LDS serves its R tiles.  They share every 32-token K/V
 // chunk through LDS: the workgroup copies the chunk's pool tiles (bytes as in
 // the pool) into one LDS buffer while the waves compute the previous chunk from
 // the other, with the chunk after that already loading into registers, so
@@ -84,38 +85,11 @@ struct Stager {
   }
 };
 
-// one wave's QK^T, causal softmax and PV over one staged chunk
+// online softmax update and PV of one column tile (S^T already computed)
 template <int D, int BS, int KVT>
-__device__ __forceinline__ void prefill_chunk(const char* lds, const u32x4 (&qop)[D / 32], f32x4 (&acc)[D / 16],
-                                              float& m, float& l, int chunk, int n, int p_lane, int p_min,
-                                              float sl, int lane) {
-  using St = Stage<D, BS, KVT>;
-  constexpr int S = St::S;
-  const int cs = chunk * 32;
-  const int mrow = lane & 15, kg = lane >> 4;
-  const char* kl = lds;
-  const char* vl = lds + St::NBCH * St::kTile;
-  // wave-uniform: some key of the chunk lies past the earliest query position of the wave
-  const bool diag = cs + 31 > p_min;
-  // ---- S^T = K Q^T for the two 16-token halves
-  f32x4 s[2];
-#pragma unroll
-  for (int a = 0; a < 2; ++a) {
-    const int tk = 16 * a + mrow;
-    const char* kb = kl + (BS >= 32 ? 0 : (tk / BS) * St::kTile) + (size_t)(kg * BS + tk % BS) * 16;
-    s[a] = f32x4{0.f, 0.f, 0.f, 0.f};
-    if constexpr (KVT == PKV_BF16) {
-#pragma unroll
-      for (int c = 0; c < D / 32; ++c) s[a] = mfma16x16x32(*(const u32x4*)(kb + (size_t)c * 64 * BS), qop[c], s[a]);
-    } else {
-#pragma unroll
-      for (int u = 0; u < D / 64; ++u) {
-        const u32x4 w = *(const u32x4*)(kb + (size_t)u * 64 * BS);
-        s[a] = mfma16x16x32(e4m3x8_to_bf16x8(w.x, w.y), qop[2 * u], s[a]);
-        s[a] = mfma16x16x32(e4m3x8_to_bf16x8(w.z, w.w), qop[2 * u + 1], s[a]);
-      }
-    }
-  }
+__device__ __forceinline__ void softmax_pv(const f32x4 (&s)[2], const u32x4* vops, f32x4 (&acc)[D / 16], float& m,
+                                           float& l, int cs, int p_lane, bool diag, float sl, int lane) {
+  const int kg = lane >> 4;
   float x[8];
 #pragma unroll
   for (int a = 0; a < 2; ++a)
@@ -164,7 +138,56 @@ __device__ __forceinline__ void prefill_chunk(const char* lds, const u32x4 (&qop
   }
   ph = tokens_by_eight(ph);
   pl = tokens_by_eight(pl);
-  // V rows past the sequence end may hold anything: zero-select them (their weights are 0)
+#pragma unroll
+  for (int t = 0; t < D / 16; ++t) {
+    acc[t] = mfma16x16x32(ph, vops[t], acc[t]);
+    acc[t] = mfma16x16x32(pl, vops[t], acc[t]);
+  }
+}
+
+// one wave's R column tiles over one staged chunk: every K and V operand read
+// from LDS serves all R tiles
+template <int D, int BS, int KVT, int R>
+__device__ __forceinline__ void prefill_chunk(const char* lds, const u32x4 (&qop)[R][D / 32],
+                                              f32x4 (&acc)[R][D / 16], float (&m)[R], float (&l)[R], int chunk,
+                                              int n, const int (&p_lane)[R], int p_min, float sl, int lane) {
+  using St = Stage<D, BS, KVT>;
+  constexpr int S = St::S;
+  const int cs = chunk * 32;
+  const int mrow = lane & 15, kg = lane >> 4;
+  const char* kl = lds;
+  const char* vl = lds + St::NBCH * St::kTile;
+  // wave-uniform: some key of the chunk lies past the earliest query position of the wave
+  const bool diag = cs + 31 > p_min;
+  // ---- S^T = K Q^T for the two 16-token halves, every tile
+  f32x4 s[R][2];
+#pragma unroll
+  for (int a = 0; a < 2; ++a) {
+    const int tk = 16 * a + mrow;
+    const char* kb = kl + (BS >= 32 ? 0 : (tk / BS) * St::kTile) + (size_t)(kg * BS + tk % BS) * 16;
+#pragma unroll
+    for (int r = 0; r < R; ++r) s[r][a] = f32x4{0.f, 0.f, 0.f, 0.f};
+    if constexpr (KVT == PKV_BF16) {
+#pragma unroll
+      for (int c = 0; c < D / 32; ++c) {
+        const u32x4 kop = *(const u32x4*)(kb + (size_t)c * 64 * BS);
+#pragma unroll
+        for (int r = 0; r < R; ++r) s[r][a] = mfma16x16x32(kop, qop[r][c], s[r][a]);
+      }
+    } else {
+#pragma unroll
+      for (int u = 0; u < D / 64; ++u) {
+        const u32x4 w = *(const u32x4*)(kb + (size_t)u * 64 * BS);
+        const u32x4 k0 = e4m3x8_to_bf16x8(w.x, w.y), k1 = e4m3x8_to_bf16x8(w.z, w.w);
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+          s[r][a] = mfma16x16x32(k0, qop[r][2 * u], s[r][a]);
+          s[r][a] = mfma16x16x32(k1, qop[r][2 * u + 1], s[r][a]);
+        }
+      }
+    }
+  }
+  // ---- V operands: 8 consecutive tokens of one column per lane; rows past n zero-selected
   const bool tail = cs + 32 > n;
   u32x4 vmask = u32x4{~0u, ~0u, ~0u, ~0u};
   if (tail) {
@@ -176,22 +199,23 @@ __device__ __forceinline__ void prefill_chunk(const char* lds, const u32x4 (&qop
   }
   const int tv = 8 * kg;
   const char* vb = vl + (BS >= 32 ? 0 : (tv / BS) * St::kTile) + ((size_t)mrow * BS + tv % BS) * S;
+  u32x4 vops[D / 16];
 #pragma unroll
   for (int t = 0; t < D / 16; ++t) {
-    u32x4 vop;
     if constexpr (KVT == PKV_BF16) {
-      vop = *(const u32x4*)(vb + (size_t)t * 16 * BS * S);
+      vops[t] = *(const u32x4*)(vb + (size_t)t * 16 * BS * S);
     } else {
       const u32x2 w = *(const u32x2*)(vb + (size_t)t * 16 * BS * S);
-      vop = e4m3x8_to_bf16x8(w.x, w.y);
+      vops[t] = e4m3x8_to_bf16x8(w.x, w.y);
     }
-    if (tail) vop &= vmask;
-    acc[t] = mfma16x16x32(ph, vop, acc[t]);
-    acc[t] = mfma16x16x32(pl, vop, acc[t]);
+    if (tail) vops[t] &= vmask;
   }
+#pragma unroll
+  for (int r = 0; r < R; ++r)
+    softmax_pv<D, BS, KVT>(s[r], vops, acc[r], m[r], l[r], cs, p_lane[r], diag, sl, lane);
 }
 
-template <int D, int BS, int KVT, int NW>
+template <int D, int BS, int KVT, int NW, int R>
 __global__ __launch_bounds__(64 * NW, 2) void prefill_kernel(PrefillArgs a) {
   using St = Stage<D, BS, KVT>;
   constexpr int NT = 64 * NW;
@@ -199,7 +223,8 @@ __global__ __launch_bounds__(64 * NW, 2) void prefill_kernel(PrefillArgs a) {
   const int tid = threadIdx.x, lane = tid & 63, w = uniform(tid >> 6);
   const int G = a.G;
   const int tok_per_tile = 16 / G;
-  const int tok_per_wg = NW * tok_per_tile;
+  const int tok_per_wave = R * tok_per_tile;
+  const int tok_per_wg = NW * tok_per_wave;
   // ---- work item: XCD-aware deal of (sequence, KV head, tile group), latest tile group first
   const int items = a.items;
   const int per_xcd = (items + 7) / 8;
@@ -227,29 +252,37 @@ __global__ __launch_bounds__(64 * NW, 2) void prefill_kernel(PrefillArgs a) {
   // this workgroup's queries: positions n - C + tok0 .. ; its last chunk covers the latest one
   const int p_wg_max = n - C + min(C, tok0 + tok_per_wg) - 1;
   const int nch = p_wg_max / 32 + 1;
-  // ---- this wave's column tile: columns c = (token tok0 + w * tok_per_tile + c / G, head c % G)
+  // ---- this wave's R column tiles: tile r, column c = (token wtok0 + r * tok_per_tile + c / G, head c % G)
   const int col = lane & 15, kgq = lane >> 4;
-  const int wtok0 = tok0 + w * tok_per_tile;
-  const int qtok = wtok0 + col / G;  // chunk-relative token of this lane's column
-  const bool qvalid = qtok < C;
-  const int p_lane = n - C + (qvalid ? qtok : min(wtok0, C - 1));  // never past the sequence
+  const int wtok0 = tok0 + w * tok_per_wave;
   const int p_min = uniform(n - C + min(wtok0, C - 1));
-  u32x4 qop[D / 32];
-  {
-    const uint16_t* qrow = (const uint16_t*)a.q + ((size_t)(q0 + (qvalid ? qtok : 0)) * a.H_q + g * G + col % G) * D;
+  u32x4 qop[R][D / 32];
+  int p_lane[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const int qtok = wtok0 + r * tok_per_tile + col / G;  // chunk-relative token of this lane's column
+    const bool qvalid = qtok < C;
+    p_lane[r] = n - C + (qvalid ? qtok : min(wtok0, C - 1));  // never past the sequence
+    const uint16_t* qrow =
+        (const uint16_t*)a.q + ((size_t)(q0 + (qvalid ? qtok : 0)) * a.H_q + g * G + col % G) * D;
 #pragma unroll
     for (int c = 0; c < D / 32; ++c) {
       u32x4 v = u32x4{0u, 0u, 0u, 0u};
       if (qvalid) v = *(const u32x4*)(qrow + qk_dofs<KVT>(c, kgq));
-      qop[c] = v;
+      qop[r][c] = v;
     }
   }
   float sl = a.scale_log2;
   if constexpr (KVT == PKV_FP8_E4M3) sl *= a.k_scale[g];
-  f32x4 acc[D / 16];
+  f32x4 acc[R][D / 16];
+  float m[R], l[R];
 #pragma unroll
-  for (int t = 0; t < D / 16; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m = -INFINITY, l = 0.f;
+  for (int r = 0; r < R; ++r) {
+#pragma unroll
+    for (int t = 0; t < D / 16; ++t) acc[r][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+    m[r] = -INFINITY;
+    l[r] = 0.f;
+  }
   // ---- pipeline: chunk c computed from LDS while chunks c+1 (registers) and c+2 (loads) are in flight
   const char* kpool = (const char*)a.k_pool;
   const char* vpool = (const char*)a.v_pool;
@@ -260,34 +293,39 @@ __global__ __launch_bounds__(64 * NW, 2) void prefill_kernel(PrefillArgs a) {
   __syncthreads();
   for (int c = 0; c < nch; ++c) {
     if (c + 2 < nch) Bx.load(kpool, vpool, tab, c + 2, last_blk, a.NB, a.H_kv, g, tid);
-    prefill_chunk<D, BS, KVT>(sh_stage[c % kStages], qop, acc, m, l, c, n, p_lane, p_min, sl, lane);
+    prefill_chunk<D, BS, KVT, R>(sh_stage[c % kStages], qop, acc, m, l, c, n, p_lane, p_min, sl, lane);
     if (c + 1 < nch) A.store(sh_stage[(c + 1) % kStages], tid);
     __syncthreads();
     A = Bx;
   }
-  // ---- normalise and write this wave's rows (row r = column r of the tile)
-  float lt = l;
-  lt += __shfl_xor(lt, 16, 64);
-  lt += __shfl_xor(lt, 32, 64);
+  // ---- normalise and write this wave's rows (row i of tile r = column i of that tile)
   const float vs = KVT == PKV_FP8_E4M3 ? a.v_scale[g] : 1.f;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int r = 4 * kgq + i;
-    const float lr = __shfl(lt, r, 64);
-    const int rt = wtok0 + r / G;
-    if (rt < C) {
-      float* orow = a.out + ((size_t)(q0 + rt) * a.H_q + g * G + r % G) * D;
+  for (int r = 0; r < R; ++r) {
+    float lt = l[r];
+    lt += __shfl_xor(lt, 16, 64);
+    lt += __shfl_xor(lt, 32, 64);
 #pragma unroll
-      for (int t = 0; t < D / 16; ++t) orow[16 * t + col] = acc[t][i] * vs / lr;
+    for (int i = 0; i < 4; ++i) {
+      const int row = 4 * kgq + i;
+      const float lr = __shfl(lt, row, 64);
+      const int rt = wtok0 + r * tok_per_tile + row / G;
+      if (rt < C) {
+        float* orow = a.out + ((size_t)(q0 + rt) * a.H_q + g * G + row % G) * D;
+#pragma unroll
+        for (int t = 0; t < D / 16; ++t) orow[16 * t + col] = acc[r][t][i] * vs / lr;
+      }
     }
   }
 }
 
+constexpr int kPrefillWaves = 8;
+constexpr int kPrefillTiles = 1;  // column tiles per wave (2 measured the same: the loop is VALU-bound)
+
 template <int D, int BS, int KVT>
 hipError_t launch_prefill_t(const PrefillArgs& a, hipStream_t s) {
-  constexpr int NW = 8;
-  hipLaunchKernelGGL((prefill_kernel<D, BS, KVT, NW>), dim3((unsigned)((a.items + 7) / 8 * 8)), dim3(64 * NW), 0,
-                     s, a);
+  hipLaunchKernelGGL((prefill_kernel<D, BS, KVT, kPrefillWaves, kPrefillTiles>),
+                     dim3((unsigned)((a.items + 7) / 8 * 8)), dim3(64 * kPrefillWaves), 0, s, a);
   return hipGetLastError();
 }
 
@@ -302,7 +340,7 @@ hipError_t launch_prefill_bs(const PrefillArgs& a, hipStream_t s) {
 
 }  // namespace
 
-int prefill_wg_tokens(int G) { return 8 * (16 / G); }
+int prefill_wg_tokens(int G) { return kPrefillWaves * kPrefillTiles * (16 / G); }
 
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t s) {
   if (a.kv_dtype == PKV_BF16)
