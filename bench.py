@@ -30,7 +30,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "paged decode attention KV GB/s (% of HBM peak) and sequences/s per layer"
 HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E
-KERNEL_SOURCE = os.path.join(ROOT, "paged_kv_cache_223_amd", "csrc", "paged_decode.hip")
+KERNEL_SOURCE = [os.path.join(ROOT, "paged_kv_cache_223_amd", "csrc", f) for f in ("paged_decode.hip", "tile_ops.h")]
 COUNTERS = os.path.join(ROOT, "profiles", "decode_counters.json")
 
 WORKLOADS = {
@@ -101,10 +101,10 @@ def algorithmic_bytes(tables, lens, bs, B, H_q, H_kv, D, s_kv, s_q, T_append, s_
                 decode_logical=kv_logical + other, append=append)
 
 
-def source_hash(path):
-    """Hash of a C++/HIP source with comments and whitespace removed, so that the counters
+def source_hash(paths):
+    """Hash of C++/HIP sources with comments and whitespace removed, so that the counters
     taken on a kernel stay valid across comment-only edits."""
-    text = open(path).read()
+    text = "".join(open(p).read() for p in paths)
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     text = re.sub(r"//[^\n]*", "", text)
     text = re.sub(r"\s+", "", text)

@@ -14,6 +14,10 @@ and writes profiles/decode_<W>.md plus the workload's entry of profiles/decode_c
 the decode kernel's code so that a changed kernel reports null until it is profiled again).
 
     python profile_report.py W T F R CF CW
+    python profile_report.py --kernels prefill_kernel --name prefill_70b --cmd "--op prefill" T F R CF CW
+
+The second form summarises other kernels of other bench modes into profiles/<name>.md (the trace
+and counter runs then use `bench.py <cmd>` in place of `--workload W`); it writes no counters JSON.
 """
 from __future__ import annotations
 
@@ -66,9 +70,68 @@ def counter_kib(d, counter):
 
 
 def main(argv):
-    if len(argv) != 6:
+    kernels, name, cmd = DECODE_KERNELS, None, None
+    while argv and argv[0].startswith("--"):
+        opt, val, argv = argv[0], argv[1], argv[2:]
+        if opt == "--kernels":
+            kernels = tuple(val.split(","))
+        elif opt == "--name":
+            name = val
+        elif opt == "--cmd":
+            cmd = val
+        else:
+            raise SystemExit(__doc__)
+    if name is None and len(argv) == 6:
+        report_decode(*argv, kernels)
+    elif name is not None and cmd is not None and len(argv) == 5:
+        report_other(name, cmd, kernels, *argv)
+    else:
         raise SystemExit(__doc__)
-    w, t_dir, f_dir, r_dir, cf_dir, cw_dir = argv
+
+
+def _calibration(cf_dir, cw_dir):
+    cf, cw = counter_kib(cf_dir, "FETCH_SIZE")["copy_kernel"][0], counter_kib(cw_dir, "WRITE_SIZE")["copy_kernel"][0]
+    return cf, cw, COPY_BYTES / (cf * 1024), COPY_BYTES / (cw * 1024)
+
+
+def _trace_lines(stats, launch, kernels, trace_cmd):
+    L = ["Kernel trace (rocprofv3 --kernel-trace --stats), one GPU.", "", "Command (from the repository root):", "",
+         "    " + trace_cmd, "", "| kernel | calls | total us | average us | % |", "|---|---|---|---|---|"]
+    for n, c, t, a, p in stats:
+        L.append(f"| {n} | {c} | {t:.1f} | {a:.2f} | {p:.1f} |")
+    L.append("")
+    for k in kernels:
+        if k in launch:
+            g, wg, v, ag, sg, lds, scr = launch[k]
+            L.append(f"{k} launch: grid {g} threads in workgroups of {wg}; VGPR field {v}, AGPR {ag}, "
+                     f"SGPR {sg}, LDS {lds} B, scratch {scr} B.")
+    return L
+
+
+def report_other(name, cmd, kernels, t_dir, f_dir, r_dir, cf_dir, cw_dir):
+    stats, launch = trace_stats(t_dir)
+    fetch, write = counter_kib(f_dir, "FETCH_SIZE"), counter_kib(r_dir, "WRITE_SIZE")
+    cf, cw, ff, wf = _calibration(cf_dir, cw_dir)
+    trace_cmd = f"rocprofv3 --kernel-trace --stats -T -d <out> -o trace -- python3 bench.py {cmd} --steps 20 --warmup 5"
+    pmc = f"timeout -s KILL 150 rocprofv3 --pmc {{c}} -T -d <out> -o {{o}} -- python3 bench.py {cmd} --steps 20 --warmup 2"
+    L = [f"# {name} on MI355X (`bench.py {cmd}`)", ""] + _trace_lines(stats, launch, kernels, trace_cmd)
+    L += ["", "## HBM traffic (rocprofv3 --pmc, one counter per run)", "", "Commands:", "",
+          "    " + pmc.format(c="FETCH_SIZE", o="fetch"), "    " + pmc.format(c="WRITE_SIZE", o="write"),
+          "    " + COPY_CMD.format(c="FETCH_SIZE", o="cf"), "    " + COPY_CMD.format(c="WRITE_SIZE", o="cw"), "",
+          f"Calibration: bytes = FETCH_SIZE x {ff:.4f} x 1024 and WRITE_SIZE x {wf:.4f} x 1024 (copy kernel over 1 GiB).",
+          "", "| kernel | FETCH_SIZE KiB/dispatch | WRITE_SIZE KiB/dispatch | dispatches | fetched MB | written MB |",
+          "|---|---|---|---|---|---|"]
+    for k in kernels:
+        if k in fetch and k in write:
+            L.append(f"| {k} | {fetch[k][0]:.1f} | {write[k][0]:.1f} | {fetch[k][1]} | "
+                     f"{fetch[k][0] * 1024 * ff / 1e6:.2f} | {write[k][0] * 1024 * wf / 1e6:.2f} |")
+    L.append("")
+    with open(os.path.join(ROOT, "profiles", f"{name}.md"), "w") as f:
+        f.write("\n".join(L))
+    print(name, {k: round(a, 2) for k, _, _, a, _ in stats if k in kernels})
+
+
+def report_decode(w, t_dir, f_dir, r_dir, cf_dir, cw_dir, kernels=DECODE_KERNELS):
     stats, launch = trace_stats(t_dir)
     fetch, write = counter_kib(f_dir, "FETCH_SIZE"), counter_kib(r_dir, "WRITE_SIZE")
     cf, cw = counter_kib(cf_dir, "FETCH_SIZE")["copy_kernel"][0], counter_kib(cw_dir, "WRITE_SIZE")["copy_kernel"][0]
