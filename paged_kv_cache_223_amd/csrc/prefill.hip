@@ -85,10 +85,11 @@ struct Stager {
   }
 };
 
-// online softmax update and PV of one column tile (S^T already computed)
-template <int D, int BS, int KVT>
-__device__ __forceinline__ void softmax_pv(const f32x4 (&s)[2], const u32x4* vops, f32x4 (&acc)[D / 16], float& m,
-                                           float& l, int cs, int p_lane, bool diag, float sl, int lane) {
+// online softmax update of one column tile (S^T already computed): rescales
+// acc when the running maximum moves and returns P as bf16 hi + lo operands
+template <int D>
+__device__ __forceinline__ void softmax_p(const f32x4 (&s)[2], f32x4 (&acc)[D / 16], float& m, float& l, int cs,
+                                          int p_lane, bool diag, float sl, int lane, u32x4& ph, u32x4& pl) {
   const int kg = lane >> 4;
   float x[8];
 #pragma unroll
@@ -129,7 +130,6 @@ __device__ __forceinline__ void softmax_pv(const f32x4 (&s)[2], const u32x4* vop
     lo[j] = p - __builtin_bit_cast(float, bits & 0xFFFF0000u);
   }
   l += psum;
-  u32x4 ph, pl;
 #pragma unroll
   for (int w = 0; w < 4; ++w) {
     ph[w] = __builtin_amdgcn_perm(hb[2 * w + 1], hb[2 * w], 0x07060302u);
@@ -138,11 +138,6 @@ __device__ __forceinline__ void softmax_pv(const f32x4 (&s)[2], const u32x4* vop
   }
   ph = tokens_by_eight(ph);
   pl = tokens_by_eight(pl);
-#pragma unroll
-  for (int t = 0; t < D / 16; ++t) {
-    acc[t] = mfma16x16x32(ph, vops[t], acc[t]);
-    acc[t] = mfma16x16x32(pl, vops[t], acc[t]);
-  }
 }
 
 // one wave's R column tiles over one staged chunk: every K and V operand read
@@ -187,7 +182,11 @@ __device__ __forceinline__ void prefill_chunk(const char* lds, const u32x4 (&qop
       }
     }
   }
-  // ---- V operands: 8 consecutive tokens of one column per lane; rows past n zero-selected
+  // ---- P of every tile, then each V operand (8 consecutive tokens of one column per lane)
+  // read once from LDS for all tiles; V rows past n are zero-selected
+  u32x4 ph[R], pl[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) softmax_p<D>(s[r], acc[r], m[r], l[r], cs, p_lane[r], diag, sl, lane, ph[r], pl[r]);
   const bool tail = cs + 32 > n;
   u32x4 vmask = u32x4{~0u, ~0u, ~0u, ~0u};
   if (tail) {
@@ -199,20 +198,22 @@ __device__ __forceinline__ void prefill_chunk(const char* lds, const u32x4 (&qop
   }
   const int tv = 8 * kg;
   const char* vb = vl + (BS >= 32 ? 0 : (tv / BS) * St::kTile) + ((size_t)mrow * BS + tv % BS) * S;
-  u32x4 vops[D / 16];
 #pragma unroll
   for (int t = 0; t < D / 16; ++t) {
+    u32x4 vop;
     if constexpr (KVT == PKV_BF16) {
-      vops[t] = *(const u32x4*)(vb + (size_t)t * 16 * BS * S);
+      vop = *(const u32x4*)(vb + (size_t)t * 16 * BS * S);
     } else {
       const u32x2 w = *(const u32x2*)(vb + (size_t)t * 16 * BS * S);
-      vops[t] = e4m3x8_to_bf16x8(w.x, w.y);
+      vop = e4m3x8_to_bf16x8(w.x, w.y);
     }
-    if (tail) vops[t] &= vmask;
-  }
+    if (tail) vop &= vmask;
 #pragma unroll
-  for (int r = 0; r < R; ++r)
-    softmax_pv<D, BS, KVT>(s[r], vops, acc[r], m[r], l[r], cs, p_lane[r], diag, sl, lane);
+    for (int r = 0; r < R; ++r) {
+      acc[r][t] = mfma16x16x32(ph[r], vop, acc[r][t]);
+      acc[r][t] = mfma16x16x32(pl[r], vop, acc[r][t]);
+    }
+  }
 }
 
 template <int D, int BS, int KVT, int NW, int R>
