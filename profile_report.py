@@ -109,12 +109,18 @@ def _trace_lines(stats, launch, kernels, trace_cmd):
 
 
 def report_other(name, cmd, kernels, t_dir, f_dir, r_dir, cf_dir, cw_dir):
+    """F and R may be '-' for a trace-only summary."""
     stats, launch = trace_stats(t_dir)
+    trace_cmd = f"rocprofv3 --kernel-trace --stats -T -d <out> -o trace -- python3 bench.py {cmd} --steps 20 --warmup 5"
+    L = [f"# {name} on MI355X (`bench.py {cmd}`)", ""] + _trace_lines(stats, launch, kernels, trace_cmd)
+    if f_dir == "-" or r_dir == "-":
+        with open(os.path.join(ROOT, "profiles", f"{name}.md"), "w") as f:
+            f.write("\n".join(L + [""]))
+        print(name, {k: round(a, 2) for k, _, _, a, _ in stats if k in kernels})
+        return
     fetch, write = counter_kib(f_dir, "FETCH_SIZE"), counter_kib(r_dir, "WRITE_SIZE")
     cf, cw, ff, wf = _calibration(cf_dir, cw_dir)
-    trace_cmd = f"rocprofv3 --kernel-trace --stats -T -d <out> -o trace -- python3 bench.py {cmd} --steps 20 --warmup 5"
     pmc = f"timeout -s KILL 150 rocprofv3 --pmc {{c}} -T -d <out> -o {{o}} -- python3 bench.py {cmd} --steps 20 --warmup 2"
-    L = [f"# {name} on MI355X (`bench.py {cmd}`)", ""] + _trace_lines(stats, launch, kernels, trace_cmd)
     L += ["", "## HBM traffic (rocprofv3 --pmc, one counter per run)", "", "Commands:", "",
           "    " + pmc.format(c="FETCH_SIZE", o="fetch"), "    " + pmc.format(c="WRITE_SIZE", o="write"),
           "    " + COPY_CMD.format(c="FETCH_SIZE", o="cf"), "    " + COPY_CMD.format(c="WRITE_SIZE", o="cw"), "",
