@@ -3,7 +3,8 @@
 
 A step is one pass of the whole hot path over one batch: kv_append of this step's token
 for every sequence, then paged decode attention of every sequence's query over its paged
-KV (piece kernel + piece merge).  The default workload is a
+KV (piece kernel + piece merge); with one new token per sequence the two run as one fused
+pkv_decode_step call (--unfused issues them separately).  The default workload is a
 Llama-3.1-70B-shaped layer: 32 sequences at 8192 tokens (16 of them share one refcounted
 2048-token prefix), H_q 64, H_kv 8, head dim 128, bf16 KV, 16-token blocks scattered by
 the allocator.  Inputs are synthetic and resident in HBM before the timed region.  A
@@ -67,6 +68,8 @@ def parse():
     p.add_argument("--seqs", type=int, default=4, help="sequences (--op prefill)")
     p.add_argument("--blocks", type=int, default=4096, help="blocks moved per swap call (--op swap)")
     p.add_argument("--pairs", type=int, default=4096, help="block pairs per copy_blocks call (--op copy_blocks)")
+    p.add_argument("--unfused", action="store_true",
+                   help="issue the step as kv_append + decode instead of the fused pkv_decode_step")
     p.add_argument("--sets", type=int, default=0,
                    help="independent copies of the inputs the steps rotate through (0 = enough for 1 GB of "
                         "KV, so the 256 MB last-level cache cannot hold the working set)")
@@ -207,16 +210,24 @@ def main():
     print(f"# setup {time.time() - t_setup:.1f}s: {wname} B={B} NB={case.NB} pool {2 * k_pool.numel() * k_pool.element_size() / 1e9:.2f} GB"
           f" x {n_sets} input set(s)", file=sys.stderr, flush=True)
 
+    # one new token per sequence into bf16 pools: the step is one fused call (the append runs
+    # inside the decode launch); E4M3 pools take kv_append + decode
+    fused = not args.unfused and len(mat.step_slots) == B and case.spec.kv_dtype == "bf16"
+
     def step(i=0, e0=None, e1=None, e2=None):
         kp, vp, q_, tab, ln, sk, sv, ss = sets[i % n_sets]
         if e0 is not None:
             e0.record()
-        if len(mat.step_slots):
+        if len(mat.step_slots) and not fused:
             pkv.kv_append(sk, sv, ss, kp, vp, k_scale, v_scale)
         if e1 is not None:
             e1.record()
-        pkv.paged_attn_decode(q_, kp, vp, tab, ln, float(case.scale), mcl, k_scale, v_scale,
-                              out=out, workspace=ws)
+        if fused:
+            pkv.decode_step(q_, sk, sv, ss, kp, vp, tab, ln, float(case.scale), mcl, k_scale, v_scale,
+                            out=out, workspace=ws)
+        else:
+            pkv.paged_attn_decode(q_, kp, vp, tab, ln, float(case.scale), mcl, k_scale, v_scale,
+                                  out=out, workspace=ws)
         if e2 is not None:
             e2.record()
 
@@ -258,7 +269,8 @@ def main():
           file=sys.stderr, flush=True)
 
     dec_avg_s = decode_ms.mean() / 1e3
-    dec_gbps = by["decode"] / dec_avg_s / 1e9
+    call_bytes = by["decode"] + (by["append"] if fused else 0)  # bytes of the timed call
+    dec_gbps = call_bytes / dec_avg_s / 1e9
     step_gbps = (by["decode"] + by["append"]) / (step_ms / 1e3) / 1e9
 
     # practical read ceiling: the library's non-temporal 16-byte streaming read over 4 GiB
@@ -297,7 +309,9 @@ def main():
         "seqs_per_s": round(B / (step_ms / 1e3), 1),
         "frac_of_hbm_peak": round(step_gbps / HBM_PEAK_GBPS, 4),
         "decode_us_p50": round(float(np.median(decode_ms)) * 1e3, 2),
-        "append_us_p50": round(float(np.median(append_ms)) * 1e3, 2),
+        "append_us_p50": None if fused else round(float(np.median(append_ms)) * 1e3, 2),
+        "step_call": "pkv_decode_step (append fused into the decode launch)" if fused else
+                     ("kv_append + paged_attn_decode" if len(mat.step_slots) else "paged_attn_decode"),
         "eager_ms_per_step": round(eager_step_ms, 5),
         "step_launch": "eager" if graphs is None else "hip_graph",
         "decode_GBps_unique": round(dec_gbps, 1),
@@ -309,10 +323,12 @@ def main():
     }
     traffic = measured_traffic(args.workload)
     res["roofline"] = {
-        "bound": "hbm", "kernel": "paged_attn_decode call = decode_piece_kernel + piece_merge_kernel",
+        "bound": "hbm",
+        "kernel": ("decode step call (append fused) = decode_piece_kernel + piece_merge_kernel" if fused else
+                   "paged_attn_decode call = decode_piece_kernel + piece_merge_kernel"),
         "achieved": round(dec_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
         "frac": round(dec_gbps / HBM_PEAK_GBPS, 4),
-        "algorithmic_bytes_per_launch": by["decode"],
+        "algorithmic_bytes_per_launch": call_bytes,
         "avg_launch_us": round(dec_avg_s * 1e6, 2),
         "traffic": traffic,
     }

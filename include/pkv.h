@@ -20,6 +20,8 @@
  *                          recent window (StreamingLLM; with pkv_seq_streaming_evict)
  *   pkv_paged_prefill      causal attention of a chunk of new tokens per sequence
  *                          (prompt or chunked prefill) over the same pools
+ *   pkv_decode_step        kv_append of one new token per sequence, then the
+ *                          decode, fused into the decode launch where it can be
  *   pkv_alloc_* / pkv_seq_* host-side fixed-block free-list allocator
  *
  * ---------------------------------------------------------------------------
@@ -195,6 +197,30 @@ int pkv_paged_attn_decode(float* out, const void* q, int q_dtype, const void* k_
                           int32_t D, int32_t NB, int32_t bs, float scale, const float* k_scale,
                           const float* v_scale, void* workspace, size_t workspace_bytes,
                           void* stream);
+
+/*
+ * pkv_decode_step — one decode step: the same result (output and pools) as
+ *     pkv_kv_append(k_new, v_new, src_dtype, new_slots, T = B, ...);
+ *     pkv_paged_attn_decode(...);
+ * where sequence b's new token is its last position: context_lens[b] counts
+ * it and new_slots[b] is the slot of position context_lens[b] - 1 (or < 0:
+ * the sequence appends nothing this step).
+ *   k_new, v_new   device [B][H_kv][D] of src_dtype; new_slots device int64 [B]
+ *   others         as pkv_paged_attn_decode / pkv_kv_append
+ * With bf16 q, bf16 source and bf16 pools on the matrix-core path, the append
+ * runs inside the decode launch: the piece that reads position n - 1 takes the
+ * new token from k_new/v_new (the bits the append stores) and stores it into
+ * the pool after its reads, saving the append launch.  Other combinations
+ * issue the two calls.  In the fused form, a new_slots[b] that is not the slot
+ * of position n - 1 (or a sequence with n = 0) is a caller error: the token is
+ * then stored (when its position's piece exists) but not attended.
+ */
+int pkv_decode_step(float* out, const void* q, int q_dtype, const void* k_new, const void* v_new,
+                    int src_dtype, const int64_t* new_slots, void* k_pool, void* v_pool, int kv_dtype,
+                    const int32_t* block_tables, int32_t max_blocks_per_seq, const int32_t* context_lens,
+                    int32_t max_context_len, int32_t B, int32_t H_q, int32_t H_kv, int32_t D, int32_t NB,
+                    int32_t bs, float scale, const float* k_scale, const float* v_scale, void* workspace,
+                    size_t workspace_bytes, void* stream);
 
 /*
  * pkv_paged_attn_decode_window — pkv_paged_attn_decode over part of each

@@ -56,6 +56,9 @@ SIGNATURES = {
     "pkv_paged_attn_decode_window": (ctypes.c_int, [_P, _P, ctypes.c_int, _P, _P, ctypes.c_int, _P, _I32, _P,
                                                     _I32, _P, _P, _I32, _I32, _I32, _I32, _I32, _I32,
                                                     ctypes.c_float, _P, _P, _P, _SZ, _P]),
+    "pkv_decode_step": (ctypes.c_int, [_P, _P, ctypes.c_int, _P, _P, ctypes.c_int, _P, _P, _P, ctypes.c_int, _P,
+                                       _I32, _P, _I32, _I32, _I32, _I32, _I32, _I32, _I32, ctypes.c_float, _P, _P,
+                                       _P, _SZ, _P]),
     "pkv_paged_prefill": (ctypes.c_int, [_P, _P, ctypes.c_int, _P, _P, ctypes.c_int, _P, _I32, _P, _P, _I32, _I32,
                                          _I32, _I32, _I32, _I32, _I32, _I32, ctypes.c_float, _P, _P, _P]),
     "pkv_alloc_create": (ctypes.c_int, [_I32, _I32, _P, ctypes.POINTER(_P)]),
@@ -314,6 +317,40 @@ def paged_attn_decode(q, k_pool, v_pool, block_tables, context_lens, scale: floa
     return out
 
 
+def decode_step(q, k_new, v_new, new_slots, k_pool, v_pool, block_tables, context_lens, scale: float,
+                max_context_len: int, k_scale=None, v_scale=None, out=None, workspace=None):
+    """kv_append(k_new, v_new, new_slots) then paged_attn_decode, fused into one launch where possible.
+    k_new, v_new: [B, H_kv, D] (sequence b's token at its last position); new_slots: int64 [B]."""
+    torch = _torch()
+    _dev(q, k_new, v_new, new_slots, k_pool, v_pool, block_tables, context_lens, k_scale, v_scale, out, workspace)
+    kv, NB, H_kv, D, bs = _pool_dims(k_pool, v_pool)
+    if q.dim() != 3 or q.shape[2] != D:
+        raise ValueError("q must be [B, H_q, D]")
+    B, H_q, _ = q.shape
+    src = dtype_code(k_new)
+    if dtype_code(v_new) != src or tuple(k_new.shape) != (B, H_kv, D) or tuple(v_new.shape) != (B, H_kv, D):
+        raise ValueError("k_new and v_new must both be [B, H_kv, D] of one dtype")
+    if new_slots.dtype != torch.int64 or new_slots.shape != (B,):
+        raise ValueError("new_slots must be int64 [B]")
+    if block_tables.dtype != torch.int32 or block_tables.dim() != 2 or block_tables.shape[0] != B:
+        raise ValueError("block_tables must be int32 [B, max_blocks]")
+    if context_lens.dtype != torch.int32 or context_lens.shape != (B,):
+        raise ValueError("context_lens must be int32 [B]")
+    if out is None:
+        out = torch.empty((B, H_q, D), dtype=torch.float32, device=q.device)
+    elif out.dtype != torch.float32 or tuple(out.shape) != (B, H_q, D):
+        raise ValueError("out must be fp32 [B, H_q, D]")
+    need = decode_workspace_bytes(B, H_q, H_kv, D, max_context_len, bs)
+    if workspace is None and need:
+        workspace = _cached_workspace(q.device, need)
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(lib.pkv_decode_step(_ptr(out), _ptr(q), dtype_code(q), _ptr(k_new), _ptr(v_new), src, _ptr(new_slots),
+                               _ptr(k_pool), _ptr(v_pool), kv, _ptr(block_tables), block_tables.shape[1],
+                               _ptr(context_lens), int(max_context_len), B, H_q, H_kv, D, NB, bs, float(scale),
+                               _ptr(k_scale), _ptr(v_scale), _ptr(workspace), ws_bytes, _stream()))
+    return out
+
+
 def paged_prefill(q, k_pool, v_pool, block_tables, context_lens, query_start, scale: float, max_query_len: int,
                   k_scale=None, v_scale=None, out=None):
     """Causal prefill of the last C_b tokens of each sequence (K/V already appended); q bf16 [T, H_q, D]
@@ -463,7 +500,7 @@ class Allocator:
 
 
 __all__ = ["lib", "LIB_PATH", "PkvError", "last_error", "kv_append", "copy_blocks", "gather_blocks",
-           "scatter_blocks", "paged_attn_decode", "paged_prefill",
+           "scatter_blocks", "paged_attn_decode", "paged_prefill", "decode_step",
            "decode_workspace_bytes",
            "decode_workspace",
            "pool_shapes", "dtype_code", "stream_read", "copy_", "Allocator", "SIGNATURES",

@@ -217,7 +217,8 @@ static int decode_impl(float* out, const void* q, int q_dtype, const void* k_poo
                        int32_t max_context_len, const int32_t* sink_lens, const int32_t* window_starts, int32_t B,
                        int32_t H_q, int32_t H_kv, int32_t D, int32_t NB, int32_t bs, float scale,
                        const float* k_scale, const float* v_scale, void* workspace, size_t workspace_bytes,
-                       void* stream) {
+                       void* stream, const void* new_k = nullptr, const void* new_v = nullptr,
+                       const int64_t* new_slots = nullptr) {
   if (B < 0 || H_q <= 0 || H_kv <= 0 || NB <= 0 || max_blocks_per_seq <= 0 || max_context_len < 0) {
     set_error("decode: bad sizes B=%d H_q=%d H_kv=%d NB=%d max_blocks=%d max_context_len=%d", B, H_q, H_kv, NB,
               max_blocks_per_seq, max_context_len);
@@ -273,6 +274,9 @@ static int decode_impl(float* out, const void* q, int q_dtype, const void* k_poo
   a.context_lens = context_lens;
   a.sink_lens = sink_lens;
   a.window_starts = window_starts;
+  a.new_k = new_k;
+  a.new_v = new_v;
+  a.new_slots = new_slots;
   a.k_scale = k_scale;
   a.v_scale = v_scale;
   if (need > 0) {
@@ -394,6 +398,35 @@ int pkv_paged_prefill(float* out, const void* q, int q_dtype, const void* k_pool
   a.items = (int)items;
   a.groups_per_seq = (int)groups;
   return hip_status(launch_prefill(a, (hipStream_t)stream), "prefill launch");
+}
+
+int pkv_decode_step(float* out, const void* q, int q_dtype, const void* k_new, const void* v_new, int src_dtype,
+                    const int64_t* new_slots, void* k_pool, void* v_pool, int kv_dtype, const int32_t* block_tables,
+                    int32_t max_blocks_per_seq, const int32_t* context_lens, int32_t max_context_len, int32_t B,
+                    int32_t H_q, int32_t H_kv, int32_t D, int32_t NB, int32_t bs, float scale, const float* k_scale,
+                    const float* v_scale, void* workspace, size_t workspace_bytes, void* stream) {
+  g_err[0] = 0;
+  const bool fused = B > 0 && H_kv > 0 && H_q % H_kv == 0 && kv_dtype == PKV_BF16 && src_dtype == PKV_BF16 &&
+                     decode_fast_path_supported(q_dtype, kv_dtype, H_q / H_kv, D, bs);
+  if (!fused) {  // the two calls, in order, on the stream
+    const int st = pkv_kv_append(k_new, v_new, src_dtype, new_slots, B, k_pool, v_pool, kv_dtype, NB, bs, H_kv, D,
+                                 k_scale, v_scale, stream);
+    if (st != PKV_OK) return st;
+    return decode_impl(out, q, q_dtype, k_pool, v_pool, kv_dtype, block_tables, max_blocks_per_seq, context_lens,
+                       max_context_len, nullptr, nullptr, B, H_q, H_kv, D, NB, bs, scale, k_scale, v_scale,
+                       workspace, workspace_bytes, stream);
+  }
+  if (!k_new || !v_new || !new_slots) {
+    set_error("decode_step: null new-token pointer");
+    return PKV_ERR_INVALID_ARG;
+  }
+  if (NB <= 0 || bs <= 0 || (long long)NB * bs > 0x7FFFFFFFFFFFLL) {
+    set_error("decode_step: bad pool size NB=%d bs=%d", NB, bs);
+    return PKV_ERR_INVALID_ARG;
+  }
+  return decode_impl(out, q, q_dtype, k_pool, v_pool, kv_dtype, block_tables, max_blocks_per_seq, context_lens,
+                     max_context_len, nullptr, nullptr, B, H_q, H_kv, D, NB, bs, scale, k_scale, v_scale, workspace,
+                     workspace_bytes, stream, k_new, v_new, new_slots);
 }
 
 size_t pkv_stream_read_sink_floats(size_t bytes) { return stream_read_blocks(bytes); }

@@ -78,6 +78,9 @@ struct DecodeArgs {
   const void* v_pool;
   const int32_t* block_tables;
   const int32_t* context_lens;
+  const void* new_k;            // fused step: the step's K rows [B][H_kv][D] bf16 (null: plain decode)
+  const void* new_v;            // fused step: the step's V rows [B][H_kv][D] bf16
+  const int64_t* new_slots;     // fused step: slot of sequence b's new token ([B]; < 0: none)
   const int32_t* sink_lens;      // optional [B]: attend t < sink_lens[b] ...
   const int32_t* window_starts;  // optional [B]: ... or t >= window_starts[b] (both null: every t < n)
   const float* k_scale;

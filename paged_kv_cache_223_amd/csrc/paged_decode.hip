@@ -266,6 +266,55 @@ __device__ __forceinline__ void process_chunk(const Chunk<D, BS, KVT>& ch, const
 }
 
 // ---------------------------------------------------------------------------
+// fused step (append + decode): the step's new token of (b, g) at position n - 1
+// ---------------------------------------------------------------------------
+// Put the new token straight into the loaded operands of the chunk holding
+// position n - 1 (tk = its offset in the chunk, wave-uniform): in a bf16 pool
+// the append stores the row's bits as they are, so the decode sees the
+// appended token while the pool store waits until after the chunk loop.
+template <int D, int BS, int KVT>
+__device__ __forceinline__ void inject_new_token(Chunk<D, BS, KVT>& ch, const DecodeArgs& a, int b, int g, int tk,
+                                                 int lane) {
+  static_assert(KVT == PKV_BF16, "the fused step serves bf16 pools");
+  const uint16_t* nk = (const uint16_t*)a.new_k + ((size_t)b * a.H_kv + g) * D;
+  const uint16_t* nv = (const uint16_t*)a.new_v + ((size_t)b * a.H_kv + g) * D;
+  const int m = lane & 15, kg = lane >> 4;
+  if (m == (tk & 15)) {  // K: lane m of half tk / 16 holds the token's row, dim groups kg + 4c
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      if (half != (tk >> 4)) continue;
+#pragma unroll
+      for (int c = 0; c < Chunk<D, BS, KVT>::kKLoads; ++c) ch.k[half][c] = *(const u32x4*)(nk + (kg + 4 * c) * 8);
+    }
+  }
+  if (kg == (tk >> 3)) {  // V: element tk % 8 of lane (m, kg)'s 8 tokens of column 16 t + m
+    const int j = tk & 7, sh = 16 * (j & 1);
+#pragma unroll
+    for (int t = 0; t < D / 16; ++t) {
+      const uint32_t x = nv[16 * t + m];
+#pragma unroll
+      for (int wd = 0; wd < 4; ++wd)
+        if (wd == j / 2) ch.v[t][wd] = (ch.v[t][wd] & ~(0xFFFFu << sh)) | (x << sh);
+    }
+  }
+}
+
+// The pool store of the new token's K and V rows of head g (one wave, after
+// the chunk loop), the same bytes pkv_kv_append writes into a bf16 pool.
+template <int D, int BS>
+__device__ __forceinline__ void write_new_token(const DecodeArgs& a, int b, int g, long long slot, int lane) {
+  const uint16_t* nk = (const uint16_t*)a.new_k + ((size_t)b * a.H_kv + g) * D;
+  const uint16_t* nv = (const uint16_t*)a.new_v + ((size_t)b * a.H_kv + g) * D;
+  const size_t tile = ((size_t)(slot / BS) * a.H_kv + g) * (size_t)D * BS;  // bf16 elements
+  const int off = (int)(slot % BS);
+  uint16_t* kp = (uint16_t*)a.k_pool + tile;
+  uint16_t* vp = (uint16_t*)a.v_pool + tile;
+  if (lane < D / 8)  // K [D/8][BS][8]: one 16-byte dim group per lane
+    *(u32x4*)(kp + ((size_t)lane * BS + off) * 8) = *(const u32x4*)(nk + lane * 8);
+  for (int d = lane; d < D; d += 64) vp[(size_t)d * BS + off] = nv[d];  // V [D][BS]
+}
+
+// ---------------------------------------------------------------------------
 // matrix-core path: one piece per workgroup, pieces planned from the lengths
 //
 // The batch's work is c_b = ceil(n_b / 32) chunks per (sequence b, KV head g)
@@ -361,11 +410,23 @@ __device__ int plan_piece(const DecodeArgs& a, int target, int item, int lane, P
   return upw;
 }
 
+// process one chunk; in the fused step the new token enters the operands of
+// its chunk just before they are used
+template <int D, int BS, int KVT, bool APPEND>
+__device__ __forceinline__ void proc_chunk(Chunk<D, BS, KVT>& X, const DecodeArgs& a, const u32x4 (&qop)[D / 32],
+                                           f32x4 (&acc)[D / 16], WaveState& st, int c, int n, int hlo, int hhi,
+                                           float sl, int inject_chunk, int b, int g, int lane) {
+  if constexpr (APPEND)
+    if (c == inject_chunk) inject_new_token(X, a, b, g, n - 1 - 32 * c, lane);
+  process_chunk(X, qop, acc, st, c, n, hlo, hhi, sl, lane);
+}
+
 // The wave's share of one piece: chunks first, first + NW, ... below c_end of
 // segment (b, g), with the next chunk's loads in flight while one is computed.
-template <int D, int BS, int KVT, int NW>
+template <int D, int BS, int KVT, int NW, bool APPEND>
 __device__ __forceinline__ void run_piece(const DecodeArgs& a, int b, int g, int n, int hlo, int hhi, int first,
-                                          int c_end, f32x4 (&acc)[D / 16], WaveState& st, int lane) {
+                                          int c_end, int inject_chunk, f32x4 (&acc)[D / 16], WaveState& st,
+                                          int lane) {
   const int G = a.G;
   const int last_blk = (n + BS - 1) / BS - 1;
   const int32_t* tab = a.block_tables + (size_t)b * a.max_blocks;
@@ -396,22 +457,23 @@ __device__ __forceinline__ void run_piece(const DecodeArgs& a, int b, int g, int
   int k = 0;
   for (; k + 2 < cnt; k += 2) {
     load_chunk(Bf, kpool, vpool, tab, c + NW, last_blk, a.NB, a.H_kv, g, lane);
-    process_chunk(A, qop, acc, st, c, n, hlo, hhi, sl, lane);
+    proc_chunk<D, BS, KVT, APPEND>(A, a, qop, acc, st, c, n, hlo, hhi, sl, inject_chunk, b, g, lane);
     load_chunk(A, kpool, vpool, tab, c + 2 * NW, last_blk, a.NB, a.H_kv, g, lane);
-    process_chunk(Bf, qop, acc, st, c + NW, n, hlo, hhi, sl, lane);
+    proc_chunk<D, BS, KVT, APPEND>(Bf, a, qop, acc, st, c + NW, n, hlo, hhi, sl, inject_chunk, b, g, lane);
     c += 2 * NW;
   }
   if (k + 1 < cnt) {
     load_chunk(Bf, kpool, vpool, tab, c + NW, last_blk, a.NB, a.H_kv, g, lane);
-    process_chunk(A, qop, acc, st, c, n, hlo, hhi, sl, lane);
-    process_chunk(Bf, qop, acc, st, c + NW, n, hlo, hhi, sl, lane);
+    proc_chunk<D, BS, KVT, APPEND>(A, a, qop, acc, st, c, n, hlo, hhi, sl, inject_chunk, b, g, lane);
+    proc_chunk<D, BS, KVT, APPEND>(Bf, a, qop, acc, st, c + NW, n, hlo, hhi, sl, inject_chunk, b, g, lane);
   } else {
-    process_chunk(A, qop, acc, st, c, n, hlo, hhi, sl, lane);
+    proc_chunk<D, BS, KVT, APPEND>(A, a, qop, acc, st, c, n, hlo, hhi, sl, inject_chunk, b, g, lane);
   }
 }
 
-template <int D, int BS, int KVT, int NW>
-__global__ __launch_bounds__(64 * NW, KVT == PKV_FP8_E4M3 ? 3 : 2) void decode_piece_kernel(DecodeArgs a, int target) {
+template <int D, int BS, int KVT, int NW, bool APPEND>
+__global__ __launch_bounds__(64 * NW, KVT == PKV_FP8_E4M3 ? 3 : 2) void decode_piece_kernel(DecodeArgs a,
+                                                                                          int target) {
   constexpr int NT = 64 * NW;
   __shared__ float sh_acc[NW][16][D];
   __shared__ float sh_m[NW][16];
@@ -437,9 +499,25 @@ __global__ __launch_bounds__(64 * NW, KVT == PKV_FP8_E4M3 ? 3 : 2) void decode_p
   seq_hole(a, b, hlo, hhi);
   hlo = uniform(hlo);
   hhi = uniform(hhi);
+  // fused step: the piece holding position n - 1 takes the new token from the
+  // step's rows when its slot is that position's slot (else the pool is read as is)
+  int inject_chunk = -1;
+  bool writer = false;  // this piece stores the new token into the pool after its loop
+  long long new_slot = -1;
+  if constexpr (APPEND) {
+    new_slot = a.new_slots[b];
+    const int last = n - 1, uc = last / 32;
+    writer = n > 0 && lo <= uc && uc < hi && new_slot >= 0 && new_slot < (long long)a.NB * BS;
+    if (writer) {
+      const int32_t* tab = a.block_tables + (size_t)b * a.max_blocks;
+      const long long expect = (long long)tab[last / BS] * BS + last % BS;
+      if (expect == new_slot) inject_chunk = uc;
+    }
+    inject_chunk = uniform(inject_chunk);
+  }
   f32x4 acc[D / 16];
   WaveState st;
-  run_piece<D, BS, KVT, NW>(a, b, g, n, hlo, hhi, lo + w, hi, acc, st, lane);
+  run_piece<D, BS, KVT, NW, APPEND>(a, b, g, n, hlo, hhi, lo + w, hi, inject_chunk, acc, st, lane);
   // ---- merge the NW waves' shares through LDS
   const int kg = lane >> 4;
   float lt = st.l;
@@ -480,6 +558,8 @@ __global__ __launch_bounds__(64 * NW, KVT == PKV_FP8_E4M3 ? 3 : 2) void decode_p
       }
     }
   }
+  if constexpr (APPEND)
+    if (writer && w == 0) write_new_token<D, BS>(a, b, g, new_slot, lane);
 }
 
 // Merge the pieces of every segment cut into several; one workgroup per
@@ -719,12 +799,12 @@ __global__ __launch_bounds__(256) void split_merge_kernel(DecodeArgs a) {
   }
 }
 
-// workgroups of decode_piece_kernel<D, BS, KVT, NW> one CU holds at once
-template <int D, int BS, int KVT, int NW>
+// workgroups of decode_piece_kernel<D, BS, KVT, NW, APPEND> one CU holds at once
+template <int D, int BS, int KVT, int NW, bool APPEND>
 int piece_groups_per_cu() {
   static const int per_cu = [] {
     int nb = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, decode_piece_kernel<D, BS, KVT, NW>, 64 * NW, 0) !=
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, decode_piece_kernel<D, BS, KVT, NW, APPEND>, 64 * NW, 0) !=
             hipSuccess ||
         nb <= 0)
       nb = 1;
@@ -733,8 +813,8 @@ int piece_groups_per_cu() {
   return per_cu;
 }
 
-template <int D, int BS, int KVT>
-hipError_t launch_mfma_t(const DecodeArgs& a, hipStream_t s) {
+template <int D, int BS, int KVT, bool APPEND>
+hipError_t launch_mfma_a(const DecodeArgs& a, hipStream_t s) {
   // target pieces = one round of resident workgroups; the plan never makes more
   // than target + B * H_kv pieces, which sizes the grid (the rest exit at once).
   // 8-wave workgroups when every (sequence, KV head) segment fits one round
@@ -742,18 +822,25 @@ hipError_t launch_mfma_t(const DecodeArgs& a, hipStream_t s) {
   // workgroups, twice as many, so that piece boundaries of one workgroup
   // overlap another's streaming on the same CU.
   const long long segments = (long long)a.B * a.H_kv;
-  const int target8 = piece_groups_per_cu<D, BS, KVT, 8>() * a.num_cus;
+  const int target8 = piece_groups_per_cu<D, BS, KVT, 8, APPEND>() * a.num_cus;
   const bool wide = segments <= target8;
-  const int target = wide ? target8 : piece_groups_per_cu<D, BS, KVT, 4>() * a.num_cus;
+  const int target = wide ? target8 : piece_groups_per_cu<D, BS, KVT, 4, APPEND>() * a.num_cus;
   const long long grid = (long long)target + segments;
   if (wide)
-    hipLaunchKernelGGL((decode_piece_kernel<D, BS, KVT, 8>), dim3((unsigned)grid), dim3(512), 0, s, a, target);
+    hipLaunchKernelGGL((decode_piece_kernel<D, BS, KVT, 8, APPEND>), dim3((unsigned)grid), dim3(512), 0, s, a, target);
   else
-    hipLaunchKernelGGL((decode_piece_kernel<D, BS, KVT, 4>), dim3((unsigned)grid), dim3(256), 0, s, a, target);
+    hipLaunchKernelGGL((decode_piece_kernel<D, BS, KVT, 4, APPEND>), dim3((unsigned)grid), dim3(256), 0, s, a, target);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(piece_merge_kernel, dim3((unsigned)(a.B * a.H_kv)), dim3(256), 0, s, a, target);
   return hipGetLastError();
+}
+
+template <int D, int BS, int KVT>
+hipError_t launch_mfma_t(const DecodeArgs& a, hipStream_t s) {
+  if constexpr (KVT == PKV_BF16)  // the fused step exists for bf16 pools (the host routes the others)
+    if (a.new_k) return launch_mfma_a<D, BS, KVT, true>(a, s);
+  return launch_mfma_a<D, BS, KVT, false>(a, s);
 }
 
 template <int D, int KVT>

@@ -175,7 +175,8 @@ def report_decode(w, t_dir, f_dir, r_dir, cf_dir, cw_dir, kernels=DECODE_KERNELS
             g, wg, v, ag, sg, lds, scr = launch[k]
             L.append(f"{k} launch: grid {g} threads in workgroups of {wg}; VGPR field {v}, AGPR {ag}, "
                      f"SGPR {sg}, LDS {lds} B, scratch {scr} B.")
-    L += ["", "kv_append calls of the step are the short ones; the long ones are the setup's prefill.", "",
+    L += ["", "With bf16 pools the step's append runs inside decode_piece_kernel (pkv_decode_step), so every",
+          "kv_append call is the setup's prefill; with E4M3 pools the step's kv_append calls are the short ones.", "",
           "## HBM traffic (rocprofv3 --pmc, one counter per run)", "", "Commands:", "",
           "    " + PMC_CMD.format(c="FETCH_SIZE", o="fetch", w=w), "    " + PMC_CMD.format(c="WRITE_SIZE", o="write", w=w),
           "    " + COPY_CMD.format(c="FETCH_SIZE", o="cf"), "    " + COPY_CMD.format(c="WRITE_SIZE", o="cw"), "",

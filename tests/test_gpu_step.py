@@ -1,0 +1,134 @@
+"""The fused decode step (pkv_decode_step) against kv_append followed by the decode, from the same
+pools: the output and the pools are identical bit for bit (the fused piece takes the new token's
+operands from the step's rows, the same bits the append stores, and keeps the reduction order), and
+the output matches the oracle.  Covers the fused form (bf16 pools, several block sizes, a sequence
+without a new token, a captured graph) and the two-launch form (E4M3 pools)."""
+import numpy as np
+import pytest
+import torch
+
+import paged_kv_cache_223_amd as pkv
+import workloads
+from tests.gpu_helpers import DEV, from_dev, src_dtype, to_dev
+from tests.oracle_cases import materialize_with_model, oracle_decode, oracle_pools, row_rel_err
+
+pytestmark = pytest.mark.gpu
+
+
+def _pre_step_pools(case, mat):
+    """Device pools holding everything but the step's tokens (NaN / 0x7F elsewhere)."""
+    spec = case.spec
+    kvd = {"bf16": pkv.BF16, "e4m3": pkv.FP8_E4M3, "f32": pkv.F32}[spec.kv_dtype]
+    ks, vs = pkv.pool_shapes(case.NB, spec.H_kv, spec.d, case.bs, kvd)
+    if spec.kv_dtype == "e4m3":
+        kp = torch.full(ks, 0x7F, dtype=torch.uint8, device=DEV)
+        vp = torch.full(vs, 0x7F, dtype=torch.uint8, device=DEV)
+    else:
+        kp = torch.full(ks, float("nan"), dtype=torch.bfloat16, device=DEV)
+        vp = torch.full(vs, float("nan"), dtype=torch.bfloat16, device=DEV)
+    k_s = None if case.k_scale is None else torch.from_numpy(case.k_scale).to(DEV)
+    v_s = None if case.v_scale is None else torch.from_numpy(case.v_scale).to(DEV)
+    sd = src_dtype(case)
+    for i in range(0, len(mat.slots), 65536):
+        pkv.kv_append(to_dev(mat.k_src[i:i + 65536], sd), to_dev(mat.v_src[i:i + 65536], sd),
+                      torch.from_numpy(np.ascontiguousarray(mat.slots[i:i + 65536])).to(DEV), kp, vp, k_s, v_s)
+    torch.cuda.synchronize()
+    return kp, vp, k_s, v_s
+
+
+def _both_ways(case, mat, drop=()):
+    """(unfused out, unfused pools, fused out, fused pools); sequences in `drop` append nothing."""
+    slots = mat.step_slots.copy()
+    lens = mat.context_lens.copy()
+    for b in drop:
+        slots[b] = -1
+        lens[b] -= 1
+    q = to_dev(case.q, "bf16")
+    sk, sv = to_dev(mat.step_k.reshape(case.B, case.spec.H_kv, case.spec.d), "bf16"), \
+        to_dev(mat.step_v.reshape(case.B, case.spec.H_kv, case.spec.d), "bf16")
+    tab = torch.from_numpy(mat.block_tables).to(DEV)
+    ln = torch.from_numpy(lens).to(DEV)
+    sl = torch.from_numpy(slots).to(DEV)
+    res = []
+    for fused in (False, True):
+        kp, vp, k_s, v_s = _pre_step_pools(case, mat)
+        if fused:
+            out = pkv.decode_step(q, sk, sv, sl, kp, vp, tab, ln, float(case.scale), case.max_context_len, k_s, v_s)
+        else:
+            pkv.kv_append(sk, sv, sl, kp, vp, k_s, v_s)
+            out = pkv.paged_attn_decode(q, kp, vp, tab, ln, float(case.scale), case.max_context_len, k_s, v_s)
+        torch.cuda.synchronize()
+        res += [out.cpu().numpy(), from_dev(kp), from_dev(vp)]
+    return res, lens
+
+
+def _with_step(case):
+    """A custom case whose last token of every sequence is this step's append."""
+    steps = []
+    for op in list(case.ops):
+        if op[0] == "append":
+            _, sid, n, (key, start) = op
+            case.ops.remove(op)
+            if n > 1:
+                case.ops.append(("append", sid, n - 1, (key, start)))
+            steps.append(("append", sid, 1, (key, start + n - 1)))
+    case.step_ops = steps
+    return case
+
+
+CASES = {
+    "llama70b_B6_ctx700": lambda: workloads.llama70b_bf16(B=6, ctx=700, prefix=256),
+    "llama70b_B3_ctx33": lambda: workloads.llama70b_bf16(B=3, ctx=33, prefix=16),
+    "e4m3_two_launch": lambda: _with_step(workloads.custom("step_e4m3", 4, 64, 8, 128, 16, "e4m3", "bf16",
+                                                           [300, 17, 1, 128], 91)),
+}
+
+
+@pytest.mark.parametrize("name", sorted(CASES))
+def test_fused_step_equals_append_then_decode_bitwise(name):
+    print(f"decode step {name}", flush=True)
+    case = CASES[name]()
+    mat = materialize_with_model(case)
+    (o0, k0, v0, o1, k1, v1), lens = _both_ways(case, mat)
+    assert np.array_equal(k0, k1) and np.array_equal(v0, v1)
+    assert np.array_equal(o0.view(np.uint32), o1.view(np.uint32))
+    kp, vp = oracle_pools(case, mat)
+    ref = oracle_decode(case, mat, kp, vp)
+    tol = 2e-2 if case.spec.kv_dtype == "e4m3" else 2e-3
+    assert row_rel_err(o1.astype(np.float64), ref) <= tol
+
+
+@pytest.mark.parametrize("bs", [8, 16, 32])
+def test_fused_step_block_sizes_and_a_sequence_without_a_token(bs):
+    case = _with_step(workloads.custom(f"step_bs{bs}", 5, 32, 8, 128, bs, "bf16", "bf16", [1, 40, 97, 500, 33], 92))
+    mat = materialize_with_model(case)
+    (o0, k0, v0, o1, k1, v1), lens = _both_ways(case, mat, drop=(2,))
+    assert np.array_equal(k0, k1) and np.array_equal(v0, v1)
+    assert np.array_equal(o0.view(np.uint32), o1.view(np.uint32))
+
+
+def test_fused_full_70b_step_and_graph_replay():
+    case = workloads.llama70b_bf16()
+    mat = materialize_with_model(case)
+    (o0, k0, v0, o1, k1, v1), lens = _both_ways(case, mat)
+    assert np.array_equal(o0.view(np.uint32), o1.view(np.uint32))
+    assert np.array_equal(k0, k1) and np.array_equal(v0, v1)
+    # replays of a captured fused step equal the eager result
+    kp, vp, _, _ = _pre_step_pools(case, mat)
+    q = to_dev(case.q, "bf16")
+    sk = to_dev(mat.step_k.reshape(case.B, 8, 128), "bf16")
+    sv = to_dev(mat.step_v.reshape(case.B, 8, 128), "bf16")
+    tab, ln = torch.from_numpy(mat.block_tables).to(DEV), torch.from_numpy(mat.context_lens).to(DEV)
+    sl = torch.from_numpy(mat.step_slots).to(DEV)
+    out = torch.empty((case.B, 64, 128), dtype=torch.float32, device=DEV)
+    ws = pkv.decode_workspace(case.B, 64, 8, 128, case.max_context_len, case.bs, device=DEV)
+    pkv.decode_step(q, sk, sv, sl, kp, vp, tab, ln, float(case.scale), case.max_context_len, out=out, workspace=ws)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        pkv.decode_step(q, sk, sv, sl, kp, vp, tab, ln, float(case.scale), case.max_context_len, out=out,
+                        workspace=ws)
+    for _ in range(3):
+        out.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(out.cpu().numpy().view(np.uint32), o1.view(np.uint32))
