@@ -76,35 +76,57 @@ struct Stager {
     }
   }
 
-  __device__ __forceinline__ void store(char* lds, int tid) const {
+  // Copy into LDS.  nvalid = tokens of the chunk before the sequence's end: on
+  // the chunk holding the end (nvalid < 32, uniform) the V elements of later
+  // tokens are zeroed, since a P of 0 does not cancel whatever the pool holds
+  // there (K needs nothing: masked scores are selected, not multiplied).
+  __device__ __forceinline__ void store(char* lds, int tid, int nvalid) const {
+    constexpr int tileU = St::kTile / 16;
+    constexpr int E = 16 / St::S;  // elements per 16-byte unit
+    static_assert(St::S <= 2, "prefill pools hold bf16 or E4M3");
 #pragma unroll
     for (int k = 0; k < kPer; ++k) {
       const int u = tid + k * NT;
-      if (St::kUnits % NT == 0 || u < St::kUnits) *(u32x4*)(lds + (size_t)u * 16) = r[k];
+      if (St::kUnits % NT == 0 || u < St::kUnits) {
+        u32x4 v = r[k];
+        if (nvalid < 32 && u >= St::NBCH * tileU) {  // a V unit of the chunk holding the end
+          const int w = u - St::NBCH * tileU;
+          const int tok0 = (w / tileU) * BS, e0 = (w % tileU) * E;  // tile [D][BS]: element e is token e % BS
+#pragma unroll
+          for (int j = 0; j < E; ++j)
+            if (tok0 + (e0 + j) % BS >= nvalid) v[j * St::S / 4] &= ~(((1u << (8 * St::S)) - 1u) << (8 * ((j * St::S) % 4)));
+        }
+        *(u32x4*)(lds + (size_t)u * 16) = v;
+      }
     }
   }
 };
 
 // online softmax update of one column tile (S^T already computed): rescales
-// acc when the running maximum moves and returns P as bf16 hi + lo operands
+// acc when the running maximum moves and returns P as bf16 hi + lo operands.
+// sl >= 0 (a negative scale is folded into the sign of q).  The causal mask
+// is applied only on chunks that reach past some column's position (diag,
+// wave-uniform, marked unlikely so that the compiler branches around it
+// rather than computing both forms): masked keys are left out of the maximum
+// and their P is selected to 0 after the exponential, which also holds for
+// sl = 0 and for whatever the pool holds past the sequence's end.
 template <int D>
 __device__ __forceinline__ void softmax_p(const f32x4 (&s)[2], f32x4 (&acc)[D / 16], float& m, float& l, int cs,
                                           int p_lane, bool diag, float sl, int lane, u32x4& ph, u32x4& pl) {
   const int kg = lane >> 4;
-  float x[8];
+  float cm = -INFINITY;
+  if (__builtin_expect(diag, 0)) {
 #pragma unroll
-  for (int a = 0; a < 2; ++a)
+    for (int a = 0; a < 2; ++a)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      float v = s[a][i] * sl;
-      if (diag) v = (cs + 16 * a + 4 * kg + i <= p_lane) ? v : -INFINITY;
-      x[4 * a + i] = v;
-    }
-  float cm = x[0];
+      for (int i = 0; i < 4; ++i) cm = fmaxf(cm, cs + 16 * a + 4 * kg + i <= p_lane ? s[a][i] : -INFINITY);
+  } else {
 #pragma unroll
-  for (int j = 1; j < 8; ++j) cm = fmaxf(cm, x[j]);
-  cm = fmaxf(cm, __shfl_xor(cm, 16, 64));
-  cm = fmaxf(cm, __shfl_xor(cm, 32, 64));
+    for (int a = 0; a < 2; ++a)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) cm = fmaxf(cm, s[a][i]);
+  }
+  cm = max_over_groups(cm) * sl;  // the chunk's scaled maximum of the column (log2 units)
   const bool need = cm > m + kRescaleLog2;
   if (__ballot(need)) {
     const float mu = need ? cm : m;
@@ -118,18 +140,26 @@ __device__ __forceinline__ void softmax_p(const f32x4 (&s)[2], f32x4 (&acc)[D / 
     }
     m = mu;
   }
+  float p[8];
+#pragma unroll
+  for (int a = 0; a < 2; ++a)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) p[4 * a + i] = exp2_fast(fmaf(s[a][i], sl, -m));  // key 0 is in every column's range: m is finite
+  if (__builtin_expect(diag, 0)) {
+#pragma unroll
+    for (int a = 0; a < 2; ++a)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) p[4 * a + i] = cs + 16 * a + 4 * kg + i <= p_lane ? p[4 * a + i] : 0.f;
+  }
+  l += ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
   uint32_t hb[8];
   float lo[8];
-  float psum = 0.f;
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
-    const float p = exp2_fast(x[j] - m);  // key 0 is in every column's range, so m is finite here
-    psum += p;
-    const uint32_t bits = __builtin_bit_cast(uint32_t, p);
+    const uint32_t bits = __builtin_bit_cast(uint32_t, p[j]);
     hb[j] = bits;
-    lo[j] = p - __builtin_bit_cast(float, bits & 0xFFFF0000u);
+    lo[j] = p[j] - __builtin_bit_cast(float, bits & 0xFFFF0000u);
   }
-  l += psum;
 #pragma unroll
   for (int w = 0; w < 4; ++w) {
     ph[w] = __builtin_amdgcn_perm(hb[2 * w + 1], hb[2 * w], 0x07060302u);
@@ -140,12 +170,36 @@ __device__ __forceinline__ void softmax_p(const f32x4 (&s)[2], f32x4 (&acc)[D / 
   pl = tokens_by_eight(pl);
 }
 
+// O += P V over one staged chunk for R tiles: each V operand (8 consecutive
+// tokens of one column per lane) is read once from LDS for all tiles.
+template <int D, int BS, int KVT, int R>
+__device__ __forceinline__ void pv_chunk(const char* vb, const u32x4 (&ph)[R], const u32x4 (&pl)[R],
+                                         f32x4 (&acc)[R][D / 16]) {
+  using St = Stage<D, BS, KVT>;
+  constexpr int S = St::S;
+#pragma unroll
+  for (int t = 0; t < D / 16; ++t) {
+    u32x4 vop;
+    if constexpr (KVT == PKV_BF16) {
+      vop = *(const u32x4*)(vb + (size_t)t * 16 * BS * S);
+    } else {
+      const u32x2 w = *(const u32x2*)(vb + (size_t)t * 16 * BS * S);
+      vop = e4m3x8_to_bf16x8(w.x, w.y);
+    }
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      acc[r][t] = mfma16x16x32(ph[r], vop, acc[r][t]);
+      acc[r][t] = mfma16x16x32(pl[r], vop, acc[r][t]);
+    }
+  }
+}
+
 // one wave's R column tiles over one staged chunk: every K and V operand read
 // from LDS serves all R tiles
 template <int D, int BS, int KVT, int R>
 __device__ __forceinline__ void prefill_chunk(const char* lds, const u32x4 (&qop)[R][D / 32],
                                               f32x4 (&acc)[R][D / 16], float (&m)[R], float (&l)[R], int chunk,
-                                              int n, const int (&p_lane)[R], int p_min, float sl, int lane) {
+                                              const int (&p_lane)[R], int p_min, float sl, int lane) {
   using St = Stage<D, BS, KVT>;
   constexpr int S = St::S;
   const int cs = chunk * 32;
@@ -183,37 +237,13 @@ __device__ __forceinline__ void prefill_chunk(const char* lds, const u32x4 (&qop
     }
   }
   // ---- P of every tile, then each V operand (8 consecutive tokens of one column per lane)
-  // read once from LDS for all tiles; V rows past n are zero-selected
+  // read once from LDS for all tiles (V rows past n were zeroed when the chunk was staged)
   u32x4 ph[R], pl[R];
 #pragma unroll
   for (int r = 0; r < R; ++r) softmax_p<D>(s[r], acc[r], m[r], l[r], cs, p_lane[r], diag, sl, lane, ph[r], pl[r]);
-  const bool tail = cs + 32 > n;
-  u32x4 vmask = u32x4{~0u, ~0u, ~0u, ~0u};
-  if (tail) {
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      const int t0 = cs + 8 * kg + 2 * w;
-      vmask[w] = (t0 < n ? 0x0000FFFFu : 0u) | (t0 + 1 < n ? 0xFFFF0000u : 0u);
-    }
-  }
   const int tv = 8 * kg;
   const char* vb = vl + (BS >= 32 ? 0 : (tv / BS) * St::kTile) + ((size_t)mrow * BS + tv % BS) * S;
-#pragma unroll
-  for (int t = 0; t < D / 16; ++t) {
-    u32x4 vop;
-    if constexpr (KVT == PKV_BF16) {
-      vop = *(const u32x4*)(vb + (size_t)t * 16 * BS * S);
-    } else {
-      const u32x2 w = *(const u32x2*)(vb + (size_t)t * 16 * BS * S);
-      vop = e4m3x8_to_bf16x8(w.x, w.y);
-    }
-    if (tail) vop &= vmask;
-#pragma unroll
-    for (int r = 0; r < R; ++r) {
-      acc[r][t] = mfma16x16x32(ph[r], vop, acc[r][t]);
-      acc[r][t] = mfma16x16x32(pl[r], vop, acc[r][t]);
-    }
-  }
+  pv_chunk<D, BS, KVT, R>(vb, ph, pl, acc);
 }
 
 template <int D, int BS, int KVT, int NW, int R>
@@ -257,6 +287,12 @@ __global__ __launch_bounds__(64 * NW, 2) void prefill_kernel(PrefillArgs a) {
   const int col = lane & 15, kgq = lane >> 4;
   const int wtok0 = tok0 + w * tok_per_wave;
   const int p_min = uniform(n - C + min(wtok0, C - 1));
+  // scores in log2 units: (q . k) * sl; a negative sl is taken as |sl| with q negated
+  // (a sign flip of each bf16, exact), so that the chunk maximum can be taken before scaling
+  float sl = a.scale_log2;
+  if constexpr (KVT == PKV_FP8_E4M3) sl *= a.k_scale[g];
+  const uint32_t qsign = sl < 0.f ? 0x80008000u : 0u;
+  sl = fabsf(sl);
   u32x4 qop[R][D / 32];
   int p_lane[R];
 #pragma unroll
@@ -270,11 +306,9 @@ __global__ __launch_bounds__(64 * NW, 2) void prefill_kernel(PrefillArgs a) {
     for (int c = 0; c < D / 32; ++c) {
       u32x4 v = u32x4{0u, 0u, 0u, 0u};
       if (qvalid) v = *(const u32x4*)(qrow + qk_dofs<KVT>(c, kgq));
-      qop[r][c] = v;
+      qop[r][c] = v ^ qsign;
     }
   }
-  float sl = a.scale_log2;
-  if constexpr (KVT == PKV_FP8_E4M3) sl *= a.k_scale[g];
   f32x4 acc[R][D / 16];
   float m[R], l[R];
 #pragma unroll
@@ -289,13 +323,13 @@ __global__ __launch_bounds__(64 * NW, 2) void prefill_kernel(PrefillArgs a) {
   const char* vpool = (const char*)a.v_pool;
   Stager<D, BS, KVT, NT> A, Bx;
   A.load(kpool, vpool, tab, 0, last_blk, a.NB, a.H_kv, g, tid);
-  A.store(sh_stage[0], tid);
+  A.store(sh_stage[0], tid, n);
   if (nch > 1) A.load(kpool, vpool, tab, 1, last_blk, a.NB, a.H_kv, g, tid);
   __syncthreads();
   for (int c = 0; c < nch; ++c) {
     if (c + 2 < nch) Bx.load(kpool, vpool, tab, c + 2, last_blk, a.NB, a.H_kv, g, tid);
-    prefill_chunk<D, BS, KVT, R>(sh_stage[c % kStages], qop, acc, m, l, c, n, p_lane, p_min, sl, lane);
-    if (c + 1 < nch) A.store(sh_stage[(c + 1) % kStages], tid);
+    prefill_chunk<D, BS, KVT, R>(sh_stage[c % kStages], qop, acc, m, l, c, p_lane, p_min, sl, lane);
+    if (c + 1 < nch) A.store(sh_stage[(c + 1) % kStages], tid, n - 32 * (c + 1));
     __syncthreads();
     A = Bx;
   }

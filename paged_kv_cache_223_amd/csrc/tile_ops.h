@@ -91,5 +91,23 @@ __device__ __forceinline__ u32x4 tokens_by_eight(u32x4 v) {
   return r;
 }
 
+// Maximum over the four lane groups, i.e. over lanes l, l ^ 16, l ^ 32 and
+// l ^ 48, without a round trip through LDS: swapping a register with itself
+// across halves (permlane32_swap) leaves each lane with its own value and
+// that of lane l ^ 32 in the two results, and across adjacent rows
+// (permlane16_swap) with that of lane l ^ 16.  The results are copied into
+// scalars before the bit casts: this compiler reads element 0 for a
+// __builtin_bit_cast of element 1 of the returned pair.
+__device__ __forceinline__ float max_over_groups(float x) {
+  const uint32_t u = __builtin_bit_cast(uint32_t, x);
+  const auto a = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  const uint32_t a0 = a[0], a1 = a[1];
+  const float y = fmaxf(__builtin_bit_cast(float, a0), __builtin_bit_cast(float, a1));
+  const uint32_t v = __builtin_bit_cast(uint32_t, y);
+  const auto b = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+  const uint32_t b0 = b[0], b1 = b[1];
+  return fmaxf(__builtin_bit_cast(float, b0), __builtin_bit_cast(float, b1));
+}
+
 }  // namespace
 }  // namespace pkv

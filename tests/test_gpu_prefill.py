@@ -108,6 +108,24 @@ def test_prefill_matches_oracle(name, kv_dtype):
     assert row_rel_err(got, ref) <= (2e-2 if kv_dtype == "e4m3" else 2e-3)
 
 
+@pytest.mark.parametrize("kv_dtype", ["bf16", "e4m3"])
+@pytest.mark.parametrize("scale", [-0.09, 0.0, 0.6, 8.0])
+def test_prefill_any_scale(scale, kv_dtype):
+    """A negative scale (the kernel takes |scale| with q negated), a zero scale (uniform weights
+    over each query's keys; masked keys must still weigh 0) and large ones (frequent rescales; at
+    8.0 the scores of one column spread over hundreds of log2 units, so a running maximum that is
+    not the column's true maximum overflows the exponential)."""
+    print(f"prefill scale {scale} {kv_dtype}", flush=True)
+    c = Case(priors=[0, 45], chunks=[40, 30], H_q=16, H_kv=2, d=64, bs=16, kv_dtype=kv_dtype, seed=21).device()
+    c.scale = float(np.float32(scale))
+    got = c.prefill()
+    kp, vp = c.oracle_pools()
+    ref = oracle.ref_prefill(c.q, "bf16", kp, vp, kv_dtype, c.tables, np.array(c.lens, np.int32), c.query_start,
+                             c.scale, c.bs, c.k_scale, c.v_scale)
+    assert np.isfinite(got).all()
+    assert row_rel_err(got, ref) <= (2e-2 if kv_dtype == "e4m3" else 2e-3)
+
+
 def test_prefill_70b_layer_shape_sampled_rows():
     """Two sequences of the 70B layer shape with 2048 earlier tokens and a 2048-token chunk each:
     every row the GPU computes is checked on a sample (first, last, tile edges, random)."""
