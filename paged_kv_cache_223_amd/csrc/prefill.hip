@@ -36,7 +36,7 @@
 namespace pkv {
 namespace {
 
-constexpr int kStages = 2;  // the chunk being computed and the one being filled
+constexpr int kStages = 2;  // the chunk being computed and the next one, written at the iteration's start
 
 template <int D, int BS, int KVT>
 struct Stage {
@@ -318,20 +318,23 @@ __global__ __launch_bounds__(64 * NW, 2) void prefill_kernel(PrefillArgs a) {
     m[r] = -INFINITY;
     l[r] = 0.f;
   }
-  // ---- pipeline: chunk c computed from LDS while chunks c+1 (registers) and c+2 (loads) are in flight
+  // ---- pipeline: iteration c first writes chunk c+1 (loaded into registers during
+  // iteration c-1) into the LDS buffer chunk c-1 used, then reuses those registers for the
+  // loads of chunk c+2, then computes chunk c; the barrier closes both buffers' hand-over
   const char* kpool = (const char*)a.k_pool;
   const char* vpool = (const char*)a.v_pool;
-  Stager<D, BS, KVT, NT> A, Bx;
+  Stager<D, BS, KVT, NT> A;
   A.load(kpool, vpool, tab, 0, last_blk, a.NB, a.H_kv, g, tid);
   A.store(sh_stage[0], tid, n);
   if (nch > 1) A.load(kpool, vpool, tab, 1, last_blk, a.NB, a.H_kv, g, tid);
   __syncthreads();
   for (int c = 0; c < nch; ++c) {
-    if (c + 2 < nch) Bx.load(kpool, vpool, tab, c + 2, last_blk, a.NB, a.H_kv, g, tid);
+    if (c + 1 < nch) {
+      A.store(sh_stage[(c + 1) % kStages], tid, n - 32 * (c + 1));
+      if (c + 2 < nch) A.load(kpool, vpool, tab, c + 2, last_blk, a.NB, a.H_kv, g, tid);
+    }
     prefill_chunk<D, BS, KVT, R>(sh_stage[c % kStages], qop, acc, m, l, c, p_lane, p_min, sl, lane);
-    if (c + 1 < nch) A.store(sh_stage[(c + 1) % kStages], tid, n - 32 * (c + 1));
     __syncthreads();
-    A = Bx;
   }
   // ---- normalise and write this wave's rows (row i of tile r = column i of that tile)
   const float vs = KVT == PKV_FP8_E4M3 ? a.v_scale[g] : 1.f;
