@@ -70,6 +70,8 @@ def parse():
     p.add_argument("--pairs", type=int, default=4096, help="block pairs per copy_blocks call (--op copy_blocks)")
     p.add_argument("--unfused", action="store_true",
                    help="issue the step as kv_append + decode instead of the fused pkv_decode_step")
+    p.add_argument("--no-length-hint", action="store_true",
+                   help="do not pass the batch's length sum to pkv_decode_step (the merge is then always launched)")
     p.add_argument("--sets", type=int, default=0,
                    help="independent copies of the inputs the steps rotate through (0 = enough for 1 GB of "
                         "KV, so the 256 MB last-level cache cannot hold the working set)")
@@ -213,6 +215,8 @@ def main():
     # one new token per sequence into bf16 pools: the step is one fused call (the append runs
     # inside the decode launch); E4M3 pools take kv_append + decode
     fused = not args.unfused and len(mat.step_slots) == B and case.spec.kv_dtype == "bf16"
+    # the host's own count of the batch's tokens: a split hint for the step call, no device sync
+    sum_lens = -1 if args.no_length_hint else int(mat.context_lens.astype(np.int64).sum())
 
     def step(i=0, e0=None, e1=None, e2=None):
         kp, vp, q_, tab, ln, sk, sv, ss = sets[i % n_sets]
@@ -224,7 +228,7 @@ def main():
             e1.record()
         if fused:
             pkv.decode_step(q_, sk, sv, ss, kp, vp, tab, ln, float(case.scale), mcl, k_scale, v_scale,
-                            out=out, workspace=ws)
+                            out=out, workspace=ws, sum_context_lens=sum_lens)
         else:
             pkv.paged_attn_decode(q_, kp, vp, tab, ln, float(case.scale), mcl, k_scale, v_scale,
                                   out=out, workspace=ws)
@@ -324,7 +328,8 @@ def main():
     traffic = measured_traffic(args.workload)
     res["roofline"] = {
         "bound": "hbm",
-        "kernel": ("decode step call (append fused) = decode_piece_kernel + piece_merge_kernel" if fused else
+        "kernel": ("decode step call (append fused) = decode_piece_kernel (+ piece_merge_kernel when a segment "
+                   "is cut into pieces)" if fused else
                    "paged_attn_decode call = decode_piece_kernel + piece_merge_kernel"),
         "achieved": round(dec_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
         "frac": round(dec_gbps / HBM_PEAK_GBPS, 4),

@@ -214,13 +214,19 @@ int pkv_paged_attn_decode(float* out, const void* q, int q_dtype, const void* k_
  * issue the two calls.  In the fused form, a new_slots[b] that is not the slot
  * of position n - 1 (or a sequence with n = 0) is a caller error: the token is
  * then stored (when its position's piece exists) but not attended.
+ *   sum_context_lens  host hint: the sum of context_lens[b] over the batch, as
+ *     the caller's allocator knows it, or -1 if unknown.  It only chooses the
+ *     work split: when it shows that the planned split would keep every
+ *     (sequence, KV head) segment whole, the call runs one piece per segment
+ *     and skips the merge launch.  A wrong value never changes the result;
+ *     an overestimate on a batch of very mixed lengths can unbalance the work.
  */
 int pkv_decode_step(float* out, const void* q, int q_dtype, const void* k_new, const void* v_new,
                     int src_dtype, const int64_t* new_slots, void* k_pool, void* v_pool, int kv_dtype,
                     const int32_t* block_tables, int32_t max_blocks_per_seq, const int32_t* context_lens,
-                    int32_t max_context_len, int32_t B, int32_t H_q, int32_t H_kv, int32_t D, int32_t NB,
-                    int32_t bs, float scale, const float* k_scale, const float* v_scale, void* workspace,
-                    size_t workspace_bytes, void* stream);
+                    int32_t max_context_len, int64_t sum_context_lens, int32_t B, int32_t H_q, int32_t H_kv,
+                    int32_t D, int32_t NB, int32_t bs, float scale, const float* k_scale, const float* v_scale,
+                    void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * pkv_paged_attn_decode_window — pkv_paged_attn_decode over part of each

@@ -57,8 +57,8 @@ SIGNATURES = {
                                                     _I32, _P, _P, _I32, _I32, _I32, _I32, _I32, _I32,
                                                     ctypes.c_float, _P, _P, _P, _SZ, _P]),
     "pkv_decode_step": (ctypes.c_int, [_P, _P, ctypes.c_int, _P, _P, ctypes.c_int, _P, _P, _P, ctypes.c_int, _P,
-                                       _I32, _P, _I32, _I32, _I32, _I32, _I32, _I32, _I32, ctypes.c_float, _P, _P,
-                                       _P, _SZ, _P]),
+                                       _I32, _P, _I32, ctypes.c_int64, _I32, _I32, _I32, _I32, _I32, _I32,
+                                       ctypes.c_float, _P, _P, _P, _SZ, _P]),
     "pkv_paged_prefill": (ctypes.c_int, [_P, _P, ctypes.c_int, _P, _P, ctypes.c_int, _P, _I32, _P, _P, _I32, _I32,
                                          _I32, _I32, _I32, _I32, _I32, _I32, ctypes.c_float, _P, _P, _P]),
     "pkv_alloc_create": (ctypes.c_int, [_I32, _I32, _P, ctypes.POINTER(_P)]),
@@ -318,9 +318,11 @@ def paged_attn_decode(q, k_pool, v_pool, block_tables, context_lens, scale: floa
 
 
 def decode_step(q, k_new, v_new, new_slots, k_pool, v_pool, block_tables, context_lens, scale: float,
-                max_context_len: int, k_scale=None, v_scale=None, out=None, workspace=None):
+                max_context_len: int, k_scale=None, v_scale=None, out=None, workspace=None,
+                sum_context_lens: int = -1):
     """kv_append(k_new, v_new, new_slots) then paged_attn_decode, fused into one launch where possible.
-    k_new, v_new: [B, H_kv, D] (sequence b's token at its last position); new_slots: int64 [B]."""
+    k_new, v_new: [B, H_kv, D] (sequence b's token at its last position); new_slots: int64 [B].
+    sum_context_lens: the host's sum of context_lens (-1 unknown); it only chooses the work split."""
     torch = _torch()
     _dev(q, k_new, v_new, new_slots, k_pool, v_pool, block_tables, context_lens, k_scale, v_scale, out, workspace)
     kv, NB, H_kv, D, bs = _pool_dims(k_pool, v_pool)
@@ -346,8 +348,9 @@ def decode_step(q, k_new, v_new, new_slots, k_pool, v_pool, block_tables, contex
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     _check(lib.pkv_decode_step(_ptr(out), _ptr(q), dtype_code(q), _ptr(k_new), _ptr(v_new), src, _ptr(new_slots),
                                _ptr(k_pool), _ptr(v_pool), kv, _ptr(block_tables), block_tables.shape[1],
-                               _ptr(context_lens), int(max_context_len), B, H_q, H_kv, D, NB, bs, float(scale),
-                               _ptr(k_scale), _ptr(v_scale), _ptr(workspace), ws_bytes, _stream()))
+                               _ptr(context_lens), int(max_context_len), int(sum_context_lens), B, H_q, H_kv, D,
+                               NB, bs, float(scale), _ptr(k_scale), _ptr(v_scale), _ptr(workspace), ws_bytes,
+                               _stream()))
     return out
 
 

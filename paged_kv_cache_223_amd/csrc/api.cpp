@@ -218,7 +218,7 @@ static int decode_impl(float* out, const void* q, int q_dtype, const void* k_poo
                        int32_t H_q, int32_t H_kv, int32_t D, int32_t NB, int32_t bs, float scale,
                        const float* k_scale, const float* v_scale, void* workspace, size_t workspace_bytes,
                        void* stream, const void* new_k = nullptr, const void* new_v = nullptr,
-                       const int64_t* new_slots = nullptr) {
+                       const int64_t* new_slots = nullptr, int64_t sum_len_hint = -1) {
   if (B < 0 || H_q <= 0 || H_kv <= 0 || NB <= 0 || max_blocks_per_seq <= 0 || max_context_len < 0) {
     set_error("decode: bad sizes B=%d H_q=%d H_kv=%d NB=%d max_blocks=%d max_context_len=%d", B, H_q, H_kv, NB,
               max_blocks_per_seq, max_context_len);
@@ -300,6 +300,7 @@ static int decode_impl(float* out, const void* q, int q_dtype, const void* k_poo
   a.q_dtype = q_dtype;
   a.kv_dtype = kv_dtype;
   a.num_cus = num_cus;
+  a.sum_len_hint = sum_len_hint;
   hipStream_t s = (hipStream_t)stream;
   if (fast) return hip_status(launch_decode_mfma(a, s), "decode launch");
   const int st = hip_status(launch_decode_vector(a, s), "decode launch");
@@ -402,9 +403,10 @@ int pkv_paged_prefill(float* out, const void* q, int q_dtype, const void* k_pool
 
 int pkv_decode_step(float* out, const void* q, int q_dtype, const void* k_new, const void* v_new, int src_dtype,
                     const int64_t* new_slots, void* k_pool, void* v_pool, int kv_dtype, const int32_t* block_tables,
-                    int32_t max_blocks_per_seq, const int32_t* context_lens, int32_t max_context_len, int32_t B,
-                    int32_t H_q, int32_t H_kv, int32_t D, int32_t NB, int32_t bs, float scale, const float* k_scale,
-                    const float* v_scale, void* workspace, size_t workspace_bytes, void* stream) {
+                    int32_t max_blocks_per_seq, const int32_t* context_lens, int32_t max_context_len,
+                    int64_t sum_context_lens, int32_t B, int32_t H_q, int32_t H_kv, int32_t D, int32_t NB,
+                    int32_t bs, float scale, const float* k_scale, const float* v_scale, void* workspace,
+                    size_t workspace_bytes, void* stream) {
   g_err[0] = 0;
   const bool fused = B > 0 && H_kv > 0 && H_q % H_kv == 0 && kv_dtype == PKV_BF16 && src_dtype == PKV_BF16 &&
                      decode_fast_path_supported(q_dtype, kv_dtype, H_q / H_kv, D, bs);
@@ -414,7 +416,7 @@ int pkv_decode_step(float* out, const void* q, int q_dtype, const void* k_new, c
     if (st != PKV_OK) return st;
     return decode_impl(out, q, q_dtype, k_pool, v_pool, kv_dtype, block_tables, max_blocks_per_seq, context_lens,
                        max_context_len, nullptr, nullptr, B, H_q, H_kv, D, NB, bs, scale, k_scale, v_scale,
-                       workspace, workspace_bytes, stream);
+                       workspace, workspace_bytes, stream, nullptr, nullptr, nullptr, sum_context_lens);
   }
   if (!k_new || !v_new || !new_slots) {
     set_error("decode_step: null new-token pointer");
@@ -426,7 +428,7 @@ int pkv_decode_step(float* out, const void* q, int q_dtype, const void* k_new, c
   }
   return decode_impl(out, q, q_dtype, k_pool, v_pool, kv_dtype, block_tables, max_blocks_per_seq, context_lens,
                      max_context_len, nullptr, nullptr, B, H_q, H_kv, D, NB, bs, scale, k_scale, v_scale, workspace,
-                     workspace_bytes, stream, k_new, v_new, new_slots);
+                     workspace_bytes, stream, k_new, v_new, new_slots, sum_context_lens);
 }
 
 size_t pkv_stream_read_sink_floats(size_t bytes) { return stream_read_blocks(bytes); }

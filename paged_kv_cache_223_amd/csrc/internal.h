@@ -95,6 +95,8 @@ struct DecodeArgs {
   float scale_log2;  // scale * log2(e)
   int q_dtype, kv_dtype;
   int num_cus;       // compute units of the device (sizes the matrix-core launch)
+  long long sum_len_hint;  // caller's sum of context_lens (< 0: unknown); picks single-piece mode
+  int single_piece;        // set by the launcher: one piece per segment, no merge launch
 };
 
 // Kernel launchers (paged_decode.hip).  Return hipError_t of the launch.

@@ -349,6 +349,12 @@ __device__ __forceinline__ int wave_sum(int x) {
   return x;
 }
 
+__device__ __forceinline__ int wave_max(int x) {
+#pragma unroll
+  for (int o = 32; o; o >>= 1) x = max(x, __shfl_xor(x, o, 64));
+  return x;
+}
+
 __device__ __forceinline__ int wave_incl_scan(int x, int lane) {
 #pragma unroll
   for (int o = 1; o < 64; o <<= 1) {
@@ -367,17 +373,26 @@ struct PiecePlan {
 __device__ int plan_piece(const DecodeArgs& a, int target, int item, int lane, PiecePlan& pp) {
   const int B = a.B, H_kv = a.H_kv, cap = a.len_cap;
   int c[kLensInRegs];
-  int part = 0;
+  int part = 0, cmax = 0;
 #pragma unroll
   for (int k = 0; k < kLensInRegs; ++k) {
     const int b0 = lane + 64 * k;
     c[k] = b0 < B ? chunks_of(a.context_lens[b0], cap) : 0;
     part += c[k];
+    cmax = max(cmax, c[k]);
   }
-  for (int b0 = lane + 64 * kLensInRegs; b0 < B; b0 += 64) part += chunks_of(a.context_lens[b0], cap);
+  for (int b0 = lane + 64 * kLensInRegs; b0 < B; b0 += 64) {
+    const int cb = chunks_of(a.context_lens[b0], cap);
+    part += cb;
+    cmax = max(cmax, cb);
+  }
   const int total = uniform(wave_sum(part)) * H_kv;
   int upw = (total + target - 1) / target;
   upw = upw < kMinUnits ? kMinUnits : upw;
+  if (a.single_piece) {  // every segment whole, whatever the host's estimate was
+    const int m = uniform(wave_max(cmax));
+    upw = upw < m ? m : upw;
+  }
   pp.b = -1;
   if (item < 0) return upw;
   // locate: prefix over sequences of H_kv * np_b pieces
@@ -830,13 +845,26 @@ hipError_t launch_mfma_a(const DecodeArgs& a, hipStream_t s) {
   const bool wide = segments <= target8;
   const int target = wide ? target8 : piece_groups_per_cu<D, BS, KVT, 4, APPEND>() * a.num_cus;
   const long long grid = (long long)target + segments;
+  // Single-piece mode when the caller's length sum shows that the plan would not cut any
+  // segment: ceil(sum / 32) is at most the sum of per-sequence chunk counts, so upw_lo is at
+  // most the plan's upw; if even upw_lo covers the longest segment the plan is one piece per
+  // segment and the merge launch can be skipped.  The kernel then raises upw to its own
+  // longest segment, so a wrong sum only changes the balance of the work, never the result.
+  DecodeArgs b = a;
+  b.single_piece = 0;
+  if (a.sum_len_hint >= 0) {
+    // cmax <= max(kMinUnits, ceil(csum * H_kv / target)), written without a product of csum
+    const long long cmax = ((long long)a.len_cap + 31) / 32;
+    const long long csum = (a.sum_len_hint + 31) / 32;
+    b.single_piece = cmax <= kMinUnits || csum > (cmax - 1) * target / a.H_kv;
+  }
   if (wide)
-    hipLaunchKernelGGL((decode_piece_kernel<D, BS, KVT, 8, APPEND>), dim3((unsigned)grid), dim3(512), 0, s, a, target);
+    hipLaunchKernelGGL((decode_piece_kernel<D, BS, KVT, 8, APPEND>), dim3((unsigned)grid), dim3(512), 0, s, b, target);
   else
-    hipLaunchKernelGGL((decode_piece_kernel<D, BS, KVT, 4, APPEND>), dim3((unsigned)grid), dim3(256), 0, s, a, target);
+    hipLaunchKernelGGL((decode_piece_kernel<D, BS, KVT, 4, APPEND>), dim3((unsigned)grid), dim3(256), 0, s, b, target);
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(piece_merge_kernel, dim3((unsigned)(a.B * a.H_kv)), dim3(256), 0, s, a, target);
+  if (e != hipSuccess || b.single_piece) return e;
+  hipLaunchKernelGGL(piece_merge_kernel, dim3((unsigned)(a.B * a.H_kv)), dim3(256), 0, s, b, target);
   return hipGetLastError();
 }
 

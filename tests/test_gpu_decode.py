@@ -258,3 +258,16 @@ def test_decode_many_segments_mixed_lengths(kv):
     case = workloads.custom(f"many_{kv}", 48, 32, 8, 128, 16, kv, "bf16", lens, seed=3100 + len(kv))
     got, _, _ = _parity(case)
     assert (got[40] == 0).all()
+
+
+@pytest.mark.parametrize("kv", ["bf16", "e4m3"])
+def test_decode_more_sequences_than_the_plan_keeps_in_registers(kv):
+    """1100 sequences: the plan keeps the lengths of the first 1024 in registers and reads the
+    rest from memory, in the piece kernel and in the merge; two long sequences are cut into
+    pieces among many short whole ones, and one is empty."""
+    rng = np.random.default_rng(41)
+    lens = rng.integers(1, 200, size=1100).tolist()
+    lens[7], lens[900], lens[501] = 3000, 2100, 0
+    case = workloads.custom(f"b1100_{kv}", 1100, 16, 2, 128, 16, kv, "bf16", lens, seed=4100 + len(kv))
+    got, _, _ = _parity(case)
+    assert (got[501] == 0).all()

@@ -132,3 +132,48 @@ def test_fused_full_70b_step_and_graph_replay():
         g.replay()
         torch.cuda.synchronize()
         assert np.array_equal(out.cpu().numpy().view(np.uint32), o1.view(np.uint32))
+    # with the batch's length sum the plan is the same one piece per segment and the merge
+    # launch is skipped: the result is the same, bit for bit, also from a captured graph
+    hint = int(mat.context_lens.astype(np.int64).sum())
+    kp, vp, _, _ = _pre_step_pools(case, mat)
+    pkv.decode_step(q, sk, sv, sl, kp, vp, tab, ln, float(case.scale), case.max_context_len, out=out, workspace=ws,
+                    sum_context_lens=hint)
+    torch.cuda.synchronize()
+    assert np.array_equal(out.cpu().numpy().view(np.uint32), o1.view(np.uint32))
+    assert np.array_equal(from_dev(kp), k1) and np.array_equal(from_dev(vp), v1)
+    g2 = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g2):
+        pkv.decode_step(q, sk, sv, sl, kp, vp, tab, ln, float(case.scale), case.max_context_len, out=out,
+                        workspace=ws, sum_context_lens=hint)
+    for _ in range(3):
+        out.zero_()
+        g2.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(out.cpu().numpy().view(np.uint32), o1.view(np.uint32))
+
+
+@pytest.mark.parametrize("kv", ["bf16", "e4m3"])
+def test_length_hint_only_chooses_the_split(kv):
+    """A batch of very mixed lengths: a hint far above the true sum forces one piece per segment
+    (unbalanced but still the oracle's result); a hint of 0 leaves the planned split unchanged."""
+    print(f"length hint {kv}", flush=True)
+    case = _with_step(workloads.custom(f"hint_{kv}", 6, 32, 8, 128, 16, kv, "bf16", [5000, 30, 1, 700, 2049, 64],
+                                       93 + len(kv)))
+    mat = materialize_with_model(case)
+    q = to_dev(case.q, "bf16")
+    sk = to_dev(mat.step_k.reshape(case.B, 8, 128), "bf16")
+    sv = to_dev(mat.step_v.reshape(case.B, 8, 128), "bf16")
+    tab, ln = torch.from_numpy(mat.block_tables).to(DEV), torch.from_numpy(mat.context_lens).to(DEV)
+    sl = torch.from_numpy(mat.step_slots).to(DEV)
+    outs = {}
+    for hint in (-1, 0, 10 ** 12):
+        kp, vp, k_s, v_s = _pre_step_pools(case, mat)
+        outs[hint] = pkv.decode_step(q, sk, sv, sl, kp, vp, tab, ln, float(case.scale), case.max_context_len, k_s,
+                                     v_s, sum_context_lens=hint).cpu().numpy()
+    assert np.array_equal(outs[-1].view(np.uint32), outs[0].view(np.uint32))
+    kp, vp = oracle_pools(case, mat)
+    ref = oracle_decode(case, mat, kp, vp)
+    tol = 2e-2 if kv == "e4m3" else 2e-3
+    for hint, o in outs.items():
+        assert np.isfinite(o).all()
+        assert row_rel_err(o.astype(np.float64), ref) <= tol, hint
