@@ -163,10 +163,16 @@ def _stream():
 
 
 def _dev(*ts):
+    """Every tensor on the current GPU (the calls launch on its current stream), contiguous."""
+    cur = None
     for t in ts:
         if t is not None:
             if not t.is_cuda:
                 raise ValueError("tensor is not on a GPU")
+            if cur is None:
+                cur = _torch().cuda.current_device()
+            if t.device.index != cur:
+                raise ValueError(f"tensor is on cuda:{t.device.index}, the current device is cuda:{cur}")
             if not t.is_contiguous():
                 raise ValueError("tensor is not contiguous")
 
@@ -270,8 +276,11 @@ _ws_cache = {}
 
 
 def _cached_workspace(device, need: int):
-    """Per-device workspace reused by calls that pass none (ordered on torch's current stream)."""
-    key = (device.type, device.index)
+    """Workspace reused by calls that pass none, one per (device, stream): calls on one stream run
+    in order, so they may share it; calls on different streams get their own.  It is allocated
+    while that stream is current, so torch's allocator orders its eventual reuse on that stream."""
+    torch = _torch()
+    key = (device.type, device.index, torch.cuda.current_stream(device).cuda_stream)
     ws = _ws_cache.get(key)
     if ws is None or ws.numel() < need:
         ws = torch.empty(max(need, 1 << 20), dtype=torch.uint8, device=device)

@@ -271,3 +271,31 @@ def test_decode_more_sequences_than_the_plan_keeps_in_registers(kv):
     case = workloads.custom(f"b1100_{kv}", 1100, 16, 2, 128, 16, kv, "bf16", lens, seed=4100 + len(kv))
     got, _, _ = _parity(case)
     assert (got[501] == 0).all()
+
+
+def test_cached_workspace_is_per_stream():
+    """Two streams decode different batches at once with the binding's own workspace (both cut
+    segments into pieces, so the partials live in it): each gets its own workspace and the
+    same bits as when run alone."""
+    import paged_kv_cache_223_amd as pkv
+    cases = [workloads.long128k_bf16(B=2, ctx=6000), workloads.long128k_bf16(B=3, ctx=4000)]
+    devs, alone = [], []
+    for c in cases:
+        mat = materialize_with_model(c)
+        kp, vp = oracle_pools(c, mat)
+        d = device_inputs(c, mat, kp, vp)
+        devs.append((c, d))
+        alone.append(decode(c, d))
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    torch.cuda.synchronize()
+    for _ in range(3):
+        outs = []
+        for (c, d), s in zip(devs, streams):
+            with torch.cuda.stream(s):
+                outs.append(pkv.paged_attn_decode(d["q"], d["k_pool"], d["v_pool"], d["block_tables"],
+                                                  d["context_lens"], float(c.scale), c.max_context_len))
+        torch.cuda.synchronize()
+        for o, a in zip(outs, alone):
+            assert np.array_equal(o.cpu().numpy().astype(np.float64), a)
+    keys = [k for k in pkv._ws_cache if k[2] in (streams[0].cuda_stream, streams[1].cuda_stream)]
+    assert len(keys) == 2
