@@ -218,7 +218,7 @@ static int decode_impl(float* out, const void* q, int q_dtype, const void* k_poo
                        int32_t H_q, int32_t H_kv, int32_t D, int32_t NB, int32_t bs, float scale,
                        const float* k_scale, const float* v_scale, void* workspace, size_t workspace_bytes,
                        void* stream, const void* new_k = nullptr, const void* new_v = nullptr,
-                       const int64_t* new_slots = nullptr, int64_t sum_len_hint = -1) {
+                       const int64_t* new_slots = nullptr, int64_t sum_len_hint = -1, bool check_only = false) {
   if (B < 0 || H_q <= 0 || H_kv <= 0 || NB <= 0 || max_blocks_per_seq <= 0 || max_context_len < 0) {
     set_error("decode: bad sizes B=%d H_q=%d H_kv=%d NB=%d max_blocks=%d max_context_len=%d", B, H_q, H_kv, NB,
               max_blocks_per_seq, max_context_len);
@@ -265,6 +265,7 @@ static int decode_impl(float* out, const void* q, int q_dtype, const void* k_poo
     set_error("decode: launch too large (%lld work items)", items);
     return PKV_ERR_INVALID_ARG;
   }
+  if (check_only) return PKV_OK;
   DecodeArgs a{};
   a.out = out;
   a.q = q;
@@ -410,9 +411,13 @@ int pkv_decode_step(float* out, const void* q, int q_dtype, const void* k_new, c
   g_err[0] = 0;
   const bool fused = B > 0 && H_kv > 0 && H_q % H_kv == 0 && kv_dtype == PKV_BF16 && src_dtype == PKV_BF16 &&
                      decode_fast_path_supported(q_dtype, kv_dtype, H_q / H_kv, D, bs);
-  if (!fused) {  // the two calls, in order, on the stream
-    const int st = pkv_kv_append(k_new, v_new, src_dtype, new_slots, B, k_pool, v_pool, kv_dtype, NB, bs, H_kv, D,
-                                 k_scale, v_scale, stream);
+  if (!fused) {  // the two calls, in order, on the stream; the decode's arguments are checked first
+    int st = decode_impl(out, q, q_dtype, k_pool, v_pool, kv_dtype, block_tables, max_blocks_per_seq, context_lens,
+                         max_context_len, nullptr, nullptr, B, H_q, H_kv, D, NB, bs, scale, k_scale, v_scale,
+                         workspace, workspace_bytes, stream, nullptr, nullptr, nullptr, sum_context_lens, true);
+    if (st != PKV_OK) return st;
+    st = pkv_kv_append(k_new, v_new, src_dtype, new_slots, B, k_pool, v_pool, kv_dtype, NB, bs, H_kv, D, k_scale,
+                       v_scale, stream);
     if (st != PKV_OK) return st;
     return decode_impl(out, q, q_dtype, k_pool, v_pool, kv_dtype, block_tables, max_blocks_per_seq, context_lens,
                        max_context_len, nullptr, nullptr, B, H_q, H_kv, D, NB, bs, scale, k_scale, v_scale,

@@ -82,6 +82,37 @@ def test_decode_empty_batch_is_a_no_op():
     assert _decode(B=0) == pkv.OK
 
 
+def _step(**kw):
+    a = dict(out=P, q=P, q_dtype=pkv.BF16, kn=P, vn=P, src=pkv.BF16, slots=P, k=P, v=P, kv=pkv.BF16, tab=P, mb=4,
+             lens=P, mcl=64, hint=-1, B=2, H_q=8, H_kv=2, D=128, NB=16, bs=16, scale=0.1, ks=None, vs=None, ws=None,
+             wsb=0, stream=None)
+    a.update(kw)
+    return pkv.lib.pkv_decode_step(a["out"], a["q"], a["q_dtype"], a["kn"], a["vn"], a["src"], a["slots"], a["k"],
+                                   a["v"], a["kv"], a["tab"], a["mb"], a["lens"], a["mcl"], a["hint"], a["B"],
+                                   a["H_q"], a["H_kv"], a["D"], a["NB"], a["bs"], a["scale"], a["ks"], a["vs"],
+                                   a["ws"], a["wsb"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(H_q=6, H_kv=4), pkv.ERR_INVALID_ARG),  # two-call route: refused before the append runs
+    (dict(D=96), pkv.ERR_UNSUPPORTED),
+    (dict(kv=pkv.FP8_E4M3), pkv.ERR_INVALID_ARG),  # two-call route, scales missing
+    (dict(kn=None), pkv.ERR_INVALID_ARG),  # fused route
+    (dict(out=None), pkv.ERR_INVALID_ARG),
+    (dict(), pkv.ERR_INVALID_ARG),  # needs a workspace, none given
+    (dict(hint=1 << 40), pkv.ERR_INVALID_ARG),  # the hint does not lift any check
+])
+def test_decode_step_rejects_bad_arguments_before_launch(kw, status):
+    # the dummy pointers would fail any launch (HIP error); the status shows nothing was launched
+    assert _step(**kw) == status
+    assert pkv.last_error()
+
+
+def test_decode_step_empty_batch_is_a_no_op():
+    assert _step(B=0) == pkv.OK
+    assert _step(B=0, kv=pkv.FP8_E4M3, ks=P, vs=P) == pkv.OK
+
+
 def _decode_window(**kw):
     a = dict(out=P, q=P, q_dtype=pkv.BF16, k=P, v=P, kv=pkv.BF16, tab=P, mb=4, lens=P, mcl=64, sinks=P, wins=P, B=2,
              H_q=8, H_kv=2, D=128, NB=16, bs=16, scale=0.1, ks=None, vs=None, ws=None, wsb=0, stream=None)
