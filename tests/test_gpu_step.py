@@ -107,6 +107,22 @@ def test_fused_step_block_sizes_and_a_sequence_without_a_token(bs):
     assert np.array_equal(o0.view(np.uint32), o1.view(np.uint32))
 
 
+@pytest.mark.parametrize("H_q,H_kv,D,bs", [(32, 2, 64, 8), (4, 4, 128, 32), (16, 8, 64, 16), (48, 3, 128, 16)])
+def test_fused_step_head_shapes(H_q, H_kv, D, bs):
+    """Head dims 64 and 128 with GQA groups of 16, 1, 2 and 16 (3 KV heads): the fused step's
+    operand injection and pool store follow each layout; the result equals append + decode and
+    the oracle's."""
+    print(f"fused step H_q={H_q} H_kv={H_kv} D={D} bs={bs}", flush=True)
+    case = _with_step(workloads.custom(f"step_{H_q}_{H_kv}_{D}_{bs}", 4, H_q, H_kv, D, bs, "bf16", "bf16",
+                                       [3, 70, 257, 1000], 94 + H_q + D))
+    mat = materialize_with_model(case)
+    (o0, k0, v0, o1, k1, v1), lens = _both_ways(case, mat)
+    assert np.array_equal(k0, k1) and np.array_equal(v0, v1)
+    assert np.array_equal(o0.view(np.uint32), o1.view(np.uint32))
+    kp, vp = oracle_pools(case, mat)
+    assert row_rel_err(o1.astype(np.float64), oracle_decode(case, mat, kp, vp)) <= 2e-3
+
+
 def test_fused_full_70b_step_and_graph_replay():
     case = workloads.llama70b_bf16()
     mat = materialize_with_model(case)
