@@ -93,11 +93,20 @@ struct Chunk {
   typename std::conditional<KVT == PKV_BF16, u32x4, u32x2>::type v[D / 16];
 };
 
+// ids[idx] for a per-lane idx over wave-uniform ids, as a select chain.  Each
+// id passes through an empty asm first: otherwise the optimizer turns the
+// selects of loads from the local array into one load at a selected index,
+// which puts the array in scratch memory (it did at 4 blocks per chunk).
 template <int NBCH>
 __device__ __forceinline__ int pick(const int (&ids)[NBCH], int idx) {
   int r = ids[0];
+  asm("" : "+s"(r));
 #pragma unroll
-  for (int i = 1; i < NBCH; ++i) r = idx == i ? ids[i] : r;
+  for (int i = 1; i < NBCH; ++i) {
+    int v = ids[i];
+    asm("" : "+s"(v));
+    r = idx == i ? v : r;
+  }
   return r;
 }
 
