@@ -313,6 +313,8 @@ def main():
         "seqs_per_s": round(B / (step_ms / 1e3), 1),
         "frac_of_hbm_peak": round(step_gbps / HBM_PEAK_GBPS, 4),
         "decode_us_p50": round(float(np.median(decode_ms)) * 1e3, 2),
+        "decode_us_p10_p90": [round(float(np.percentile(decode_ms, 10)) * 1e3, 2),
+                              round(float(np.percentile(decode_ms, 90)) * 1e3, 2)],
         "append_us_p50": None if fused else round(float(np.median(append_ms)) * 1e3, 2),
         "step_call": "pkv_decode_step (append fused into the decode launch)" if fused else
                      ("kv_append + paged_attn_decode" if len(mat.step_slots) else "paged_attn_decode"),
@@ -324,6 +326,7 @@ def main():
         "kv_bytes_logical": by["kv_logical"],
         "read_ceiling_GBps": round(ceiling, 1),
         "frac_of_read_ceiling": round(step_gbps / ceiling, 4),
+        "kv_waste": block_waste(mat.block_tables, mat.context_lens, case.bs),
     }
     traffic = measured_traffic(args.workload)
     res["roofline"] = {
@@ -340,6 +343,20 @@ def main():
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(case, mat, out, args.cpu_seconds, by, B)
     print(json.dumps(res), flush=True)
+
+
+def block_waste(tables, lens, bs):
+    """Internal waste of the allocator's blocks in use: each distinct block counts once (a shared
+    prefix block holds its tokens once), filled to the furthest token any of its holders uses."""
+    fill = {}
+    for row, n in zip(tables, lens):
+        for j in range(-(-int(n) // bs)):
+            b = int(row[j])
+            fill[b] = max(fill.get(b, 0), min(bs, int(n) - j * bs))
+    slots = len(fill) * bs
+    used = sum(fill.values())
+    return {"blocks_in_use": len(fill), "slots": slots, "tokens": used,
+            "internal_frac": round(1 - used / slots, 6) if slots else 0.0}
 
 
 def bench_copy_blocks(args, torch, pkv, dev):
