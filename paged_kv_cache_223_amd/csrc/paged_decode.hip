@@ -36,11 +36,12 @@
 //     chunk exceeds it by more than 2^8, so the rescale of the accumulators is
 //     rare; the sum stays per lane until the end.
 //   O[16 heads][D] += P[16 heads][32 tok] . V[32 tok][D] with P split into
-//     bf16 hi + lo parts (two MFMAs per tile) so P keeps ~16 bits: the
-//     accumulator layout of S^T is exactly the A-operand layout P needs.
+//     bf16 hi + lo parts (two MFMAs per tile) so P keeps ~16 bits; P is
+//     regrouped across lane groups (permlane32/16 swaps) so that lane group r
+//     holds tokens 8r .. 8r+7.
 // The pool layout makes every MFMA operand a 16- or 8-byte lane load: the K
 // tile is [D/X][bs][X] (16 tokens x 16 bytes contiguous per 16 lanes) and the
-// V tile is [D][bs] (4 consecutive tokens of one column per lane), so no LDS
+// V tile is [D][bs] (8 consecutive tokens of one column per lane), so no LDS
 // staging or transposition is needed on the hot loop.
 //
 // A piece that covers its whole segment writes the final rows; otherwise it
@@ -51,6 +52,13 @@
 // (Merging inside the piece kernel by the last-arriving workgroup needs a
 // device-scope release/acquire per workgroup; on gfx950 those are whole-L2
 // writeback/invalidate operations, which cost far more than the launch.)
+// When the caller's length sum shows that no segment would be cut, the launch
+// runs in single-piece mode (each workgroup raises upw to the longest segment
+// itself) and piece_merge is not launched.
+//
+// Fused step (bf16 pools): the step's new token of each sequence is put into
+// the loaded operands of the chunk holding position n - 1 and stored into the
+// pool after the chunk loop, which saves the append launch.
 //
 // Vector path: one wave per (sequence, context split, query head), fp32 VALU,
 // fixed-size splits and split_merge; used for fp32 q or KV, G > 16 or D = 256.

@@ -1,6 +1,7 @@
 // Matrix-core tile operations shared by the paged decode and prefill kernels
 // (gfx950): operand types, the bf16 MFMA, E4M3 -> bf16 conversion, the P
-// regroup across lane groups, and the clamped block-table lookup.
+// regroup across lane groups, the maximum over lane groups, and the clamped
+// block-table lookup.
 //
 // MFMA v_mfma_f32_16x16x32_bf16 lane layouts (checked on the device):
 //   A[16][32]: lane l holds A[l % 16][8 * (l / 16) + j], j = 0..7
