@@ -193,3 +193,54 @@ def test_length_hint_only_chooses_the_split(kv):
     for hint, o in outs.items():
         assert np.isfinite(o).all()
         assert row_rel_err(o.astype(np.float64), ref) <= tol, hint
+
+
+def test_blocks_past_4_gib_of_pool():
+    """The same step with its blocks moved near the top of pools larger than 4 GiB (byte offsets
+    past 2^32): the fused step's output and pool stores, copy_blocks and the swap gather give the
+    same bits as in the small pools."""
+    case = workloads.llama70b_bf16(B=3, ctx=900, prefix=256)
+    mat = materialize_with_model(case)
+    (o0, k0, v0, o1, k1, v1), lens = _both_ways(case, mat)
+    kp, vp, _, _ = _pre_step_pools(case, mat)
+    blk_bytes = kp[0].numel() * kp.element_size()
+    big_nb = (5 << 30) // blk_bytes + 64  # each pool just over 5 GiB
+    used = np.unique(mat.block_tables[mat.block_tables >= 0])
+    used = used[used < case.NB]
+    remap = np.full(case.NB, -1, np.int64)
+    remap[used] = big_nb - 1 - np.arange(len(used))  # the top blocks of the big pools, reversed
+    assert remap[used].min() * blk_bytes > (4 << 30)
+    print(f"big pools: {big_nb} blocks of {blk_bytes} B, blocks used from {int(remap[used].min())}", flush=True)
+    kb = torch.zeros((big_nb,) + tuple(kp.shape[1:]), dtype=kp.dtype, device=DEV)
+    vb = torch.zeros((big_nb,) + tuple(vp.shape[1:]), dtype=vp.dtype, device=DEV)
+    src = torch.from_numpy(used).to(DEV)
+    dst = torch.from_numpy(remap[used]).to(DEV)
+    kb.index_copy_(0, dst, kp.index_select(0, src))
+    vb.index_copy_(0, dst, vp.index_select(0, src))
+    tab = mat.block_tables.copy()
+    tab[tab >= 0] = remap[tab[tab >= 0]]
+    slots = mat.step_slots.copy()
+    slots = remap[slots // case.bs] * case.bs + slots % case.bs
+    q = to_dev(case.q, "bf16")
+    sk = to_dev(mat.step_k.reshape(case.B, 8, 128), "bf16")
+    sv = to_dev(mat.step_v.reshape(case.B, 8, 128), "bf16")
+    ln = torch.from_numpy(mat.context_lens).to(DEV)
+    out = pkv.decode_step(q, sk, sv, torch.from_numpy(slots).to(DEV), kb, vb, torch.from_numpy(tab).to(DEV), ln,
+                          float(case.scale), case.max_context_len)
+    torch.cuda.synchronize()
+    assert np.array_equal(out.cpu().numpy().view(np.uint32), o1.view(np.uint32))
+    assert np.array_equal(from_dev(kb.index_select(0, dst)), k1[used])
+    assert np.array_equal(from_dev(vb.index_select(0, dst)), v1[used])
+    # copy_blocks between two high blocks, then the gather of a few high blocks into staging
+    a, b = int(remap[used[0]]), int(big_nb - 1 - len(used) - 5)
+    pkv.copy_blocks(kb, vb, torch.tensor([a], dtype=torch.int32, device=DEV),
+                    torch.tensor([b], dtype=torch.int32, device=DEV))
+    st = pkv.gather_blocks(kb, vb, torch.tensor([b, a], dtype=torch.int32, device=DEV))
+    torch.cuda.synchronize()
+    rec = st.cpu().numpy().reshape(2, 2, -1)
+    kraw = from_dev(kb.index_select(0, torch.tensor([a], device=DEV))).reshape(1, -1).view(np.uint8)
+    vraw = from_dev(vb.index_select(0, torch.tensor([a], device=DEV))).reshape(1, -1).view(np.uint8)
+    assert np.array_equal(rec[0, 0], kraw[0]) and np.array_equal(rec[1, 0], kraw[0])
+    assert np.array_equal(rec[0, 1], vraw[0]) and np.array_equal(rec[1, 1], vraw[0])
+    del kb, vb
+    torch.cuda.empty_cache()
