@@ -197,8 +197,8 @@ def test_length_hint_only_chooses_the_split(kv):
 
 def test_blocks_past_4_gib_of_pool():
     """The same step with its blocks moved near the top of pools larger than 4 GiB (byte offsets
-    past 2^32): the fused step's output and pool stores, copy_blocks and the swap gather give the
-    same bits as in the small pools."""
+    past 2^32): the fused step's output and pool stores, copy_blocks, the swap gather and the
+    prefill give the same bits as in the small pools, and kv_append stores rows there exactly."""
     case = workloads.llama70b_bf16(B=3, ctx=900, prefix=256)
     mat = materialize_with_model(case)
     (o0, k0, v0, o1, k1, v1), lens = _both_ways(case, mat)
@@ -242,5 +242,25 @@ def test_blocks_past_4_gib_of_pool():
     vraw = from_dev(vb.index_select(0, torch.tensor([a], device=DEV))).reshape(1, -1).view(np.uint8)
     assert np.array_equal(rec[0, 0], kraw[0]) and np.array_equal(rec[1, 0], kraw[0])
     assert np.array_equal(rec[0, 1], vraw[0]) and np.array_equal(rec[1, 1], vraw[0])
+    # prefill of each sequence's last 5 tokens over the big pools equals that over the small ones
+    kp2, vp2, _, _ = _pre_step_pools(case, mat)
+    pkv.kv_append(sk, sv, torch.from_numpy(mat.step_slots).to(DEV), kp2, vp2)
+    qp = torch.randn((case.B * 5, 64, 128), device=DEV).to(torch.bfloat16)
+    qs = torch.arange(0, case.B * 5 + 1, 5, dtype=torch.int32, device=DEV)
+    small = pkv.paged_prefill(qp, kp2, vp2, torch.from_numpy(mat.block_tables).to(DEV), ln, qs, float(case.scale), 5)
+    big = pkv.paged_prefill(qp, kb, vb, torch.from_numpy(tab).to(DEV), ln, qs, float(case.scale), 5)
+    torch.cuda.synchronize()
+    assert torch.equal(small.view(torch.int32), big.view(torch.int32))
+    # kv_append of a block's worth of rows into a free block past 4 GiB
+    c = int(big_nb - 1 - len(used) - 9)
+    rows_k = torch.randn((case.bs, 8, 128), device=DEV).to(torch.bfloat16)
+    rows_v = torch.randn((case.bs, 8, 128), device=DEV).to(torch.bfloat16)
+    hs = torch.arange(c * case.bs, (c + 1) * case.bs, dtype=torch.int64, device=DEV)
+    pkv.kv_append(rows_k, rows_v, hs, kb, vb)
+    torch.cuda.synchronize()
+    vt = from_dev(vb[c])  # [H_kv][D][bs]
+    assert np.array_equal(vt.transpose(2, 0, 1), from_dev(rows_v))
+    kt = from_dev(kb[c])  # [H_kv][D/8][bs][8]
+    assert np.array_equal(kt.transpose(2, 0, 1, 3).reshape(case.bs, 8, 128), from_dev(rows_k))
     del kb, vb
     torch.cuda.empty_cache()
