@@ -17,11 +17,13 @@
 // reads the lengths and computes the same plan: upw = max(8, ceil(H_kv *
 // sum_b c_b / target)) chunks per piece, where target is one round of
 // resident workgroups (occupancy x CUs); segment (b, g) is cut into
-// np_b = ceil(c_b / upw) pieces of near-equal chunk counts, numbered
-// sequence-major.  Workgroup i takes piece i (a prefix scan over sequences
-// finds it); workgroups past the last piece exit.  So every resident
-// workgroup streams about the same number of bytes whatever the length mix,
-// and a batch whose segments all fit one round needs no partial results.
+// np_b = ceil(c_b / upw) pieces of near-equal chunk counts.  Workgroups take
+// the pieces largest first (size classes a factor sqrt(2) apart, then
+// sequence-major; prefix scans over the sequences find a workgroup's piece),
+// so the short pieces fill the slots that free up at the end; workgroups past
+// the last piece exit.  So no resident workgroup streams more than about
+// upw chunks whatever the length mix, and a batch whose segments all fit one
+// round needs no partial results.
 // Workgroups have 8 waves when every segment fits one round whole, else 4
 // (twice as many workgroups, so one workgroup's start and end overlap
 // another's streaming on the same CU).  Inside a piece the waves take chunks
@@ -71,6 +73,7 @@
 
 #include "internal.h"
 #include "tile_ops.h"
+#include "wave_scan.h"
 
 namespace pkv {
 namespace {
@@ -360,90 +363,139 @@ __device__ __forceinline__ int chunks_of(int n, int cap) {
   return (n + 31) / 32;
 }
 
-__device__ __forceinline__ int wave_sum(int x) {
-#pragma unroll
-  for (int o = 32; o; o >>= 1) x += __shfl_xor(x, o, 64);
-  return x;
-}
-
-__device__ __forceinline__ int wave_max(int x) {
-#pragma unroll
-  for (int o = 32; o; o >>= 1) x = max(x, __shfl_xor(x, o, 64));
-  return x;
-}
-
-__device__ __forceinline__ int wave_incl_scan(int x, int lane) {
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int y = __shfl_up(x, o, 64);
-    if (lane >= o) x += y;
-  }
-  return x;
-}
-
 struct PiecePlan {
-  int b, g, n, lo, hi, np;  // piece [lo, hi) of segment (b, g); np pieces in the segment
+  int b, g, n, lo, hi, np;  // piece [lo, hi) of segment (b, g); np pieces in the segment; n = its length
+  int id;                   // the piece's number in sequence-major order (its workspace row)
 };
 
-// Plan step shared by the decode and merge kernels (one wave computes it).
-// Returns upw and, for `item` >= 0, the piece it names (b = -1 if none).
-__device__ int plan_piece(const DecodeArgs& a, int target, int item, int lane, PiecePlan& pp) {
-  const int B = a.B, H_kv = a.H_kv, cap = a.len_cap;
-  int c[kLensInRegs];
+constexpr int kSizeClasses = 8;  // piece-size classes, a factor sqrt(2) apart
+
+// Size class of a segment cut into np pieces from c chunks: the largest k < kSizeClasses with
+// (c / np) * sqrt(2)^k <= upw, i.e. c^2 * 2^k <= (upw * np)^2.  Class 0 holds the largest pieces.
+// (c < 2^26 and upw * np < c + upw keep both sides inside 64 bits.)
+__device__ __forceinline__ int size_class(int c, int np, int upw) {
+  const long long lhs = (long long)c * c;
+  const long long un = (long long)upw * np;
+  const long long rhs = un * un;
+  int k = 0;
+  while (k < kSizeClasses - 1 && (lhs << (k + 1)) <= rhs) ++k;
+  return k;
+}
+
+// Chunks per piece (upw) of the plan, from the lengths; every wave that calls it gets the same
+// value.  nl receives the clamped lengths of sequences lane, lane + 64, ... (the first
+// kLensInRegs * 64 sequences; len_at reads the rest from memory again).
+__device__ int plan_upw(const DecodeArgs& a, int target, int lane, int (&nl)[kLensInRegs]) {
+  const int B = a.B, cap = a.len_cap;
   int part = 0, cmax = 0;
 #pragma unroll
   for (int k = 0; k < kLensInRegs; ++k) {
     const int b0 = lane + 64 * k;
-    c[k] = b0 < B ? chunks_of(a.context_lens[b0], cap) : 0;
-    part += c[k];
-    cmax = max(cmax, c[k]);
+    nl[k] = b0 < B ? seq_len(a.context_lens, b0, cap) : 0;
+    const int cb = (nl[k] + 31) / 32;
+    part += cb;
+    cmax = max(cmax, cb);
   }
   for (int b0 = lane + 64 * kLensInRegs; b0 < B; b0 += 64) {
     const int cb = chunks_of(a.context_lens[b0], cap);
     part += cb;
     cmax = max(cmax, cb);
   }
-  const int total = uniform(wave_sum(part)) * H_kv;
+  const int total = uniform(wave_sum(part)) * a.H_kv;
   int upw = (total + target - 1) / target;
   upw = upw < kMinUnits ? kMinUnits : upw;
   if (a.single_piece) {  // every segment whole, whatever the host's estimate was
     const int m = uniform(wave_max(cmax));
     upw = upw < m ? m : upw;
   }
-  pp.b = -1;
-  if (item < 0) return upw;
-  // locate: prefix over sequences of H_kv * np_b pieces
-  int base = 0;
-  for (int k = 0; k * 64 < B && pp.b < 0; ++k) {
-    const int b0 = lane + 64 * k;
-    int cb = 0;
-    if (k < kLensInRegs) {
+  return upw;
+}
+
+// clamped length of sequence lane + 64 k (0 past the batch)
+__device__ __forceinline__ int len_at(const DecodeArgs& a, const int (&nl)[kLensInRegs], int k, int lane) {
+  int n = 0;
+  if (k < kLensInRegs) {
 #pragma unroll
-      for (int kk = 0; kk < kLensInRegs; ++kk) cb = kk == k ? c[kk] : cb;
-    } else {
-      cb = b0 < B ? chunks_of(a.context_lens[b0], cap) : 0;
+    for (int kk = 0; kk < kLensInRegs; ++kk) n = kk == k ? nl[kk] : n;
+  } else {
+    const int b0 = lane + 64 * k;
+    n = b0 < a.B ? seq_len(a.context_lens, b0, a.len_cap) : 0;
+  }
+  return n;
+}
+
+// The piece that workgroup `item` runs (one wave computes it; pp.b = -1 if none).
+//
+// Pieces are numbered sequence-major (segment (b, g) owns np_b consecutive numbers) and that
+// number is the piece's workspace row, which the merge finds again from the lengths alone.  The
+// workgroups take them in another order: size class by size class, largest first, and
+// sequence-major inside a class.  The dispatcher starts workgroups in grid order, so long pieces
+// start in the first round and the short ones fill the slots that free up at the end (a
+// longest-first list schedule, to within a factor sqrt(2) of piece size).
+__device__ void plan_piece(const DecodeArgs& a, int target, int item, int lane, PiecePlan& pp) {
+  const int B = a.B, H_kv = a.H_kv;
+  int nl[kLensInRegs];
+  const int upw = plan_upw(a, target, lane, nl);
+  pp.b = -1;
+  // size class of every sequence's pieces; a batch in one class needs no class counts
+  int ccnt[kSizeClasses];
+#pragma unroll
+  for (int kk = 0; kk < kSizeClasses; ++kk) ccnt[kk] = 0;
+  int cls0 = -1;
+  bool mixed = false;
+  for (int k = 0; k * 64 < B; ++k) {
+    const int n = len_at(a, nl, k, lane);
+    const int cb = (n + 31) / 32, npb = (cb + upw - 1) / upw;
+    const int cls = npb > 0 ? size_class(cb, npb, upw) : -1;
+    if (k == 0) cls0 = uniform(cls);  // sequence 0's class (-1: empty)
+    mixed = mixed || (cls >= 0 && cls != cls0);
+#pragma unroll
+    for (int kk = 0; kk < kSizeClasses; ++kk) ccnt[kk] += kk == cls ? npb * H_kv : 0;
+  }
+  mixed = __ballot(mixed) != 0ull;
+  // the class holding `item`, and its rank r inside that class (-1: every class)
+  int cls_item = -1, r = item;
+  if (mixed) {
+#pragma unroll
+    for (int kk = 0; kk < kSizeClasses; ++kk) {
+      const int tot = uniform(wave_sum(ccnt[kk]));
+      if (cls_item < 0) {
+        if (r < tot)
+          cls_item = kk;
+        else
+          r -= tot;
+      }
     }
-    const int npb = (cb + upw - 1) / upw;
-    const int cnt = npb * H_kv;
-    const int incl = wave_incl_scan(cnt, lane);
-    const bool hit = cnt > 0 && base + incl - cnt <= item && item < base + incl;
+    if (cls_item < 0) return;  // past the last piece
+  }
+  // locate rank r among the class's pieces (sequence-major), with the sequence-major number
+  int base = 0, cbase = 0;
+  for (int k = 0; k * 64 < B && pp.b < 0; ++k) {
+    const int n = len_at(a, nl, k, lane);
+    const int cb = (n + 31) / 32, npb = (cb + upw - 1) / upw;
+    const int all = npb * H_kv;
+    const int cnt = cls_item < 0 || (npb > 0 && size_class(cb, npb, upw) == cls_item) ? all : 0;
+    const int incl = wave_incl_scan(cnt);
+    const int call = wave_incl_scan(all);
+    const bool hit = cnt > 0 && base + incl - cnt <= r && r < base + incl;
     const unsigned long long m = __ballot(hit);
     if (m) {
       const int src = __ffsll((long long)m) - 1;
-      const int b = 64 * k + src;
-      const int r = item - __shfl(base + incl - cnt, src, 64);
-      const int np = __shfl(npb, src, 64), cbb = __shfl(cb, src, 64);
-      const int j = r % np;
-      pp.b = b;
-      pp.g = r / np;
+      const int rr = r - lane_value(base + incl - cnt, src);  // = g * np + j inside the sequence
+      const int np = lane_value(npb, src), cbb = lane_value(cb, src);
+      const int j = rr % np;
+      pp.b = 64 * k + src;
+      pp.g = rr / np;
       pp.np = np;
+      pp.n = lane_value(n, src);
+      pp.id = lane_value(cbase + call - all, src) + rr;
       pp.lo = (int)((long long)j * cbb / np);
       pp.hi = (int)((long long)(j + 1) * cbb / np);
     }
-    base += __shfl(incl, 63, 64);
+    base += lane_value(incl, 63);
+    cbase += lane_value(call, 63);
   }
   pp.b = uniform(pp.b);
-  return upw;
 }
 
 // process one chunk; in the fused step the new token enters the operands of
@@ -527,10 +579,12 @@ __global__ __launch_bounds__(64 * NW, KVT == PKV_FP8_E4M3 ? 3 : 2) void decode_p
     for (int e = tid; e < a.H_q * D; e += NT) a.out[(size_t)item * a.H_q * D + e] = 0.f;
   PiecePlan pp;
   plan_piece(a, target, item, lane, pp);
-  if (pp.b < 0) return;
+  // no piece for this workgroup (a plan naming a segment outside the batch runs nothing either)
+  if (pp.b < 0 || pp.b >= a.B || (unsigned)uniform(pp.g) >= (unsigned)a.H_kv) return;
   const int b = pp.b, g = uniform(pp.g), np = uniform(pp.np);
   const int lo = uniform(pp.lo), hi = uniform(pp.hi);
-  const int n = uniform(seq_len(a.context_lens, b, cap));
+  const int n = uniform(pp.n);
+  const int pid = uniform(pp.id);
   int hlo, hhi;
   seq_hole(a, b, hlo, hhi);
   hlo = uniform(hlo);
@@ -570,7 +624,7 @@ __global__ __launch_bounds__(64 * NW, KVT == PKV_FP8_E4M3 ? 3 : 2) void decode_p
   __syncthreads();
   const float vs = KVT == PKV_FP8_E4M3 ? a.v_scale[g] : 1.f;
   const size_t orow = ((size_t)b * a.H_q + g * G) * D;
-  const size_t prow = (size_t)item * 16;
+  const size_t prow = (size_t)pid * 16;  // workspace row: the sequence-major piece number
   for (int e = tid; e < G * D; e += NT) {
     const int hh = e / D, col = e % D;
     float M = sh_m[0][hh];
@@ -598,83 +652,70 @@ __global__ __launch_bounds__(64 * NW, KVT == PKV_FP8_E4M3 ? 3 : 2) void decode_p
     if (writer && w == 0) write_new_token<D, BS>(a, b, g, new_slot, lane);
 }
 
-// Merge the pieces of every segment cut into several; one workgroup per
-// (sequence, KV head).  Wave 0 recomputes the plan; all piece loads are
-// independent of each other.
-__global__ __launch_bounds__(256) void piece_merge_kernel(DecodeArgs a, int target) {
-  __shared__ int sh_info[2];
-  __shared__ float sh_red[16][16][2];
-  __shared__ float sh_M[16], sh_iL[16];
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int b = blockIdx.x / a.H_kv, g = blockIdx.x % a.H_kv;
-  const int cap = a.len_cap, G = a.G, D = a.D, H_kv = a.H_kv;
-  const int cb = chunks_of(a.context_lens[b], cap);
-  if (cb == 0) return;
-  if (tid < 64) {
-    PiecePlan pp;
-    const int upw = plan_piece(a, target, -1, lane, pp);
-    const int np = (cb + upw - 1) / upw;
-    // first piece id of sequence b: sum over b' < b of H_kv * np_b'
-    int before = 0;
-    for (int b0 = lane; b0 < b; b0 += 64) before += H_kv * ((chunks_of(a.context_lens[b0], cap) + upw - 1) / upw);
-    before = wave_sum(before);
-    if (lane == 0) {
-      sh_info[0] = np;
-      sh_info[1] = before + g * np;
+// Merge the pieces of every segment cut into several.  Workgroup i takes the i-th such segment in
+// sequence-major order (fewer than `target` segments can be cut: each holds more than upw of the
+// at most upw * target chunks); one thread per output element of the segment's G heads.  Every
+// wave finds its segment from the lengths (the plan's upw, then prefix scans over sequences of
+// cut segments and of pieces), then takes the pieces eight at a time, every load of a batch in
+// flight at once, with an online rescale:
+//     o = sum_i 2^(m_i - M) o_i / sum_i 2^(m_i - M) l_i,  M = max_i m_i.
+// Two dependent memory round trips for up to eight pieces: the lengths, then the partials.
+constexpr int kMergeBatch = 8;
+
+__global__ __launch_bounds__(1024) void piece_merge_kernel(DecodeArgs a, int target) {
+  const int lane = threadIdx.x & 63;
+  const int B = a.B, G = a.G, D = a.D, H_kv = a.H_kv;
+  int nl[kLensInRegs];
+  const int upw = plan_upw(a, target, lane, nl);
+  const int item = blockIdx.x;
+  int base = 0, pbase = 0, sb = -1, sg = 0, snp = 0, sfirst = 0;
+  for (int k = 0; k * 64 < B && sb < 0; ++k) {
+    const int npb = ((len_at(a, nl, k, lane) + 31) / 32 + upw - 1) / upw;
+    const int all = npb * H_kv;         // pieces of the sequence
+    const int cnt = npb > 1 ? H_kv : 0;  // its segments that were cut
+    const int incl = wave_incl_scan(cnt);
+    const int pincl = wave_incl_scan(all);
+    const bool hit = cnt > 0 && base + incl - cnt <= item && item < base + incl;
+    const unsigned long long m = __ballot(hit);
+    if (m) {
+      const int src = __ffsll((long long)m) - 1;
+      sb = 64 * k + src;
+      sg = item - lane_value(base + incl - cnt, src);
+      snp = lane_value(npb, src);
+      sfirst = lane_value(pbase + pincl - all, src) + sg * snp;
     }
+    base += lane_value(incl, 63);
+    pbase += lane_value(pincl, 63);
   }
-  __syncthreads();
-  const int np = sh_info[0], first = sh_info[1];
-  if (np <= 1) return;  // the single piece wrote the final rows
-  // ---- per head h: M = max_p m_p, L = sum_p 2^(m_p - M) l_p.  Thread t takes head t % 16
-  // and pieces t / 16, t / 16 + 16, ...; the 16 partial results of a head meet in LDS.
-  {
-    const int h = tid & 15, p0 = tid >> 4;
-    float m = -INFINITY, l = 0.f;
-    if (h < G) {
-      for (int p = p0; p < np; p += 16) {
-        const size_t r = (size_t)(first + p) * 16 + h;
-        const float mp = a.ws_ml[2 * r], lp = a.ws_ml[2 * r + 1];
-        if (mp == -INFINITY) continue;  // a piece that attended nothing
-        const float mn = fmaxf(m, mp);
-        l = (m == -INFINITY ? 0.f : l * exp2_fast(m - mn)) + lp * exp2_fast(mp - mn);
-        m = mn;
+  sb = uniform(sb);
+  if (sb < 0 || sb >= B || (unsigned)uniform(sg) >= (unsigned)H_kv) return;  // fewer segments were cut
+                                                                               // than there are workgroups
+  const int np = uniform(snp), first = uniform(sfirst), g = uniform(sg);
+  const size_t orow = (size_t)sb * a.H_q + (size_t)g * G;
+  for (int e = threadIdx.x; e < G * D; e += blockDim.x) {
+    const int hl = e / D, col = e % D;
+    float M = -INFINITY, L = 0.f, O = 0.f;
+    for (int p = 0; p < np; p += kMergeBatch) {
+      float mp[kMergeBatch], lp[kMergeBatch], op[kMergeBatch];
+#pragma unroll
+      for (int i = 0; i < kMergeBatch; ++i) {  // past the last piece: reload the last, weigh it 0
+        const size_t r = (size_t)(first + min(p + i, np - 1)) * 16 + hl;
+        mp[i] = a.ws_ml[2 * r];
+        lp[i] = a.ws_ml[2 * r + 1];
+        op[i] = a.ws_o[r * D + col];
+      }
+#pragma unroll
+      for (int i = 0; i < kMergeBatch; ++i) {
+        if (p + i >= np || mp[i] == -INFINITY) continue;  // no piece, or one that attended nothing
+        const float mn = fmaxf(M, mp[i]);
+        const float so = M == -INFINITY ? 0.f : exp2_fast(M - mn);
+        const float sn = exp2_fast(mp[i] - mn);
+        L = L * so + lp[i] * sn;
+        O = O * so + op[i] * sn;
+        M = mn;
       }
     }
-    sh_red[p0][h][0] = m;
-    sh_red[p0][h][1] = l;
-  }
-  __syncthreads();
-  if (tid < G) {
-    float M = -INFINITY;
-    for (int i = 0; i < 16; ++i) M = fmaxf(M, sh_red[i][tid][0]);
-    float L = 0.f;
-    for (int i = 0; i < 16; ++i)
-      if (sh_red[i][tid][0] != -INFINITY) L += sh_red[i][tid][1] * exp2_fast(sh_red[i][tid][0] - M);
-    // nothing attended in any piece: zero row (every piece weight exp2(-inf - 0) is 0)
-    sh_M[tid] = M == -INFINITY ? 0.f : M;
-    sh_iL[tid] = L > 0.f ? 1.f / L : 0.f;
-  }
-  __syncthreads();
-  // ---- outputs: each thread owns (head, column) elements and sums their pieces
-  const size_t orow = (size_t)b * a.H_q + g * G;
-  for (int e = tid; e < G * D; e += 256) {
-    const int h = e / D, col = e % D;
-    const float M = sh_M[h];
-    float O = 0.f;
-    int p = 0;
-    for (; p + 4 <= np; p += 4) {  // four independent piece loads in flight
-      const size_t r0 = (size_t)(first + p) * 16 + h, r1 = r0 + 16, r2 = r0 + 32, r3 = r0 + 48;
-      const float o0 = a.ws_o[r0 * D + col], o1 = a.ws_o[r1 * D + col];
-      const float o2 = a.ws_o[r2 * D + col], o3 = a.ws_o[r3 * D + col];
-      O += exp2_fast(a.ws_ml[2 * r0] - M) * o0 + exp2_fast(a.ws_ml[2 * r1] - M) * o1 +
-           exp2_fast(a.ws_ml[2 * r2] - M) * o2 + exp2_fast(a.ws_ml[2 * r3] - M) * o3;
-    }
-    for (; p < np; ++p) {
-      const size_t r = (size_t)(first + p) * 16 + h;
-      O += exp2_fast(a.ws_ml[2 * r] - M) * a.ws_o[r * D + col];
-    }
-    a.out[(orow + h) * D + col] = O * sh_iL[h];
+    a.out[(orow + hl) * D + col] = L > 0.f ? O / L : 0.f;  // nothing attended: zero row
   }
 }
 
@@ -881,7 +922,8 @@ hipError_t launch_mfma_a(const DecodeArgs& a, hipStream_t s) {
     hipLaunchKernelGGL((decode_piece_kernel<D, BS, KVT, 4, APPEND>), dim3((unsigned)grid), dim3(256), 0, s, b, target);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || b.single_piece) return e;
-  hipLaunchKernelGGL(piece_merge_kernel, dim3((unsigned)(a.B * a.H_kv)), dim3(256), 0, s, b, target);
+  const int merge_threads = a.G * D < 1024 ? a.G * D : 1024;  // a multiple of 64
+  hipLaunchKernelGGL(piece_merge_kernel, dim3((unsigned)target), dim3(merge_threads), 0, s, b, target);
   return hipGetLastError();
 }
 
