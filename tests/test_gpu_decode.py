@@ -261,6 +261,18 @@ def test_decode_many_segments_mixed_lengths(kv):
 
 
 @pytest.mark.parametrize("kv", ["bf16", "e4m3"])
+def test_decode_pieces_in_every_size_class(kv):
+    """Lengths spread geometrically from 1 to 6000 tokens in a shuffled order: the plan's pieces
+    fall in every size class (workgroups take them largest class first), long segments are cut
+    and merged, and every piece lands in its own workspace row."""
+    rng = np.random.default_rng(51)
+    lens = np.unique(np.geomspace(1, 6000, 40).astype(int)).tolist()
+    lens = [int(n) for n in rng.permutation(lens)]
+    case = workloads.custom(f"classes_{kv}", len(lens), 32, 8, 128, 16, kv, "bf16", lens, seed=5100 + len(kv))
+    _parity(case)
+
+
+@pytest.mark.parametrize("kv", ["bf16", "e4m3"])
 def test_decode_more_sequences_than_the_plan_keeps_in_registers(kv):
     """1100 sequences: the plan keeps the lengths of the first 1024 in registers and reads the
     rest from memory, in the piece kernel and in the merge; two long sequences are cut into
