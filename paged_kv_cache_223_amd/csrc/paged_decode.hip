@@ -370,16 +370,32 @@ struct PiecePlan {
 
 constexpr int kSizeClasses = 8;  // piece-size classes, a factor sqrt(2) apart
 
-// Size class of a segment cut into np pieces from c chunks: the largest k < kSizeClasses with
-// (c / np) * sqrt(2)^k <= upw, i.e. c^2 * 2^k <= (upw * np)^2.  Class 0 holds the largest pieces.
-// (c < 2^26 and upw * np < c + upw keep both sides inside 64 bits.)
+// ceil(c / u) for c >= 0 and a divisor u >= kMinUnits that is the same in every lane: a float
+// estimate of the quotient, corrected once each way, which is exact while c < 2^24 (the estimate
+// is then within 0.4 of c / u); larger counts take the integer division.
+__device__ __forceinline__ int ceil_div_units(int c, int u) {
+  if (c >= (1 << 24)) return (c + u - 1) / u;
+  int q = (int)((float)c * __builtin_amdgcn_rcpf((float)u));
+  int r = c - q * u;
+  if (r < 0) {
+    q -= 1;
+    r += u;
+  }
+  if (r >= u) {
+    q += 1;
+    r -= u;
+  }
+  return q + (r > 0);
+}
+
+// Size class of a segment cut into np pieces from c chunks: floor(2 log2(upw * np / c)), clamped
+// to [0, kSizeClasses - 1], i.e. the pieces hold about upw / sqrt(2)^k chunks in class k; class 0
+// holds the largest.  v_log_f32 gives the same bits for the same inputs in every wave, so every
+// pass of every workgroup puts a segment in the same class.
 __device__ __forceinline__ int size_class(int c, int np, int upw) {
-  const long long lhs = (long long)c * c;
-  const long long un = (long long)upw * np;
-  const long long rhs = un * un;
-  int k = 0;
-  while (k < kSizeClasses - 1 && (lhs << (k + 1)) <= rhs) ++k;
-  return k;
+  const float k = 2.f * (__builtin_amdgcn_logf((float)upw * (float)np) - __builtin_amdgcn_logf((float)c));
+  const int ki = (int)k;
+  return ki < 0 ? 0 : (ki > kSizeClasses - 1 ? kSizeClasses - 1 : ki);
 }
 
 // Chunks per piece (upw) of the plan, from the lengths; every wave that calls it gets the same
@@ -445,7 +461,7 @@ __device__ void plan_piece(const DecodeArgs& a, int target, int item, int lane, 
   bool mixed = false;
   for (int k = 0; k * 64 < B; ++k) {
     const int n = len_at(a, nl, k, lane);
-    const int cb = (n + 31) / 32, npb = (cb + upw - 1) / upw;
+    const int cb = (n + 31) / 32, npb = ceil_div_units(cb, upw);
     const int cls = npb > 0 ? size_class(cb, npb, upw) : -1;
     if (k == 0) cls0 = uniform(cls);  // sequence 0's class (-1: empty)
     mixed = mixed || (cls >= 0 && cls != cls0);
@@ -472,7 +488,7 @@ __device__ void plan_piece(const DecodeArgs& a, int target, int item, int lane, 
   int base = 0, cbase = 0;
   for (int k = 0; k * 64 < B && pp.b < 0; ++k) {
     const int n = len_at(a, nl, k, lane);
-    const int cb = (n + 31) / 32, npb = (cb + upw - 1) / upw;
+    const int cb = (n + 31) / 32, npb = ceil_div_units(cb, upw);
     const int all = npb * H_kv;
     const int cnt = cls_item < 0 || (npb > 0 && size_class(cb, npb, upw) == cls_item) ? all : 0;
     const int incl = wave_incl_scan(cnt);
@@ -577,14 +593,27 @@ __global__ __launch_bounds__(64 * NW, KVT == PKV_FP8_E4M3 ? 3 : 2) void decode_p
   // wait for memory on every chunk.
   if (item < a.B && uniform(seq_len(a.context_lens, item, cap)) == 0)
     for (int e = tid; e < a.H_q * D; e += NT) a.out[(size_t)item * a.H_q * D + e] = 0.f;
-  PiecePlan pp;
-  plan_piece(a, target, item, lane, pp);
+  // wave 0 plans; the other waves wait at the barrier rather than repeat its scalar work
+  __shared__ int sh_plan[7];
+  if (w == 0) {
+    PiecePlan pp;
+    plan_piece(a, target, item, lane, pp);
+    if (lane == 0) {
+      sh_plan[0] = pp.b;
+      sh_plan[1] = pp.g;
+      sh_plan[2] = pp.np;
+      sh_plan[3] = pp.lo;
+      sh_plan[4] = pp.hi;
+      sh_plan[5] = pp.n;
+      sh_plan[6] = pp.id;
+    }
+  }
+  __syncthreads();
+  const int b = uniform(sh_plan[0]), g = uniform(sh_plan[1]);
   // no piece for this workgroup (a plan naming a segment outside the batch runs nothing either)
-  if (pp.b < 0 || pp.b >= a.B || (unsigned)uniform(pp.g) >= (unsigned)a.H_kv) return;
-  const int b = pp.b, g = uniform(pp.g), np = uniform(pp.np);
-  const int lo = uniform(pp.lo), hi = uniform(pp.hi);
-  const int n = uniform(pp.n);
-  const int pid = uniform(pp.id);
+  if (b < 0 || b >= a.B || (unsigned)g >= (unsigned)a.H_kv) return;
+  const int np = uniform(sh_plan[2]), lo = uniform(sh_plan[3]), hi = uniform(sh_plan[4]);
+  const int n = uniform(sh_plan[5]), pid = uniform(sh_plan[6]);
   int hlo, hhi;
   seq_hole(a, b, hlo, hhi);
   hlo = uniform(hlo);
@@ -655,9 +684,9 @@ __global__ __launch_bounds__(64 * NW, KVT == PKV_FP8_E4M3 ? 3 : 2) void decode_p
 // Merge the pieces of every segment cut into several.  Workgroup i takes the i-th such segment in
 // sequence-major order (fewer than `target` segments can be cut: each holds more than upw of the
 // at most upw * target chunks); one thread per output element of the segment's G heads.  Every
-// wave finds its segment from the lengths (the plan's upw, then prefix scans over sequences of
-// cut segments and of pieces), then takes the pieces eight at a time, every load of a batch in
-// flight at once, with an online rescale:
+// workgroup's first wave finds its segment from the lengths (the plan's upw, then prefix scans
+// over sequences of cut segments and of pieces); every thread then takes the pieces eight at a
+// time, every load of a batch in flight at once, with an online rescale:
 //     o = sum_i 2^(m_i - M) o_i / sum_i 2^(m_i - M) l_i,  M = max_i m_i.
 // Two dependent memory round trips for up to eight pieces: the lengths, then the partials.
 constexpr int kMergeBatch = 8;
@@ -665,32 +694,42 @@ constexpr int kMergeBatch = 8;
 __global__ __launch_bounds__(1024) void piece_merge_kernel(DecodeArgs a, int target) {
   const int lane = threadIdx.x & 63;
   const int B = a.B, G = a.G, D = a.D, H_kv = a.H_kv;
-  int nl[kLensInRegs];
-  const int upw = plan_upw(a, target, lane, nl);
-  const int item = blockIdx.x;
-  int base = 0, pbase = 0, sb = -1, sg = 0, snp = 0, sfirst = 0;
-  for (int k = 0; k * 64 < B && sb < 0; ++k) {
-    const int npb = ((len_at(a, nl, k, lane) + 31) / 32 + upw - 1) / upw;
-    const int all = npb * H_kv;         // pieces of the sequence
-    const int cnt = npb > 1 ? H_kv : 0;  // its segments that were cut
-    const int incl = wave_incl_scan(cnt);
-    const int pincl = wave_incl_scan(all);
-    const bool hit = cnt > 0 && base + incl - cnt <= item && item < base + incl;
-    const unsigned long long m = __ballot(hit);
-    if (m) {
-      const int src = __ffsll((long long)m) - 1;
-      sb = 64 * k + src;
-      sg = item - lane_value(base + incl - cnt, src);
-      snp = lane_value(npb, src);
-      sfirst = lane_value(pbase + pincl - all, src) + sg * snp;
+  __shared__ int sh_seg[4];
+  if (threadIdx.x < 64) {  // wave 0 finds the segment; the others wait at the barrier
+    int nl[kLensInRegs];
+    const int upw = plan_upw(a, target, lane, nl);
+    const int item = blockIdx.x;
+    int base = 0, pbase = 0, sb = -1, sg = 0, snp = 0, sfirst = 0;
+    for (int k = 0; k * 64 < B && sb < 0; ++k) {
+      const int npb = ceil_div_units((len_at(a, nl, k, lane) + 31) / 32, upw);
+      const int all = npb * H_kv;         // pieces of the sequence
+      const int cnt = npb > 1 ? H_kv : 0;  // its segments that were cut
+      const int incl = wave_incl_scan(cnt);
+      const int pincl = wave_incl_scan(all);
+      const bool hit = cnt > 0 && base + incl - cnt <= item && item < base + incl;
+      const unsigned long long m = __ballot(hit);
+      if (m) {
+        const int src = __ffsll((long long)m) - 1;
+        sb = 64 * k + src;
+        sg = item - lane_value(base + incl - cnt, src);
+        snp = lane_value(npb, src);
+        sfirst = lane_value(pbase + pincl - all, src) + sg * snp;
+      }
+      base += lane_value(incl, 63);
+      pbase += lane_value(pincl, 63);
     }
-    base += lane_value(incl, 63);
-    pbase += lane_value(pincl, 63);
+    if (lane == 0) {
+      sh_seg[0] = uniform(sb);
+      sh_seg[1] = sg;
+      sh_seg[2] = snp;
+      sh_seg[3] = sfirst;
+    }
   }
-  sb = uniform(sb);
-  if (sb < 0 || sb >= B || (unsigned)uniform(sg) >= (unsigned)H_kv) return;  // fewer segments were cut
-                                                                               // than there are workgroups
-  const int np = uniform(snp), first = uniform(sfirst), g = uniform(sg);
+  __syncthreads();
+  const int sb = uniform(sh_seg[0]), g = uniform(sh_seg[1]);
+  if (sb < 0 || sb >= B || (unsigned)g >= (unsigned)H_kv) return;  // fewer segments were cut than
+                                                                     // there are workgroups
+  const int np = uniform(sh_seg[2]), first = uniform(sh_seg[3]);
   const size_t orow = (size_t)sb * a.H_q + (size_t)g * G;
   for (int e = threadIdx.x; e < G * D; e += blockDim.x) {
     const int hl = e / D, col = e % D;
