@@ -97,6 +97,8 @@ struct DecodeArgs {
   int num_cus;       // compute units of the device (sizes the matrix-core launch)
   long long sum_len_hint;  // caller's sum of context_lens (< 0: unknown); picks single-piece mode
   int single_piece;        // set by the launcher: one piece per segment, no merge launch
+  int speculate;           // set by the launcher: the length sum says every length is len_cap, so a
+                           // workgroup may load its likely segment's first chunk before its plan
 };
 
 // Kernel launchers (paged_decode.hip).  Return hipError_t of the launch.

@@ -527,11 +527,27 @@ __device__ __forceinline__ void proc_chunk(Chunk<D, BS, KVT>& X, const DecodeArg
 
 // The wave's share of one piece: chunks first, first + NW, ... below c_end of
 // segment (b, g), with the next chunk's loads in flight while one is computed.
+// resident Q operand of KV head g of sequence b: lane holds head (lane & 15), 8 head-dim values
+// per MFMA (heads >= G zero)
+template <int D, int KVT>
+__device__ __forceinline__ void load_q(u32x4 (&qop)[D / 32], const DecodeArgs& a, int b, int g, int lane) {
+  const int h = lane & 15, kg = lane >> 4;
+  const uint16_t* qrow = (const uint16_t*)a.q + ((size_t)b * a.H_q + g * a.G + h) * D;
+#pragma unroll
+  for (int c = 0; c < D / 32; ++c) {
+    u32x4 v = u32x4{0u, 0u, 0u, 0u};
+    if (h < a.G) v = *(const u32x4*)(qrow + qk_dofs<KVT>(c, kg));
+    qop[c] = v;
+  }
+}
+
+// The wave's share of one piece: chunks first, first + NW, ... below c_end of segment (b, g),
+// with the next chunk's loads in flight while one is computed.  With `pre`, qop and A already hold
+// the Q operand and chunk `first` (loaded before the plan was known).
 template <int D, int BS, int KVT, int NW, bool APPEND>
 __device__ __forceinline__ void run_piece(const DecodeArgs& a, int b, int g, int n, int hlo, int hhi, int first,
                                           int c_end, int inject_chunk, f32x4 (&acc)[D / 16], WaveState& st,
-                                          int lane) {
-  const int G = a.G;
+                                          Chunk<D, BS, KVT>& A, u32x4 (&qop)[D / 32], bool pre, int lane) {
   const int last_blk = (n + BS - 1) / BS - 1;
   const int32_t* tab = a.block_tables + (size_t)b * a.max_blocks;
   const char* kpool = (const char*)a.k_pool;
@@ -541,23 +557,12 @@ __device__ __forceinline__ void run_piece(const DecodeArgs& a, int b, int g, int
   st = WaveState{-INFINITY, 0.f};
   const int cnt = first < c_end ? (c_end - first + NW - 1) / NW : 0;
   if (cnt == 0) return;
-  // resident Q operand: lane holds head (lane & 15), 8 head-dim values per MFMA
-  const int h = lane & 15, kg = lane >> 4;
-  u32x4 qop[D / 32];
-  {
-    const uint16_t* qrow = (const uint16_t*)a.q + ((size_t)b * a.H_q + g * G + h) * D;
-#pragma unroll
-    for (int c = 0; c < D / 32; ++c) {
-      u32x4 v = u32x4{0u, 0u, 0u, 0u};
-      if (h < G) v = *(const u32x4*)(qrow + qk_dofs<KVT>(c, kg));
-      qop[c] = v;
-    }
-  }
+  if (!pre) load_q<D, KVT>(qop, a, b, g, lane);
   float sl = a.scale_log2;
   if constexpr (KVT == PKV_FP8_E4M3) sl *= a.k_scale[g];
-  Chunk<D, BS, KVT> A, Bf;
+  Chunk<D, BS, KVT> Bf;
   int c = first;
-  load_chunk(A, kpool, vpool, tab, c, last_blk, a.NB, a.H_kv, g, lane);
+  if (!pre) load_chunk(A, kpool, vpool, tab, c, last_blk, a.NB, a.H_kv, g, lane);
   int k = 0;
   for (; k + 2 < cnt; k += 2) {
     load_chunk(Bf, kpool, vpool, tab, c + NW, last_blk, a.NB, a.H_kv, g, lane);
@@ -593,6 +598,21 @@ __global__ __launch_bounds__(64 * NW, KVT == PKV_FP8_E4M3 ? 3 : 2) void decode_p
   // wait for memory on every chunk.
   if (item < a.B && uniform(seq_len(a.context_lens, item, cap)) == 0)
     for (int e = tid; e < a.H_q * D; e += NT) a.out[(size_t)item * a.H_q * D + e] = 0.f;
+  // When the caller's length sum says every length equals len_cap (single-piece mode, one size
+  // class, no empty sequence), workgroup `item` runs segment (item / H_kv, item % H_kv) whole:
+  // every wave loads that guess's Q operand and its first chunk before the plan is known, so the
+  // loads overlap the plan's round trip; a plan that disagrees (a wrong sum) loads again.  The guess's block indices are clamped
+  // to the table row (the plan's clamp is the sequence's last block); the blocks the two clamps
+  // can differ on hold only positions past the sequence's end, which the chunk's masks drop.
+  Chunk<D, BS, KVT> A;
+  u32x4 qop[D / 32];
+  const int guess_b = item / a.H_kv, guess_g = item % a.H_kv;
+  const bool guess = a.speculate && guess_b < a.B;
+  if (guess) {
+    load_q<D, KVT>(qop, a, guess_b, guess_g, lane);
+    load_chunk(A, (const char*)a.k_pool, (const char*)a.v_pool, a.block_tables + (size_t)guess_b * a.max_blocks, w,
+               a.max_blocks - 1, a.NB, a.H_kv, guess_g, lane);
+  }
   // wave 0 plans; the other waves wait at the barrier rather than repeat its scalar work
   __shared__ int sh_plan[7];
   if (w == 0) {
@@ -636,7 +656,8 @@ __global__ __launch_bounds__(64 * NW, KVT == PKV_FP8_E4M3 ? 3 : 2) void decode_p
   }
   f32x4 acc[D / 16];
   WaveState st;
-  run_piece<D, BS, KVT, NW, APPEND>(a, b, g, n, hlo, hhi, lo + w, hi, inject_chunk, acc, st, lane);
+  const bool pre = guess && b == guess_b && g == guess_g && lo == 0;
+  run_piece<D, BS, KVT, NW, APPEND>(a, b, g, n, hlo, hhi, lo + w, hi, inject_chunk, acc, st, A, qop, pre, lane);
   // ---- merge the NW waves' shares through LDS
   const int kg = lane >> 4;
   float lt = st.l;
@@ -949,11 +970,15 @@ hipError_t launch_mfma_a(const DecodeArgs& a, hipStream_t s) {
   // longest segment, so a wrong sum only changes the balance of the work, never the result.
   DecodeArgs b = a;
   b.single_piece = 0;
+  b.speculate = 0;
   if (a.sum_len_hint >= 0) {
     // cmax <= max(kMinUnits, ceil(csum * H_kv / target)), written without a product of csum
     const long long cmax = ((long long)a.len_cap + 31) / 32;
     const long long csum = (a.sum_len_hint + 31) / 32;
     b.single_piece = cmax <= kMinUnits || csum > (cmax - 1) * target / a.H_kv;
+    // every length at len_cap: one size class and no empty sequence, so workgroup i's segment is
+    // (i / H_kv, i % H_kv), which the kernel checks against its plan before using the early loads
+    b.speculate = b.single_piece && a.len_cap > 0 && a.sum_len_hint == (long long)a.B * a.len_cap;
   }
   if (wide)
     hipLaunchKernelGGL((decode_piece_kernel<D, BS, KVT, 8, APPEND>), dim3((unsigned)grid), dim3(512), 0, s, b, target);

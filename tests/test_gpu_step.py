@@ -195,6 +195,52 @@ def test_length_hint_only_chooses_the_split(kv):
         assert row_rel_err(o.astype(np.float64), ref) <= tol, hint
 
 
+@pytest.mark.parametrize("name", ["uniform", "lying_mixed", "lying_empty"])
+def test_uniform_length_sum_loads_early(name):
+    """A length sum equal to B * max_context_len lets each workgroup load its likely segment's first
+    chunk before its plan (sequences of at most 8 chunks always run in single-piece mode).  With
+    every length at the maximum the output equals, bit for bit, the same single-piece step without
+    the early loads (sum + 1); a sum that lies about uneven lengths (or a sequence with no tokens,
+    which shifts every later segment) still gives the oracle's result and the same bits as without
+    the early loads."""
+    print(f"early loads {name}", flush=True)
+    if name == "uniform":
+        case = workloads.llama70b_bf16(B=6, ctx=200, prefix=64)
+    elif name == "lying_mixed":
+        case = _with_step(workloads.custom("early_mixed", 6, 64, 8, 128, 16, "bf16", "bf16",
+                                           [256, 30, 1, 200, 129, 64], 97))
+    else:
+        case = _with_step(workloads.custom("early_empty", 4, 64, 8, 128, 16, "bf16", "bf16", [200, 1, 200, 200], 98))
+    mat = materialize_with_model(case)
+    drop = (1,) if name == "lying_empty" else ()
+    slots, lens = mat.step_slots.copy(), mat.context_lens.copy()
+    for b in drop:  # sequence 1 appends nothing and holds no tokens
+        slots[b], lens[b] = -1, 0
+    q = to_dev(case.q, "bf16")
+    sk = to_dev(mat.step_k.reshape(case.B, 8, 128), "bf16")
+    sv = to_dev(mat.step_v.reshape(case.B, 8, 128), "bf16")
+    tab, ln = torch.from_numpy(mat.block_tables).to(DEV), torch.from_numpy(lens).to(DEV)
+    sl = torch.from_numpy(slots).to(DEV)
+    mcl = int(lens.max())
+    early = case.B * mcl  # claims every length is the maximum
+    outs = {}
+    for hint in (early, early + 1):
+        kp, vp, k_s, v_s = _pre_step_pools(case, mat)
+        outs[hint] = pkv.decode_step(q, sk, sv, sl, kp, vp, tab, ln, float(case.scale), mcl, k_s, v_s,
+                                     sum_context_lens=hint).cpu().numpy()
+    assert np.array_equal(outs[early].view(np.uint32), outs[early + 1].view(np.uint32))
+    if name == "uniform":
+        assert int(lens.sum()) == early
+    mat.context_lens = lens
+    kp, vp = oracle_pools(case, mat)
+    ref = oracle_decode(case, mat, kp, vp)
+    got = outs[early].astype(np.float64)
+    for b in drop:
+        assert (got[b] == 0).all()
+    keep = [b for b in range(case.B) if b not in drop]
+    assert row_rel_err(got[keep], ref[keep]) <= 2e-3
+
+
 def test_blocks_past_4_gib_of_pool():
     """The same step with its blocks moved near the top of pools larger than 4 GiB (byte offsets
     past 2^32): the fused step's output and pool stores, copy_blocks, the swap gather and the
