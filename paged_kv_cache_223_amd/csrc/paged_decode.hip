@@ -48,7 +48,7 @@
 //
 // A piece that covers its whole segment writes the final rows; otherwise it
 // writes its unnormalised output and (max, sum) per head to the workspace,
-// and piece_merge (a second, small launch, one workgroup per segment)
+// and piece_merge (a second, small launch, one workgroup per cut segment)
 // combines the pieces:
 //     o = sum_i 2^(m_i - M) o_i / sum_i 2^(m_i - M) l_i,  M = max_i m_i.
 // (Merging inside the piece kernel by the last-arriving workgroup needs a
@@ -345,11 +345,13 @@ __device__ __forceinline__ void write_new_token(const DecodeArgs& a, int b, int 
 // segment.  Every workgroup derives the same plan from the lengths: with
 // total = H_kv * sum_b c_b units and T target pieces (the workgroups the GPU
 // holds at once), upw = ceil(total / T), and each segment of sequence b is cut
-// into np_b = ceil(c_b / upw) balanced pieces.  Workgroup i takes piece i,
-// counting sequence-major, then KV head, then piece.  A uniform batch thus
-// runs as exactly one round of equal pieces (no second-round bubble); a batch
-// of mixed lengths gets many segment-aligned pieces, at most upw chunks each,
-// which the hardware dispatcher balances.  Each workgroup runs a single piece,
+// into np_b = ceil(c_b / upw) balanced pieces, numbered sequence-major, then
+// KV head, then piece (the workspace row of a piece's partials).  Workgroup i
+// takes the i-th piece in size-class order (largest class first, then that
+// numbering; see plan_piece).  A uniform batch thus runs as exactly one round
+// of equal pieces (no second-round bubble); a batch of mixed lengths gets many
+// segment-aligned pieces, at most upw chunks each, which the hardware
+// dispatcher balances.  Each workgroup runs a single piece,
 // which keeps register use (and so occupancy) at its single-piece minimum.
 // The workgroup's NW (4 or 8) waves take the piece's chunks round-robin and
 // merge through LDS; a piece that is a whole segment writes its final rows,
