@@ -957,12 +957,16 @@ hipError_t launch_mfma_a(const DecodeArgs& a, hipStream_t s) {
   // target pieces = one round of resident workgroups; the plan never makes more
   // than target + B * H_kv pieces, which sizes the grid (the rest exit at once).
   // 8-wave workgroups when every (sequence, KV head) segment fits one round
-  // whole: a uniform batch then needs no partials at all; otherwise 4-wave
+  // whole: a uniform batch then needs no partials at all.  With bf16 pools
+  // also up to two rounds of segments: measured on seeded batches of 48-64
+  // sequences with uniform lengths up to 4096 or 8192 tokens (384-512
+  // segments), 8 waves were 1-4 % faster in 7 of 8 batches; at 2048 segments
+  // (256 sequences of mixed lengths) they were 2-5 % slower.  Otherwise 4-wave
   // workgroups, twice as many, so that piece boundaries of one workgroup
-  // overlap another's streaming on the same CU.
+  // overlap another's streaming on the same CU (E4M3 keeps 3 of them per CU).
   const long long segments = (long long)a.B * a.H_kv;
   const int target8 = piece_groups_per_cu<D, BS, KVT, 8, APPEND>() * a.num_cus;
-  const bool wide = segments <= target8;
+  const bool wide = segments <= target8 || (KVT == PKV_BF16 && segments <= 2LL * target8);
   const int target = wide ? target8 : piece_groups_per_cu<D, BS, KVT, 4, APPEND>() * a.num_cus;
   const long long grid = (long long)target + segments;
   // Single-piece mode when the caller's length sum shows that the plan would not cut any
