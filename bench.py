@@ -72,7 +72,8 @@ def parse():
     p.add_argument("--unfused", action="store_true",
                    help="issue the step as kv_append + decode instead of the fused pkv_decode_step")
     p.add_argument("--no-length-hint", action="store_true",
-                   help="do not pass the batch's length sum to pkv_decode_step (the merge is then always launched)")
+                   help="do not pass the batch's length sum to the decode call (pkv_decode_step or "
+                        "pkv_paged_attn_decode_hinted); the merge is then always launched")
     p.add_argument("--sets", type=int, default=0,
                    help="independent copies of the inputs the steps rotate through (0 = enough for 1 GB of "
                         "KV, so the 256 MB last-level cache cannot hold the working set)")
@@ -216,7 +217,8 @@ def main():
     # one new token per sequence into bf16 pools: the step is one fused call (the append runs
     # inside the decode launch); E4M3 pools take kv_append + decode
     fused = not args.unfused and len(mat.step_slots) == B and case.spec.kv_dtype == "bf16"
-    # the host's own count of the batch's tokens: a split hint for the step call, no device sync
+    # the host's own count of the batch's tokens (its allocator holds the lengths): a split hint
+    # for the decode call, no device sync
     sum_lens = -1 if args.no_length_hint else int(mat.context_lens.astype(np.int64).sum())
 
     def step(i=0, e0=None, e1=None, e2=None):
@@ -232,7 +234,7 @@ def main():
                             out=out, workspace=ws, sum_context_lens=sum_lens)
         else:
             pkv.paged_attn_decode(q_, kp, vp, tab, ln, float(case.scale), mcl, k_scale, v_scale,
-                                  out=out, workspace=ws)
+                                  out=out, workspace=ws, sum_context_lens=sum_lens)
         if e2 is not None:
             e2.record()
 
@@ -318,7 +320,8 @@ def main():
                               round(float(np.percentile(decode_ms, 90)) * 1e3, 2)],
         "append_us_p50": None if fused else round(float(np.median(append_ms)) * 1e3, 2),
         "step_call": "pkv_decode_step (append fused into the decode launch)" if fused else
-                     ("kv_append + paged_attn_decode" if len(mat.step_slots) else "paged_attn_decode"),
+                     ("kv_append + paged_attn_decode" if len(mat.step_slots) else "paged_attn_decode") +
+                     ("" if sum_lens < 0 else " (with the host's length sum)"),
         "eager_ms_per_step": round(eager_step_ms, 5),
         "step_launch": "eager" if graphs is None else "hip_graph",
         "decode_GBps_unique": round(dec_gbps, 1),

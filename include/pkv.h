@@ -199,6 +199,26 @@ int pkv_paged_attn_decode(float* out, const void* q, int q_dtype, const void* k_
                           void* stream);
 
 /*
+ * pkv_paged_attn_decode_hinted — pkv_paged_attn_decode with the host's sum of
+ * the context lengths, for callers whose allocator holds the lengths (the sum
+ * is the same hint pkv_decode_step takes):
+ *   sum_context_lens  the sum of context_lens[b] over the batch, or -1 if
+ *     unknown (then the call is pkv_paged_attn_decode).  It only chooses the
+ *     work split: when it shows that the planned split keeps every (sequence,
+ *     KV head) segment whole, the call runs one piece per segment and skips
+ *     the merge launch.  A wrong value never changes the result; an
+ *     overestimate on a batch of very mixed lengths can unbalance the work.
+ *   other arguments, errors and ownership as pkv_paged_attn_decode.
+ */
+int pkv_paged_attn_decode_hinted(float* out, const void* q, int q_dtype, const void* k_pool,
+                                 const void* v_pool, int kv_dtype, const int32_t* block_tables,
+                                 int32_t max_blocks_per_seq, const int32_t* context_lens,
+                                 int32_t max_context_len, int64_t sum_context_lens, int32_t B,
+                                 int32_t H_q, int32_t H_kv, int32_t D, int32_t NB, int32_t bs,
+                                 float scale, const float* k_scale, const float* v_scale,
+                                 void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * pkv_decode_step — one decode step: the same result (output and pools) as
  *     pkv_kv_append(k_new, v_new, src_dtype, new_slots, T = B, ...);
  *     pkv_paged_attn_decode(...);

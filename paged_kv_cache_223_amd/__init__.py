@@ -53,6 +53,9 @@ SIGNATURES = {
     "pkv_paged_attn_decode": (ctypes.c_int, [_P, _P, ctypes.c_int, _P, _P, ctypes.c_int, _P, _I32, _P, _I32,
                                              _I32, _I32, _I32, _I32, _I32, _I32, ctypes.c_float, _P, _P, _P,
                                              _SZ, _P]),
+    "pkv_paged_attn_decode_hinted": (ctypes.c_int, [_P, _P, ctypes.c_int, _P, _P, ctypes.c_int, _P, _I32, _P, _I32,
+                                                    ctypes.c_int64, _I32, _I32, _I32, _I32, _I32, _I32,
+                                                    ctypes.c_float, _P, _P, _P, _SZ, _P]),
     "pkv_paged_attn_decode_window": (ctypes.c_int, [_P, _P, ctypes.c_int, _P, _P, ctypes.c_int, _P, _I32, _P,
                                                     _I32, _P, _P, _I32, _I32, _I32, _I32, _I32, _I32,
                                                     ctypes.c_float, _P, _P, _P, _SZ, _P]),
@@ -289,10 +292,12 @@ def _cached_workspace(device, need: int):
 
 
 def paged_attn_decode(q, k_pool, v_pool, block_tables, context_lens, scale: float, max_context_len: int,
-                      k_scale=None, v_scale=None, out=None, workspace=None, sink_lens=None, window_starts=None):
+                      k_scale=None, v_scale=None, out=None, workspace=None, sink_lens=None, window_starts=None,
+                      sum_context_lens: int = -1):
     """Decode attention of one query token per sequence over its paged KV; fp32 [B, H_q, D].
     With sink_lens and/or window_starts (int32 [B]) sequence b attends only t < sink_lens[b] or
-    t >= window_starts[b] (pkv_paged_attn_decode_window)."""
+    t >= window_starts[b] (pkv_paged_attn_decode_window).  sum_context_lens: the host's sum of
+    context_lens (-1 unknown); it only chooses the work split (pkv_paged_attn_decode_hinted)."""
     torch = _torch()
     _dev(q, k_pool, v_pool, block_tables, context_lens, k_scale, v_scale, out, workspace, sink_lens, window_starts)
     kv, NB, H_kv, D, bs = _pool_dims(k_pool, v_pool)
@@ -312,7 +317,12 @@ def paged_attn_decode(q, k_pool, v_pool, block_tables, context_lens, scale: floa
     if workspace is None and need:
         workspace = _cached_workspace(q.device, need)
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
-    if sink_lens is None and window_starts is None:
+    if sink_lens is None and window_starts is None and sum_context_lens >= 0:
+        _check(lib.pkv_paged_attn_decode_hinted(
+            _ptr(out), _ptr(q), dtype_code(q), _ptr(k_pool), _ptr(v_pool), kv, _ptr(block_tables),
+            block_tables.shape[1], _ptr(context_lens), int(max_context_len), int(sum_context_lens), B, H_q, H_kv,
+            D, NB, bs, float(scale), _ptr(k_scale), _ptr(v_scale), _ptr(workspace), ws_bytes, _stream()))
+    elif sink_lens is None and window_starts is None:
         _check(lib.pkv_paged_attn_decode(
             _ptr(out), _ptr(q), dtype_code(q), _ptr(k_pool), _ptr(v_pool), kv, _ptr(block_tables),
             block_tables.shape[1], _ptr(context_lens), int(max_context_len), B, H_q, H_kv, D, NB, bs,

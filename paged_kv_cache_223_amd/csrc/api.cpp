@@ -320,6 +320,18 @@ int pkv_paged_attn_decode(float* out, const void* q, int q_dtype, const void* k_
                      workspace_bytes, stream);
 }
 
+int pkv_paged_attn_decode_hinted(float* out, const void* q, int q_dtype, const void* k_pool, const void* v_pool,
+                                 int kv_dtype, const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                 const int32_t* context_lens, int32_t max_context_len, int64_t sum_context_lens,
+                                 int32_t B, int32_t H_q, int32_t H_kv, int32_t D, int32_t NB, int32_t bs, float scale,
+                                 const float* k_scale, const float* v_scale, void* workspace, size_t workspace_bytes,
+                                 void* stream) {
+  g_err[0] = 0;
+  return decode_impl(out, q, q_dtype, k_pool, v_pool, kv_dtype, block_tables, max_blocks_per_seq, context_lens,
+                     max_context_len, nullptr, nullptr, B, H_q, H_kv, D, NB, bs, scale, k_scale, v_scale, workspace,
+                     workspace_bytes, stream, nullptr, nullptr, nullptr, sum_context_lens);
+}
+
 int pkv_paged_attn_decode_window(float* out, const void* q, int q_dtype, const void* k_pool, const void* v_pool,
                                  int kv_dtype, const int32_t* block_tables, int32_t max_blocks_per_seq,
                                  const int32_t* context_lens, int32_t max_context_len, const int32_t* sink_lens,

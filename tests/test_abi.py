@@ -47,10 +47,15 @@ def test_status_and_dtype_codes_match_header():
 P = ctypes.c_void_p(0x1000)
 
 
-def _decode(**kw):
+def _decode(hinted=None, **kw):
     a = dict(out=P, q=P, q_dtype=pkv.BF16, k=P, v=P, kv=pkv.BF16, tab=P, mb=4, lens=P, mcl=64, B=2, H_q=8, H_kv=2,
              D=128, NB=16, bs=16, scale=0.1, ks=None, vs=None, ws=None, wsb=0, stream=None)
     a.update(kw)
+    if hinted is not None:  # the same call with a length-sum hint
+        return pkv.lib.pkv_paged_attn_decode_hinted(a["out"], a["q"], a["q_dtype"], a["k"], a["v"], a["kv"], a["tab"],
+                                                    a["mb"], a["lens"], a["mcl"], hinted, a["B"], a["H_q"],
+                                                    a["H_kv"], a["D"], a["NB"], a["bs"], a["scale"], a["ks"], a["vs"],
+                                                    a["ws"], a["wsb"], a["stream"])
     return pkv.lib.pkv_paged_attn_decode(a["out"], a["q"], a["q_dtype"], a["k"], a["v"], a["kv"], a["tab"], a["mb"],
                                          a["lens"], a["mcl"], a["B"], a["H_q"], a["H_kv"], a["D"], a["NB"], a["bs"],
                                          a["scale"], a["ks"], a["vs"], a["ws"], a["wsb"], a["stream"])
@@ -76,10 +81,14 @@ def _decode(**kw):
 def test_decode_rejects_bad_arguments_before_launch(kw, status):
     assert _decode(**kw) == status
     assert pkv.last_error()
+    for hint in (-1, 0, 128):  # the hinted entry checks the same arguments
+        assert _decode(hinted=hint, **kw) == status
+        assert pkv.last_error()
 
 
 def test_decode_empty_batch_is_a_no_op():
     assert _decode(B=0) == pkv.OK
+    assert _decode(hinted=0, B=0) == pkv.OK
 
 
 def _step(**kw):
