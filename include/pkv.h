@@ -16,6 +16,8 @@
  *   pkv_gather_blocks / pkv_scatter_blocks  pack blocks into / unpack from a
  *                          contiguous staging buffer (swap-out / swap-in)
  *   pkv_paged_attn_decode  one query token per sequence attends over its paged KV
+ *   pkv_paged_attn_decode_hinted  the same, given the host's sum of the context
+ *                          lengths (skips the merge launch when nothing is cut)
  *   pkv_paged_attn_decode_window  the same, attending only sink tokens and a
  *                          recent window (StreamingLLM; with pkv_seq_streaming_evict)
  *   pkv_paged_prefill      causal attention of a chunk of new tokens per sequence
