@@ -197,7 +197,7 @@ def main():
     B, H_q, H_kv, D = case.B, spec.H_q, spec.H_kv, spec.d
     mcl = case.max_context_len
     out = torch.empty((B, H_q, D), dtype=torch.float32, device=dev)
-    ws = pkv.decode_workspace(B, H_q, H_kv, D, mcl, case.bs, device=dev)
+    ws = pkv.decode_workspace(B, H_q, D, mcl, case.bs, H_kv=H_kv, device=dev)
 
     s_kv = {"bf16": 2, "e4m3": 1, "f32": 4}[spec.kv_dtype]
     s_q = 4 if spec.q_dtype == "f32" else 2
@@ -230,10 +230,10 @@ def main():
         if e1 is not None:
             e1.record()
         if fused:
-            pkv.decode_step(q_, sk, sv, ss, kp, vp, tab, ln, float(case.scale), mcl, k_scale, v_scale,
+            pkv.decode_step(q_, sk, sv, ss, kp, vp, tab, ln, float(case.scale), k_scale, v_scale, max_context_len=mcl,
                             out=out, workspace=ws, sum_context_lens=sum_lens)
         else:
-            pkv.paged_attn_decode(q_, kp, vp, tab, ln, float(case.scale), mcl, k_scale, v_scale,
+            pkv.paged_attn_decode(q_, kp, vp, tab, ln, float(case.scale), k_scale, v_scale, max_context_len=mcl,
                                   out=out, workspace=ws, sum_context_lens=sum_lens)
         if e2 is not None:
             e2.record()

@@ -80,10 +80,13 @@ enum pkv_status {
 
 enum pkv_dtype { PKV_F32 = 0, PKV_BF16 = 1, PKV_FP8_E4M3 = 2 };
 
-/* Thread-local text of the last error set by a call on this thread ("" if none). */
+/*
+ * Design (not on the pages): error text and versioning of this library.
+ * pkv_last_error: thread-local text of the last error set by a call on this
+ * thread ("" if none).  pkv_abi_version: bumped on incompatible changes (2:
+ * pkv_decode_workspace_bytes takes no H_kv).
+ */
 const char* pkv_last_error(void);
-
-/* ABI version (bumped on incompatible changes). */
 int pkv_abi_version(void);
 
 /*
@@ -154,23 +157,39 @@ int pkv_scatter_blocks(void* k_pool, void* v_pool, int pool_dtype, int32_t NB, i
                        int32_t D, const int32_t* blocks, int32_t n, const void* staging, void* stream);
 
 /*
- * pkv_decode_workspace_bytes — size of the scratch buffer pkv_paged_attn_decode
- * needs for these sizes (0 is possible).  The same arguments must be passed to
- * the decode call.  Returns 0 and sets the last error for invalid sizes.
+ * Design (not on the pages): the decode's scratch.  A sequence whose context
+ * is cut into several pieces keeps per-piece partial results (the unnormalised
+ * output and the running max and sum of every query head) until a second small
+ * launch merges them; the caller owns that memory.
+ *
+ * pkv_decode_workspace_bytes — bytes of scratch pkv_paged_attn_decode (and the
+ * hinted, window and step variants) needs for a batch of B sequences with H_q
+ * query heads of dimension D, contexts of at most max_context_len tokens and
+ * block size bs, whatever the KV head count H_kv (a divisor of H_q).  0 is
+ * possible.  pkv_decode_workspace_bytes_gqa gives the exact, smaller figure for
+ * one H_kv.  Both return 0 and set the last error for invalid sizes; the decode
+ * call must receive at least the figure for its own arguments.
  */
-size_t pkv_decode_workspace_bytes(int32_t B, int32_t H_q, int32_t H_kv, int32_t D,
-                                  int32_t max_context_len, int32_t bs);
+size_t pkv_decode_workspace_bytes(int32_t B, int32_t H_q, int32_t D, int32_t max_context_len, int32_t bs);
+size_t pkv_decode_workspace_bytes_gqa(int32_t B, int32_t H_q, int32_t H_kv, int32_t D,
+                                      int32_t max_context_len, int32_t bs);
 
 /*
  * pkv_paged_attn_decode — one query token per sequence attends over its paged KV.
  * For sequence b with n = context_lens[b] and query head h (KV head g):
  *     out[b][h] = sum_{t<n} softmax_t(scale * <q[b][h], K_b[g][t]>) V_b[g][t]
  * where K_b, V_b are the sequence's tokens in logical order reached through
- * block_tables[b].  Each (context split, sequence, KV head) work item runs
- * an online softmax over its tokens without writing scores to memory; when
- * a sequence has several splits a second small launch merges their partial
- * results.  n = 0 gives a zero row.  context_lens counts the token appended
- * this step.
+ * block_tables[b].  ("KV Cache Fragmentation" field guide, section
+ * "Definition": the cache is cut into fixed-size pages and the attention
+ * kernel follows the per-request table from logical to physical pages;
+ * "Paged Attention and KV Cache Fragmentation", sections "How PagedAttention
+ * maps an OS concept onto GPU memory" and "The non-contiguous memory layout
+ * PagedAttention introduces and its overhead": every attention step goes
+ * through the block table, and paging moves where the bytes live, not what
+ * attention computes.)  Each (sequence, KV head) segment runs an online
+ * softmax over its tokens without writing scores to memory; when a segment is
+ * cut into several pieces a second small launch merges their partial results.
+ * n = 0 gives a zero row.  context_lens counts the token appended this step.
  *
  *   out            device fp32 [B][H_q][D]
  *   q              device [B][H_q][D], q_dtype F32 or BF16
@@ -189,8 +208,9 @@ size_t pkv_decode_workspace_bytes(int32_t B, int32_t H_q, int32_t H_kv, int32_t 
  *                  or synchronised); concurrent calls on one workspace race.
  *   Requires H_q % H_kv == 0, D in {64, 128, 256}, bs in {8, 16, 32}.
  *   bf16 q with bf16/E4M3 KV, H_q/H_kv <= 16 and D in {64, 128} take the
- *   matrix-core path; other supported combinations take a vector path.
- *   All accumulation is fp32.
+ *   matrix-core path; other supported combinations (fp32 q or KV, larger
+ *   groups, and D = 256, a head size beyond the layers the pages discuss)
+ *   take a vector path.  All accumulation is fp32.
  */
 int pkv_paged_attn_decode(float* out, const void* q, int q_dtype, const void* k_pool,
                           const void* v_pool, int kv_dtype, const int32_t* block_tables,
@@ -208,8 +228,14 @@ int pkv_paged_attn_decode(float* out, const void* q, int q_dtype, const void* k_
  *     unknown (then the call is pkv_paged_attn_decode).  It only chooses the
  *     work split: when it shows that the planned split keeps every (sequence,
  *     KV head) segment whole, the call runs one piece per segment and skips
- *     the merge launch.  A wrong value never changes the result; an
- *     overestimate on a batch of very mixed lengths can unbalance the work.
+ *     the merge launch.  A value above B * min(max_context_len,
+ *     max_blocks_per_seq * bs) cannot be a sum of lengths and is taken as -1.
+ *     A wrong value keeps the result within the decode's tolerance; it gives
+ *     the same bits as the unhinted call only when it leaves the split
+ *     unchanged (an overestimate can keep long segments whole, which changes
+ *     the order of the reduction and unbalances the work).
+ * (Design, not on the pages: the host's allocator knows the lengths, so the
+ * sum costs no device read.)
  *   other arguments, errors and ownership as pkv_paged_attn_decode.
  */
 int pkv_paged_attn_decode_hinted(float* out, const void* q, int q_dtype, const void* k_pool,
@@ -237,11 +263,12 @@ int pkv_paged_attn_decode_hinted(float* out, const void* q, int q_dtype, const v
  * of position n - 1 (or a sequence with n = 0) is a caller error: the token is
  * then stored (when its position's piece exists) but not attended.
  *   sum_context_lens  host hint: the sum of context_lens[b] over the batch, as
- *     the caller's allocator knows it, or -1 if unknown.  It only chooses the
- *     work split: when it shows that the planned split would keep every
- *     (sequence, KV head) segment whole, the call runs one piece per segment
- *     and skips the merge launch.  A wrong value never changes the result;
- *     an overestimate on a batch of very mixed lengths can unbalance the work.
+ *     the caller's allocator knows it, or -1 if unknown; as for
+ *     pkv_paged_attn_decode_hinted (a wrong value keeps the result within
+ *     the decode's tolerance, bit-identical only when the split is unchanged).
+ * ("Paged Attention and KV Cache Fragmentation", section "How PagedAttention
+ * maps an OS concept onto GPU memory": each step appends the new token into
+ * the block its table maps it to, then attends over the whole sequence.)
  */
 int pkv_decode_step(float* out, const void* q, int q_dtype, const void* k_new, const void* v_new,
                     int src_dtype, const int64_t* new_slots, void* k_pool, void* v_pool, int kv_dtype,
@@ -385,7 +412,7 @@ int pkv_block_tables(const pkv_allocator* a, const int64_t* seqs, int32_t n, int
 int32_t pkv_block_refcount(const pkv_allocator* a, int32_t block);
 
 /* ---------------------------------------------------------------------------
- * Measurement helpers (not part of the method).
+ * Measurement helpers.  Design, not on the pages and not part of the method.
  * pkv_stream_read: reads `bytes` (multiple of 16) from `src` with the
  * library's load pattern and writes one fp32 per workgroup to `sink`
  * (device, >= pkv_stream_read_sink_floats(bytes) floats): a read-bandwidth

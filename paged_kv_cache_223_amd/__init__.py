@@ -8,8 +8,11 @@ if the library is not built, importing this package fails.
 
     kv_append(k, v, slot_mapping, k_pool, v_pool, k_scale=None, v_scale=None)
     paged_attn_decode(q, k_pool, v_pool, block_tables, context_lens, scale,
-                      max_context_len, k_scale=None, v_scale=None) -> out
+                      k_scale=None, v_scale=None, max_context_len=None) -> out
     Allocator(NB, bs, initial_free_order=None)
+
+A max_context_len of None is taken as block_tables.shape[1] * block size, the
+longest context the table can describe (no device read).
 
 Pool layout (see pkv.h): K [NB, H_kv, D // X, bs, X], V [NB, H_kv, D, bs],
 X = 16 bytes / element size; E4M3 pools are uint8 (or float8_e4m3fn) tensors.
@@ -49,7 +52,8 @@ SIGNATURES = {
     "pkv_block_record_bytes": (_SZ, [ctypes.c_int, _I32, _I32, _I32]),
     "pkv_gather_blocks": (ctypes.c_int, [_P, _P, ctypes.c_int, _I32, _I32, _I32, _I32, _P, _I32, _P, _P]),
     "pkv_scatter_blocks": (ctypes.c_int, [_P, _P, ctypes.c_int, _I32, _I32, _I32, _I32, _P, _I32, _P, _P]),
-    "pkv_decode_workspace_bytes": (_SZ, [_I32, _I32, _I32, _I32, _I32, _I32]),
+    "pkv_decode_workspace_bytes": (_SZ, [_I32, _I32, _I32, _I32, _I32]),
+    "pkv_decode_workspace_bytes_gqa": (_SZ, [_I32, _I32, _I32, _I32, _I32, _I32]),
     "pkv_paged_attn_decode": (ctypes.c_int, [_P, _P, ctypes.c_int, _P, _P, ctypes.c_int, _P, _I32, _P, _I32,
                                              _I32, _I32, _I32, _I32, _I32, _I32, ctypes.c_float, _P, _P, _P,
                                              _SZ, _P]),
@@ -265,14 +269,24 @@ def scatter_blocks(k_pool, v_pool, blocks, staging):
                                   _ptr(staging), _stream()))
 
 
-def decode_workspace_bytes(B: int, H_q: int, H_kv: int, D: int, max_context_len: int, bs: int) -> int:
-    return int(lib.pkv_decode_workspace_bytes(B, H_q, H_kv, D, max_context_len, bs))
+def decode_workspace_bytes(B: int, H_q: int, D: int, max_context_len: int, bs: int, H_kv: int | None = None) -> int:
+    """Scratch bytes of a decode call (pkv_decode_workspace_bytes; with H_kv, the exact figure
+    for that KV head count, pkv_decode_workspace_bytes_gqa)."""
+    if H_kv is None:
+        return int(lib.pkv_decode_workspace_bytes(B, H_q, D, max_context_len, bs))
+    return int(lib.pkv_decode_workspace_bytes_gqa(B, H_q, H_kv, D, max_context_len, bs))
 
 
-def decode_workspace(B: int, H_q: int, H_kv: int, D: int, max_context_len: int, bs: int, device="cuda"):
+def decode_workspace(B: int, H_q: int, D: int, max_context_len: int, bs: int, H_kv: int | None = None,
+                     device="cuda"):
     """A workspace for these sizes (contents need no initialisation)."""
-    n = decode_workspace_bytes(B, H_q, H_kv, D, max_context_len, bs)
+    n = decode_workspace_bytes(B, H_q, D, max_context_len, bs, H_kv)
     return torch.empty(max(n, 256), dtype=torch.uint8, device=device)
+
+
+def _max_context_len(max_context_len, block_tables, bs: int) -> int:
+    """The host's bound on the batch's context lengths; None: what the table can describe."""
+    return int(block_tables.shape[1]) * int(bs) if max_context_len is None else int(max_context_len)
 
 
 _ws_cache = {}
@@ -291,10 +305,11 @@ def _cached_workspace(device, need: int):
     return ws
 
 
-def paged_attn_decode(q, k_pool, v_pool, block_tables, context_lens, scale: float, max_context_len: int,
-                      k_scale=None, v_scale=None, out=None, workspace=None, sink_lens=None, window_starts=None,
-                      sum_context_lens: int = -1):
+def paged_attn_decode(q, k_pool, v_pool, block_tables, context_lens, scale: float, k_scale=None, v_scale=None,
+                      max_context_len: int | None = None, *, out=None, workspace=None, sink_lens=None,
+                      window_starts=None, sum_context_lens: int = -1):
     """Decode attention of one query token per sequence over its paged KV; fp32 [B, H_q, D].
+    max_context_len: host bound on context_lens (None: block_tables.shape[1] * block size).
     With sink_lens and/or window_starts (int32 [B]) sequence b attends only t < sink_lens[b] or
     t >= window_starts[b] (pkv_paged_attn_decode_window).  sum_context_lens: the host's sum of
     context_lens (-1 unknown); it only chooses the work split (pkv_paged_attn_decode_hinted)."""
@@ -313,7 +328,8 @@ def paged_attn_decode(q, k_pool, v_pool, block_tables, context_lens, scale: floa
         out = torch.empty((B, H_q, D), dtype=torch.float32, device=q.device)
     elif out.dtype != torch.float32 or tuple(out.shape) != (B, H_q, D):
         raise ValueError("out must be fp32 [B, H_q, D]")
-    need = decode_workspace_bytes(B, H_q, H_kv, D, max_context_len, bs)
+    max_context_len = _max_context_len(max_context_len, block_tables, bs)
+    need = decode_workspace_bytes(B, H_q, D, max_context_len, bs, H_kv)
     if workspace is None and need:
         workspace = _cached_workspace(q.device, need)
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
@@ -337,11 +353,12 @@ def paged_attn_decode(q, k_pool, v_pool, block_tables, context_lens, scale: floa
 
 
 def decode_step(q, k_new, v_new, new_slots, k_pool, v_pool, block_tables, context_lens, scale: float,
-                max_context_len: int, k_scale=None, v_scale=None, out=None, workspace=None,
+                k_scale=None, v_scale=None, max_context_len: int | None = None, *, out=None, workspace=None,
                 sum_context_lens: int = -1):
     """kv_append(k_new, v_new, new_slots) then paged_attn_decode, fused into one launch where possible.
     k_new, v_new: [B, H_kv, D] (sequence b's token at its last position); new_slots: int64 [B].
-    sum_context_lens: the host's sum of context_lens (-1 unknown); it only chooses the work split."""
+    max_context_len as for paged_attn_decode.  sum_context_lens: the host's sum of context_lens
+    (-1 unknown); it only chooses the work split."""
     torch = _torch()
     _dev(q, k_new, v_new, new_slots, k_pool, v_pool, block_tables, context_lens, k_scale, v_scale, out, workspace)
     kv, NB, H_kv, D, bs = _pool_dims(k_pool, v_pool)
@@ -361,7 +378,8 @@ def decode_step(q, k_new, v_new, new_slots, k_pool, v_pool, block_tables, contex
         out = torch.empty((B, H_q, D), dtype=torch.float32, device=q.device)
     elif out.dtype != torch.float32 or tuple(out.shape) != (B, H_q, D):
         raise ValueError("out must be fp32 [B, H_q, D]")
-    need = decode_workspace_bytes(B, H_q, H_kv, D, max_context_len, bs)
+    max_context_len = _max_context_len(max_context_len, block_tables, bs)
+    need = decode_workspace_bytes(B, H_q, D, max_context_len, bs, H_kv)
     if workspace is None and need:
         workspace = _cached_workspace(q.device, need)
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0

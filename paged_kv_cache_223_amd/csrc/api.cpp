@@ -48,7 +48,7 @@ extern "C" {
 
 const char* pkv_last_error(void) { return g_err; }
 
-int pkv_abi_version(void) { return 1; }
+int pkv_abi_version(void) { return 2; }
 
 int pkv_kv_append(const void* k, const void* v, int src_dtype, const int64_t* slot_mapping, int32_t T,
                   void* k_pool, void* v_pool, int pool_dtype, int32_t NB, int32_t bs, int32_t H_kv, int32_t D,
@@ -202,14 +202,32 @@ int pkv_scatter_blocks(void* k_pool, void* v_pool, int pool_dtype, int32_t NB, i
   return hip_status(launch_block_move(a, kMoveScatter, (hipStream_t)stream), "scatter_blocks launch");
 }
 
-size_t pkv_decode_workspace_bytes(int32_t B, int32_t H_q, int32_t H_kv, int32_t D, int32_t max_context_len,
-                                  int32_t bs) {
+size_t pkv_decode_workspace_bytes_gqa(int32_t B, int32_t H_q, int32_t H_kv, int32_t D, int32_t max_context_len,
+                                      int32_t bs) {
   g_err[0] = 0;
   if (B < 0 || H_q <= 0 || H_kv <= 0 || D <= 0 || max_context_len < 0 || bs <= 0) {
     set_error("decode_workspace_bytes: bad sizes");
     return 0;
   }
   return workspace_bytes_for(B, H_q, H_kv, D, plan_splits(B, H_kv, max_context_len), current_num_cus());
+}
+
+// Without H_kv: the largest size over every KV head count that divides H_q, so the result
+// serves a decode call with any of them.
+size_t pkv_decode_workspace_bytes(int32_t B, int32_t H_q, int32_t D, int32_t max_context_len, int32_t bs) {
+  g_err[0] = 0;
+  if (B < 0 || H_q <= 0 || D <= 0 || max_context_len < 0 || bs <= 0) {
+    set_error("decode_workspace_bytes: bad sizes");
+    return 0;
+  }
+  const int cus = current_num_cus();
+  size_t best = 0;
+  for (int32_t h = 1; h <= H_q; ++h) {
+    if (H_q % h) continue;
+    const size_t n = workspace_bytes_for(B, H_q, h, D, plan_splits(B, h, max_context_len), cus);
+    best = n > best ? n : best;
+  }
+  return best;
 }
 
 static int decode_impl(float* out, const void* q, int q_dtype, const void* k_pool, const void* v_pool, int kv_dtype,
@@ -301,7 +319,9 @@ static int decode_impl(float* out, const void* q, int q_dtype, const void* k_poo
   a.q_dtype = q_dtype;
   a.kv_dtype = kv_dtype;
   a.num_cus = num_cus;
-  a.sum_len_hint = sum_len_hint;
+  // A length sum above B * len_cap is impossible (every length is cut to len_cap): the hint is then
+  // taken as unknown rather than as a reason to keep every segment whole.
+  a.sum_len_hint = sum_len_hint > (long long)B * a.len_cap ? -1 : sum_len_hint;
   hipStream_t s = (hipStream_t)stream;
   if (fast) return hip_status(launch_decode_mfma(a, s), "decode launch");
   const int st = hip_status(launch_decode_vector(a, s), "decode launch");

@@ -980,7 +980,7 @@ hipError_t launch_mfma_a(const DecodeArgs& a, hipStream_t s) {
   if (a.sum_len_hint >= 0) {
     // cmax <= max(kMinUnits, ceil(csum * H_kv / target)), written without a product of csum
     const long long cmax = ((long long)a.len_cap + 31) / 32;
-    const long long csum = (a.sum_len_hint + 31) / 32;
+    const long long csum = a.sum_len_hint / 32 + (a.sum_len_hint % 32 != 0);  // at most B * len_cap / 32 + 1
     b.single_piece = cmax <= kMinUnits || csum > (cmax - 1) * target / a.H_kv;
     // every length at len_cap: one size class and no empty sequence, so workgroup i's segment is
     // (i / H_kv, i % H_kv), which the kernel checks against its plan before using the early loads

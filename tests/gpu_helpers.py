@@ -70,7 +70,7 @@ def gpu_pools_by_append(case, mat, chunk=65536):
 def decode(case, dev, max_context_len=None):
     mcl = case.max_context_len if max_context_len is None else max_context_len
     out = pkv.paged_attn_decode(dev["q"], dev["k_pool"], dev["v_pool"], dev["block_tables"], dev["context_lens"],
-                                float(case.scale), mcl, dev["k_scale"], dev["v_scale"])
+                                float(case.scale), dev["k_scale"], dev["v_scale"], max_context_len=mcl)
     torch.cuda.synchronize()
     return out.cpu().numpy().astype(np.float64)
 

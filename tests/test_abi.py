@@ -27,7 +27,102 @@ def test_every_declared_symbol_is_exported_and_bound():
 
 
 def test_abi_version():
-    assert pkv.lib.pkv_abi_version() == 1
+    assert pkv.lib.pkv_abi_version() == 2
+
+
+def _prototypes():
+    """name -> list of parameter types (names dropped, whitespace normalised) from pkv.h."""
+    text = re.sub(r"/\*.*?\*/", "", open(HEADER).read(), flags=re.S)
+    protos = {}
+    for m in re.finditer(r"\b(pkv_[a-z0-9_]+)\s*\(([^()]*)\)\s*;", text):
+        params = [" ".join(p.split()) for p in m.group(2).split(",")]
+        types = []
+        for p in params:
+            if p == "void":
+                continue
+            t = re.sub(r"\s*\b[A-Za-z_][A-Za-z0-9_]*$", "", p)  # drop the parameter name
+            types.append(t.replace(" *", "*"))
+        protos[m.group(1)] = types
+    return protos
+
+
+# The calls of the boundary as the hot-path contract lists them (types in order).
+CONTRACT = {
+    "pkv_kv_append": "const void* k, const void* v, int src_dtype, const int64_t* slot_mapping, int32_t T, "
+                     "void* k_pool, void* v_pool, int pool_dtype, int32_t NB, int32_t bs, int32_t H_kv, int32_t d, "
+                     "const float* k_scale, const float* v_scale, void* stream",
+    "pkv_decode_workspace_bytes": "int32_t B, int32_t H_q, int32_t d, int32_t max_context_len, int32_t bs",
+    "pkv_paged_attn_decode": "float* out, const void* q, int q_dtype, const void* k_pool, const void* v_pool, "
+                             "int kv_dtype, const int32_t* block_tables, int32_t max_blocks_per_seq, "
+                             "const int32_t* context_lens, int32_t max_context_len, int32_t B, int32_t H_q, "
+                             "int32_t H_kv, int32_t d, int32_t NB, int32_t bs, float scale, const float* k_scale, "
+                             "const float* v_scale, void* workspace, size_t workspace_bytes, void* stream",
+    "pkv_alloc_create": "int32_t NB, int32_t bs, const int32_t* initial_free_order, pkv_allocator** out",
+    "pkv_alloc_destroy": "pkv_allocator* a",
+    "pkv_alloc_num_free": "const pkv_allocator* a",
+    "pkv_seq_add": "pkv_allocator* a, int64_t seq",
+    "pkv_seq_append_slots": "pkv_allocator* a, int64_t seq, int32_t n, int64_t* slots_out",
+    "pkv_seq_fork": "pkv_allocator* a, int64_t parent, int64_t child",
+    "pkv_seq_free": "pkv_allocator* a, int64_t seq",
+    "pkv_seq_len": "const pkv_allocator* a, int64_t seq, int32_t* len",
+    "pkv_block_tables": "const pkv_allocator* a, const int64_t* seqs, int32_t n, int32_t max_blocks, "
+                        "int32_t* table_out, int32_t* lens_out",
+    "pkv_block_refcount": "const pkv_allocator* a, int32_t block",
+}
+
+
+def test_contract_signatures():
+    protos = _prototypes()
+    for name, params in CONTRACT.items():
+        want = [re.sub(r"\s*\b[A-Za-z_][A-Za-z0-9_]*$", "", " ".join(p.split())).replace(" *", "*")
+                for p in params.split(",")]
+        assert protos[name] == want, (name, protos[name], want)
+    assert len(pkv.SIGNATURES["pkv_kv_append"][1]) == 15
+    assert len(pkv.SIGNATURES["pkv_paged_attn_decode"][1]) == 22
+    assert len(pkv.SIGNATURES["pkv_decode_workspace_bytes"][1]) == 5
+
+
+def test_python_contract_signatures():
+    """The binding's names and argument order as the contract gives them."""
+    import inspect
+    want = {
+        "kv_append": ["k", "v", "slot_mapping", "k_pool", "v_pool", "k_scale", "v_scale"],
+        "paged_attn_decode": ["q", "k_pool", "v_pool", "block_tables", "context_lens", "scale", "k_scale", "v_scale",
+                              "max_context_len"],
+    }
+    for fn, names in want.items():
+        ps = list(inspect.signature(getattr(pkv, fn)).parameters.values())
+        assert [p.name for p in ps[:len(names)]] == names, fn
+        for p in ps[len(names):]:
+            assert p.kind is inspect.Parameter.KEYWORD_ONLY or p.default is not inspect.Parameter.empty
+        for p in ps:
+            if p.name in ("k_scale", "v_scale", "max_context_len"):
+                assert p.default is None, (fn, p.name)
+    assert [p for p in inspect.signature(pkv.Allocator).parameters] == ["NB", "bs", "initial_free_order"]
+
+
+def test_every_call_cites_a_passage_or_says_design():
+    """Each declaration sits under a multi-line comment block that names the page passage
+    defining the operation, or says that the call is a design of this library."""
+    lines = open(HEADER).read().splitlines()
+    cites = ("Paged Attention and KV Cache Fragmentation", "KV Cache Fragmentation", "Design")
+    block, doc, inside = [], "", False
+    seen = set()
+    for ln in lines:
+        st = ln.strip()
+        if not inside and (st == "/*" or st.startswith("/* ---")):  # a documentation block opens
+            inside, block = True, [st]
+            continue
+        if inside:
+            block.append(st)
+            if "*/" in st:
+                inside, doc = False, " ".join(block)
+            continue
+        for name in re.findall(r"\b(pkv_[a-z0-9_]+)\s*\(", ln):
+            if name in pkv.SIGNATURES and name not in seen:
+                seen.add(name)
+                assert any(c in doc for c in cites), name
+    assert seen == set(pkv.SIGNATURES)
 
 
 def test_status_and_dtype_codes_match_header():
@@ -81,7 +176,7 @@ def _decode(hinted=None, **kw):
 def test_decode_rejects_bad_arguments_before_launch(kw, status):
     assert _decode(**kw) == status
     assert pkv.last_error()
-    for hint in (-1, 0, 128):  # the hinted entry checks the same arguments
+    for hint in (-1, 0, 128, 2 ** 63 - 1):  # the hinted entry checks the same arguments
         assert _decode(hinted=hint, **kw) == status
         assert pkv.last_error()
 
@@ -149,11 +244,22 @@ def test_decode_window_empty_batch_is_a_no_op():
 
 
 def test_workspace_size_covers_both_paths():
-    small = pkv.decode_workspace_bytes(4, 64, 8, 128, 200, 16)
+    small = pkv.decode_workspace_bytes(4, 64, 128, 200, 16, H_kv=8)
     assert small > 0 and small % 4 == 0  # the matrix-core path always keeps its partial slots
-    big = pkv.decode_workspace_bytes(4096, 64, 8, 128, 131072, 32)  # vector-path splits dominate
+    big = pkv.decode_workspace_bytes(4096, 64, 128, 131072, 32, H_kv=8)  # vector-path splits dominate
     assert big > small
-    assert pkv.decode_workspace_bytes(-1, 64, 8, 128, 10, 16) == 0 and pkv.last_error()
+    assert pkv.decode_workspace_bytes(-1, 64, 128, 10, 16, H_kv=8) == 0 and pkv.last_error()
+    assert pkv.decode_workspace_bytes(-1, 64, 128, 10, 16) == 0 and pkv.last_error()
+
+
+def test_workspace_size_without_h_kv_bounds_every_divisor():
+    """The contract's query takes no KV head count: its figure is the largest over every H_kv
+    that divides H_q, so it serves any of them."""
+    for B, H_q, D, mcl, bs in ((4, 64, 128, 200, 16), (4096, 64, 128, 131072, 32), (256, 32, 128, 20000, 8),
+                               (3, 6, 64, 77, 8)):
+        bound = pkv.decode_workspace_bytes(B, H_q, D, mcl, bs)
+        exact = [pkv.decode_workspace_bytes(B, H_q, D, mcl, bs, H_kv=h) for h in range(1, H_q + 1) if H_q % h == 0]
+        assert bound == max(exact) and min(exact) > 0
 
 
 def _append(**kw):

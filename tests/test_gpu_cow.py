@@ -114,7 +114,7 @@ def _replay_gpu(sc):
             st, tab, lens = a.block_tables(sids, mb)
             assert st == 0
             out = pkv.paged_attn_decode(to_dev(sc.qs[qi], "bf16"), kp, vp, torch.from_numpy(tab).to(DEV),
-                                        torch.from_numpy(lens).to(DEV), sc.scale, int(lens.max()), ks, vs)
+                                        torch.from_numpy(lens).to(DEV), sc.scale, ks, vs, max_context_len=int(lens.max()))
             outs.append((tab, lens, out.cpu().numpy().astype(np.float64)))
     torch.cuda.synchronize()
     return from_dev(kp), from_dev(vp), outs

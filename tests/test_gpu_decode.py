@@ -184,7 +184,7 @@ def test_every_e4m3_code_decodes_exactly():
     import paged_kv_cache_223_amd as pkv
     out = pkv.paged_attn_decode(to_dev(q, "bf16"), to_dev(kp, "e4m3"), to_dev(vp, "e4m3"),
                                 torch.from_numpy(table).to(DEV), torch.tensor([1, 1], dtype=torch.int32, device=DEV),
-                                0.1, 1, one, one)
+                                0.1, one, one, max_context_len=1)
     got = out.cpu().numpy().reshape(-1)
     want = oracle.e4m3_decode(codes).astype(np.float32)
     assert (got == want).all()
@@ -202,10 +202,10 @@ def test_workspace_reused_across_calls_and_shapes():
         mat = materialize_with_model(case)
         kp, vp = oracle_pools(case, mat)
         dev = device_inputs(case, mat, kp, vp)
-        assert pkv.decode_workspace_bytes(case.B, case.spec.H_q, case.spec.H_kv, case.spec.d,
-                                          case.max_context_len, case.bs) > 0
+        assert pkv.decode_workspace_bytes(case.B, case.spec.H_q, case.spec.d, case.max_context_len, case.bs,
+                                          case.spec.H_kv) > 0
         out = pkv.paged_attn_decode(dev["q"], dev["k_pool"], dev["v_pool"], dev["block_tables"],
-                                    dev["context_lens"], float(case.scale), case.max_context_len, workspace=ws)
+                                    dev["context_lens"], float(case.scale), max_context_len=case.max_context_len, workspace=ws)
         torch.cuda.synchronize()
         got = out.cpu().numpy().astype(np.float64)
         assert row_rel_err(got, oracle_decode(case, mat, kp, vp)) <= tol(case)
@@ -224,13 +224,14 @@ def test_captured_step_replays_match_eager():
     step_k = to_dev(mat.step_k, "bf16")
     step_v = to_dev(mat.step_v, "bf16")
     slots = torch.from_numpy(mat.step_slots).to(DEV)
-    ws = pkv.decode_workspace(case.B, 64, 8, 128, case.max_context_len, case.bs)
+    ws = pkv.decode_workspace(case.B, 64, 128, case.max_context_len, case.bs, H_kv=8)
     out = torch.empty((case.B, 64, 128), dtype=torch.float32, device=DEV)
 
     def step():
         pkv.kv_append(step_k, step_v, slots, dev["k_pool"], dev["v_pool"])
         pkv.paged_attn_decode(dev["q"], dev["k_pool"], dev["v_pool"], dev["block_tables"], dev["context_lens"],
-                              float(case.scale), case.max_context_len, out=out, workspace=ws)
+                              float(case.scale), max_context_len=case.max_context_len, out=out,
+                              workspace=ws)
 
     step()
     torch.cuda.synchronize()
@@ -286,28 +287,36 @@ def test_decode_more_sequences_than_the_plan_keeps_in_registers(kv):
 
 
 @pytest.mark.parametrize("kv", ["bf16", "e4m3"])
-@pytest.mark.parametrize("name", ["short", "cut", "cut_forced_whole"])
+@pytest.mark.parametrize("name", ["short", "cut", "impossible", "forced_whole"])
 def test_hinted_decode(name, kv):
     """pkv_paged_attn_decode_hinted: with the true length sum, a batch whose plan cuts no segment
     (all lengths within 8 chunks) and one whose plan cuts segments give the bits of the unhinted
-    call; a sum far above the truth forces every segment whole and still gives the oracle's
-    result."""
+    call; a sum above B * max_context_len cannot be a sum of lengths and is ignored (same bits);
+    the largest possible sum on a batch of one long and many short sequences keeps every segment
+    whole (another reduction order) and still gives the oracle's result."""
     import paged_kv_cache_223_amd as pkv
-    lens = [256, 30, 1, 200, 129, 64] if name == "short" else [5000, 30, 1, 700, 2049, 64]
+    if name == "short":
+        lens = [256, 30, 1, 200, 129, 64]
+    elif name == "forced_whole":
+        lens = [6000] + [40] * 127
+    else:
+        lens = [5000, 30, 1, 700, 2049, 64]
     case = workloads.custom(f"hinted_{name}_{kv}", len(lens), 32, 8, 128, 16, kv, "bf16", lens,
                             seed=6100 + len(name) + len(kv))
     mat = materialize_with_model(case)
     kp, vp = oracle_pools(case, mat)
     d = device_inputs(case, mat, kp, vp)
     args = (d["q"], d["k_pool"], d["v_pool"], d["block_tables"], d["context_lens"], float(case.scale),
-            case.max_context_len, d["k_scale"], d["v_scale"])
+            d["k_scale"], d["v_scale"], case.max_context_len)
     plain = pkv.paged_attn_decode(*args).cpu().numpy()
     true_sum = int(np.sum(mat.context_lens))
-    hint = 10 ** 12 if name == "cut_forced_whole" else true_sum
+    hint = {"impossible": 2 ** 63 - 1, "forced_whole": case.B * case.max_context_len}.get(name, true_sum)
     hinted = pkv.paged_attn_decode(*args, sum_context_lens=hint).cpu().numpy()
     torch.cuda.synchronize()
-    if name != "cut_forced_whole":
-        assert np.array_equal(plain.view(np.uint32), hinted.view(np.uint32))
+    same = np.array_equal(plain.view(np.uint32), hinted.view(np.uint32))
+    print(f"hinted {name} {kv}: hint {hint}, same bits as unhinted: {same}", flush=True)
+    if name != "forced_whole":
+        assert same
     ref = oracle_decode(case, mat, kp, vp)
     assert np.isfinite(hinted).all()
     assert row_rel_err(hinted.astype(np.float64), ref) <= tol(case)
@@ -333,7 +342,7 @@ def test_cached_workspace_is_per_stream():
         for (c, d), s in zip(devs, streams):
             with torch.cuda.stream(s):
                 outs.append(pkv.paged_attn_decode(d["q"], d["k_pool"], d["v_pool"], d["block_tables"],
-                                                  d["context_lens"], float(c.scale), c.max_context_len))
+                                                  d["context_lens"], float(c.scale), max_context_len=c.max_context_len))
         torch.cuda.synchronize()
         for o, a in zip(outs, alone):
             assert np.array_equal(o.cpu().numpy().astype(np.float64), a)

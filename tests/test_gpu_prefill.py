@@ -147,7 +147,7 @@ def test_last_query_of_a_chunk_matches_the_decode_and_two_chunks_match_one():
     full = c.prefill()
     last_rows = [int(x) - 1 for x in c.query_start[1:]]
     dec = pkv.paged_attn_decode(to_dev(c.q[last_rows], "bf16"), c.kp, c.vp, c.tab_d, c.lens_d, c.scale,
-                                max(c.lens)).cpu().numpy().astype(np.float64)
+                                max_context_len=max(c.lens)).cpu().numpy().astype(np.float64)
     assert row_rel_err(full[last_rows], dec) <= 2e-3
     # the same chunks split in two: first part with the shorter context, then the rest
     first = [120, 64, 1]

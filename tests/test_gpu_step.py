@@ -53,10 +53,10 @@ def _both_ways(case, mat, drop=()):
     for fused in (False, True):
         kp, vp, k_s, v_s = _pre_step_pools(case, mat)
         if fused:
-            out = pkv.decode_step(q, sk, sv, sl, kp, vp, tab, ln, float(case.scale), case.max_context_len, k_s, v_s)
+            out = pkv.decode_step(q, sk, sv, sl, kp, vp, tab, ln, float(case.scale), k_s, v_s, case.max_context_len)
         else:
             pkv.kv_append(sk, sv, sl, kp, vp, k_s, v_s)
-            out = pkv.paged_attn_decode(q, kp, vp, tab, ln, float(case.scale), case.max_context_len, k_s, v_s)
+            out = pkv.paged_attn_decode(q, kp, vp, tab, ln, float(case.scale), k_s, v_s, case.max_context_len)
         torch.cuda.synchronize()
         res += [out.cpu().numpy(), from_dev(kp), from_dev(vp)]
     return res, lens
@@ -137,11 +137,11 @@ def test_fused_full_70b_step_and_graph_replay():
     tab, ln = torch.from_numpy(mat.block_tables).to(DEV), torch.from_numpy(mat.context_lens).to(DEV)
     sl = torch.from_numpy(mat.step_slots).to(DEV)
     out = torch.empty((case.B, 64, 128), dtype=torch.float32, device=DEV)
-    ws = pkv.decode_workspace(case.B, 64, 8, 128, case.max_context_len, case.bs, device=DEV)
-    pkv.decode_step(q, sk, sv, sl, kp, vp, tab, ln, float(case.scale), case.max_context_len, out=out, workspace=ws)
+    ws = pkv.decode_workspace(case.B, 64, 128, case.max_context_len, case.bs, H_kv=8, device=DEV)
+    pkv.decode_step(q, sk, sv, sl, kp, vp, tab, ln, float(case.scale), max_context_len=case.max_context_len, out=out, workspace=ws)
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
-        pkv.decode_step(q, sk, sv, sl, kp, vp, tab, ln, float(case.scale), case.max_context_len, out=out,
+        pkv.decode_step(q, sk, sv, sl, kp, vp, tab, ln, float(case.scale), max_context_len=case.max_context_len, out=out,
                         workspace=ws)
     for _ in range(3):
         out.zero_()
@@ -152,14 +152,14 @@ def test_fused_full_70b_step_and_graph_replay():
     # launch is skipped: the result is the same, bit for bit, also from a captured graph
     hint = int(mat.context_lens.astype(np.int64).sum())
     kp, vp, _, _ = _pre_step_pools(case, mat)
-    pkv.decode_step(q, sk, sv, sl, kp, vp, tab, ln, float(case.scale), case.max_context_len, out=out, workspace=ws,
+    pkv.decode_step(q, sk, sv, sl, kp, vp, tab, ln, float(case.scale), max_context_len=case.max_context_len, out=out, workspace=ws,
                     sum_context_lens=hint)
     torch.cuda.synchronize()
     assert np.array_equal(out.cpu().numpy().view(np.uint32), o1.view(np.uint32))
     assert np.array_equal(from_dev(kp), k1) and np.array_equal(from_dev(vp), v1)
     g2 = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g2):
-        pkv.decode_step(q, sk, sv, sl, kp, vp, tab, ln, float(case.scale), case.max_context_len, out=out,
+        pkv.decode_step(q, sk, sv, sl, kp, vp, tab, ln, float(case.scale), max_context_len=case.max_context_len, out=out,
                         workspace=ws, sum_context_lens=hint)
     for _ in range(3):
         out.zero_()
@@ -170,8 +170,9 @@ def test_fused_full_70b_step_and_graph_replay():
 
 @pytest.mark.parametrize("kv", ["bf16", "e4m3"])
 def test_length_hint_only_chooses_the_split(kv):
-    """A batch of very mixed lengths: a hint far above the true sum forces one piece per segment
-    (unbalanced but still the oracle's result); a hint of 0 leaves the planned split unchanged."""
+    """A batch of very mixed lengths: a hint of 0, or one above B * max_context_len (no sum of
+    lengths can be that large, so it is ignored), leaves the planned split unchanged (same bits);
+    the largest possible hint still gives the oracle's result."""
     print(f"length hint {kv}", flush=True)
     case = _with_step(workloads.custom(f"hint_{kv}", 6, 32, 8, 128, 16, kv, "bf16", [5000, 30, 1, 700, 2049, 64],
                                        93 + len(kv)))
@@ -182,11 +183,12 @@ def test_length_hint_only_chooses_the_split(kv):
     tab, ln = torch.from_numpy(mat.block_tables).to(DEV), torch.from_numpy(mat.context_lens).to(DEV)
     sl = torch.from_numpy(mat.step_slots).to(DEV)
     outs = {}
-    for hint in (-1, 0, 10 ** 12):
+    for hint in (-1, 0, 10 ** 12, case.B * case.max_context_len):
         kp, vp, k_s, v_s = _pre_step_pools(case, mat)
-        outs[hint] = pkv.decode_step(q, sk, sv, sl, kp, vp, tab, ln, float(case.scale), case.max_context_len, k_s,
-                                     v_s, sum_context_lens=hint).cpu().numpy()
+        outs[hint] = pkv.decode_step(q, sk, sv, sl, kp, vp, tab, ln, float(case.scale), k_s, v_s,
+                                     case.max_context_len, sum_context_lens=hint).cpu().numpy()
     assert np.array_equal(outs[-1].view(np.uint32), outs[0].view(np.uint32))
+    assert np.array_equal(outs[-1].view(np.uint32), outs[10 ** 12].view(np.uint32))
     kp, vp = oracle_pools(case, mat)
     ref = oracle_decode(case, mat, kp, vp)
     tol = 2e-2 if kv == "e4m3" else 2e-3
@@ -200,7 +202,7 @@ def test_uniform_length_sum_loads_early(name):
     """A length sum equal to B * max_context_len lets each workgroup load its likely segment's first
     chunk before its plan (sequences of at most 8 chunks always run in single-piece mode).  With
     every length at the maximum the output equals, bit for bit, the same single-piece step without
-    the early loads (sum + 1); a sum that lies about uneven lengths (or a sequence with no tokens,
+    the early loads (sum - 1); a sum that lies about uneven lengths (or a sequence with no tokens,
     which shifts every later segment) still gives the oracle's result and the same bits as without
     the early loads."""
     print(f"early loads {name}", flush=True)
@@ -224,11 +226,11 @@ def test_uniform_length_sum_loads_early(name):
     mcl = int(lens.max())
     early = case.B * mcl  # claims every length is the maximum
     outs = {}
-    for hint in (early, early + 1):
+    for hint in (early, early - 1):
         kp, vp, k_s, v_s = _pre_step_pools(case, mat)
-        outs[hint] = pkv.decode_step(q, sk, sv, sl, kp, vp, tab, ln, float(case.scale), mcl, k_s, v_s,
+        outs[hint] = pkv.decode_step(q, sk, sv, sl, kp, vp, tab, ln, float(case.scale), k_s, v_s, mcl,
                                      sum_context_lens=hint).cpu().numpy()
-    assert np.array_equal(outs[early].view(np.uint32), outs[early + 1].view(np.uint32))
+    assert np.array_equal(outs[early].view(np.uint32), outs[early - 1].view(np.uint32))
     if name == "uniform":
         assert int(lens.sum()) == early
     mat.context_lens = lens
@@ -272,7 +274,7 @@ def test_blocks_past_4_gib_of_pool():
     sv = to_dev(mat.step_v.reshape(case.B, 8, 128), "bf16")
     ln = torch.from_numpy(mat.context_lens).to(DEV)
     out = pkv.decode_step(q, sk, sv, torch.from_numpy(slots).to(DEV), kb, vb, torch.from_numpy(tab).to(DEV), ln,
-                          float(case.scale), case.max_context_len)
+                          float(case.scale), max_context_len=case.max_context_len)
     torch.cuda.synchronize()
     assert np.array_equal(out.cpu().numpy().view(np.uint32), o1.view(np.uint32))
     assert np.array_equal(from_dev(kb.index_select(0, dst)), k1[used])

@@ -61,7 +61,7 @@ def test_window_decode_matches_oracle(name):
     dev = device_inputs(case, mat, kp, vp)
     sinks, wins = _masks(np.random.default_rng(5), mat.context_lens)
     out = pkv.paged_attn_decode(dev["q"], dev["k_pool"], dev["v_pool"], dev["block_tables"], dev["context_lens"],
-                                float(case.scale), case.max_context_len, dev["k_scale"], dev["v_scale"],
+                                float(case.scale), dev["k_scale"], dev["v_scale"], case.max_context_len,
                                 sink_lens=torch.from_numpy(sinks).to(DEV), window_starts=torch.from_numpy(wins).to(DEV))
     got = out.cpu().numpy().astype(np.float64)
     ref = oracle.ref_decode(case.q, case.spec.q_dtype, kp, vp, case.spec.kv_dtype, mat.block_tables,
@@ -82,7 +82,7 @@ def test_window_decode_without_masks_is_the_plain_decode_bitwise():
     plain = decode(case, dev)
     zeros = torch.zeros(case.B, dtype=torch.int32, device=DEV)
     w = pkv.paged_attn_decode(dev["q"], dev["k_pool"], dev["v_pool"], dev["block_tables"], dev["context_lens"],
-                              float(case.scale), case.max_context_len, sink_lens=zeros, window_starts=zeros)
+                              float(case.scale), max_context_len=case.max_context_len, sink_lens=zeros, window_starts=zeros)
     assert np.array_equal(plain.astype(np.float32).view(np.uint32), w.cpu().numpy().view(np.uint32))
 
 
@@ -103,7 +103,7 @@ def test_hole_spanning_many_pieces_with_nan_inside():
     sinks = np.array([hole[0], 0], np.int32)
     wins = np.array([hole[1], 4000], np.int32)
     out = pkv.paged_attn_decode(dev["q"], dev["k_pool"], dev["v_pool"], dev["block_tables"], dev["context_lens"],
-                                float(case.scale), n, sink_lens=torch.from_numpy(sinks).to(DEV),
+                                float(case.scale), max_context_len=n, sink_lens=torch.from_numpy(sinks).to(DEV),
                                 window_starts=torch.from_numpy(wins).to(DEV))
     got = out.cpu().numpy().astype(np.float64)
     assert np.isfinite(got).all()
@@ -148,7 +148,7 @@ def test_streaming_eviction_attends_first_and_last_tokens(kv_dtype, bs, S, W):
         q = workloads.round_bf16(rng.standard_normal((1, H_q, d), dtype=np.float32))
         q_t = torch.from_numpy(q.view(np.int16)).to(DEV).view(torch.bfloat16)
         out = pkv.paged_attn_decode(q_t, kp, vp, torch.from_numpy(tab).to(DEV), torch.from_numpy(ln).to(DEV),
-                                    1 / np.sqrt(d), L, scale_k, scale_v,
+                                    1 / np.sqrt(d), scale_k, scale_v, L,
                                     sink_lens=torch.tensor([sink_len], dtype=torch.int32, device=DEV),
                                     window_starts=torch.tensor([win], dtype=torch.int32, device=DEV))
         got = out.cpu().numpy().astype(np.float64)

@@ -104,7 +104,7 @@ def test_swap_out_reuse_swap_in_decodes_as_before(kv_dtype, bs):
         st, tab, ln = a.block_tables(seqs, mb)
         assert st == 0
         out = pkv.paged_attn_decode(q, kp, vp, torch.from_numpy(tab).to(DEV), torch.from_numpy(ln).to(DEV),
-                                    float(case.scale), max(lens), k_s, v_s)
+                                    float(case.scale), k_s, v_s, max_context_len=max(lens))
         torch.cuda.synchronize()
         return out.cpu().numpy(), tab
 
