@@ -221,6 +221,29 @@ int pkv_paged_attn_decode(float* out, const void* q, int q_dtype, const void* k_
                           void* stream);
 
 /*
+ * pkv_paged_attn_decode_noalloc — pkv_paged_attn_decode without a workspace
+ * argument.  Design, for the callers that cannot allocate device memory: code
+ * under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.  The
+ * same kernels keep their partials in the library's static scratch instead:
+ * a device array of 32 MiB that every device running the library holds until
+ * the process ends.  The call itself allocates nothing (no hipMalloc, no
+ * hipFree, no allocating library routine).
+ *   Sizes whose scratch need (pkv_decode_workspace_bytes_gqa) exceeds 32 MiB
+ *   are refused with PKV_ERR_INVALID_ARG before anything is launched; use
+ *   pkv_paged_attn_decode with a workspace for those.
+ *   Every call on a device shares that device's scratch and leaves its last
+ *   contents there: calls that overlap on one device (several streams or
+ *   threads) race.  Nothing in the scratch needs to start at zero.
+ *   Other arguments, results and errors as pkv_paged_attn_decode.
+ */
+int pkv_paged_attn_decode_noalloc(float* out, const void* q, int q_dtype, const void* k_pool,
+                                  const void* v_pool, int kv_dtype, const int32_t* block_tables,
+                                  int32_t max_blocks_per_seq, const int32_t* context_lens,
+                                  int32_t max_context_len, int32_t B, int32_t H_q, int32_t H_kv,
+                                  int32_t D, int32_t NB, int32_t bs, float scale, const float* k_scale,
+                                  const float* v_scale, void* stream);
+
+/*
  * pkv_paged_attn_decode_hinted — pkv_paged_attn_decode with the host's sum of
  * the context lengths, for callers whose allocator holds the lengths (the sum
  * is the same hint pkv_decode_step takes):

@@ -57,6 +57,9 @@ SIGNATURES = {
     "pkv_paged_attn_decode": (ctypes.c_int, [_P, _P, ctypes.c_int, _P, _P, ctypes.c_int, _P, _I32, _P, _I32,
                                              _I32, _I32, _I32, _I32, _I32, _I32, ctypes.c_float, _P, _P, _P,
                                              _SZ, _P]),
+    "pkv_paged_attn_decode_noalloc": (ctypes.c_int, [_P, _P, ctypes.c_int, _P, _P, ctypes.c_int, _P, _I32, _P, _I32,
+                                                     _I32, _I32, _I32, _I32, _I32, _I32, ctypes.c_float, _P, _P,
+                                                     _P]),
     "pkv_paged_attn_decode_hinted": (ctypes.c_int, [_P, _P, ctypes.c_int, _P, _P, ctypes.c_int, _P, _I32, _P, _I32,
                                                     ctypes.c_int64, _I32, _I32, _I32, _I32, _I32, _I32,
                                                     ctypes.c_float, _P, _P, _P, _SZ, _P]),
@@ -352,6 +355,31 @@ def paged_attn_decode(q, k_pool, v_pool, block_tables, context_lens, scale: floa
     return out
 
 
+def paged_attn_decode_noalloc(q, k_pool, v_pool, block_tables, context_lens, scale: float, k_scale=None,
+                              v_scale=None, max_context_len: int | None = None, *, out):
+    """paged_attn_decode with its partials in the library's static scratch (32 MiB per device):
+    for callers that cannot allocate, so `out` (fp32 [B, H_q, D]) must be given.  Calls that
+    overlap on one device race on that scratch."""
+    torch = _torch()
+    _dev(q, k_pool, v_pool, block_tables, context_lens, k_scale, v_scale, out)
+    kv, NB, H_kv, D, bs = _pool_dims(k_pool, v_pool)
+    if q.dim() != 3 or q.shape[2] != D:
+        raise ValueError("q must be [B, H_q, D]")
+    B, H_q, _ = q.shape
+    if block_tables.dtype != torch.int32 or block_tables.dim() != 2 or block_tables.shape[0] != B:
+        raise ValueError("block_tables must be int32 [B, max_blocks]")
+    if context_lens.dtype != torch.int32 or context_lens.shape != (B,):
+        raise ValueError("context_lens must be int32 [B]")
+    if out.dtype != torch.float32 or tuple(out.shape) != (B, H_q, D):
+        raise ValueError("out must be fp32 [B, H_q, D]")
+    max_context_len = _max_context_len(max_context_len, block_tables, bs)
+    _check(lib.pkv_paged_attn_decode_noalloc(
+        _ptr(out), _ptr(q), dtype_code(q), _ptr(k_pool), _ptr(v_pool), kv, _ptr(block_tables), block_tables.shape[1],
+        _ptr(context_lens), max_context_len, B, H_q, H_kv, D, NB, bs, float(scale), _ptr(k_scale), _ptr(v_scale),
+        _stream()))
+    return out
+
+
 def decode_step(q, k_new, v_new, new_slots, k_pool, v_pool, block_tables, context_lens, scale: float,
                 k_scale=None, v_scale=None, max_context_len: int | None = None, *, out=None, workspace=None,
                 sum_context_lens: int = -1):
@@ -540,7 +568,7 @@ class Allocator:
 
 
 __all__ = ["lib", "LIB_PATH", "PkvError", "last_error", "kv_append", "copy_blocks", "gather_blocks",
-           "scatter_blocks", "paged_attn_decode", "paged_prefill", "decode_step",
+           "scatter_blocks", "paged_attn_decode", "paged_attn_decode_noalloc", "paged_prefill", "decode_step",
            "decode_workspace_bytes",
            "decode_workspace",
            "pool_shapes", "dtype_code", "stream_read", "copy_", "Allocator", "SIGNATURES",

@@ -236,7 +236,8 @@ static int decode_impl(float* out, const void* q, int q_dtype, const void* k_poo
                        int32_t H_q, int32_t H_kv, int32_t D, int32_t NB, int32_t bs, float scale,
                        const float* k_scale, const float* v_scale, void* workspace, size_t workspace_bytes,
                        void* stream, const void* new_k = nullptr, const void* new_v = nullptr,
-                       const int64_t* new_slots = nullptr, int64_t sum_len_hint = -1, bool check_only = false) {
+                       const int64_t* new_slots = nullptr, int64_t sum_len_hint = -1, bool check_only = false,
+                       bool static_ws = false) {
   if (B < 0 || H_q <= 0 || H_kv <= 0 || NB <= 0 || max_blocks_per_seq <= 0 || max_context_len < 0) {
     set_error("decode: bad sizes B=%d H_q=%d H_kv=%d NB=%d max_blocks=%d max_context_len=%d", B, H_q, H_kv, NB,
               max_blocks_per_seq, max_context_len);
@@ -269,14 +270,22 @@ static int decode_impl(float* out, const void* q, int q_dtype, const void* k_poo
   }
   const SplitPlan plan = plan_splits(B, H_kv, max_context_len);
   const int num_cus = current_num_cus();
-  const size_t need = workspace_bytes_for(B, H_q, H_kv, D, plan, num_cus);
-  if (need > 0 && (!workspace || workspace_bytes < need || ((uintptr_t)workspace & 255u))) {
+  const int G = H_q / H_kv;
+  const bool fast = decode_fast_path_supported(q_dtype, kv_dtype, G, D, bs);
+  // a caller's workspace is sized for either path; the static scratch only for the path that runs
+  const int paths = static_ws ? (fast ? 2 : 1) : 3;
+  const size_t need = workspace_bytes_for(B, H_q, H_kv, D, plan, num_cus, paths);
+  if (static_ws) {  // the library's own scratch (pkv_paged_attn_decode_noalloc)
+    if (need > kStaticScratchBytes) {
+      set_error("decode_noalloc: these sizes need %zu bytes of scratch, more than the %zu of the library's static "
+                "scratch; call pkv_paged_attn_decode with a workspace", need, kStaticScratchBytes);
+      return PKV_ERR_INVALID_ARG;
+    }
+  } else if (need > 0 && (!workspace || workspace_bytes < need || ((uintptr_t)workspace & 255u))) {
     set_error("decode: workspace needs %zu bytes, 256-byte aligned (got %zu at %p)", need, workspace_bytes,
               workspace);
     return PKV_ERR_INVALID_ARG;
   }
-  const int G = H_q / H_kv;
-  const bool fast = decode_fast_path_supported(q_dtype, kv_dtype, G, D, bs);
   const long long items = fast ? (long long)num_cus * kMaxGroupsPerCU + (long long)B * H_kv
                                : (long long)B * plan.max_splits * H_q;
   if (items > 0x7FFFFFFFLL) {
@@ -284,6 +293,11 @@ static int decode_impl(float* out, const void* q, int q_dtype, const void* k_poo
     return PKV_ERR_INVALID_ARG;
   }
   if (check_only) return PKV_OK;
+  if (static_ws) {
+    const int st = hip_status(static_scratch(&workspace), "decode_noalloc: static scratch lookup");
+    if (st != PKV_OK) return st;
+    workspace_bytes = kStaticScratchBytes;
+  }
   DecodeArgs a{};
   a.out = out;
   a.q = q;
@@ -299,7 +313,7 @@ static int decode_impl(float* out, const void* q, int q_dtype, const void* k_poo
   a.k_scale = k_scale;
   a.v_scale = v_scale;
   if (need > 0) {
-    const WorkspaceLayout wl = workspace_layout(B, H_q, H_kv, D, plan, num_cus);
+    const WorkspaceLayout wl = workspace_layout(B, H_q, H_kv, D, plan, num_cus, paths);
     a.ws_o = (float*)((char*)workspace + wl.o);
     a.ws_ml = (float*)((char*)workspace + wl.ml);
   }
@@ -338,6 +352,17 @@ int pkv_paged_attn_decode(float* out, const void* q, int q_dtype, const void* k_
   return decode_impl(out, q, q_dtype, k_pool, v_pool, kv_dtype, block_tables, max_blocks_per_seq, context_lens,
                      max_context_len, nullptr, nullptr, B, H_q, H_kv, D, NB, bs, scale, k_scale, v_scale, workspace,
                      workspace_bytes, stream);
+}
+
+int pkv_paged_attn_decode_noalloc(float* out, const void* q, int q_dtype, const void* k_pool, const void* v_pool,
+                                  int kv_dtype, const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                  const int32_t* context_lens, int32_t max_context_len, int32_t B, int32_t H_q,
+                                  int32_t H_kv, int32_t D, int32_t NB, int32_t bs, float scale,
+                                  const float* k_scale, const float* v_scale, void* stream) {
+  g_err[0] = 0;
+  return decode_impl(out, q, q_dtype, k_pool, v_pool, kv_dtype, block_tables, max_blocks_per_seq, context_lens,
+                     max_context_len, nullptr, nullptr, B, H_q, H_kv, D, NB, bs, scale, k_scale, v_scale, nullptr, 0,
+                     stream, nullptr, nullptr, nullptr, -1, false, true);
 }
 
 int pkv_paged_attn_decode_hinted(float* out, const void* q, int q_dtype, const void* k_pool, const void* v_pool,

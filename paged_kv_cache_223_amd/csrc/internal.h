@@ -56,9 +56,11 @@ struct WorkspaceLayout {
 
 inline size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 
-inline WorkspaceLayout workspace_layout(int B, int H_q, int H_kv, int D, const SplitPlan& p, int num_cus) {
-  const size_t vec_rows = p.max_splits > 1 ? (size_t)B * H_q * p.max_splits : 0;
-  const size_t mfma_rows = ((size_t)num_cus * kMaxGroupsPerCU + (size_t)B * H_kv) * 16;
+// paths: 1 = vector path only, 2 = matrix-core path only, 3 = either (what a caller's workspace covers)
+inline WorkspaceLayout workspace_layout(int B, int H_q, int H_kv, int D, const SplitPlan& p, int num_cus,
+                                        int paths = 3) {
+  const size_t vec_rows = (paths & 1) && p.max_splits > 1 ? (size_t)B * H_q * p.max_splits : 0;
+  const size_t mfma_rows = (paths & 2) ? ((size_t)num_cus * kMaxGroupsPerCU + (size_t)B * H_kv) * 16 : 0;
   const size_t rows = vec_rows > mfma_rows ? vec_rows : mfma_rows;
   WorkspaceLayout w;
   w.o = 0;
@@ -67,8 +69,9 @@ inline WorkspaceLayout workspace_layout(int B, int H_q, int H_kv, int D, const S
   return w;
 }
 
-inline size_t workspace_bytes_for(int B, int H_q, int H_kv, int D, const SplitPlan& p, int num_cus) {
-  return workspace_layout(B, H_q, H_kv, D, p, num_cus).total;
+inline size_t workspace_bytes_for(int B, int H_q, int H_kv, int D, const SplitPlan& p, int num_cus,
+                                  int paths = 3) {
+  return workspace_layout(B, H_q, H_kv, D, p, num_cus, paths).total;
 }
 
 struct DecodeArgs {
@@ -100,6 +103,12 @@ struct DecodeArgs {
   int speculate;           // set by the launcher: the length sum says every length is len_cap, so a
                            // workgroup may load its likely segment's first chunk before its plan
 };
+
+// Scratch of pkv_paged_attn_decode_noalloc: a file-scope device array in paged_decode.hip, one copy
+// per device, holding the decode's partials for callers that cannot allocate.  static_scratch looks
+// up its address on the current device (once per device) and returns it with its size.
+constexpr size_t kStaticScratchBytes = size_t(32) << 20;
+hipError_t static_scratch(void** ptr);
 
 // Kernel launchers (paged_decode.hip).  Return hipError_t of the launch.
 bool decode_fast_path_supported(int q_dtype, int kv_dtype, int G, int D, int bs);

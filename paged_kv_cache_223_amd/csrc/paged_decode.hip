@@ -69,6 +69,7 @@
 
 #include <math.h>
 
+#include <mutex>
 #include <type_traits>
 
 #include "internal.h"
@@ -1015,6 +1016,33 @@ hipError_t launch_mfma_bs(const DecodeArgs& a, hipStream_t s) {
 }
 
 }  // namespace
+
+// Partials of pkv_paged_attn_decode_noalloc (the same layout a caller's workspace holds).  Each
+// device that loads the library holds its own copy until the process ends; every call on a device
+// shares it, so calls that overlap on one device race.  Nothing in it has to start at zero: a call
+// writes every partial it reads.  Host code never passes the array's name to a kernel (on the host
+// it is only a stand-in); it uses the device address static_scratch looked up.
+static __device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
+
+hipError_t static_scratch(void** ptr) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void* addr[kMaxDevices] = {};
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {  // once per device, with that device current
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    addr[dev] = p;
+  }
+  *ptr = addr[dev];
+  return hipSuccess;
+}
 
 hipError_t launch_split_merge(const DecodeArgs& a, hipStream_t s) {
   hipLaunchKernelGGL(split_merge_kernel, dim3((unsigned)(a.B * a.H_kv)), dim3(256), 0, s, a);

@@ -398,3 +398,40 @@ def test_prefill_empty_is_a_no_op():
     assert _prefill(B=0) == pkv.OK
     assert _prefill(T=0) == pkv.OK
 
+
+
+def _decode_noalloc(**kw):
+    a = dict(out=P, q=P, q_dtype=pkv.BF16, k=P, v=P, kv=pkv.BF16, tab=P, mb=4, lens=P, mcl=64, B=2, H_q=8, H_kv=2,
+             D=128, NB=16, bs=16, scale=0.1, ks=None, vs=None, stream=None)
+    a.update(kw)
+    return pkv.lib.pkv_paged_attn_decode_noalloc(a["out"], a["q"], a["q_dtype"], a["k"], a["v"], a["kv"], a["tab"],
+                                                 a["mb"], a["lens"], a["mcl"], a["B"], a["H_q"], a["H_kv"], a["D"],
+                                                 a["NB"], a["bs"], a["scale"], a["ks"], a["vs"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(H_q=6, H_kv=4), pkv.ERR_INVALID_ARG),
+    (dict(D=96), pkv.ERR_UNSUPPORTED),
+    (dict(bs=12), pkv.ERR_UNSUPPORTED),
+    (dict(q=None), pkv.ERR_INVALID_ARG),
+    (dict(kv=pkv.FP8_E4M3), pkv.ERR_INVALID_ARG),  # E4M3 without scales
+    (dict(scale=float("nan")), pkv.ERR_INVALID_ARG),
+    (dict(B=0), pkv.OK),  # nothing to do: no launch, no scratch lookup
+])
+def test_noalloc_decode_checks_arguments_on_the_host(kw, status):
+    assert _decode_noalloc(**kw) == status
+
+
+def test_noalloc_decode_refuses_sizes_beyond_its_scratch():
+    """A batch whose partials need more than the 32 MiB static scratch is refused before any
+    launch, with a message that names the workspace call."""
+    B, H_q, H_kv, D, mcl, bs = 8192, 64, 8, 128, 131072, 16
+    assert pkv.decode_workspace_bytes(B, H_q, D, mcl, bs, H_kv) > 32 << 20
+    assert _decode_noalloc(B=B, H_q=H_q, H_kv=H_kv, D=D, mcl=mcl, bs=bs, mb=mcl // bs, NB=1 << 20) == \
+        pkv.ERR_INVALID_ARG
+    msg = pkv.last_error()
+    assert "static" in msg and "workspace" in msg, msg
+    # matrix-core path only (what the noalloc call sizes for these shapes): the 70B and 128K layers
+    # and the E4M3 mix fit, well inside the limit
+    for B, H_kv in ((32, 8), (4, 8), (256, 8)):
+        assert (256 * 4 + B * H_kv) * 16 * (128 + 2) * 4 + 256 <= 32 << 20
