@@ -33,6 +33,8 @@ METRIC = "paged decode attention KV GB/s (% of HBM peak) and sequences/s per lay
 HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E
 KERNEL_SOURCE = [os.path.join(ROOT, "paged_kv_cache_223_amd", "csrc", f) for f in ("paged_decode.hip", "tile_ops.h", "wave_scan.h")]
 COUNTERS = os.path.join(ROOT, "profiles", "decode_counters.json")
+PREFILL_SOURCE = [os.path.join(ROOT, "paged_kv_cache_223_amd", "csrc", f) for f in ("prefill.hip", "tile_ops.h")]
+PREFILL_COUNTERS = os.path.join(ROOT, "profiles", "prefill_counters.json")
 
 WORKLOADS = {
     "llama70b": ("llama70b_bf16", {}),
@@ -42,6 +44,8 @@ WORKLOADS = {
     "fp8_bs16": ("mixed_fp8", {"bs": 16}),
     "fp8_bs32": ("mixed_fp8", {"bs": 32}),
 }
+# timed after the headline workload by the default invocation
+OTHER_CONFIGS = ("llama8b", "long128k", "fp8_bs8", "fp8_bs16", "fp8_bs32")
 
 
 def parse():
@@ -59,10 +63,11 @@ def parse():
                    help="launch the step's kernels one by one instead of replaying a captured HIP graph")
     p.add_argument("--identity-tables", action="store_true",
                    help="lay every sequence out contiguously (identity block order) instead of scattered")
-    p.add_argument("--op", default="step", choices=["step", "copy_blocks", "swap", "prefill"],
+    p.add_argument("--op", default="step", choices=["step", "copy_blocks", "swap", "prefill", "mixes"],
                    help="step: the decode step (default); copy_blocks: copy-on-write block copies alone; "
                         "swap: swap-out / swap-in of scattered blocks to and from pinned host memory; "
-                        "prefill: causal chunked prefill over the paged pools")
+                        "prefill: causal chunked prefill over the paged pools; mixes: decode call time on "
+                        "seeded length mixes beyond the five workloads")
     p.add_argument("--prior", type=int, default=2048, help="earlier tokens per sequence (--op prefill)")
     p.add_argument("--chunk", type=int, default=2048, help="new tokens per sequence (--op prefill)")
     p.add_argument("--seqs", type=int, default=4, help="sequences (--op prefill)")
@@ -74,6 +79,13 @@ def parse():
     p.add_argument("--no-length-hint", action="store_true",
                    help="do not pass the batch's length sum to the decode call (pkv_decode_step or "
                         "pkv_paged_attn_decode_hinted); the merge is then always launched")
+    p.add_argument("--only", action="store_true",
+                   help="time the named workload only (by default the 70B workload is followed by the other "
+                        "configurations: " + ", ".join(OTHER_CONFIGS) + ", and the tiny fp32 one)")
+    p.add_argument("--extra-steps", type=int, default=100, help="timed steps of each other configuration")
+    p.add_argument("--extra-warmup", type=int, default=10, help="warm-up steps of each other configuration")
+    p.add_argument("--extra-cpu-seconds", type=float, default=4.0,
+                   help="budget of each other configuration's oracle baseline sample")
     p.add_argument("--sets", type=int, default=0,
                    help="independent copies of the inputs the steps rotate through (0 = enough for 1 GB of "
                         "KV, so the 256 MB last-level cache cannot hold the working set)")
@@ -118,15 +130,15 @@ def source_hash(paths):
     return hashlib.sha256(text.encode()).hexdigest()[:16]
 
 
-def measured_traffic(workload):
-    """HBM bytes per decode launch from committed rocprofv3 counter runs, if they were taken
-    on the current kernel source and this workload; else None."""
+def measured_traffic(workload, counters=COUNTERS, sources=KERNEL_SOURCE):
+    """HBM bytes per launch from committed rocprofv3 counter runs, if they were taken on the
+    current kernel source and this workload; else None."""
     try:
-        rec = json.load(open(COUNTERS))
+        rec = json.load(open(counters))
     except (OSError, ValueError):
         return None
     ent = rec.get(workload)
-    if not ent or ent.get("code_sha256_16") != source_hash(KERNEL_SOURCE):
+    if not ent or ent.get("code_sha256_16") != source_hash(sources):
         return None
     return ent.get("hbm_bytes_per_launch")
 
@@ -141,7 +153,6 @@ def main():
     import torch
 
     import paged_kv_cache_223_amd as pkv
-    import workloads
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     dev = "cuda"
@@ -163,9 +174,39 @@ def main():
     if args.op == "prefill":
         bench_prefill(args, torch, pkv, dev)
         return
+    if args.op == "mixes":
+        bench_mixes(args, torch, pkv, dev)
+        return
+    shared = {}  # drawn K/V rows shared by the E4M3 workload's block sizes (the same logical data)
+    res = bench_decode(args.workload, args, torch, pkv, dev, args.steps, args.warmup, args.cpu_seconds,
+                       headline=True, shared=shared)
+    if not args.only and args.workload == "llama70b":
+        # the other configurations, each with its own (shorter) timing and oracle baseline; `value`
+        # and `config` stay on the headline workload
+        res["other_configs"] = {}
+        for w in OTHER_CONFIGS:
+            res["other_configs"][w] = bench_decode(w, args, torch, pkv, dev, args.extra_steps, args.extra_warmup,
+                                                   args.extra_cpu_seconds, headline=False, shared=shared)
+        shared.clear()
+        res["other_configs"]["tiny_f32"] = bench_tiny(args, torch, pkv, dev)
+    print(json.dumps(res), flush=True)
+
+
+def _build_case(wkey, shared):
+    import workloads
+    wname, kw = WORKLOADS[wkey]
+    if wname == "mixed_fp8":
+        kw = dict(kw, stream_cache=shared.setdefault("mixed_fp8", {}))
+    return workloads.BUILDERS[wname](**kw)
+
+
+def bench_decode(wkey, args, torch, pkv, dev, steps, warmup, cpu_seconds, headline, shared):
+    """One decode workload: setup, eager per-call timing, graph-replayed steps, roofline, oracle
+    baseline.  Returns the JSON object (the headline form carries the whole line's keys)."""
+    import workloads
+
     t_setup = time.time()
-    wname, kw = WORKLOADS[args.workload]
-    case = workloads.BUILDERS[wname](**kw)
+    case = _build_case(wkey, shared)
     if args.identity_tables:
         case.initial_free_order = np.arange(case.NB, dtype=np.int32)
     spec = case.spec
@@ -211,8 +252,9 @@ def main():
     for _ in range(n_sets - 1):
         sets.append(tuple(t.clone() for t in sets[0]))
     torch.cuda.synchronize()
-    print(f"# setup {time.time() - t_setup:.1f}s: {wname} B={B} NB={case.NB} pool {2 * k_pool.numel() * k_pool.element_size() / 1e9:.2f} GB"
-          f" x {n_sets} input set(s)", file=sys.stderr, flush=True)
+    print(f"# {wkey}: setup {time.time() - t_setup:.1f}s: {spec.name} B={B} NB={case.NB} pool "
+          f"{2 * k_pool.numel() * k_pool.element_size() / 1e9:.2f} GB x {n_sets} input set(s)", file=sys.stderr,
+          flush=True)
 
     # one new token per sequence into bf16 pools: the step is one fused call (the append runs
     # inside the decode launch); E4M3 pools take kv_append + decode
@@ -238,10 +280,10 @@ def main():
         if e2 is not None:
             e2.record()
 
-    for i in range(args.warmup):
+    for i in range(warmup):
         step(i)
     torch.cuda.synchronize()
-    K = args.steps
+    K = steps
     # decode alone, eager launches: per-call duration of the dominant kernel(s) on the launch stream
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
     for i in range(K):
@@ -259,7 +301,7 @@ def main():
             with torch.cuda.graph(g):
                 step(i)
             graphs.append(g)
-        for i in range(args.warmup):
+        for i in range(warmup):
             graphs[i % n_sets].replay()
     torch.cuda.synchronize()
     g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -271,54 +313,34 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     step_ms = g0.elapsed_time(g1) / K
-    print(f"# timed {K} steps in {wall:.3f}s wall ({'eager' if graphs is None else 'graph'}); eager decode p10/p50/p90 "
-          f"{np.percentile(decode_ms, 10) * 1e3:.1f}/{np.median(decode_ms) * 1e3:.1f}/{np.percentile(decode_ms, 90) * 1e3:.1f} us",
-          file=sys.stderr, flush=True)
+    print(f"# {wkey}: timed {K} steps in {wall:.3f}s wall ({'eager' if graphs is None else 'graph'}); "
+          f"step {step_ms * 1e3:.1f} us; eager decode p10/p50/p90 {np.percentile(decode_ms, 10) * 1e3:.1f}/"
+          f"{np.median(decode_ms) * 1e3:.1f}/{np.percentile(decode_ms, 90) * 1e3:.1f} us", file=sys.stderr, flush=True)
 
     dec_avg_s = decode_ms.mean() / 1e3
     call_bytes = by["decode"] + (by["append"] if fused else 0)  # bytes of the timed call
     dec_gbps = call_bytes / dec_avg_s / 1e9
     step_gbps = (by["decode"] + by["append"]) / (step_ms / 1e3) / 1e9
-
-    # practical read ceiling: the library's non-temporal 16-byte streaming read over 4 GiB
-    buf = torch.empty(4 << 30, dtype=torch.uint8, device=dev)
-    sink = pkv.stream_read(buf)
-    torch.cuda.synchronize()
-    r0, r1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    r0.record()
-    for _ in range(10):
-        pkv.stream_read(buf, sink)
-    r1.record()
-    torch.cuda.synchronize()
-    ceiling = buf.numel() * 10 / (r0.elapsed_time(r1) / 1e3) / 1e9
-    del buf
-
-    res = {
-        "metric": METRIC,
-        "value": round(step_gbps, 1),
-        "unit": "GB/s",
-        "n_gpus": 1,
-        "steps": K,
-        "warmup": args.warmup,
-        "ms_per_step": round(step_ms, 5),
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": spec.kv_dtype,
-        "data": "synthetic (seeded N(0,1) K/V/q rounded to the KV dtype; allocator-scattered block tables)",
-        "config": {
-            "workload": spec.desc, "batch": B, "H_q": H_q, "H_kv": H_kv, "head_dim": D, "block_size": case.bs,
-            "max_context": mcl, "mean_context": float(np.mean(mat.context_lens)), "pool_blocks": case.NB,
-            "append_tokens_per_step": int(len(mat.step_slots)),
-            "tables": "identity" if args.identity_tables else "scattered",
-            "input_sets": n_sets,
-        },
+    traffic = measured_traffic(wkey)
+    roofline = {
+        "bound": "hbm",
+        "kernel": ("decode step call (append fused) = decode_piece_kernel (+ piece_merge_kernel when a segment "
+                   "is cut into pieces)" if fused else
+                   "paged_attn_decode call = decode_piece_kernel (+ piece_merge_kernel when a segment is cut into "
+                   "pieces)"),
+        "achieved": round(dec_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+        "frac": round(dec_gbps / HBM_PEAK_GBPS, 4),
+        "algorithmic_bytes_per_launch": call_bytes,
+        "avg_launch_us": round(dec_avg_s * 1e6, 2),
+        "traffic": traffic,
+    }
+    common = {
         "seqs_per_s": round(B / (step_ms / 1e3), 1),
         "frac_of_hbm_peak": round(step_gbps / HBM_PEAK_GBPS, 4),
         "decode_us_p50": round(float(np.median(decode_ms)) * 1e3, 2),
         "decode_us_p10_p90": [round(float(np.percentile(decode_ms, 10)) * 1e3, 2),
                               round(float(np.percentile(decode_ms, 90)) * 1e3, 2)],
-        "append_us_p50": None if fused else round(float(np.median(append_ms)) * 1e3, 2),
+        "append_us_p50": None if fused or not len(mat.step_slots) else round(float(np.median(append_ms)) * 1e3, 2),
         "step_call": "pkv_decode_step (append fused into the decode launch)" if fused else
                      ("kv_append + paged_attn_decode" if len(mat.step_slots) else "paged_attn_decode") +
                      ("" if sum_lens < 0 else " (with the host's length sum)"),
@@ -328,25 +350,167 @@ def main():
         "decode_GBps_logical": round(by["decode_logical"] / dec_avg_s / 1e9, 1),
         "kv_bytes_unique": by["kv_unique"],
         "kv_bytes_logical": by["kv_logical"],
-        "read_ceiling_GBps": round(ceiling, 1),
-        "frac_of_read_ceiling": round(step_gbps / ceiling, 4),
         "kv_waste": block_waste(mat.block_tables, mat.context_lens, case.bs),
     }
-    traffic = measured_traffic(args.workload)
-    res["roofline"] = {
-        "bound": "hbm",
-        "kernel": ("decode step call (append fused) = decode_piece_kernel (+ piece_merge_kernel when a segment "
-                   "is cut into pieces)" if fused else
-                   "paged_attn_decode call = decode_piece_kernel + piece_merge_kernel"),
-        "achieved": round(dec_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-        "frac": round(dec_gbps / HBM_PEAK_GBPS, 4),
-        "algorithmic_bytes_per_launch": call_bytes,
-        "avg_launch_us": round(dec_avg_s * 1e6, 2),
-        "traffic": traffic,
+    cfg = {
+        "workload": spec.desc, "batch": B, "H_q": H_q, "H_kv": H_kv, "head_dim": D, "block_size": case.bs,
+        "kv_dtype": spec.kv_dtype, "max_context": mcl, "mean_context": float(np.mean(mat.context_lens)),
+        "pool_blocks": case.NB, "append_tokens_per_step": int(len(mat.step_slots)),
+        "tables": "identity" if args.identity_tables else "scattered", "input_sets": n_sets,
     }
+    if headline:
+        # practical read ceiling: the library's non-temporal 16-byte streaming read over 4 GiB
+        buf = torch.empty(4 << 30, dtype=torch.uint8, device=dev)
+        sink = pkv.stream_read(buf)
+        torch.cuda.synchronize()
+        r0, r1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        r0.record()
+        for _ in range(10):
+            pkv.stream_read(buf, sink)
+        r1.record()
+        torch.cuda.synchronize()
+        ceiling = buf.numel() * 10 / (r0.elapsed_time(r1) / 1e3) / 1e9
+        del buf
+        res = {
+            "metric": METRIC, "value": round(step_gbps, 1), "unit": "GB/s", "n_gpus": 1, "steps": K,
+            "warmup": warmup, "ms_per_step": round(step_ms, 5), "higher_is_better": True, "scaling": "weak",
+            "vs_baseline": None, "dtype": spec.kv_dtype,
+            "data": "synthetic (seeded N(0,1) K/V/q rounded to the KV dtype; allocator-scattered block tables)",
+            "config": cfg, **common,
+            "read_ceiling_GBps": round(ceiling, 1), "frac_of_read_ceiling": round(step_gbps / ceiling, 4),
+            "roofline": roofline,
+        }
+    else:
+        res = {"config": cfg, "steps": K, "warmup": warmup, "step_us": round(step_ms * 1e3, 2),
+               "value_GBps": round(step_gbps, 1), **common, "roofline": roofline}
     if not args.no_cpu_baseline:
-        res["cpu_baseline"] = cpu_baseline(case, mat, out, args.cpu_seconds, by, B)
-    print(json.dumps(res), flush=True)
+        sample = 1 if wkey == "long128k" else 16  # a 131072-token sequence takes seconds in the oracle
+        res["cpu_baseline"] = cpu_baseline(case, mat, out, cpu_seconds, by, B, max_sample=sample)
+        if wkey in ("llama70b", "llama8b"):  # the oracle on one host thread as well
+            res["cpu_baseline_1thread"] = cpu_baseline(case, mat, out, min(cpu_seconds, 6.0), by, B, threads=1)
+    del sets, k_pool, v_pool, out, ws
+    torch.cuda.empty_cache()
+    return res
+
+
+def bench_tiny(args, torch, pkv, dev):
+    """The tiny fp32 workload (4 sequences, lengths 1/17/33/64): launch-bound, so reported for
+    completeness: GPU call time, and the oracle on the host with all its BLAS threads and with one,
+    checked against the GPU output."""
+    import oracle
+    import workloads
+    from threadpoolctl import threadpool_limits
+
+    case = workloads.tiny_f32()
+    spec = case.spec
+    mat = workloads.materialize(case, pkv.Allocator(case.NB, case.bs, case.initial_free_order))
+    ks, vs = pkv.pool_shapes(case.NB, spec.H_kv, spec.d, case.bs, pkv.F32)
+    kp0 = workloads.initial_pool_fill(case, "k", ks)
+    vp0 = workloads.initial_pool_fill(case, "v", vs)
+    kp, vp = torch.from_numpy(kp0).to(dev), torch.from_numpy(vp0).to(dev)
+    pkv.kv_append(torch.from_numpy(mat.k_src).to(dev), torch.from_numpy(mat.v_src).to(dev),
+                  torch.from_numpy(mat.slots).to(dev), kp, vp)
+    q, tab, ln = (torch.from_numpy(x).to(dev) for x in (case.q, mat.block_tables, mat.context_lens))
+    out = torch.empty((case.B, spec.H_q, spec.d), dtype=torch.float32, device=dev)
+
+    def call():
+        pkv.paged_attn_decode(q, kp, vp, tab, ln, float(case.scale), max_context_len=case.max_context_len, out=out)
+
+    for _ in range(20):
+        call()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(200)]
+    for e0, e1 in ev:
+        e0.record()
+        call()
+        e1.record()
+    torch.cuda.synchronize()
+    ms = np.array([e0.elapsed_time(e1) for e0, e1 in ev])
+    got = out.cpu().numpy().astype(np.float64)
+    kr, vr = oracle.ref_append(kp0, vp0, mat.k_src, mat.v_src, "f32", mat.slots, case.bs, "f32")
+    res = {"config": {"workload": spec.desc, "batch": case.B}, "decode_us_p50": round(float(np.median(ms)) * 1e3, 2),
+           "seqs_per_s": round(case.B / (np.median(ms) / 1e3), 1),
+           "kv_bytes": int(mat.context_lens.sum()) * spec.H_kv * spec.d * 2 * 4}
+    for label, threads in (("cpu_baseline", None), ("cpu_baseline_1thread", 1)):
+        with threadpool_limits(threads):
+            n, t0 = 0, time.perf_counter()
+            while time.perf_counter() - t0 < 1.0:
+                ref = oracle.ref_decode(case.q, "f32", kr, vr, "f32", mat.block_tables, mat.context_lens, case.scale,
+                                        case.bs)
+                n += 1
+            dt = time.perf_counter() - t0
+        err = float((np.abs(got - ref).max(-1) / np.abs(ref).max(-1)).max())
+        res[label] = {"value": round(n * case.B / dt, 1), "unit": "sequences/s", "cores": _blas_threads(),
+                      "kind": "oracle", "sample": f"{n} passes over all {case.B} sequences",
+                      "seconds": round(dt, 2), "gpu_vs_oracle_max_row_rel_err": err}
+        if threads == 1:
+            res[label]["cores"] = 1
+    print(f"# tiny_f32: decode p50 {res['decode_us_p50']} us", file=sys.stderr, flush=True)
+    return res
+
+
+def bench_mixes(args, torch, pkv, dev):
+    """Decode call time on seeded length mixes beyond the five workloads (workloads.length_mix):
+    random pools, scattered tables, decode call p50 over 60 eager calls after 10 warm-up calls,
+    no length hint.  One JSON line with every batch's p50."""
+    import workloads
+    cases = [("u4k", s, "bf16") for s in (11, 12, 13, 14)] + [("u8k", 15, "bf16"), ("mix", 16, "bf16")] + \
+        [("mix", s, "e4m3") for s in (17, 18, 19)] + [("uni", 20, "e4m3"), ("uni", 21, "bf16")]
+    H_q, H_kv, D, bs = 32, 8, 128, 16
+    rows = []
+    for kind, seed, kv in cases:
+        lens = workloads.length_mix(kind, seed)
+        B = len(lens)
+        nblk = (lens.astype(np.int64) + bs - 1) // bs
+        NB = int(nblk.sum()) + 8
+        perm = np.random.default_rng(seed).permutation(NB).astype(np.int32)
+        tab = np.full((B, int(nblk.max())), -1, np.int32)
+        o = 0
+        for b in range(B):
+            tab[b, :nblk[b]] = perm[o:o + nblk[b]]
+            o += nblk[b]
+        kvd = pkv.BF16 if kv == "bf16" else pkv.FP8_E4M3
+        ks, vs = pkv.pool_shapes(NB, H_kv, D, bs, kvd)
+        g = torch.Generator(device=dev).manual_seed(seed)
+        if kv == "bf16":
+            kp = torch.randn(ks, device=dev, generator=g).to(torch.bfloat16)
+            vp = torch.randn(vs, device=dev, generator=g).to(torch.bfloat16)
+            ksc = vsc = None
+        else:
+            kp = torch.randint(0, 120, ks, dtype=torch.uint8, device=dev, generator=g)
+            vp = torch.randint(0, 120, vs, dtype=torch.uint8, device=dev, generator=g)
+            ksc = torch.full((H_kv,), 0.01, device=dev)
+            vsc = torch.full((H_kv,), 0.01, device=dev)
+        q = torch.randn((B, H_q, D), device=dev, generator=g).to(torch.bfloat16)
+        tabd, lensd = torch.from_numpy(tab).to(dev), torch.from_numpy(lens).to(dev)
+        out = torch.empty((B, H_q, D), device=dev)
+        mcl = int(lens.max())
+        ws = pkv.decode_workspace(B, H_q, D, mcl, bs, H_kv=H_kv, device=dev)
+
+        def call():
+            pkv.paged_attn_decode(q, kp, vp, tabd, lensd, 1 / math.sqrt(D), ksc, vsc, max_context_len=mcl, out=out,
+                                  workspace=ws)
+
+        for _ in range(10):
+            call()
+        torch.cuda.synchronize()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(60)]
+        for e0, e1 in ev:
+            e0.record()
+            call()
+            e1.record()
+        torch.cuda.synchronize()
+        us = float(np.median([e0.elapsed_time(e1) * 1e3 for e0, e1 in ev]))
+        kv_bytes = int(lens.astype(np.int64).sum()) * H_kv * D * 2 * (2 if kv == "bf16" else 1)
+        rows.append({"batch": f"{kind}-{seed}-{kv}", "B": B, "decode_us_p50": round(us, 1),
+                     "kv_GBps": round(kv_bytes / us / 1e3, 1)})
+        print(f"# mix {rows[-1]}", file=sys.stderr, flush=True)
+        del kp, vp, ws
+        torch.cuda.empty_cache()
+    print(json.dumps({"metric": "decode call p50 on seeded length mixes", "unit": "us", "n_gpus": 1,
+                      "config": {"workload": "seeded length mixes (workloads.length_mix)", "H_q": H_q, "H_kv": H_kv,
+                                 "head_dim": D, "block_size": bs},
+                      "batches": rows}), flush=True)
 
 
 def block_waste(tables, lens, bs):
@@ -514,7 +678,7 @@ def bench_prefill(args, torch, pkv, dev):
     for _ in range(args.warmup):
         call()
     torch.cuda.synchronize()
-    K = max(args.steps // 10, 5)
+    K = args.steps
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
     for e0, e1 in ev:
         e0.record()
@@ -526,7 +690,9 @@ def bench_prefill(args, torch, pkv, dev):
     kv_bytes = B * n * H_kv * D * 2 * (1 if fp8 else 2)
     avg_s = ms.mean() / 1e3
     tf = flops / avg_s / 1e12
-    print(json.dumps({
+    print(f"# prefill: {K} timed calls, average {avg_s * 1e6:.1f} us, {tf:.1f} TFLOP/s", file=sys.stderr, flush=True)
+    wkey = f"prefill_{args.prefill_kv}_{B}x{prior}+{C}"
+    res = {
         "metric": "paged prefill TFLOP/s (causal, bf16 MFMA)", "value": round(tf, 1), "unit": "TFLOP/s",
         "n_gpus": 1, "steps": K, "warmup": args.warmup, "ms_per_step": round(float(ms.mean()), 4),
         "higher_is_better": True, "dtype": "bf16", "data": "synthetic (N(0,1) K/V/q, allocator-scattered tables)",
@@ -534,18 +700,76 @@ def bench_prefill(args, torch, pkv, dev):
                                f"(H_q 64, H_kv 8, D 128, bs 16), {args.prefill_kv} KV", "seqs": B, "prior": prior,
                    "chunk": C, "kv": args.prefill_kv},
         "us_p50": round(float(np.median(ms)) * 1e3, 1), "flops_per_call": flops,
-        "roofline": {"bound": "mfma", "achieved": round(tf, 1), "peak": 2500.0, "unit": "TFLOP/s",
-                     "frac": round(tf / 2500.0, 4), "traffic": None},
-        "kv_bytes": kv_bytes, "kv_GBps": round(kv_bytes / avg_s / 1e9, 1)}), flush=True)
+        "roofline": {"bound": "mfma", "kernel": "prefill_kernel", "achieved": round(tf, 1), "peak": 2500.0,
+                     "unit": "TFLOP/s", "frac": round(tf / 2500.0, 4), "avg_launch_us": round(avg_s * 1e6, 2),
+                     "traffic": measured_traffic(wkey, PREFILL_COUNTERS, PREFILL_SOURCE),
+                     "algorithmic_bytes_per_launch": kv_bytes + B * C * H_q * D * (2 + 4) + B * 4 * 2},
+        "kv_bytes": kv_bytes, "kv_GBps": round(kv_bytes / avg_s / 1e9, 1)}
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = prefill_cpu_baseline(torch, k_pool, v_pool, q, out, tab, lens, qs, scale, bs, fp8,
+                                                   k_scale, v_scale, prior, C, B, args.cpu_seconds)
+    print(json.dumps(res), flush=True)
 
 
-def cpu_baseline(case, mat, out_dev, budget_s, by, B):
-    """The oracle (numpy fp64 gather-then-attend) on a bounded sample of the same batch."""
+def prefill_cpu_baseline(torch, k_pool, v_pool, q, out, tab, lens, qs, scale, bs, fp8, k_scale, v_scale, prior, C,
+                         B, budget_s):
+    """The oracle's causal prefill (numpy fp64) on sampled query rows of the same call, until the
+    budget is spent; TFLOP/s counts the sampled rows' causal FLOPs, and the GPU's rows are checked
+    against it."""
+    import oracle
+    kvt = "e4m3" if fp8 else "bf16"
+
+    def host(t):
+        return t.cpu().numpy() if fp8 else t.view(torch.int16).cpu().numpy().view(np.uint16)
+
+    kp, vp = host(k_pool), host(v_pool)
+    qh = q.view(torch.int16).cpu().numpy().view(np.uint16)
+    got = out.cpu().numpy().astype(np.float64)
+    ks = None if k_scale is None else k_scale.cpu().numpy()
+    vs = None if v_scale is None else v_scale.cpu().numpy()
+    qs_h = qs.cpu().numpy()
+    H_q, D = q.shape[1], q.shape[2]
+    rng = np.random.default_rng(23)
+    rows, errs, flops = [], [], 0.0
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < budget_s:
+        b = int(rng.integers(B))
+        r = int(qs_h[b]) + int(rng.integers(C))
+        ref = oracle.ref_prefill(qh, "bf16", kp, vp, kvt, tab, lens, qs_h, scale, bs, ks, vs, seqs=[b], rows=[r])
+        rows.append(r)
+        flops += 4.0 * H_q * D * (prior + (r - int(qs_h[b])) + 1)
+        errs.append(float((np.abs(got[r] - ref[r]).max(-1) / np.abs(ref[r]).max(-1)).max()))
+    dt = time.perf_counter() - t0
+    return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": _blas_threads(), "kind": "oracle",
+            "sample": f"{len(rows)} query rows (all heads) drawn at random from the call, numpy fp64 gather-then-"
+                      "attend over each row's causal range",
+            "query_rows_per_s": round(len(rows) / dt, 2), "seconds": round(dt, 2), "host_cpus": os.cpu_count(),
+            "affinity_cpus": len(os.sched_getaffinity(0)), "gpu_vs_oracle_max_row_rel_err": float(max(errs))}
+
+
+def _blas_threads():
+    try:
+        from threadpoolctl import threadpool_info
+        return max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
+    except Exception:  # threadpoolctl missing: report the process's CPU affinity
+        return len(os.sched_getaffinity(0))
+
+
+def cpu_baseline(case, mat, out_dev, budget_s, by, B, threads=None, max_sample=16):
+    """The oracle (numpy fp64 gather-then-attend) on a bounded sample of the same batch (with
+    `threads` BLAS threads, else as many as numpy takes): passes over up to `max_sample`
+    sequences spread over the batch until `budget_s` seconds are spent."""
+    if threads is not None:
+        from threadpoolctl import threadpool_limits
+        with threadpool_limits(threads):
+            r = cpu_baseline(case, mat, out_dev, budget_s, by, B, max_sample=max_sample)
+        r["cores"] = threads
+        return r
     import oracle
 
     spec = case.spec
     sd = "f32" if spec.kv_dtype == "f32" else "bf16"
-    sample = list(range(0, B, max(1, B // 16)))[:16]  # up to 16 sequences spread over the batch
+    sample = list(range(0, B, max(1, B // max_sample)))[:max_sample]
     used = set()
     for b in sample:
         used.update(int(x) for x in mat.block_tables[b, :-(-int(mat.context_lens[b]) // case.bs)])
@@ -571,11 +795,7 @@ def cpu_baseline(case, mat, out_dev, budget_s, by, B):
     dt = time.perf_counter() - t0
     toks = int(sum(int(mat.context_lens[b]) for b in rows))
     kv = toks * spec.H_kv * spec.d * 2 * {"bf16": 2, "e4m3": 1, "f32": 4}[spec.kv_dtype]
-    try:
-        from threadpoolctl import threadpool_info
-        blas = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
-    except Exception:  # threadpoolctl missing: report the process's CPU affinity
-        blas = len(os.sched_getaffinity(0))
+    blas = _blas_threads()
     return {
         "value": round(len(rows) / dt, 3), "unit": "sequences/s", "cores": int(blas), "kind": "oracle",
         "sample": f"{len(rows)} sequence decodes drawn from {len(sample)} of the {B} sequences ({toks} tokens, "

@@ -250,10 +250,11 @@ def _mixed_lengths(rng, B, max_prompt=16384):
     return (prompt + decode).astype(np.int64).tolist()
 
 
-def mixed_fp8(bs=16, B=None, churn_ops=4096, max_prompt=16384, fill="noise"):
+def mixed_fp8(bs=16, B=None, churn_ops=4096, max_prompt=16384, fill="noise", stream_cache=None):
     """Workload 5: e4m3 KV with per-KV-head scales; mixed lengths; the measured batch is
     allocated from a free list scrambled by seeded alloc/free churn.  Token contents are
-    drawn per logical token, so bs 8 / 16 / 32 see the same data."""
+    drawn per logical token, so bs 8 / 16 / 32 see the same data: cases of several block sizes
+    may share one `stream_cache` dict (the drawn rows are then kept, not drawn again)."""
     spec = SPECS["mixed_fp8"]
     B = spec.B if B is None else B
     lens = _mixed_lengths(_rng(spec.seed, _LEN), B, max_prompt)
@@ -269,6 +270,8 @@ def mixed_fp8(bs=16, B=None, churn_ops=4096, max_prompt=16384, fill="noise"):
     case = Case(spec=spec, bs=bs, B=B, NB=NB, initial_free_order=order, ops=ops, step_ops=[],
                 seqs=seqs, context_lens=np.asarray(lens, np.int32), streams=streams, seq_sources=sources,
                 q=_gen_q(spec, B), scale=np.float32(1.0 / math.sqrt(spec.d)), fill=fill)
+    if stream_cache is not None:
+        case._stream_cache = stream_cache
     # per-KV-head scales amax/448 over the fp32 values of the stored bf16 samples
     amax_k = np.zeros(spec.H_kv, np.float32)
     amax_v = np.zeros(spec.H_kv, np.float32)
@@ -278,8 +281,31 @@ def mixed_fp8(bs=16, B=None, churn_ops=4096, max_prompt=16384, fill="noise"):
         amax_v = np.maximum(amax_v, np.abs(bf16_bits_as_f32(v)).max(axis=(0, 2)))
     case.k_scale = (amax_k / np.float32(448.0)).astype(np.float32)
     case.v_scale = (amax_v / np.float32(448.0)).astype(np.float32)
-    case._stream_cache.clear()
+    if stream_cache is None:
+        case._stream_cache.clear()
     return case
+
+
+def length_mix(kind: str, seed: int) -> np.ndarray:
+    """Seeded context lengths of extra batches for timing the decode's work split on length
+    mixes other than the five workloads' (int32 [B]):
+      u4k   64 sequences, uniform on [128, 4096]
+      u8k   48 sequences, uniform on [1, 8192]
+      mix   256 sequences, log-normal prompt (median 512, sigma 1, at most 16384) + geometric
+            decode (mean 415), the E4M3 workload's distribution
+      uni   32 sequences of 8192 tokens (the seed only places the blocks)"""
+    rng = _rng(seed, _LEN)
+    if kind == "u4k":
+        lens = rng.integers(128, 4097, size=64)
+    elif kind == "u8k":
+        lens = rng.integers(1, 8193, size=48)
+    elif kind == "mix":
+        lens = np.asarray(_mixed_lengths(rng, 256))
+    elif kind == "uni":
+        lens = np.full(32, 8192)
+    else:
+        raise ValueError(kind)
+    return np.asarray(lens, np.int32)
 
 
 def bf16_bits_as_f32(bits: np.ndarray) -> np.ndarray:
