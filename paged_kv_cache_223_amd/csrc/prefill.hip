@@ -7,22 +7,32 @@
 // same block table the decode walks.  Query i of the C_b new tokens of
 // sequence b sits at position p = n_b - C_b + i and attends positions 0..p.
 //
-// Tiles.  An MFMA column tile is 16 (query token, head) pairs of one KV head g:
-// 16 / G consecutive query tokens times the G query heads that share g.  The
-// QK^T and PV steps are the decode's (S^T = K Q^T, P split into bf16 hi + lo,
-// P regrouped across lane groups, O += P V); only the mask differs: column
-// (token at p, head) keeps key t iff t <= p.
+// Tiles.  A wave owns 32 columns: 32 (query token, head) pairs of one KV head
+// g, i.e. 32 / G consecutive query tokens times the G query heads sharing g.
+// Per 32-key chunk it runs, on v_mfma_f32_32x32x16_bf16,
+//     S^T[32 keys][32 cols] = K[32 keys][D] . Q^T[D][32 cols]        (D/16 MFMAs)
+//     O^T[D][32 cols]     += V^T[D][32 keys] . P^T[32 keys][32 cols] (2 D/16 MFMAs)
+// With keys as the rows of S^T and columns in lanes, a lane holds 16 scores of
+// one column: the chunk maximum is 15 maxima in the lane and one exchange with
+// lane l ^ 32, and the accumulator rows a lane holds in O^T belong to the same
+// column, so the online-softmax rescale is lane-local.  P keeps about 16 bits
+// as bf16 hi + lo parts (two MFMAs each); a single bf16 P exceeds a 2e-3
+// relative row error on short contexts.  Each P part is regrouped with four
+// v_permlane32_swap so that lane group h holds keys 8h .. 8h+7 of each 16-key
+// half, which V^T's operand (8 consecutive keys of one head-dim row) matches.
 //
-// Workgroups.  NW waves with R column tiles each cover NW * R * 16 / G
-// consecutive query tokens of one (sequence, KV head); every K and V operand
-// a wave reads from LDS serves its R tiles.  They share every 32-token K/V
-// chunk through LDS: the workgroup copies the chunk's pool tiles (bytes as in
-// the pool) into one LDS buffer while the waves compute the previous chunk from
-// the other, with the chunk after that already loading into registers, so
-// each chunk crosses the L2 once per workgroup, not once per wave.  Work
-// items are dealt to the 8 XCDs so that the workgroups of one (sequence, KV
-// head) share one XCD's L2, and the latest (longest) tiles of a sequence are
-// dispatched first.
+// Workgroups.  NW = 12 waves (three per SIMD at about 165 VGPRs) cover
+// NW * 32 / G consecutive query tokens of one (sequence, KV head); measured on
+// the 70B layer shape, 12 waves beat 8 and 4, and a software-pipelined loop
+// (the next chunk's QK^T under this chunk's softmax) lost for want of
+// registers.  They share every 32-key K/V chunk through LDS: the
+// workgroup copies the chunk's pool tiles into one of two LDS buffers while
+// the waves compute the previous chunk from the other, with the chunk after
+// that already loading into registers.  The LDS copy is laid out for the
+// operand reads, without bank conflicts: K as [D/8][32 keys][8 elements]
+// (E4M3: [D/8][32 keys][8 bytes]), V as [D][32 keys] rows padded to 80 bytes
+// (E4M3: 40).  Work items are dealt to the 8 XCDs so that the workgroups of
+// one (sequence, KV head) share one XCD's L2, latest (longest) tiles first.
 
 #include <hip/hip_runtime.h>
 
@@ -36,30 +46,46 @@
 namespace pkv {
 namespace {
 
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ f32x16 mfma32(u32x4 a, u32x4 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c,
+                                                 0, 0, 0);
+}
+
+// two fp32 -> packed bf16 pair, round to nearest even (v_cvt_pk_bf16_f32); x in the low half
+__device__ __forceinline__ uint32_t pack_bf16_rne(float x, float y) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2{x, y}), bf16x2));
+}
+
 constexpr int kStages = 2;  // the chunk being computed and the next one, written at the iteration's start
 
+// One 32-key chunk in LDS.
 template <int D, int BS, int KVT>
 struct Stage {
   static constexpr int S = KvTraits<KVT>::kBytes;
-  static constexpr int NBCH = BS >= 32 ? 1 : 32 / BS;  // blocks of one 32-token chunk
-  static constexpr int kTile = D * BS * S;             // one block's tile of one head (K or V)
-  static constexpr int kBytes = 2 * NBCH * kTile;      // the chunk in LDS: K tiles, then V tiles
-  static constexpr int kUnits = kBytes / 16;
+  static constexpr int NBCH = BS >= 32 ? 1 : 32 / BS;  // blocks of one chunk
+  static constexpr int kTile = D * BS * S;             // one block's tile of one head (K or V) in the pool
+  static constexpr int kKBytes = 32 * D * S;           // K: [D/8][32][8 elements]
+  static constexpr int kVRow = 32 * S + (S == 2 ? 16 : 8);  // V row of 32 keys, padded (bank spread)
+  static constexpr int kBytes = kKBytes + D * kVRow;
+  static constexpr int kUnits = 2 * NBCH * kTile / 16;  // 16-byte pool units of the chunk (K then V)
 };
 
-// Copy one chunk's tiles (global -> registers); the workgroup's threads take
-// 16-byte units round-robin.  Blocks past the sequence's last block read the
-// last block again (masked later), so every access stays inside the pool.
+// Copies one chunk's pool tiles (global -> registers -> LDS); the workgroup's threads take
+// 16-byte units round-robin.  Blocks past the sequence's last block read the last block again
+// (masked later), so every access stays inside the pool.
 template <int D, int BS, int KVT, int NT>
 struct Stager {
   using St = Stage<D, BS, KVT>;
   static constexpr int kPer = (St::kUnits + NT - 1) / NT;
+  static constexpr int tileU = St::kTile / 16;
   u32x4 r[kPer];
 
   __device__ __forceinline__ void load(const char* __restrict__ kpool, const char* __restrict__ vpool,
-                                       const int32_t* __restrict__ tab, int chunk, int last_blk, int NB,
-                                       int H_kv, int g, int tid) {
-    constexpr int tileU = St::kTile / 16;
+                                       const int32_t* __restrict__ tab, int chunk, int last_blk, int NB, int H_kv,
+                                       int g, int tid) {
     const size_t bstride = (size_t)H_kv * St::kTile;
 #pragma unroll
     for (int k = 0; k < kPer; ++k) {
@@ -67,8 +93,7 @@ struct Stager {
       if (St::kUnits % NT == 0 || u < St::kUnits) {
         const int part = u / (St::NBCH * tileU);  // 0 = K, 1 = V
         const int w = u % (St::NBCH * tileU);
-        const int i = w / tileU;
-        const int id = block_id(tab, chunk * 32 / BS + i, last_blk, NB);
+        const int id = block_id(tab, chunk * 32 / BS + w / tileU, last_blk, NB);
         const char* src = (part == 0 ? kpool : vpool) + (size_t)id * bstride + (size_t)g * St::kTile +
                           (size_t)(w % tileU) * 16;
         r[k] = *(const u32x4*)src;
@@ -76,192 +101,194 @@ struct Stager {
     }
   }
 
-  // Copy into LDS.  nvalid = tokens of the chunk before the sequence's end: on
-  // the chunk holding the end (nvalid < 32, uniform) the V elements of later
-  // tokens are zeroed, since a P of 0 does not cancel whatever the pool holds
-  // there (K needs nothing: masked scores are selected, not multiplied).
+  // Into the LDS layout.  nvalid = keys of the chunk before the sequence's end: on the chunk
+  // holding the end (nvalid < 32) V elements of later keys are zeroed, since a P of 0 does not
+  // cancel whatever the pool holds there (K needs nothing: masked scores are selected, not
+  // multiplied).
   __device__ __forceinline__ void store(char* lds, int tid, int nvalid) const {
-    constexpr int tileU = St::kTile / 16;
-    constexpr int E = 16 / St::S;  // elements per 16-byte unit
-    static_assert(St::S <= 2, "prefill pools hold bf16 or E4M3");
+    constexpr int S = St::S;
+    constexpr int E = 16 / S;  // elements per 16-byte unit
 #pragma unroll
     for (int k = 0; k < kPer; ++k) {
       const int u = tid + k * NT;
-      if (St::kUnits % NT == 0 || u < St::kUnits) {
-        u32x4 v = r[k];
-        if (nvalid < 32 && u >= St::NBCH * tileU) {  // a V unit of the chunk holding the end
-          const int w = u - St::NBCH * tileU;
-          const int tok0 = (w / tileU) * BS, e0 = (w % tileU) * E;  // tile [D][BS]: element e is token e % BS
-#pragma unroll
-          for (int j = 0; j < E; ++j)
-            if (tok0 + (e0 + j) % BS >= nvalid) v[j * St::S / 4] &= ~(((1u << (8 * St::S)) - 1u) << (8 * ((j * St::S) % 4)));
+      if (!(St::kUnits % NT == 0 || u < St::kUnits)) continue;
+      u32x4 v = r[k];
+      const int part = u / (St::NBCH * tileU);
+      const int w = u % (St::NBCH * tileU);
+      const int blk = w / tileU, e0 = (w % tileU) * E;  // first element of the unit inside the block's tile
+      if (part == 0) {
+        // pool K tile [D/E][BS][E]: unit (dg, t) holds E dims of key blk * BS + t
+        const int dg = e0 / (BS * E), t = (e0 / E) % BS, key = blk * BS + t;
+        if constexpr (S == 2) {
+          *(u32x4*)(lds + ((size_t)dg * 32 + key) * 16) = v;
+        } else {  // 16 dims -> planes 2 dg (low 8) and 2 dg + 1 (high 8) of [D/8][32][8 bytes]
+          *(u32x2*)(lds + ((size_t)(2 * dg) * 32 + key) * 8) = u32x2{v.x, v.y};
+          *(u32x2*)(lds + ((size_t)(2 * dg + 1) * 32 + key) * 8) = u32x2{v.z, v.w};
         }
-        *(u32x4*)(lds + (size_t)u * 16) = v;
+      } else {
+        // pool V tile [D][BS]: unit holds E consecutive elements starting at (d, t0)
+        char* vb = lds + St::kKBytes;
+        if (nvalid < 32) {
+#pragma unroll
+          for (int j = 0; j < E; ++j) {
+            const int key = blk * BS + (e0 + j) % BS;
+            if (key >= nvalid) v[j * S / 4] &= ~(((1u << (8 * S)) - 1u) << (8 * ((j * S) % 4)));
+          }
+        }
+        if constexpr (S == 2) {
+          if constexpr (BS >= 8) {  // a unit is 8 keys of one row
+            const int d = e0 / BS, t0 = e0 % BS;
+            *(u32x4*)(vb + (size_t)d * St::kVRow + (size_t)(blk * BS + t0) * 2) = v;
+          }
+        } else {
+          if constexpr (BS == 8) {  // a unit is two rows of 8 keys
+            const int d = e0 / 8;
+            *(u32x2*)(vb + (size_t)d * St::kVRow + (size_t)blk * 8) = u32x2{v.x, v.y};
+            *(u32x2*)(vb + (size_t)(d + 1) * St::kVRow + (size_t)blk * 8) = u32x2{v.z, v.w};
+          } else {  // 16 keys of one row
+            const int d = e0 / BS, t0 = e0 % BS;
+            char* p = vb + (size_t)d * St::kVRow + (size_t)(blk * BS + t0);
+            *(u32x2*)p = u32x2{v.x, v.y};
+            *(u32x2*)(p + 8) = u32x2{v.z, v.w};
+          }
+        }
       }
     }
   }
 };
 
-// online softmax update of one column tile (S^T already computed): rescales
-// acc when the running maximum moves and returns P as bf16 hi + lo operands.
-// sl >= 0 (a negative scale is folded into the sign of q).  The causal mask
-// is applied only on chunks that reach past some column's position (diag,
-// wave-uniform, marked unlikely so that the compiler branches around it
-// rather than computing both forms): masked keys are left out of the maximum
-// and their P is selected to 0 after the exponential, which also holds for
-// sl = 0 and for whatever the pool holds past the sequence's end.
-template <int D>
-__device__ __forceinline__ void softmax_p(const f32x4 (&s)[2], f32x4 (&acc)[D / 16], float& m, float& l, int cs,
-                                          int p_lane, bool diag, float sl, int lane, u32x4& ph, u32x4& pl) {
-  const int kg = lane >> 4;
-  float cm = -INFINITY;
-  if (__builtin_expect(diag, 0)) {
-#pragma unroll
-    for (int a = 0; a < 2; ++a)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) cm = fmaxf(cm, cs + 16 * a + 4 * kg + i <= p_lane ? s[a][i] : -INFINITY);
-  } else {
-#pragma unroll
-    for (int a = 0; a < 2; ++a)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) cm = fmaxf(cm, s[a][i]);
-  }
-  cm = max_over_groups(cm) * sl;  // the chunk's scaled maximum of the column (log2 units)
-  const bool need = cm > m + kRescaleLog2;
-  if (__ballot(need)) {
-    const float mu = need ? cm : m;
-    const float alpha = exp2_fast(m - mu);
-    l *= alpha;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float ai = __shfl(alpha, 4 * kg + i, 64);
-#pragma unroll
-      for (int t = 0; t < D / 16; ++t) acc[t][i] *= ai;
-    }
-    m = mu;
-  }
-  float p[8];
-#pragma unroll
-  for (int a = 0; a < 2; ++a)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) p[4 * a + i] = exp2_fast(fmaf(s[a][i], sl, -m));  // key 0 is in every column's range: m is finite
-  if (__builtin_expect(diag, 0)) {
-#pragma unroll
-    for (int a = 0; a < 2; ++a)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) p[4 * a + i] = cs + 16 * a + 4 * kg + i <= p_lane ? p[4 * a + i] : 0.f;
-  }
-  l += ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
-  uint32_t hb[8];
-  float lo[8];
-#pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const uint32_t bits = __builtin_bit_cast(uint32_t, p[j]);
-    hb[j] = bits;
-    lo[j] = p[j] - __builtin_bit_cast(float, bits & 0xFFFF0000u);
-  }
-#pragma unroll
-  for (int w = 0; w < 4; ++w) {
-    ph[w] = __builtin_amdgcn_perm(hb[2 * w + 1], hb[2 * w], 0x07060302u);
-    pl[w] = __builtin_amdgcn_perm(__builtin_bit_cast(uint32_t, lo[2 * w + 1]),
-                                  __builtin_bit_cast(uint32_t, lo[2 * w]), 0x07060302u);
-  }
-  ph = tokens_by_eight(ph);
-  pl = tokens_by_eight(pl);
-}
-
-// O += P V over one staged chunk for R tiles: each V operand (8 consecutive
-// tokens of one column per lane) is read once from LDS for all tiles.
-template <int D, int BS, int KVT, int R>
-__device__ __forceinline__ void pv_chunk(const char* vb, const u32x4 (&ph)[R], const u32x4 (&pl)[R],
-                                         f32x4 (&acc)[R][D / 16]) {
-  using St = Stage<D, BS, KVT>;
-  constexpr int S = St::S;
-#pragma unroll
-  for (int t = 0; t < D / 16; ++t) {
-    u32x4 vop;
-    if constexpr (KVT == PKV_BF16) {
-      vop = *(const u32x4*)(vb + (size_t)t * 16 * BS * S);
-    } else {
-      const u32x2 w = *(const u32x2*)(vb + (size_t)t * 16 * BS * S);
-      vop = e4m3x8_to_bf16x8(w.x, w.y);
-    }
-#pragma unroll
-    for (int r = 0; r < R; ++r) {
-      acc[r][t] = mfma16x16x32(ph[r], vop, acc[r][t]);
-      acc[r][t] = mfma16x16x32(pl[r], vop, acc[r][t]);
-    }
-  }
-}
-
-// one wave's R column tiles over one staged chunk: every K and V operand read
-// from LDS serves all R tiles
-template <int D, int BS, int KVT, int R>
-__device__ __forceinline__ void prefill_chunk(const char* lds, const u32x4 (&qop)[R][D / 32],
-                                              f32x4 (&acc)[R][D / 16], float (&m)[R], float (&l)[R], int chunk,
-                                              const int (&p_lane)[R], int p_min, float sl, int lane) {
-  using St = Stage<D, BS, KVT>;
-  constexpr int S = St::S;
-  const int cs = chunk * 32;
-  const int mrow = lane & 15, kg = lane >> 4;
-  const char* kl = lds;
-  const char* vl = lds + St::NBCH * St::kTile;
-  // wave-uniform: some key of the chunk lies past the earliest query position of the wave
-  const bool diag = cs + 31 > p_min;
-  // ---- S^T = K Q^T for the two 16-token halves, every tile
-  f32x4 s[R][2];
+// Regroup one P part for the PV MFMAs.  In: lane (col, h) holds packed bf16 pairs w[k] of keys
+// 8 (k / 2) + 4 h + 2 (k % 2) + {0, 1} (the S^T accumulator rows).  Out: op[a] holds keys
+// 16 a + 8 h .. 16 a + 8 h + 7 in order, the B operand of the a-th 16-key half.
+// permlane32_swap(x, y) leaves lanes 0-31 of x and lanes 32-63 of y in place and exchanges
+// x's lanes 32-63 with y's lanes 0-31.
+__device__ __forceinline__ void regroup_p(const uint32_t (&w)[8], u32x4 (&op)[2]) {
 #pragma unroll
   for (int a = 0; a < 2; ++a) {
-    const int tk = 16 * a + mrow;
-    const char* kb = kl + (BS >= 32 ? 0 : (tk / BS) * St::kTile) + (size_t)(kg * BS + tk % BS) * 16;
-#pragma unroll
-    for (int r = 0; r < R; ++r) s[r][a] = f32x4{0.f, 0.f, 0.f, 0.f};
-    if constexpr (KVT == PKV_BF16) {
-#pragma unroll
-      for (int c = 0; c < D / 32; ++c) {
-        const u32x4 kop = *(const u32x4*)(kb + (size_t)c * 64 * BS);
-#pragma unroll
-        for (int r = 0; r < R; ++r) s[r][a] = mfma16x16x32(kop, qop[r][c], s[r][a]);
-      }
-    } else {
-#pragma unroll
-      for (int u = 0; u < D / 64; ++u) {
-        const u32x4 w = *(const u32x4*)(kb + (size_t)u * 64 * BS);
-        const u32x4 k0 = e4m3x8_to_bf16x8(w.x, w.y), k1 = e4m3x8_to_bf16x8(w.z, w.w);
-#pragma unroll
-        for (int r = 0; r < R; ++r) {
-          s[r][a] = mfma16x16x32(k0, qop[r][2 * u], s[r][a]);
-          s[r][a] = mfma16x16x32(k1, qop[r][2 * u + 1], s[r][a]);
-        }
-      }
-    }
+    const auto s0 = __builtin_amdgcn_permlane32_swap(w[4 * a], w[4 * a + 2], false, false);
+    const auto s1 = __builtin_amdgcn_permlane32_swap(w[4 * a + 1], w[4 * a + 3], false, false);
+    const uint32_t x0 = s0[0], y0 = s0[1], x1 = s1[0], y1 = s1[1];
+    op[a] = u32x4{x0, x1, y0, y1};
   }
-  // ---- P of every tile, then each V operand (8 consecutive tokens of one column per lane)
-  // read once from LDS for all tiles (V rows past n were zeroed when the chunk was staged)
-  u32x4 ph[R], pl[R];
-#pragma unroll
-  for (int r = 0; r < R; ++r) softmax_p<D>(s[r], acc[r], m[r], l[r], cs, p_lane[r], diag, sl, lane, ph[r], pl[r]);
-  const int tv = 8 * kg;
-  const char* vb = vl + (BS >= 32 ? 0 : (tv / BS) * St::kTile) + ((size_t)mrow * BS + tv % BS) * S;
-  pv_chunk<D, BS, KVT, R>(vb, ph, pl, acc);
 }
 
-template <int D, int BS, int KVT, int NW, int R>
+// S^T[32 keys][32 cols] = K Q^T over one staged chunk: MFMA u covers dims 16 u + 8 h + j in lane
+// group h; lane (key, h) holds rows 8 (i / 4) + 4 h + i % 4 of its column.
+template <int D, int BS, int KVT>
+__device__ __forceinline__ f32x16 chunk_scores(const char* lds, const u32x4 (&qop)[D / 16], int lane) {
+  const int key = lane & 31, h = lane >> 5;
+  f32x16 s = {};
+  if constexpr (KVT == PKV_BF16) {
+#pragma unroll
+    for (int u = 0; u < D / 16; ++u) {
+      const u32x4 kop = *(const u32x4*)(lds + ((size_t)(2 * u + h) * 32 + key) * 16);
+      s = mfma32(kop, qop[u], s);
+    }
+  } else {
+#pragma unroll
+    for (int u = 0; u < D / 16; ++u) {
+      const u32x2 w = *(const u32x2*)(lds + ((size_t)(2 * u + h) * 32 + key) * 8);
+      s = mfma32(e4m3x8_to_bf16x8(w.x, w.y), qop[u], s);
+    }
+  }
+  return s;
+}
+
+// Online-softmax step of the lane's column over one chunk (branch-free): the chunk maximum (keys
+// past the column's position left out on a diagonal chunk), the running maximum m moved only when
+// the chunk exceeds it by more than 2^8 (then alpha = 2^(m_old - m_new) rescales l here, and the
+// accumulator at the caller before this chunk's PV), and P = 2^(s sl - m), 0 for masked keys.
+// sl >= 0.  Returns whether any lane moved its maximum.
+template <bool DIAG>
+__device__ __forceinline__ bool chunk_exp(const f32x16& s, float& m, float& l, float& alpha, float (&p)[16], int cs,
+                                          int p_lane, float sl, int lane) {
+  const int h = lane >> 5;
+  float cm = -INFINITY;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const bool keep = !DIAG || cs + 8 * (i / 4) + 4 * h + (i % 4) <= p_lane;
+    cm = fmaxf(cm, keep ? s[i] : -INFINITY);
+  }
+  {  // with lane l ^ 32 (the column's other 16 keys)
+    const uint32_t u = __builtin_bit_cast(uint32_t, cm);
+    const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    const uint32_t r0 = r[0], r1 = r[1];
+    cm = fmaxf(__builtin_bit_cast(float, r0), __builtin_bit_cast(float, r1));
+  }
+  cm *= sl;
+  const bool need = cm > m + kRescaleLog2;
+  const float mu = need ? cm : m;
+  alpha = exp2_fast(m - mu);  // 1 where the maximum stays (0 on the first chunk: m = -inf)
+  l *= alpha;
+  m = mu;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {  // key 0 is in every column's range: m is finite
+    const float e = exp2_fast(fmaf(s[i], sl, -m));
+    p[i] = (!DIAG || cs + 8 * (i / 4) + 4 * h + (i % 4) <= p_lane) ? e : 0.f;
+  }
+  return __ballot(need) != 0ull;
+}
+
+// P = hi + lo in bf16 (hi truncates p, lo = p - hi rounds to nearest), summed into l, regrouped
+// into the PV B operands.
+__device__ __forceinline__ void chunk_pack(const float (&p)[16], float& l, u32x4 (&ph)[2], u32x4 (&pl)[2]) {
+  float ps[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) ps[j] = (p[4 * j] + p[4 * j + 1]) + (p[4 * j + 2] + p[4 * j + 3]);
+  l += (ps[0] + ps[1]) + (ps[2] + ps[3]);
+  uint32_t wh[8], wl[8];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    const uint32_t b0 = __builtin_bit_cast(uint32_t, p[2 * k]), b1 = __builtin_bit_cast(uint32_t, p[2 * k + 1]);
+    wh[k] = __builtin_amdgcn_perm(b1, b0, 0x07060302u);
+    wl[k] = pack_bf16_rne(p[2 * k] - __builtin_bit_cast(float, b0 & 0xFFFF0000u),
+                          p[2 * k + 1] - __builtin_bit_cast(float, b1 & 0xFFFF0000u));
+  }
+  regroup_p(wh, ph);
+  regroup_p(wl, pl);
+}
+
+// O^T += V^T P^T over one staged chunk: A = 8 consecutive keys of one head-dim row (V rows past n
+// were zeroed when the chunk was staged).
+template <int D, int BS, int KVT>
+__device__ __forceinline__ void chunk_pv(const char* lds, const u32x4 (&ph)[2], const u32x4 (&pl)[2],
+                                         f32x16 (&acc)[D / 32], int lane) {
+  using St = Stage<D, BS, KVT>;
+  const int key = lane & 31, h = lane >> 5;
+  const char* vb = lds + St::kKBytes;
+#pragma unroll
+  for (int t = 0; t < D / 32; ++t) {
+#pragma unroll
+    for (int a = 0; a < 2; ++a) {
+      u32x4 vop;
+      const char* row = vb + (size_t)(32 * t + key) * St::kVRow;
+      if constexpr (KVT == PKV_BF16) {
+        vop = *(const u32x4*)(row + (16 * a + 8 * h) * 2);
+      } else {
+        const u32x2 w = *(const u32x2*)(row + 16 * a + 8 * h);
+        vop = e4m3x8_to_bf16x8(w.x, w.y);
+      }
+      acc[t] = mfma32(vop, ph[a], acc[t]);
+      acc[t] = mfma32(vop, pl[a], acc[t]);
+    }
+  }
+}
+
+template <int D, int BS, int KVT, int NW>
 __global__ __launch_bounds__(64 * NW, 2) void prefill_kernel(PrefillArgs a) {
   using St = Stage<D, BS, KVT>;
   constexpr int NT = 64 * NW;
   __shared__ __align__(16) char sh_stage[kStages][St::kBytes];
   const int tid = threadIdx.x, lane = tid & 63, w = uniform(tid >> 6);
   const int G = a.G;
-  const int tok_per_tile = 16 / G;
-  const int tok_per_wave = R * tok_per_tile;
+  const int tok_per_wave = 32 / G;
   const int tok_per_wg = NW * tok_per_wave;
-  // ---- work item: XCD-aware deal of (sequence, KV head, tile group), latest tile group first
+  // ---- work item: XCD-aware deal of (sequence, KV head, token group), latest group first
   const int items = a.items;
   const int per_xcd = (items + 7) / 8;
   const int item = (blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
   if (item >= items) return;
-  const int groups = a.groups_per_seq;  // tile groups of the longest chunk
+  const int groups = a.groups_per_seq;  // token groups of the longest chunk
   const int seg = item / groups;        // (b, g) in sequence-major order
   const int b = seg / a.H_kv, g = seg % a.H_kv;
   const int q0 = a.query_start[b], C = a.query_start[b + 1] - q0;
@@ -283,44 +310,34 @@ __global__ __launch_bounds__(64 * NW, 2) void prefill_kernel(PrefillArgs a) {
   // this workgroup's queries: positions n - C + tok0 .. ; its last chunk covers the latest one
   const int p_wg_max = n - C + min(C, tok0 + tok_per_wg) - 1;
   const int nch = p_wg_max / 32 + 1;
-  // ---- this wave's R column tiles: tile r, column c = (token wtok0 + r * tok_per_tile + c / G, head c % G)
-  const int col = lane & 15, kgq = lane >> 4;
+  // ---- this wave's 32 columns: column c = (token wtok0 + c / G, head c % G)
+  const int col = lane & 31, h = lane >> 5;
   const int wtok0 = tok0 + w * tok_per_wave;
   const int p_min = uniform(n - C + min(wtok0, C - 1));
+  const int p_wmax = uniform(n - C + min(wtok0 + tok_per_wave, C) - 1);  // the wave's latest position
   // scores in log2 units: (q . k) * sl; a negative sl is taken as |sl| with q negated
   // (a sign flip of each bf16, exact), so that the chunk maximum can be taken before scaling
   float sl = a.scale_log2;
   if constexpr (KVT == PKV_FP8_E4M3) sl *= a.k_scale[g];
   const uint32_t qsign = sl < 0.f ? 0x80008000u : 0u;
   sl = fabsf(sl);
-  u32x4 qop[R][D / 32];
-  int p_lane[R];
+  const int qtok = wtok0 + col / G;  // chunk-relative token of this lane's column
+  const bool qvalid = qtok < C;
+  const int p_lane = n - C + (qvalid ? qtok : min(wtok0, C - 1));  // never past the sequence
+  u32x4 qop[D / 16];  // B operand of MFMA u: dims 16 u + 8 h .. + 7 of the lane's column
+  {
+    const uint16_t* qrow = (const uint16_t*)a.q + ((size_t)(q0 + (qvalid ? qtok : 0)) * a.H_q + g * G + col % G) * D;
 #pragma unroll
-  for (int r = 0; r < R; ++r) {
-    const int qtok = wtok0 + r * tok_per_tile + col / G;  // chunk-relative token of this lane's column
-    const bool qvalid = qtok < C;
-    p_lane[r] = n - C + (qvalid ? qtok : min(wtok0, C - 1));  // never past the sequence
-    const uint16_t* qrow =
-        (const uint16_t*)a.q + ((size_t)(q0 + (qvalid ? qtok : 0)) * a.H_q + g * G + col % G) * D;
-#pragma unroll
-    for (int c = 0; c < D / 32; ++c) {
+    for (int u = 0; u < D / 16; ++u) {
       u32x4 v = u32x4{0u, 0u, 0u, 0u};
-      if (qvalid) v = *(const u32x4*)(qrow + qk_dofs<KVT>(c, kgq));
-      qop[r][c] = v ^ qsign;
+      if (qvalid) v = *(const u32x4*)(qrow + 16 * u + 8 * h);
+      qop[u] = v ^ qsign;
     }
   }
-  f32x4 acc[R][D / 16];
-  float m[R], l[R];
+  f32x16 acc[D / 32];
 #pragma unroll
-  for (int r = 0; r < R; ++r) {
-#pragma unroll
-    for (int t = 0; t < D / 16; ++t) acc[r][t] = f32x4{0.f, 0.f, 0.f, 0.f};
-    m[r] = -INFINITY;
-    l[r] = 0.f;
-  }
-  // ---- pipeline: iteration c first writes chunk c+1 (loaded into registers during
-  // iteration c-1) into the LDS buffer chunk c-1 used, then reuses those registers for the
-  // loads of chunk c+2, then computes chunk c; the barrier closes both buffers' hand-over
+  for (int t = 0; t < D / 32; ++t) acc[t] = f32x16{};
+  float m = -INFINITY, l = 0.f;
   const char* kpool = (const char*)a.k_pool;
   const char* vpool = (const char*)a.v_pool;
   Stager<D, BS, KVT, NT> A;
@@ -328,42 +345,51 @@ __global__ __launch_bounds__(64 * NW, 2) void prefill_kernel(PrefillArgs a) {
   A.store(sh_stage[0], tid, n);
   if (nch > 1) A.load(kpool, vpool, tab, 1, last_blk, a.NB, a.H_kv, g, tid);
   __syncthreads();
+  float p[16], alpha;
   for (int c = 0; c < nch; ++c) {
     if (c + 1 < nch) {
       A.store(sh_stage[(c + 1) % kStages], tid, n - 32 * (c + 1));
       if (c + 2 < nch) A.load(kpool, vpool, tab, c + 2, last_blk, a.NB, a.H_kv, g, tid);
     }
-    prefill_chunk<D, BS, KVT, R>(sh_stage[c % kStages], qop, acc, m, l, c, p_lane, p_min, sl, lane);
+    if (32 * c <= p_wmax) {
+      const f32x16 s = chunk_scores<D, BS, KVT>(sh_stage[c % kStages], qop, lane);
+      const bool moved = 32 * c + 31 > p_min ? chunk_exp<true>(s, m, l, alpha, p, 32 * c, p_lane, sl, lane)
+                                             : chunk_exp<false>(s, m, l, alpha, p, 32 * c, p_lane, sl, lane);
+      if (moved) {
+#pragma unroll
+        for (int t = 0; t < D / 32; ++t) acc[t] *= alpha;
+      }
+      u32x4 ph[2], pl[2];
+      chunk_pack(p, l, ph, pl);
+      chunk_pv<D, BS, KVT>(sh_stage[c % kStages], ph, pl, acc, lane);
+    }
     __syncthreads();
   }
-  // ---- normalise and write this wave's rows (row i of tile r = column i of that tile)
-  const float vs = KVT == PKV_FP8_E4M3 ? a.v_scale[g] : 1.f;
-#pragma unroll
-  for (int r = 0; r < R; ++r) {
-    float lt = l[r];
-    lt += __shfl_xor(lt, 16, 64);
-    lt += __shfl_xor(lt, 32, 64);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int row = 4 * kgq + i;
-      const float lr = __shfl(lt, row, 64);
-      const int rt = wtok0 + r * tok_per_tile + row / G;
-      if (rt < C) {
-        float* orow = a.out + ((size_t)(q0 + rt) * a.H_q + g * G + row % G) * D;
-#pragma unroll
-        for (int t = 0; t < D / 16; ++t) orow[16 * t + col] = acc[r][t][i] * vs / lr;
-      }
-    }
+  // ---- normalise and write the column's row: acc[t] register i is head-dim row
+  // 32 t + 8 (i / 4) + 4 h + i % 4 of O^T
+  if (!qvalid) return;
+  {
+    const uint32_t u = __builtin_bit_cast(uint32_t, l);
+    const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    const uint32_t r0 = r[0], r1 = r[1];
+    l = __builtin_bit_cast(float, r0) + __builtin_bit_cast(float, r1);
   }
+  const float f = (KVT == PKV_FP8_E4M3 ? a.v_scale[g] : 1.f) / l;
+  float* orow = a.out + ((size_t)(q0 + qtok) * a.H_q + g * G + col % G) * D;
+#pragma unroll
+  for (int t = 0; t < D / 32; ++t)
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+      *(f32x4*)(orow + 32 * t + 8 * k + 4 * h) =
+          f32x4{acc[t][4 * k] * f, acc[t][4 * k + 1] * f, acc[t][4 * k + 2] * f, acc[t][4 * k + 3] * f};
 }
 
-constexpr int kPrefillWaves = 8;
-constexpr int kPrefillTiles = 1;  // column tiles per wave (2 measured the same: the loop is VALU-bound)
+constexpr int kPrefillWaves = 12;
 
 template <int D, int BS, int KVT>
 hipError_t launch_prefill_t(const PrefillArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL((prefill_kernel<D, BS, KVT, kPrefillWaves, kPrefillTiles>),
-                     dim3((unsigned)((a.items + 7) / 8 * 8)), dim3(64 * kPrefillWaves), 0, s, a);
+  hipLaunchKernelGGL((prefill_kernel<D, BS, KVT, kPrefillWaves>), dim3((unsigned)((a.items + 7) / 8 * 8)),
+                     dim3(64 * kPrefillWaves), 0, s, a);
   return hipGetLastError();
 }
 
@@ -378,7 +404,7 @@ hipError_t launch_prefill_bs(const PrefillArgs& a, hipStream_t s) {
 
 }  // namespace
 
-int prefill_wg_tokens(int G) { return kPrefillWaves * kPrefillTiles * (16 / G); }
+int prefill_wg_tokens(int G) { return kPrefillWaves * (32 / G); }
 
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t s) {
   if (a.kv_dtype == PKV_BF16)

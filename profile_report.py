@@ -3,9 +3,9 @@
 
 Reads the rocpd SQLite databases of five runs of one workload (all from the repository root):
 
-    rocprofv3 --kernel-trace --stats -T -d T -o trace -- python3 bench.py --workload W --steps 20 --warmup 5 --no-cpu-baseline
-    rocprofv3 --pmc FETCH_SIZE -T -d F -o fetch -- python3 bench.py --workload W --steps 3 --warmup 1 --no-cpu-baseline --eager
-    rocprofv3 --pmc WRITE_SIZE -T -d R -o write -- python3 bench.py --workload W --steps 3 --warmup 1 --no-cpu-baseline --eager
+    rocprofv3 --kernel-trace --stats -T -d T -o trace -- python3 bench.py --workload W --only --steps 20 --warmup 5 --no-cpu-baseline
+    rocprofv3 --pmc FETCH_SIZE -T -d F -o fetch -- python3 bench.py --workload W --only --steps 3 --warmup 1 --no-cpu-baseline --eager
+    rocprofv3 --pmc WRITE_SIZE -T -d R -o write -- python3 bench.py --workload W --only --steps 3 --warmup 1 --no-cpu-baseline --eager
     rocprofv3 --pmc FETCH_SIZE -T -d CF -o cf -- python3 bench.py --copy-calibration 1024
     rocprofv3 --pmc WRITE_SIZE -T -d CW -o cw -- python3 bench.py --copy-calibration 1024
 
@@ -14,10 +14,14 @@ and writes profiles/decode_<W>.md plus the workload's entry of profiles/decode_c
 the decode kernel's code so that a changed kernel reports null until it is profiled again).
 
     python profile_report.py W T F R CF CW
-    python profile_report.py --kernels prefill_kernel --name prefill_70b --cmd "--op prefill" T F R CF CW
+    python profile_report.py --kernels prefill_kernel --name prefill_70b --cmd "--op prefill" \
+        [--timed K] [--counters-key KEY] T F R CF CW
 
 The second form summarises other kernels of other bench modes into profiles/<name>.md (the trace
-and counter runs then use `bench.py <cmd>` in place of `--workload W`); it writes no counters JSON.
+and counter runs then use `bench.py <cmd>` in place of `--workload W`).  With --timed K the
+summary also gives the first kernel's statistics over its last K dispatches (the bench's timed
+calls, after the warm-up).  With --counters-key the HBM bytes per launch of the first kernel go
+into profiles/prefill_counters.json under that key, with the hash of the prefill kernel's code.
 """
 from __future__ import annotations
 
@@ -27,13 +31,13 @@ import os
 import sqlite3
 import sys
 
-from bench import COUNTERS, KERNEL_SOURCE, ROOT, source_hash
+from bench import COUNTERS, KERNEL_SOURCE, PREFILL_COUNTERS, PREFILL_SOURCE, ROOT, source_hash
 DECODE_KERNELS = ("decode_piece_kernel", "piece_merge_kernel")
 COPY_BYTES = 1 << 30
 
-TRACE_CMD = ("rocprofv3 --kernel-trace --stats -T -d <out> -o trace -- python3 bench.py --workload {w} "
+TRACE_CMD = ("rocprofv3 --kernel-trace --stats -T -d <out> -o trace -- python3 bench.py --workload {w} --only "
              "--steps 20 --warmup 5 --no-cpu-baseline")
-PMC_CMD = ("timeout -s KILL 150 rocprofv3 --pmc {c} -T -d <out> -o {o} -- python3 bench.py --workload {w} "
+PMC_CMD = ("timeout -s KILL 150 rocprofv3 --pmc {c} -T -d <out> -o {o} -- python3 bench.py --workload {w} --only "
            "--steps 3 --warmup 1 --no-cpu-baseline --eager")
 COPY_CMD = "timeout -s KILL 90 rocprofv3 --pmc {c} -T -d <out> -o {o} -- python3 bench.py --copy-calibration 1024"
 
@@ -70,7 +74,7 @@ def counter_kib(d, counter):
 
 
 def main(argv):
-    kernels, name, cmd = DECODE_KERNELS, None, None
+    kernels, name, cmd, timed, ckey = DECODE_KERNELS, None, None, 0, None
     while argv and argv[0].startswith("--"):
         opt, val, argv = argv[0], argv[1], argv[2:]
         if opt == "--kernels":
@@ -79,14 +83,25 @@ def main(argv):
             name = val
         elif opt == "--cmd":
             cmd = val
+        elif opt == "--timed":
+            timed = int(val)
+        elif opt == "--counters-key":
+            ckey = val
         else:
             raise SystemExit(__doc__)
     if name is None and len(argv) == 6:
         report_decode(*argv, kernels)
     elif name is not None and cmd is not None and len(argv) == 5:
-        report_other(name, cmd, kernels, *argv)
+        report_other(name, cmd, kernels, *argv, timed=timed, ckey=ckey)
     else:
         raise SystemExit(__doc__)
+
+
+def dispatch_durations(d, kernel):
+    """Durations (us) of every dispatch of `kernel`, in launch order."""
+    con = _db(d)
+    return [dur / 1e3 for name, dur in con.execute("select name, duration from kernels order by start")
+            if _short(name) == kernel]
 
 
 def _calibration(cf_dir, cw_dir):
@@ -108,11 +123,21 @@ def _trace_lines(stats, launch, kernels, trace_cmd):
     return L
 
 
-def report_other(name, cmd, kernels, t_dir, f_dir, r_dir, cf_dir, cw_dir):
+def report_other(name, cmd, kernels, t_dir, f_dir, r_dir, cf_dir, cw_dir, timed=0, ckey=None):
     """F and R may be '-' for a trace-only summary."""
     stats, launch = trace_stats(t_dir)
-    trace_cmd = f"rocprofv3 --kernel-trace --stats -T -d <out> -o trace -- python3 bench.py {cmd} --steps 20 --warmup 5"
+    steps = f"--steps {timed} --warmup 20" if timed else "--steps 20 --warmup 5"
+    trace_cmd = f"rocprofv3 --kernel-trace --stats -T -d <out> -o trace -- python3 bench.py {cmd} {steps}"
     L = [f"# {name} on MI355X (`bench.py {cmd}`)", ""] + _trace_lines(stats, launch, kernels, trace_cmd)
+    timed_avg = None
+    if timed:
+        durs = dispatch_durations(t_dir, kernels[0])
+        last = sorted(durs[-timed:])
+        timed_avg = sum(last) / len(last)
+        L += ["", f"{kernels[0]}: {len(durs)} dispatches in the trace; the last {len(last)} are the bench's timed "
+              f"calls: average {timed_avg:.2f} us, median {last[len(last) // 2]:.2f} us, min {last[0]:.2f} us, "
+              f"max {last[-1]:.2f} us (the first {len(durs) - len(last)}, warm-up and setup, average "
+              f"{(sum(durs) - sum(durs[-timed:])) / max(1, len(durs) - len(last)):.2f} us)."]
     if f_dir == "-" or r_dir == "-":
         with open(os.path.join(ROOT, "profiles", f"{name}.md"), "w") as f:
             f.write("\n".join(L + [""]))
@@ -132,9 +157,25 @@ def report_other(name, cmd, kernels, t_dir, f_dir, r_dir, cf_dir, cw_dir):
             L.append(f"| {k} | {fetch[k][0]:.1f} | {write[k][0]:.1f} | {fetch[k][1]} | "
                      f"{fetch[k][0] * 1024 * ff / 1e6:.2f} | {write[k][0] * 1024 * wf / 1e6:.2f} |")
     L.append("")
+    k0 = kernels[0]
+    if ckey and k0 in fetch and k0 in write:
+        sha = source_hash(PREFILL_SOURCE)
+        fb, wb = fetch[k0][0] * 1024 * ff, write[k0][0] * 1024 * wf
+        try:
+            rec = json.load(open(PREFILL_COUNTERS))
+        except (OSError, ValueError):
+            rec = {}
+        rec[ckey] = {"code_sha256_16": sha, "fetch_factor": ff, "write_factor": wf, "fetch_bytes": round(fb),
+                     "write_bytes": round(wb), "hbm_bytes_per_launch": round(fb + wb),
+                     "avg_us_timed_calls": None if timed_avg is None else round(timed_avg, 3)}
+        with open(PREFILL_COUNTERS, "w") as f:
+            json.dump(rec, f, indent=1, sort_keys=True)
+            f.write("\n")
+        L += [f"Per launch: {(fb + wb) / 1e6:.2f} MB moved beyond L2 (kernel code sha256[:16], comments and "
+              f"whitespace removed: {sha}); bench.py reports it as roofline.traffic under `{ckey}`.", ""]
     with open(os.path.join(ROOT, "profiles", f"{name}.md"), "w") as f:
         f.write("\n".join(L))
-    print(name, {k: round(a, 2) for k, _, _, a, _ in stats if k in kernels})
+    print(name, {k: round(a, 2) for k, _, _, a, _ in stats if k in kernels}, "timed avg", timed_avg)
 
 
 def report_decode(w, t_dir, f_dir, r_dir, cf_dir, cw_dir, kernels=DECODE_KERNELS):

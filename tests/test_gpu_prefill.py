@@ -92,6 +92,10 @@ SMALL = {
     "g4_bs32_d128": dict(priors=[3, 0, 129], chunks=[90, 33, 7], H_q=16, H_kv=4, d=128, bs=32),
     "g16_bs16_d64": dict(priors=[0, 40], chunks=[9, 23], H_q=32, H_kv=2, d=64, bs=16),
     "g2_bs8_d128": dict(priors=[64, 0], chunks=[65, 127], H_q=4, H_kv=2, d=128, bs=8),
+    # chunks longer than one workgroup's query tokens (12 waves x 32 / G): several workgroups per
+    # sequence, the last one ragged, some of its waves without any query
+    "g1_bs16_d128_long": dict(priors=[10, 0], chunks=[800, 385], H_q=2, H_kv=2, d=128, bs=16),
+    "g4_bs32_d64_long": dict(priors=[300, 1], chunks=[97, 200], H_q=8, H_kv=2, d=64, bs=32),
 }
 
 
