@@ -63,7 +63,7 @@ def parse():
                    help="launch the step's kernels one by one instead of replaying a captured HIP graph")
     p.add_argument("--identity-tables", action="store_true",
                    help="lay every sequence out contiguously (identity block order) instead of scattered")
-    p.add_argument("--op", default="step", choices=["step", "copy_blocks", "swap", "prefill", "mixes"],
+    p.add_argument("--op", default="step", choices=["step", "copy_blocks", "swap", "prefill", "mixes", "paths"],
                    help="step: the decode step (default); copy_blocks: copy-on-write block copies alone; "
                         "swap: swap-out / swap-in of scattered blocks to and from pinned host memory; "
                         "prefill: causal chunked prefill over the paged pools; mixes: decode call time on "
@@ -176,6 +176,9 @@ def main():
         return
     if args.op == "mixes":
         bench_mixes(args, torch, pkv, dev)
+        return
+    if args.op == "paths":
+        bench_paths(args, torch, pkv, dev)
         return
     shared = {}  # drawn K/V rows shared by the E4M3 workload's block sizes (the same logical data)
     res = bench_decode(args.workload, args, torch, pkv, dev, args.steps, args.warmup, args.cpu_seconds,
@@ -511,6 +514,83 @@ def bench_mixes(args, torch, pkv, dev):
                       "config": {"workload": "seeded length mixes (workloads.length_mix)", "H_q": H_q, "H_kv": H_kv,
                                  "head_dim": D, "block_size": bs},
                       "batches": rows}), flush=True)
+
+
+def bench_paths(args, torch, pkv, dev):
+    """Matrix-core against vector decode on one batch: 32 sequences of 4096 tokens, H_kv 8, D 128,
+    bs 16, bf16 q, for query heads per KV head G in 1, 2, 4, 8 and bf16 or E4M3 KV.  Random pool,
+    scattered tables; the two paths' calls alternate in rounds of 20 (after 10 warm-up calls of
+    each) and each reports its p50 over 100 calls.  One JSON line."""
+    B, n, H_kv, D, bs = 32, 4096, 8, 128, 16
+    nblk = n // bs
+    NB = B * nblk + 8
+    tab = np.random.default_rng(5).permutation(NB)[:B * nblk].astype(np.int32).reshape(B, nblk)
+    lens = np.full(B, n, np.int32)
+    tabd, lensd = torch.from_numpy(tab).to(dev), torch.from_numpy(lens).to(dev)
+    rows = []
+    for kv in ("bf16", "e4m3"):
+        kvd = pkv.BF16 if kv == "bf16" else pkv.FP8_E4M3
+        ks, vs = pkv.pool_shapes(NB, H_kv, D, bs, kvd)
+        g = torch.Generator(device=dev).manual_seed(7)
+        if kv == "bf16":
+            kp = torch.randn(ks, device=dev, generator=g).to(torch.bfloat16)
+            vp = torch.randn(vs, device=dev, generator=g).to(torch.bfloat16)
+            ksc = vsc = None
+        else:
+            kp = torch.randint(0, 120, ks, dtype=torch.uint8, device=dev, generator=g)
+            vp = torch.randint(0, 120, vs, dtype=torch.uint8, device=dev, generator=g)
+            ksc = torch.full((H_kv,), 0.01, device=dev)
+            vsc = torch.full((H_kv,), 0.01, device=dev)
+        for G in (1, 2, 4, 8):
+            H_q = G * H_kv
+            q = torch.randn((B, H_q, D), device=dev, generator=g).to(torch.bfloat16)
+            ws = pkv.decode_workspace(B, H_q, D, n, bs, H_kv=H_kv, device=dev)
+            outs = {p: torch.empty((B, H_q, D), device=dev) for p in ("matrix", "vector")}
+            mode = {"matrix": pkv.DECODE_PATH_AUTO, "vector": pkv.DECODE_PATH_VECTOR}
+            times = {p: [] for p in outs}
+
+            def call(p):
+                pkv.set_decode_path(mode[p])
+                pkv.paged_attn_decode(q, kp, vp, tabd, lensd, 1 / math.sqrt(D), ksc, vsc, max_context_len=n,
+                                      out=outs[p], workspace=ws)
+
+            try:
+                for p in outs:
+                    for _ in range(10):
+                        call(p)
+                torch.cuda.synchronize()
+                for _ in range(5):
+                    for p in outs:
+                        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                              for _ in range(20)]
+                        for e0, e1 in ev:
+                            e0.record()
+                            call(p)
+                            e1.record()
+                        torch.cuda.synchronize()
+                        times[p] += [e0.elapsed_time(e1) * 1e3 for e0, e1 in ev]
+            finally:
+                pkv.set_decode_path(pkv.DECODE_PATH_AUTO)
+            om, ov = outs["matrix"].double(), outs["vector"].double()
+            rel = float(((om - ov).norm(dim=-1) / om.norm(dim=-1).clamp_min(1e-30)).max())
+            kv_bytes = B * n * H_kv * D * 2 * (2 if kv == "bf16" else 1)
+            row = {"kv": kv, "G": G, "H_q": H_q}
+            for p in outs:
+                us = float(np.median(times[p]))
+                row[f"{p}_us_p50"] = round(us, 1)
+                row[f"{p}_GBps"] = round(kv_bytes / us / 1e3, 1)
+            row["vector_over_matrix"] = round(row["vector_us_p50"] / row["matrix_us_p50"], 3)
+            row["max_row_rel_diff"] = rel
+            rows.append(row)
+            print(f"# paths {row}", file=sys.stderr, flush=True)
+            del ws, outs, q
+        del kp, vp
+        torch.cuda.empty_cache()
+    print(json.dumps({"metric": "decode call p50, matrix-core vs vector path", "unit": "us", "n_gpus": 1,
+                      "config": {"workload": "32 sequences x 4096 tokens, H_kv 8, D 128, bs 16, bf16 q, "
+                                             "scattered tables", "B": B, "context": n, "H_kv": H_kv, "head_dim": D,
+                                 "block_size": bs},
+                      "rows": rows}), flush=True)
 
 
 def block_waste(tables, lens, bs):

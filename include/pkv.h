@@ -221,6 +221,20 @@ int pkv_paged_attn_decode(float* out, const void* q, int q_dtype, const void* k_
                           void* stream);
 
 /*
+ * Design (not on the pages): which decode kernel runs.  The decode variants
+ * (plain, noalloc, hinted, step, window) pick the matrix-core path for the
+ * combinations listed under pkv_paged_attn_decode and the vector path for the
+ * rest.  pkv_set_decode_path(PKV_DECODE_PATH_VECTOR) sends every later call in
+ * the process to the vector path, to compare the two on one batch;
+ * PKV_DECODE_PATH_AUTO restores the default choice.  Results agree within
+ * the decode's tolerance, not bit for bit.  The setting is process-wide; it
+ * returns the previous setting, or PKV_ERR_INVALID_ARG for another value.  A
+ * decode already enqueued is not affected.
+ */
+enum pkv_decode_path { PKV_DECODE_PATH_AUTO = 0, PKV_DECODE_PATH_VECTOR = 1 };
+int pkv_set_decode_path(int path);
+
+/*
  * pkv_paged_attn_decode_noalloc — pkv_paged_attn_decode without a workspace
  * argument.  Design, for the callers that cannot allocate device memory: code
  * under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.  The

@@ -37,6 +37,7 @@ OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_OUT_OF_BLOCKS, ERR_UNKNOWN_SEQ, ERR_SH
     0, -1, -2, -3, -4, -5, -6
 F32, BF16, FP8_E4M3 = 0, 1, 2
 ELEM_BYTES = {F32: 4, BF16: 2, FP8_E4M3: 1}
+DECODE_PATH_AUTO, DECODE_PATH_VECTOR = 0, 1
 
 # every symbol include/pkv.h declares: name -> (restype, argtypes)
 _P = ctypes.c_void_p
@@ -46,6 +47,7 @@ _SZ = ctypes.c_size_t
 SIGNATURES = {
     "pkv_last_error": (ctypes.c_char_p, []),
     "pkv_abi_version": (ctypes.c_int, []),
+    "pkv_set_decode_path": (ctypes.c_int, [ctypes.c_int]),
     "pkv_kv_append": (ctypes.c_int, [_P, _P, ctypes.c_int, _P, _I32, _P, _P, ctypes.c_int, _I32, _I32, _I32,
                                      _I32, _P, _P, _P]),
     "pkv_copy_blocks": (ctypes.c_int, [_P, _P, ctypes.c_int, _I32, _I32, _I32, _I32, _P, _P, _I32, _P]),
@@ -137,6 +139,14 @@ def last_error() -> str:
 def _check(st: int):
     if st != OK:
         raise PkvError(st, last_error())
+
+
+def set_decode_path(path: int) -> int:
+    """Process-wide decode kernel choice (DECODE_PATH_AUTO or DECODE_PATH_VECTOR); returns the previous one."""
+    st = lib.pkv_set_decode_path(int(path))
+    if st < 0:
+        raise PkvError(st, last_error())
+    return st
 
 
 # ---------------------------------------------------------------------------
@@ -572,4 +582,5 @@ __all__ = ["lib", "LIB_PATH", "PkvError", "last_error", "kv_append", "copy_block
            "decode_workspace_bytes",
            "decode_workspace",
            "pool_shapes", "dtype_code", "stream_read", "copy_", "Allocator", "SIGNATURES",
+           "set_decode_path", "DECODE_PATH_AUTO", "DECODE_PATH_VECTOR",
            "F32", "BF16", "FP8_E4M3"]

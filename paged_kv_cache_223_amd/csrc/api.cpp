@@ -5,6 +5,7 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <atomic>
 #include <cmath>
 
 #include "internal.h"
@@ -230,6 +231,22 @@ size_t pkv_decode_workspace_bytes(int32_t B, int32_t H_q, int32_t D, int32_t max
   return best;
 }
 
+static std::atomic<int> g_decode_path{PKV_DECODE_PATH_AUTO};
+
+int pkv_set_decode_path(int path) {
+  g_err[0] = 0;
+  if (path != PKV_DECODE_PATH_AUTO && path != PKV_DECODE_PATH_VECTOR) {
+    set_error("set_decode_path: unknown path %d", path);
+    return PKV_ERR_INVALID_ARG;
+  }
+  return g_decode_path.exchange(path);
+}
+
+// the matrix-core path runs where it is supported unless the vector path is forced
+static bool use_matrix_path(int q_dtype, int kv_dtype, int G, int D, int bs) {
+  return g_decode_path.load() == PKV_DECODE_PATH_AUTO && decode_fast_path_supported(q_dtype, kv_dtype, G, D, bs);
+}
+
 static int decode_impl(float* out, const void* q, int q_dtype, const void* k_pool, const void* v_pool, int kv_dtype,
                        const int32_t* block_tables, int32_t max_blocks_per_seq, const int32_t* context_lens,
                        int32_t max_context_len, const int32_t* sink_lens, const int32_t* window_starts, int32_t B,
@@ -271,7 +288,7 @@ static int decode_impl(float* out, const void* q, int q_dtype, const void* k_poo
   const SplitPlan plan = plan_splits(B, H_kv, max_context_len);
   const int num_cus = current_num_cus();
   const int G = H_q / H_kv;
-  const bool fast = decode_fast_path_supported(q_dtype, kv_dtype, G, D, bs);
+  const bool fast = use_matrix_path(q_dtype, kv_dtype, G, D, bs);
   // a caller's workspace is sized for either path; the static scratch only for the path that runs
   const int paths = static_ws ? (fast ? 2 : 1) : 3;
   const size_t need = workspace_bytes_for(B, H_q, H_kv, D, plan, num_cus, paths);
@@ -467,7 +484,7 @@ int pkv_decode_step(float* out, const void* q, int q_dtype, const void* k_new, c
                     size_t workspace_bytes, void* stream) {
   g_err[0] = 0;
   const bool fused = B > 0 && H_kv > 0 && H_q % H_kv == 0 && kv_dtype == PKV_BF16 && src_dtype == PKV_BF16 &&
-                     decode_fast_path_supported(q_dtype, kv_dtype, H_q / H_kv, D, bs);
+                     use_matrix_path(q_dtype, kv_dtype, H_q / H_kv, D, bs);
   if (!fused) {  // the two calls, in order, on the stream; the decode's arguments are checked first
     int st = decode_impl(out, q, q_dtype, k_pool, v_pool, kv_dtype, block_tables, max_blocks_per_seq, context_lens,
                          max_context_len, nullptr, nullptr, B, H_q, H_kv, D, NB, bs, scale, k_scale, v_scale,

@@ -129,13 +129,27 @@ def test_status_and_dtype_codes_match_header():
     text = open(HEADER).read()
     for name, val in [("PKV_OK", 0), ("PKV_ERR_INVALID_ARG", -1), ("PKV_ERR_UNSUPPORTED", -2),
                       ("PKV_ERR_OUT_OF_BLOCKS", -3), ("PKV_ERR_UNKNOWN_SEQ", -4), ("PKV_ERR_SHARED_BLOCK", -5),
-                      ("PKV_ERR_HIP", -6), ("PKV_F32", 0), ("PKV_BF16", 1), ("PKV_FP8_E4M3", 2)]:
+                      ("PKV_ERR_HIP", -6), ("PKV_F32", 0), ("PKV_BF16", 1), ("PKV_FP8_E4M3", 2),
+                      ("PKV_DECODE_PATH_AUTO", pkv.DECODE_PATH_AUTO),
+                      ("PKV_DECODE_PATH_VECTOR", pkv.DECODE_PATH_VECTOR)]:
         assert re.search(rf"\b{name}\s*=\s*{val}\b", text), name
     import oracle
     import workloads
     assert workloads.STATUS_OUT_OF_BLOCKS == pkv.ERR_OUT_OF_BLOCKS == int(oracle.Status.OUT_OF_BLOCKS)
     for s in oracle.Status:
         assert int(s) == getattr(pkv, "OK" if s.name == "OK" else "ERR_" + s.name)
+
+
+def test_decode_path_setting_round_trips_and_rejects_unknown_values():
+    assert pkv.set_decode_path(pkv.DECODE_PATH_VECTOR) == pkv.DECODE_PATH_AUTO
+    try:
+        assert pkv.lib.pkv_set_decode_path(7) == pkv.ERR_INVALID_ARG
+        assert "unknown path" in pkv.last_error()
+        with pytest.raises(pkv.PkvError):
+            pkv.set_decode_path(-1)
+    finally:  # a refused value leaves the setting as it was
+        assert pkv.set_decode_path(pkv.DECODE_PATH_AUTO) == pkv.DECODE_PATH_VECTOR
+    assert pkv.set_decode_path(pkv.DECODE_PATH_AUTO) == pkv.DECODE_PATH_AUTO
 
 
 # dummy non-null device pointers: every call below must fail validation before touching them
