@@ -18,7 +18,7 @@ LIB = os.path.join(PKG, "libpkv.so")
 ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
 ARCH = "gfx950"
 
-HIP_SOURCES = ["paged_decode.hip", "prefill.hip", "kv_append.hip", "copy_blocks.hip", "stream.hip"]
+HIP_SOURCES = ["paged_decode.hip", "decode_vector.hip", "prefill.hip", "kv_append.hip", "copy_blocks.hip", "stream.hip"]
 CXX_SOURCES = ["api.cpp", "allocator.cpp"]
 
 # Packed-fp32 instructions are left to nobody: the compiler must not form them.

@@ -110,7 +110,8 @@ struct DecodeArgs {
 constexpr size_t kStaticScratchBytes = size_t(32) << 20;
 hipError_t static_scratch(void** ptr);
 
-// Kernel launchers (paged_decode.hip).  Return hipError_t of the launch.
+// Kernel launchers (matrix-core path: paged_decode.hip; vector path and its split merge:
+// decode_vector.hip).  Return hipError_t of the launch.
 bool decode_fast_path_supported(int q_dtype, int kv_dtype, int G, int D, int bs);
 hipError_t launch_decode_mfma(const DecodeArgs& a, hipStream_t s);
 hipError_t launch_decode_vector(const DecodeArgs& a, hipStream_t s);
