@@ -40,21 +40,27 @@ def _run(cmd, verbose):
 
 
 def build(verbose: bool = False, debug: bool = False) -> str:
-    """Compile every source and link libpkv.so next to this file; returns its path."""
+    """Compile every source (in parallel, one process per source) and link libpkv.so next to this
+    file; returns its path."""
+    from concurrent.futures import ThreadPoolExecutor
+
     hipcc = shutil.which("hipcc") or os.path.join(ROCM, "bin", "hipcc")
     os.makedirs(BUILD, exist_ok=True)
-    objs = []
     extra = ["-g"] if debug else []
+    steps = []
     for src in HIP_SOURCES:
         obj = os.path.join(BUILD, src.replace(".hip", ".o"))
-        _run([hipcc, *HIP_FLAGS, *extra, f"-I{INCLUDE}", f"-I{CSRC}", "-c", os.path.join(CSRC, src), "-o", obj],
-             verbose)
-        objs.append(obj)
+        steps.append((obj, [hipcc, *HIP_FLAGS, *extra, f"-I{INCLUDE}", f"-I{CSRC}", "-c", os.path.join(CSRC, src),
+                            "-o", obj]))
     for src in CXX_SOURCES:
         obj = os.path.join(BUILD, src.replace(".cpp", ".o"))
-        _run(["g++", *CXX_FLAGS, *extra, f"-I{INCLUDE}", f"-I{CSRC}", "-c", os.path.join(CSRC, src), "-o", obj],
-             verbose)
-        objs.append(obj)
+        steps.append((obj, ["g++", *CXX_FLAGS, *extra, f"-I{INCLUDE}", f"-I{CSRC}", "-c", os.path.join(CSRC, src),
+                            "-o", obj]))
+    workers = max(1, min(len(steps), os.cpu_count() or 1, 8))
+    with ThreadPoolExecutor(workers) as pool:
+        for f in [pool.submit(_run, cmd, verbose) for _, cmd in steps]:
+            f.result()
+    objs = [obj for obj, _ in steps]
     tmp = LIB + ".tmp"
     _run([hipcc, "-shared", "-fPIC", f"--offload-arch={ARCH}", *objs, "-o", tmp, f"-L{ROCM}/lib", "-lamdhip64"],
          verbose)

@@ -73,6 +73,16 @@ struct Stage {
   static constexpr int kUnits = 2 * NBCH * kTile / 16;  // 16-byte pool units of the chunk (K then V)
 };
 
+// ids[idx] for a lane-dependent idx < N, as selects between scalars (an indexed read of the local
+// array would put it in scratch memory).
+template <int N>
+__device__ __forceinline__ int pick_id(const int (&ids)[N], int idx) {
+  int r = ids[0];
+#pragma unroll
+  for (int i = 1; i < N; ++i) r = idx == i ? ids[i] : r;
+  return r;
+}
+
 // Copies one chunk's pool tiles (global -> registers -> LDS); the workgroup's threads take
 // 16-byte units round-robin.  Blocks past the sequence's last block read the last block again
 // (masked later), so every access stays inside the pool.
@@ -83,9 +93,17 @@ struct Stager {
   static constexpr int tileU = St::kTile / 16;
   u32x4 r[kPer];
 
+  // Table entries of one chunk's blocks (wave-uniform, scalar loads), clamped to the sequence's
+  // last block.  Taken one iteration ahead of the chunk's loads, so the table's latency is off the
+  // loop's critical path.
+  __device__ __forceinline__ static void chunk_ids(int (&ids)[St::NBCH], const int32_t* __restrict__ tab, int chunk,
+                                                   int last_blk, int NB) {
+#pragma unroll
+    for (int j = 0; j < St::NBCH; ++j) ids[j] = block_id(tab, chunk * 32 / BS + j, last_blk, NB);
+  }
+
   __device__ __forceinline__ void load(const char* __restrict__ kpool, const char* __restrict__ vpool,
-                                       const int32_t* __restrict__ tab, int chunk, int last_blk, int NB, int H_kv,
-                                       int g, int tid) {
+                                       const int (&ids)[St::NBCH], int H_kv, int g, int tid) {
     const size_t bstride = (size_t)H_kv * St::kTile;
 #pragma unroll
     for (int k = 0; k < kPer; ++k) {
@@ -93,7 +111,7 @@ struct Stager {
       if (St::kUnits % NT == 0 || u < St::kUnits) {
         const int part = u / (St::NBCH * tileU);  // 0 = K, 1 = V
         const int w = u % (St::NBCH * tileU);
-        const int id = block_id(tab, chunk * 32 / BS + w / tileU, last_blk, NB);
+        const int id = pick_id<St::NBCH>(ids, w / tileU);
         const char* src = (part == 0 ? kpool : vpool) + (size_t)id * bstride + (size_t)g * St::kTile +
                           (size_t)(w % tileU) * 16;
         r[k] = *(const u32x4*)src;
@@ -340,16 +358,24 @@ __global__ __launch_bounds__(64 * NW, 2) void prefill_kernel(PrefillArgs a) {
   float m = -INFINITY, l = 0.f;
   const char* kpool = (const char*)a.k_pool;
   const char* vpool = (const char*)a.v_pool;
-  Stager<D, BS, KVT, NT> A;
-  A.load(kpool, vpool, tab, 0, last_blk, a.NB, a.H_kv, g, tid);
+  using Sg = Stager<D, BS, KVT, NT>;
+  Sg A;
+  int ids[St::NBCH];
+  Sg::chunk_ids(ids, tab, 0, last_blk, a.NB);
+  A.load(kpool, vpool, ids, a.H_kv, g, tid);
   A.store(sh_stage[0], tid, n);
-  if (nch > 1) A.load(kpool, vpool, tab, 1, last_blk, a.NB, a.H_kv, g, tid);
+  Sg::chunk_ids(ids, tab, 1, last_blk, a.NB);
+  if (nch > 1) A.load(kpool, vpool, ids, a.H_kv, g, tid);
+  Sg::chunk_ids(ids, tab, 2, last_blk, a.NB);  // clamped: always inside the table row
   __syncthreads();
   float p[16], alpha;
   for (int c = 0; c < nch; ++c) {
     if (c + 1 < nch) {
       A.store(sh_stage[(c + 1) % kStages], tid, n - 32 * (c + 1));
-      if (c + 2 < nch) A.load(kpool, vpool, tab, c + 2, last_blk, a.NB, a.H_kv, g, tid);
+      if (c + 2 < nch) {
+        A.load(kpool, vpool, ids, a.H_kv, g, tid);
+        Sg::chunk_ids(ids, tab, c + 3, last_blk, a.NB);
+      }
     }
     if (32 * c <= p_wmax) {
       const f32x16 s = chunk_scores<D, BS, KVT>(sh_stage[c % kStages], qop, lane);
