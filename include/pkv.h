@@ -17,7 +17,7 @@
  *                          contiguous staging buffer (swap-out / swap-in)
  *   pkv_paged_attn_decode  one query token per sequence attends over its paged KV
  *   pkv_paged_attn_decode_hinted  the same, given the host's sum of the context
- *                          lengths (skips the merge launch when nothing is cut)
+ *                          lengths (skips the partial results when nothing is cut)
  *   pkv_paged_attn_decode_window  the same, attending only sink tokens and a
  *                          recent window (StreamingLLM; with pkv_seq_streaming_evict)
  *   pkv_paged_prefill      causal attention of a chunk of new tokens per sequence
@@ -159,8 +159,10 @@ int pkv_scatter_blocks(void* k_pool, void* v_pool, int pool_dtype, int32_t NB, i
 /*
  * Design (not on the pages): the decode's scratch.  A sequence whose context
  * is cut into several pieces keeps per-piece partial results (the unnormalised
- * output and the running max and sum of every query head) until a second small
- * launch merges them; the caller owns that memory.
+ * output and the running max and sum of every query head) until they are
+ * merged (by the segment's last piece on the matrix-core path, by a second
+ * small launch on the vector path), plus one arrival counter per segment; the
+ * caller owns that memory.
  *
  * pkv_decode_workspace_bytes — bytes of scratch pkv_paged_attn_decode (and the
  * hinted, window and step variants) needs for a batch of B sequences with H_q
@@ -188,7 +190,8 @@ size_t pkv_decode_workspace_bytes_gqa(int32_t B, int32_t H_q, int32_t H_kv, int3
  * through the block table, and paging moves where the bytes live, not what
  * attention computes.)  Each (sequence, KV head) segment runs an online
  * softmax over its tokens without writing scores to memory; when a segment is
- * cut into several pieces a second small launch merges their partial results.
+ * cut into several pieces their partial results are merged before the call's
+ * work ends (in the same launch on the matrix-core path).
  * n = 0 gives a zero row.  context_lens counts the token appended this step.
  *
  *   out            device fp32 [B][H_q][D]
@@ -204,6 +207,10 @@ size_t pkv_decode_workspace_bytes_gqa(int32_t B, int32_t H_q, int32_t H_kv, int3
  *   workspace      device scratch of >= pkv_decode_workspace_bytes(...) bytes,
  *                  256-byte aligned (may be NULL when that size is 0); its
  *                  contents need no initialisation and are overwritten.
+ *                  (A segment's arrival counter carries a 32-bit token of
+ *                  the call that set it and is cleared by the call's last
+ *                  piece; arbitrary bytes match a call's token with a
+ *                  chance of 2^-32 per counter, zero-filled memory never.)
  *                  Calls that share a workspace must be ordered (one stream,
  *                  or synchronised); concurrent calls on one workspace race.
  *   Requires H_q % H_kv == 0, D in {64, 128, 256}, bs in {8, 16, 32}.
@@ -265,7 +272,7 @@ int pkv_paged_attn_decode_noalloc(float* out, const void* q, int q_dtype, const 
  *     unknown (then the call is pkv_paged_attn_decode).  It only chooses the
  *     work split: when it shows that the planned split keeps every (sequence,
  *     KV head) segment whole, the call runs one piece per segment and skips
- *     the merge launch.  A value above B * min(max_context_len,
+ *     the partial results and their merge.  A value above B * min(max_context_len,
  *     max_blocks_per_seq * bs) cannot be a sum of lengths and is taken as -1.
  *     A wrong value keeps the result within the decode's tolerance; it gives
  *     the same bits as the unhinted call only when it leaves the split

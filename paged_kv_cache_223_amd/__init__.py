@@ -292,9 +292,10 @@ def decode_workspace_bytes(B: int, H_q: int, D: int, max_context_len: int, bs: i
 
 def decode_workspace(B: int, H_q: int, D: int, max_context_len: int, bs: int, H_kv: int | None = None,
                      device="cuda"):
-    """A workspace for these sizes (contents need no initialisation)."""
+    """A workspace for these sizes (zero-filled once; the library needs no initialisation, and
+    zeros rule out even the 2^-32 chance of a stray arrival-counter token)."""
     n = decode_workspace_bytes(B, H_q, D, max_context_len, bs, H_kv)
-    return torch.empty(max(n, 256), dtype=torch.uint8, device=device)
+    return torch.zeros(max(n, 256), dtype=torch.uint8, device=device)
 
 
 def _max_context_len(max_context_len, block_tables, bs: int) -> int:
@@ -313,7 +314,7 @@ def _cached_workspace(device, need: int):
     key = (device.type, device.index, torch.cuda.current_stream(device).cuda_stream)
     ws = _ws_cache.get(key)
     if ws is None or ws.numel() < need:
-        ws = torch.empty(max(need, 1 << 20), dtype=torch.uint8, device=device)
+        ws = torch.zeros(max(need, 1 << 20), dtype=torch.uint8, device=device)
         _ws_cache[key] = ws
     return ws
 

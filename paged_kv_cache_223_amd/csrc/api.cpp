@@ -333,6 +333,9 @@ static int decode_impl(float* out, const void* q, int q_dtype, const void* k_poo
     const WorkspaceLayout wl = workspace_layout(B, H_q, H_kv, D, plan, num_cus, paths);
     a.ws_o = (float*)((char*)workspace + wl.o);
     a.ws_ml = (float*)((char*)workspace + wl.ml);
+    a.ws_ctr = (unsigned long long*)((char*)workspace + wl.ctr);
+    static std::atomic<unsigned int> calls{0};
+    a.call_token = (calls.fetch_add(1) << 1) | 1u;  // odd, so never 0
   }
   a.B = B;
   a.H_q = H_q;

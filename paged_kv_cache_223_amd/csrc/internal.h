@@ -47,11 +47,15 @@ inline SplitPlan plan_splits(int B, int H_kv, int max_ctx) {
 constexpr int kMaxGroupsPerCU = 4;
 
 // Workspace layout, large enough for either path:
+//   [matrix path: one 64-bit arrival counter per (sequence, KV head) segment][pad to 256]
 //   [partial outputs fp32: max(vector path B*H_q*max_splits*D,
 //                              matrix path (CUs*4 + B*H_kv) pieces*16 heads*D)][pad to 256]
 //   [partial (max, sum) fp32: the same count of rows * 2]
+// A counter word is 0 between calls, or holds (call token << 32 | pieces arrived) while its
+// segment's pieces finish; a word whose upper half is not the call's token counts as empty, so
+// the workspace needs no initialisation.
 struct WorkspaceLayout {
-  size_t o, ml, total;
+  size_t ctr, o, ml, total;
 };
 
 inline size_t align256(size_t x) { return (x + 255) / 256 * 256; }
@@ -63,8 +67,9 @@ inline WorkspaceLayout workspace_layout(int B, int H_q, int H_kv, int D, const S
   const size_t mfma_rows = (paths & 2) ? ((size_t)num_cus * kMaxGroupsPerCU + (size_t)B * H_kv) * 16 : 0;
   const size_t rows = vec_rows > mfma_rows ? vec_rows : mfma_rows;
   WorkspaceLayout w;
-  w.o = 0;
-  w.ml = align256(rows * D * sizeof(float));
+  w.ctr = 0;
+  w.o = (paths & 2) ? align256((size_t)B * H_kv * sizeof(unsigned long long)) : 0;
+  w.ml = w.o + align256(rows * D * sizeof(float));
   w.total = w.ml + rows * 2 * sizeof(float);
   return w;
 }
@@ -90,6 +95,8 @@ struct DecodeArgs {
   const float* v_scale;
   float* ws_o;   // [B][H_q][max_splits][D] split partial outputs (unnormalised)
   float* ws_ml;  // [B][H_q][max_splits][2]  split running max (log2 units) and sum
+  unsigned long long* ws_ctr;  // matrix path: arrival counter per segment (see WorkspaceLayout)
+  unsigned int call_token;     // nonzero, different on consecutive calls of the process
   int B, H_q, H_kv, G, D, NB, bs;
   int max_blocks;    // table row stride
   int len_cap;       // min(max_context_len, max_blocks * bs)
@@ -99,7 +106,7 @@ struct DecodeArgs {
   int q_dtype, kv_dtype;
   int num_cus;       // compute units of the device (sizes the matrix-core launch)
   long long sum_len_hint;  // caller's sum of context_lens (< 0: unknown); picks single-piece mode
-  int single_piece;        // set by the launcher: one piece per segment, no merge launch
+  int single_piece;        // set by the launcher: one piece per segment, no partials
   int speculate;           // set by the launcher: the length sum says every length is len_cap, so a
                            // workgroup may load its likely segment's first chunk before its plan
 };

@@ -48,15 +48,15 @@
 //
 // A piece that covers its whole segment writes the final rows; otherwise it
 // writes its unnormalised output and (max, sum) per head to the workspace,
-// and piece_merge (a second, small launch, one workgroup per cut segment)
-// combines the pieces:
+// and the segment's last piece to finish combines the pieces in the same
+// launch:
 //     o = sum_i 2^(m_i - M) o_i / sum_i 2^(m_i - M) l_i,  M = max_i m_i.
-// (Merging inside the piece kernel by the last-arriving workgroup needs a
-// device-scope release/acquire per workgroup; on gfx950 those are whole-L2
-// writeback/invalidate operations, which cost far more than the launch.)
-// When the caller's length sum shows that no segment would be cut, the launch
-// runs in single-piece mode (each workgroup raises upw to the longest segment
-// itself) and piece_merge is not launched.
+// The partials go through agent-scope (cross-XCD coherent) stores and loads
+// and the pieces count themselves with one agent-scope compare-and-swap each
+// (merge_if_last); a release/acquire fence pair would instead write back and
+// invalidate a whole L2 per workgroup, which costs far more.  When the
+// caller's length sum shows that no segment would be cut, the launch runs in
+// single-piece mode (each workgroup raises upw to the longest segment itself).
 //
 // Fused step (bf16 pools): the step's new token of each sequence is put into
 // the loaded operands of the chunk holding position n - 1 and stored into the
@@ -332,7 +332,7 @@ __device__ __forceinline__ void write_new_token(const DecodeArgs& a, int b, int 
 // which keeps register use (and so occupancy) at its single-piece minimum.
 // The workgroup's NW (4 or 8) waves take the piece's chunks round-robin and
 // merge through LDS; a piece that is a whole segment writes its final rows,
-// the others write partials that piece_merge combines.
+// the others write partials that the segment's last piece combines.
 // ---------------------------------------------------------------------------
 constexpr int kMinUnits = 8;
 constexpr int kLensInRegs = 16;  // lengths a lane keeps in registers (B <= 1024 in one pass)
@@ -345,6 +345,7 @@ __device__ __forceinline__ int chunks_of(int n, int cap) {
 struct PiecePlan {
   int b, g, n, lo, hi, np;  // piece [lo, hi) of segment (b, g); np pieces in the segment; n = its length
   int id;                   // the piece's number in sequence-major order (its workspace row)
+  int first;                // the number of the segment's first piece
 };
 
 constexpr int kSizeClasses = 8;  // piece-size classes, a factor sqrt(2) apart
@@ -484,6 +485,7 @@ __device__ void plan_piece(const DecodeArgs& a, int target, int item, int lane, 
       pp.np = np;
       pp.n = lane_value(n, src);
       pp.id = lane_value(cbase + call - all, src) + rr;
+      pp.first = pp.id - j;
       pp.lo = (int)((long long)j * cbb / np);
       pp.hi = (int)((long long)(j + 1) * cbb / np);
     }
@@ -559,6 +561,64 @@ __device__ __forceinline__ void run_piece(const DecodeArgs& a, int b, int g, int
   }
 }
 
+// Merge of a cut segment inside the piece kernel, by the piece that finishes last.  Every piece
+// stores its partials with agent-scope stores (they reach the level the XCDs share), the
+// workgroup's barrier waits for them, and one thread then counts the piece in the segment's
+// arrival word with an agent-scope compare-and-swap: the word holds (call token, pieces arrived),
+// and a word carrying another token counts as 0, so neither a previous call's word nor
+// uninitialised memory is taken for this call's.  The piece that brings the count to np clears the
+// word for the next call and combines the np partials (agent-scope loads) into the output rows:
+//     o = sum_i 2^(m_i - M) o_i / sum_i 2^(m_i - M) l_i,  M = max_i m_i.
+// No piece waits for another, so nothing can hang on a piece that runs late.
+constexpr int kMergeBatch = 8;
+
+template <int NT>
+__device__ void merge_if_last(const DecodeArgs& a, int b, int g, int np, int first, size_t orow, int tid) {
+  __shared__ int sh_last;
+  __syncthreads();  // every thread's partial stores have completed
+  if (tid == 0) {
+    unsigned long long* ctr = a.ws_ctr + ((size_t)b * a.H_kv + g);
+    const unsigned long long tag = (unsigned long long)a.call_token << 32;
+    unsigned long long cur = __hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    unsigned long long arrived;
+    do {
+      arrived = ((cur >> 32) == a.call_token ? (cur & 0xFFFFFFFFull) : 0ull) + 1ull;
+    } while (!__hip_atomic_compare_exchange_strong(ctr, &cur, tag | arrived, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
+                                                   __HIP_MEMORY_SCOPE_AGENT));
+    const bool last = arrived == (unsigned long long)np;
+    if (last) __hip_atomic_store(ctr, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    sh_last = last;
+  }
+  __syncthreads();
+  if (!sh_last) return;
+  const int G = a.G, D = a.D;
+  for (int e = tid; e < G * D; e += NT) {
+    const int hl = e / D, col = e % D;
+    float M = -INFINITY, L = 0.f, O = 0.f;
+    for (int p = 0; p < np; p += kMergeBatch) {
+      float mp[kMergeBatch], lp[kMergeBatch], op[kMergeBatch];
+#pragma unroll
+      for (int i = 0; i < kMergeBatch; ++i) {  // past the last piece: reload the last, weigh it 0
+        const size_t r = (size_t)(first + min(p + i, np - 1)) * 16 + hl;
+        mp[i] = __hip_atomic_load(&a.ws_ml[2 * r], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        lp[i] = __hip_atomic_load(&a.ws_ml[2 * r + 1], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        op[i] = __hip_atomic_load(&a.ws_o[r * D + col], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+#pragma unroll
+      for (int i = 0; i < kMergeBatch; ++i) {
+        if (p + i >= np || mp[i] == -INFINITY) continue;  // no piece, or one that attended nothing
+        const float mn = fmaxf(M, mp[i]);
+        const float so = M == -INFINITY ? 0.f : exp2_fast(M - mn);
+        const float sn = exp2_fast(mp[i] - mn);
+        L = L * so + lp[i] * sn;
+        O = O * so + op[i] * sn;
+        M = mn;
+      }
+    }
+    a.out[orow + e] = L > 0.f ? O / L : 0.f;  // nothing attended: zero row
+  }
+}
+
 template <int D, int BS, int KVT, int NW, bool APPEND>
 __global__ __launch_bounds__(64 * NW, KVT == PKV_FP8_E4M3 ? 3 : 2) void decode_piece_kernel(DecodeArgs a,
                                                                                           int target) {
@@ -593,7 +653,7 @@ __global__ __launch_bounds__(64 * NW, KVT == PKV_FP8_E4M3 ? 3 : 2) void decode_p
                a.max_blocks - 1, a.NB, a.H_kv, guess_g, lane);
   }
   // wave 0 plans; the other waves wait at the barrier rather than repeat its scalar work
-  __shared__ int sh_plan[7];
+  __shared__ int sh_plan[8];
   if (w == 0) {
     PiecePlan pp;
     plan_piece(a, target, item, lane, pp);
@@ -605,6 +665,7 @@ __global__ __launch_bounds__(64 * NW, KVT == PKV_FP8_E4M3 ? 3 : 2) void decode_p
       sh_plan[4] = pp.hi;
       sh_plan[5] = pp.n;
       sh_plan[6] = pp.id;
+      sh_plan[7] = pp.first;
     }
   }
   __syncthreads();
@@ -612,7 +673,7 @@ __global__ __launch_bounds__(64 * NW, KVT == PKV_FP8_E4M3 ? 3 : 2) void decode_p
   // no piece for this workgroup (a plan naming a segment outside the batch runs nothing either)
   if (b < 0 || b >= a.B || (unsigned)g >= (unsigned)a.H_kv) return;
   const int np = uniform(sh_plan[2]), lo = uniform(sh_plan[3]), hi = uniform(sh_plan[4]);
-  const int n = uniform(sh_plan[5]), pid = uniform(sh_plan[6]);
+  const int n = uniform(sh_plan[5]), pid = uniform(sh_plan[6]), first_pid = uniform(sh_plan[7]);
   int hlo, hhi;
   seq_hole(a, b, hlo, hhi);
   hlo = uniform(hlo);
@@ -669,95 +730,18 @@ __global__ __launch_bounds__(64 * NW, KVT == PKV_FP8_E4M3 ? 3 : 2) void decode_p
     O *= vs;
     if (np == 1) {
       a.out[orow + e] = L > 0.f ? O / L : 0.f;  // nothing attended: zero row
-    } else {
-      a.ws_o[(prow + hh) * D + col] = O;
+    } else {  // partials, coherent across the XCDs' caches (agent scope)
+      __hip_atomic_store(&a.ws_o[(prow + hh) * D + col], O, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       if (col == 0) {
-        a.ws_ml[2 * (prow + hh)] = M;
-        a.ws_ml[2 * (prow + hh) + 1] = L;
+        __hip_atomic_store(&a.ws_ml[2 * (prow + hh)], M, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(&a.ws_ml[2 * (prow + hh) + 1], L, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
     }
   }
+  if (np > 1) merge_if_last<NT>(a, b, g, np, first_pid, orow, tid);
   if constexpr (APPEND)
     if (writer && w == 0) write_new_token<D, BS>(a, b, g, new_slot, lane);
 }
-
-// Merge the pieces of every segment cut into several.  Workgroup i takes the i-th such segment in
-// sequence-major order (fewer than `target` segments can be cut: each holds more than upw of the
-// at most upw * target chunks); one thread per output element of the segment's G heads.  Every
-// workgroup's first wave finds its segment from the lengths (the plan's upw, then prefix scans
-// over sequences of cut segments and of pieces); every thread then takes the pieces eight at a
-// time, every load of a batch in flight at once, with an online rescale:
-//     o = sum_i 2^(m_i - M) o_i / sum_i 2^(m_i - M) l_i,  M = max_i m_i.
-// Two dependent memory round trips for up to eight pieces: the lengths, then the partials.
-constexpr int kMergeBatch = 8;
-
-__global__ __launch_bounds__(1024) void piece_merge_kernel(DecodeArgs a, int target) {
-  const int lane = threadIdx.x & 63;
-  const int B = a.B, G = a.G, D = a.D, H_kv = a.H_kv;
-  __shared__ int sh_seg[4];
-  if (threadIdx.x < 64) {  // wave 0 finds the segment; the others wait at the barrier
-    int nl[kLensInRegs];
-    const int upw = plan_upw(a, target, lane, nl);
-    const int item = blockIdx.x;
-    int base = 0, pbase = 0, sb = -1, sg = 0, snp = 0, sfirst = 0;
-    for (int k = 0; k * 64 < B && sb < 0; ++k) {
-      const int npb = ceil_div_units((len_at(a, nl, k, lane) + 31) / 32, upw);
-      const int all = npb * H_kv;         // pieces of the sequence
-      const int cnt = npb > 1 ? H_kv : 0;  // its segments that were cut
-      const int incl = wave_incl_scan(cnt);
-      const int pincl = wave_incl_scan(all);
-      const bool hit = cnt > 0 && base + incl - cnt <= item && item < base + incl;
-      const unsigned long long m = __ballot(hit);
-      if (m) {
-        const int src = __ffsll((long long)m) - 1;
-        sb = 64 * k + src;
-        sg = item - lane_value(base + incl - cnt, src);
-        snp = lane_value(npb, src);
-        sfirst = lane_value(pbase + pincl - all, src) + sg * snp;
-      }
-      base += lane_value(incl, 63);
-      pbase += lane_value(pincl, 63);
-    }
-    if (lane == 0) {
-      sh_seg[0] = uniform(sb);
-      sh_seg[1] = sg;
-      sh_seg[2] = snp;
-      sh_seg[3] = sfirst;
-    }
-  }
-  __syncthreads();
-  const int sb = uniform(sh_seg[0]), g = uniform(sh_seg[1]);
-  if (sb < 0 || sb >= B || (unsigned)g >= (unsigned)H_kv) return;  // fewer segments were cut than
-                                                                     // there are workgroups
-  const int np = uniform(sh_seg[2]), first = uniform(sh_seg[3]);
-  const size_t orow = (size_t)sb * a.H_q + (size_t)g * G;
-  for (int e = threadIdx.x; e < G * D; e += blockDim.x) {
-    const int hl = e / D, col = e % D;
-    float M = -INFINITY, L = 0.f, O = 0.f;
-    for (int p = 0; p < np; p += kMergeBatch) {
-      float mp[kMergeBatch], lp[kMergeBatch], op[kMergeBatch];
-#pragma unroll
-      for (int i = 0; i < kMergeBatch; ++i) {  // past the last piece: reload the last, weigh it 0
-        const size_t r = (size_t)(first + min(p + i, np - 1)) * 16 + hl;
-        mp[i] = a.ws_ml[2 * r];
-        lp[i] = a.ws_ml[2 * r + 1];
-        op[i] = a.ws_o[r * D + col];
-      }
-#pragma unroll
-      for (int i = 0; i < kMergeBatch; ++i) {
-        if (p + i >= np || mp[i] == -INFINITY) continue;  // no piece, or one that attended nothing
-        const float mn = fmaxf(M, mp[i]);
-        const float so = M == -INFINITY ? 0.f : exp2_fast(M - mn);
-        const float sn = exp2_fast(mp[i] - mn);
-        L = L * so + lp[i] * sn;
-        O = O * so + op[i] * sn;
-        M = mn;
-      }
-    }
-    a.out[(orow + hl) * D + col] = L > 0.f ? O / L : 0.f;  // nothing attended: zero row
-  }
-}
-
 
 // workgroups of decode_piece_kernel<D, BS, KVT, NW, APPEND> one CU holds at once
 template <int D, int BS, int KVT, int NW, bool APPEND>
@@ -793,7 +777,7 @@ hipError_t launch_mfma_a(const DecodeArgs& a, hipStream_t s) {
   // Single-piece mode when the caller's length sum shows that the plan would not cut any
   // segment: ceil(sum / 32) is at most the sum of per-sequence chunk counts, so upw_lo is at
   // most the plan's upw; if even upw_lo covers the longest segment the plan is one piece per
-  // segment and the merge launch can be skipped.  The kernel then raises upw to its own
+  // segment and no piece writes partials.  The kernel then raises upw to its own
   // longest segment, so a wrong sum only changes the balance of the work, never the result.
   DecodeArgs b = a;
   b.single_piece = 0;
@@ -811,11 +795,7 @@ hipError_t launch_mfma_a(const DecodeArgs& a, hipStream_t s) {
     hipLaunchKernelGGL((decode_piece_kernel<D, BS, KVT, 8, APPEND>), dim3((unsigned)grid), dim3(512), 0, s, b, target);
   else
     hipLaunchKernelGGL((decode_piece_kernel<D, BS, KVT, 4, APPEND>), dim3((unsigned)grid), dim3(256), 0, s, b, target);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess || b.single_piece) return e;
-  const int merge_threads = a.G * D < 1024 ? a.G * D : 1024;  // a multiple of 64
-  hipLaunchKernelGGL(piece_merge_kernel, dim3((unsigned)target), dim3(merge_threads), 0, s, b, target);
-  return hipGetLastError();
+  return hipGetLastError();  // cut segments are merged inside the launch
 }
 
 template <int D, int BS, int KVT>
