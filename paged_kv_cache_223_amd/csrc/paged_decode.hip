@@ -773,7 +773,7 @@ hipError_t launch_mfma_a(const DecodeArgs& a, hipStream_t s) {
   const int target8 = piece_groups_per_cu<D, BS, KVT, 8, APPEND>() * a.num_cus;
   const bool wide = segments <= target8 || (KVT == PKV_BF16 && segments <= 2LL * target8);
   const int target = wide ? target8 : piece_groups_per_cu<D, BS, KVT, 4, APPEND>() * a.num_cus;
-  const long long grid = (long long)target + segments;
+  long long grid = (long long)target + segments;
   // Single-piece mode when the caller's length sum shows that the plan would not cut any
   // segment: ceil(sum / 32) is at most the sum of per-sequence chunk counts, so upw_lo is at
   // most the plan's upw; if even upw_lo covers the longest segment the plan is one piece per
@@ -790,6 +790,9 @@ hipError_t launch_mfma_a(const DecodeArgs& a, hipStream_t s) {
     // every length at len_cap: one size class and no empty sequence, so workgroup i's segment is
     // (i / H_kv, i % H_kv), which the kernel checks against its plan before using the early loads
     b.speculate = b.single_piece && a.len_cap > 0 && a.sum_len_hint == (long long)a.B * a.len_cap;
+    // one piece per segment at most: workgroups past B * H_kv would only plan and exit, and on a
+    // batch of one round they are dispatched at the end, as the last segments finish
+    if (b.single_piece) grid = segments;
   }
   if (wide)
     hipLaunchKernelGGL((decode_piece_kernel<D, BS, KVT, 8, APPEND>), dim3((unsigned)grid), dim3(512), 0, s, b, target);
