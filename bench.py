@@ -327,10 +327,8 @@ def bench_decode(wkey, args, torch, pkv, dev, steps, warmup, cpu_seconds, headli
     traffic = measured_traffic(wkey)
     roofline = {
         "bound": "hbm",
-        "kernel": ("decode step call (append fused) = decode_piece_kernel (+ piece_merge_kernel when a segment "
-                   "is cut into pieces)" if fused else
-                   "paged_attn_decode call = decode_piece_kernel (+ piece_merge_kernel when a segment is cut into "
-                   "pieces)"),
+        "kernel": ("decode step call (append fused) = decode_piece_kernel (cut segments merged inside it)"
+                   if fused else "paged_attn_decode call = decode_piece_kernel (cut segments merged inside it)"),
         "achieved": round(dec_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
         "frac": round(dec_gbps / HBM_PEAK_GBPS, 4),
         "algorithmic_bytes_per_launch": call_bytes,

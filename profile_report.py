@@ -32,7 +32,7 @@ import sqlite3
 import sys
 
 from bench import COUNTERS, KERNEL_SOURCE, PREFILL_COUNTERS, PREFILL_SOURCE, ROOT, source_hash
-DECODE_KERNELS = ("decode_piece_kernel", "piece_merge_kernel")
+DECODE_KERNELS = ("decode_piece_kernel",)  # cut segments are merged inside it
 COPY_BYTES = 1 << 30
 
 TRACE_CMD = ("rocprofv3 --kernel-trace --stats -T -d <out> -o trace -- python3 bench.py --workload {w} --only "
@@ -188,7 +188,6 @@ def report_decode(w, t_dir, f_dir, r_dir, cf_dir, cw_dir, kernels=DECODE_KERNELS
 
     entry = {"code_sha256_16": sha, "fetch_factor": ff, "write_factor": wf}
     total = 0.0
-    # the merge is not launched when every segment runs as one piece (the step's length hint)
     present = [k for k in DECODE_KERNELS if k in fetch and k in write and k in avg]
     absent = [k for k in DECODE_KERNELS if k not in present]
     for k in present:
@@ -232,7 +231,7 @@ def report_decode(w, t_dir, f_dir, r_dir, cf_dir, cw_dir, kernels=DECODE_KERNELS
         L.append(f"| {k} | {fetch[k][0]:.1f} | {write[k][0]:.1f} | {fetch[k][1]} | "
                  f"{entry[k]['fetch_bytes'] / 1e6:.2f} | {entry[k]['write_bytes'] / 1e6:.2f} |")
     for k in absent:
-        L.append(f"| {k} | not launched: every segment ran as one piece | | 0 | 0 | 0 |")
+        L.append(f"| {k} | not launched | | 0 | 0 | 0 |")
     L += ["", f"Decode call total: {total / 1e6:.2f} MB moved beyond L2 per launch "
           f"(kernel code sha256[:16], comments and whitespace removed: {sha}).", ""]
     with open(os.path.join(ROOT, "profiles", f"decode_{w}.md"), "w") as f:
