@@ -7,6 +7,7 @@
 
 #include <atomic>
 #include <cmath>
+#include <random>
 
 #include "internal.h"
 
@@ -334,8 +335,10 @@ static int decode_impl(float* out, const void* q, int q_dtype, const void* k_poo
     a.ws_o = (float*)((char*)workspace + wl.o);
     a.ws_ml = (float*)((char*)workspace + wl.ml);
     a.ws_ctr = (unsigned long long*)((char*)workspace + wl.ctr);
-    static std::atomic<unsigned int> calls{0};
-    a.call_token = (calls.fetch_add(1) << 1) | 1u;  // odd, so never 0
+    // a different odd token per call; the count starts at a per-process random value, so that a
+    // word another process left in reused memory is not taken for this process's first calls
+    static std::atomic<unsigned int> calls{(unsigned int)std::random_device{}()};
+    a.call_token = (calls.fetch_add(1) << 1) | 1u;
   }
   a.B = B;
   a.H_q = H_q;

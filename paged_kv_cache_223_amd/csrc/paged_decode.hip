@@ -567,7 +567,7 @@ __device__ __forceinline__ void run_piece(const DecodeArgs& a, int b, int g, int
 // arrival word with an agent-scope compare-and-swap: the word holds (call token, pieces arrived),
 // and a word carrying another token counts as 0, so neither a previous call's word nor
 // uninitialised memory is taken for this call's.  The piece that brings the count to np clears the
-// word for the next call and combines the np partials (agent-scope loads) into the output rows:
+// word and combines the np partials (agent-scope loads) into the output rows:
 //     o = sum_i 2^(m_i - M) o_i / sum_i 2^(m_i - M) l_i,  M = max_i m_i.
 // No piece waits for another, so nothing can hang on a piece that runs late.
 constexpr int kMergeBatch = 8;
@@ -579,14 +579,16 @@ __device__ void merge_if_last(const DecodeArgs& a, int b, int g, int np, int fir
   if (tid == 0) {
     unsigned long long* ctr = a.ws_ctr + ((size_t)b * a.H_kv + g);
     const unsigned long long tag = (unsigned long long)a.call_token << 32;
-    unsigned long long cur = __hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    // first guess: this piece is the last one (one round trip when it is, the case whose latency
+    // ends the segment); a failed exchange returns the word as it is
+    unsigned long long cur = tag | (unsigned long long)(np - 1);
     unsigned long long arrived;
     do {
       arrived = ((cur >> 32) == a.call_token ? (cur & 0xFFFFFFFFull) : 0ull) + 1ull;
     } while (!__hip_atomic_compare_exchange_strong(ctr, &cur, tag | arrived, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
                                                    __HIP_MEMORY_SCOPE_AGENT));
     const bool last = arrived == (unsigned long long)np;
-    if (last) __hip_atomic_store(ctr, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (last) __hip_atomic_store(ctr, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);  // clean for later calls
     sh_last = last;
   }
   __syncthreads();
