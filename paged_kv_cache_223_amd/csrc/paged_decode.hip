@@ -780,7 +780,8 @@ hipError_t launch_mfma_a(const DecodeArgs& a, hipStream_t s) {
   // segment: ceil(sum / 32) is at most the sum of per-sequence chunk counts, so upw_lo is at
   // most the plan's upw; if even upw_lo covers the longest segment the plan is one piece per
   // segment and no piece writes partials.  The kernel then raises upw to its own
-  // longest segment, so a wrong sum only changes the balance of the work, never the result.
+  // longest segment, so a wrong sum only changes the balance of the work and the order of the
+  // reduction (the result stays within rounding, not always bit for bit).
   DecodeArgs b = a;
   b.single_piece = 0;
   b.speculate = 0;
