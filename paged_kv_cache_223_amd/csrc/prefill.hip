@@ -48,10 +48,16 @@ namespace {
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 
 __device__ __forceinline__ f32x16 mfma32(u32x4 a, u32x4 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c,
                                                  0, 0, 0);
+}
+
+__device__ __forceinline__ f32x16 mfma32_f16(u32x4 a, u32x4 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
 }
 
 // two fp32 -> packed bf16 pair, round to nearest even (v_cvt_pk_bf16_f32); x in the low half
@@ -61,17 +67,40 @@ __device__ __forceinline__ uint32_t pack_bf16_rne(float x, float y) {
 
 constexpr int kStages = 2;  // the chunk being computed and the next one, written at the iteration's start
 
-// One 32-key chunk in LDS.
+// One 32-key chunk in LDS.  V holds two-byte elements: fp16 on the fast pass, the raw bf16 on the
+// rerun of a workgroup whose V does not fit fp16.
 template <int D, int BS, int KVT>
 struct Stage {
   static constexpr int S = KvTraits<KVT>::kBytes;
   static constexpr int NBCH = BS >= 32 ? 1 : 32 / BS;  // blocks of one chunk
   static constexpr int kTile = D * BS * S;             // one block's tile of one head (K or V) in the pool
   static constexpr int kKBytes = 32 * D * S;           // K: [D/8][32][8 elements]
-  static constexpr int kVRow = 32 * S + (S == 2 ? 16 : 8);  // V row of 32 keys, padded (bank spread)
+  static constexpr int kVRow = 32 * 2 + 16;            // V row of 32 two-byte elements, padded (bank spread)
   static constexpr int kBytes = kKBytes + D * kVRow;
   static constexpr int kUnits = 2 * NBCH * kTile / 16;  // 16-byte pool units of the chunk (K then V)
 };
+
+// bf16 pair -> fp16 pair, exact while both magnitudes are at most 65280 (the largest bf16 value
+// below fp16's maximum; bf16_pair_beyond_f16 tells)
+__device__ __forceinline__ uint32_t bf16_pair_to_f16(uint32_t w) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2{__builtin_bit_cast(float, w << 16),
+                                                                      __builtin_bit_cast(float, w & 0xFFFF0000u)}),
+                                                              f16x2));
+}
+
+// whether a bf16 pair holds a value outside [-65280, 65280], an infinity or a NaN
+__device__ __forceinline__ bool bf16_pair_beyond_f16(uint32_t w) {
+  return (w & 0x7FFFu) > 0x477Fu || ((w >> 16) & 0x7FFFu) > 0x477Fu;
+}
+
+// eight E4M3 codes (w0: codes 0-3, w1: codes 4-7) -> four fp16 pairs in order (exact: every E4M3
+// value is an fp16 value)
+__device__ __forceinline__ u32x4 e4m3x8_to_f16x8(uint32_t w0, uint32_t w1) {
+  return u32x4{__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w0, 1.0f, false)),
+               __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w0, 1.0f, true)),
+               __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w1, 1.0f, false)),
+               __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w1, 1.0f, true))};
+}
 
 // ids[idx] for a lane-dependent idx < N, as selects between scalars (an indexed read of the local
 // array would put it in scratch memory).
@@ -122,8 +151,10 @@ struct Stager {
   // Into the LDS layout.  nvalid = keys of the chunk before the sequence's end: on the chunk
   // holding the end (nvalid < 32) V elements of later keys are zeroed, since a P of 0 does not
   // cancel whatever the pool holds there (K needs nothing: masked scores are selected, not
-  // multiplied).
-  __device__ __forceinline__ void store(char* lds, int tid, int nvalid) const {
+  // multiplied).  V goes in as fp16, or (RAW) as the pool's bf16; a bf16 value that fp16 cannot
+  // hold sets *beyond.
+  template <bool RAW>
+  __device__ __forceinline__ void store(char* lds, int tid, int nvalid, int* beyond) const {
     constexpr int S = St::S;
     constexpr int E = 16 / S;  // elements per 16-byte unit
 #pragma unroll
@@ -156,18 +187,29 @@ struct Stager {
         if constexpr (S == 2) {
           if constexpr (BS >= 8) {  // a unit is 8 keys of one row
             const int d = e0 / BS, t0 = e0 % BS;
-            *(u32x4*)(vb + (size_t)d * St::kVRow + (size_t)(blk * BS + t0) * 2) = v;
+            u32x4 h = v;
+            if constexpr (!RAW) {
+              bool out = false;
+#pragma unroll
+              for (int i = 0; i < 4; ++i) {
+                out = out || bf16_pair_beyond_f16(v[i]);
+                h[i] = bf16_pair_to_f16(v[i]);
+              }
+              if (out) *beyond = 1;
+            }
+            *(u32x4*)(vb + (size_t)d * St::kVRow + (size_t)(blk * BS + t0) * 2) = h;
           }
         } else {
+          const u32x4 h0 = e4m3x8_to_f16x8(v.x, v.y), h1 = e4m3x8_to_f16x8(v.z, v.w);  // codes 0-7, 8-15
           if constexpr (BS == 8) {  // a unit is two rows of 8 keys
             const int d = e0 / 8;
-            *(u32x2*)(vb + (size_t)d * St::kVRow + (size_t)blk * 8) = u32x2{v.x, v.y};
-            *(u32x2*)(vb + (size_t)(d + 1) * St::kVRow + (size_t)blk * 8) = u32x2{v.z, v.w};
+            *(u32x4*)(vb + (size_t)d * St::kVRow + (size_t)blk * 16) = h0;
+            *(u32x4*)(vb + (size_t)(d + 1) * St::kVRow + (size_t)blk * 16) = h1;
           } else {  // 16 keys of one row
             const int d = e0 / BS, t0 = e0 % BS;
-            char* p = vb + (size_t)d * St::kVRow + (size_t)(blk * BS + t0);
-            *(u32x2*)p = u32x2{v.x, v.y};
-            *(u32x2*)(p + 8) = u32x2{v.z, v.w};
+            char* p = vb + (size_t)d * St::kVRow + (size_t)(blk * BS + t0) * 2;
+            *(u32x4*)p = h0;
+            *(u32x4*)(p + 16) = h1;
           }
         }
       }
@@ -266,9 +308,24 @@ __device__ __forceinline__ void chunk_pack(const float (&p)[16], float& l, u32x4
   regroup_p(wl, pl);
 }
 
+// P as fp16 pairs (round to nearest even: relative error 2^-11, against 2^-8 for one bf16 part),
+// summed into l from the fp32 values, regrouped into the PV B operands.
+__device__ __forceinline__ void chunk_pack16(const float (&p)[16], float& l, u32x4 (&ph)[2]) {
+  float ps[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) ps[j] = (p[4 * j] + p[4 * j + 1]) + (p[4 * j + 2] + p[4 * j + 3]);
+  l += (ps[0] + ps[1]) + (ps[2] + ps[3]);
+  uint32_t wh[8];
+#pragma unroll
+  for (int k = 0; k < 8; ++k)
+    wh[k] = __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2{p[2 * k], p[2 * k + 1]}), f16x2));
+  regroup_p(wh, ph);
+}
+
 // O^T += V^T P^T over one staged chunk: A = 8 consecutive keys of one head-dim row (V rows past n
-// were zeroed when the chunk was staged).
-template <int D, int BS, int KVT>
+// were zeroed when the chunk was staged).  Fast pass: V and P in fp16, one MFMA per 16-key half.
+// RAW (a rerun with the pool's bf16 V): P as bf16 hi + lo, two MFMAs per half.
+template <int D, int BS, int KVT, bool RAW>
 __device__ __forceinline__ void chunk_pv(const char* lds, const u32x4 (&ph)[2], const u32x4 (&pl)[2],
                                          f32x16 (&acc)[D / 32], int lane) {
   using St = Stage<D, BS, KVT>;
@@ -278,16 +335,13 @@ __device__ __forceinline__ void chunk_pv(const char* lds, const u32x4 (&ph)[2], 
   for (int t = 0; t < D / 32; ++t) {
 #pragma unroll
     for (int a = 0; a < 2; ++a) {
-      u32x4 vop;
-      const char* row = vb + (size_t)(32 * t + key) * St::kVRow;
-      if constexpr (KVT == PKV_BF16) {
-        vop = *(const u32x4*)(row + (16 * a + 8 * h) * 2);
+      const u32x4 vop = *(const u32x4*)(vb + (size_t)(32 * t + key) * St::kVRow + (16 * a + 8 * h) * 2);
+      if constexpr (RAW) {
+        acc[t] = mfma32(vop, ph[a], acc[t]);
+        acc[t] = mfma32(vop, pl[a], acc[t]);
       } else {
-        const u32x2 w = *(const u32x2*)(row + 16 * a + 8 * h);
-        vop = e4m3x8_to_bf16x8(w.x, w.y);
+        acc[t] = mfma32_f16(vop, ph[a], acc[t]);
       }
-      acc[t] = mfma32(vop, ph[a], acc[t]);
-      acc[t] = mfma32(vop, pl[a], acc[t]);
     }
   }
 }
@@ -358,39 +412,57 @@ __global__ __launch_bounds__(64 * NW, 2) void prefill_kernel(PrefillArgs a) {
   float m = -INFINITY, l = 0.f;
   const char* kpool = (const char*)a.k_pool;
   const char* vpool = (const char*)a.v_pool;
+  // Fast pass with V and P in fp16.  A bf16 V value that fp16 cannot hold (beyond +-65280, or not
+  // finite) raises sh_beyond while the chunks are staged; the workgroup then runs again with the
+  // pool's bf16 V and P as bf16 hi + lo parts, which holds any input (E4M3 values always fit).
+  __shared__ int sh_beyond;
+  if (tid == 0) sh_beyond = 0;
   using Sg = Stager<D, BS, KVT, NT>;
-  Sg A;
-  int ids[St::NBCH];
-  Sg::chunk_ids(ids, tab, 0, last_blk, a.NB);
-  A.load(kpool, vpool, ids, a.H_kv, g, tid);
-  A.store(sh_stage[0], tid, n);
-  Sg::chunk_ids(ids, tab, 1, last_blk, a.NB);
-  if (nch > 1) A.load(kpool, vpool, ids, a.H_kv, g, tid);
-  Sg::chunk_ids(ids, tab, 2, last_blk, a.NB);  // clamped: always inside the table row
-  __syncthreads();
-  float p[16], alpha;
-  for (int c = 0; c < nch; ++c) {
-    if (c + 1 < nch) {
-      A.store(sh_stage[(c + 1) % kStages], tid, n - 32 * (c + 1));
-      if (c + 2 < nch) {
-        A.load(kpool, vpool, ids, a.H_kv, g, tid);
-        Sg::chunk_ids(ids, tab, c + 3, last_blk, a.NB);
-      }
-    }
-    if (32 * c <= p_wmax) {
-      const f32x16 s = chunk_scores<D, BS, KVT>(sh_stage[c % kStages], qop, lane);
-      const bool moved = 32 * c + 31 > p_min ? chunk_exp<true>(s, m, l, alpha, p, 32 * c, p_lane, sl, lane)
-                                             : chunk_exp<false>(s, m, l, alpha, p, 32 * c, p_lane, sl, lane);
-      if (moved) {
+  auto run = [&](auto raw_tag) {
+    constexpr bool RAW = decltype(raw_tag)::value;
 #pragma unroll
-        for (int t = 0; t < D / 32; ++t) acc[t] *= alpha;
-      }
-      u32x4 ph[2], pl[2];
-      chunk_pack(p, l, ph, pl);
-      chunk_pv<D, BS, KVT>(sh_stage[c % kStages], ph, pl, acc, lane);
-    }
+    for (int t = 0; t < D / 32; ++t) acc[t] = f32x16{};
+    m = -INFINITY;
+    l = 0.f;
+    Sg A;
+    int ids[St::NBCH];
+    Sg::chunk_ids(ids, tab, 0, last_blk, a.NB);
+    A.load(kpool, vpool, ids, a.H_kv, g, tid);
+    A.template store<RAW>(sh_stage[0], tid, n, &sh_beyond);
+    Sg::chunk_ids(ids, tab, 1, last_blk, a.NB);
+    if (nch > 1) A.load(kpool, vpool, ids, a.H_kv, g, tid);
+    Sg::chunk_ids(ids, tab, 2, last_blk, a.NB);  // clamped: always inside the table row
     __syncthreads();
-  }
+    float p[16], alpha;
+    for (int c = 0; c < nch; ++c) {
+      if (c + 1 < nch) {
+        A.template store<RAW>(sh_stage[(c + 1) % kStages], tid, n - 32 * (c + 1), &sh_beyond);
+        if (c + 2 < nch) {
+          A.load(kpool, vpool, ids, a.H_kv, g, tid);
+          Sg::chunk_ids(ids, tab, c + 3, last_blk, a.NB);
+        }
+      }
+      if (32 * c <= p_wmax) {
+        const f32x16 s = chunk_scores<D, BS, KVT>(sh_stage[c % kStages], qop, lane);
+        const bool moved = 32 * c + 31 > p_min ? chunk_exp<true>(s, m, l, alpha, p, 32 * c, p_lane, sl, lane)
+                                               : chunk_exp<false>(s, m, l, alpha, p, 32 * c, p_lane, sl, lane);
+        if (moved) {
+#pragma unroll
+          for (int t = 0; t < D / 32; ++t) acc[t] *= alpha;
+        }
+        u32x4 ph[2], pl[2];
+        if constexpr (RAW)
+          chunk_pack(p, l, ph, pl);
+        else
+          chunk_pack16(p, l, ph);
+        chunk_pv<D, BS, KVT, RAW>(sh_stage[c % kStages], ph, pl, acc, lane);
+      }
+      __syncthreads();
+    }
+  };
+  run(std::false_type{});
+  if constexpr (KVT == PKV_BF16)
+    if (uniform(sh_beyond)) run(std::true_type{});  // every store to sh_beyond was before the last barrier
   // ---- normalise and write the column's row: acc[t] register i is head-dim row
   // 32 t + 8 (i / 4) + 4 h + i % 4 of O^T
   if (!qvalid) return;

@@ -183,3 +183,26 @@ def test_prefill_edge_cases():
     o = out.cpu().numpy()
     assert not o[0:20].any()
     assert row_rel_err(o[20:50].astype(np.float64), ref[20:50]) <= 2e-3
+
+
+@pytest.mark.parametrize("bs", [8, 16, 32])
+def test_prefill_v_beyond_fp16_range(bs):
+    """The fast pass holds V in fp16; a workgroup whose bf16 V holds a value fp16 cannot (here a
+    whole sequence's V scaled past 65280, and one sequence with a single such value) runs again
+    with the pool's bf16 V.  Every row matches the oracle, including the sequences with ordinary
+    V beside them."""
+    print(f"prefill large V bs={bs}", flush=True)
+    c = Case(priors=[100, 20, 64], chunks=[60, 90, 33], H_q=32, H_kv=4, d=128, bs=bs, kv_dtype="bf16", seed=31)
+    as_f32 = lambda bits: (bits.astype(np.uint32) << 16).view(np.float32)  # noqa: E731
+    c.v_rows[0] = workloads.round_bf16(as_f32(c.v_rows[0]) * np.float32(3e5))  # |v| up to about 1.5e6
+    v2 = as_f32(c.v_rows[2])
+    v2[40, 1, 7] = np.float32(7.0e4)  # one value past fp16's range (bf16 70144), in a chunk queries read
+    c.v_rows[2] = workloads.round_bf16(v2)
+    c.device()
+    got = c.prefill()
+    kp, vp = c.oracle_pools()
+    ref = oracle.ref_prefill(c.q, "bf16", kp, vp, "bf16", c.tables, np.array(c.lens, np.int32), c.query_start,
+                             c.scale, c.bs)
+    assert np.isfinite(got).all()
+    assert row_rel_err(got, ref) <= 2e-3
+    assert np.abs(got[:60]).max() > 1e4  # the scaled sequence's rows carry its large values
