@@ -212,9 +212,8 @@ __device__ __forceinline__ void process_chunk(const Chunk<D, BS, KVT>& ch, const
     }
     st.m = mu;
   }
-  // ---- P = exp2(x - m): keep fp32 sum, split into bf16 hi + lo for the MFMA
-  uint32_t hb[8];
-  float lo[8];
+  // ---- P = exp2(x - m): keep the fp32 sum.  bf16 V: P as bf16 hi + lo for two MFMAs; E4M3 V:
+  // P and V in fp16 (every E4M3 value is an fp16 value), one MFMA
   float pj[8];
 #pragma unroll
   for (int j = 0; j < 8; ++j) pj[j] = exp2_fast(x[j] - st.m);
@@ -223,24 +222,25 @@ __device__ __forceinline__ void process_chunk(const Chunk<D, BS, KVT>& ch, const
     for (int j = 0; j < 8; ++j) pj[j] = x[j] == -INFINITY ? 0.f : pj[j];
   float psum = 0.f;
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const float p = pj[j];
-    psum += p;
-    const uint32_t bits = __builtin_bit_cast(uint32_t, p);
-    hb[j] = bits;
-    lo[j] = p - __builtin_bit_cast(float, bits & 0xFFFF0000u);
-  }
+  for (int j = 0; j < 8; ++j) psum += pj[j];
   st.l += psum;
-  // bf16 pairs: words 0,1 = tokens 4kg..4kg+3 of half 0, words 2,3 = the same of half 1
+  // pairs: words 0,1 = tokens 4kg..4kg+3 of half 0, words 2,3 = the same of half 1
   u32x4 ph, pl;
+  if constexpr (KVT == PKV_BF16) {
 #pragma unroll
-  for (int w = 0; w < 4; ++w) {
-    ph[w] = __builtin_amdgcn_perm(hb[2 * w + 1], hb[2 * w], 0x07060302u);
-    pl[w] = __builtin_amdgcn_perm(__builtin_bit_cast(uint32_t, lo[2 * w + 1]),
-                                  __builtin_bit_cast(uint32_t, lo[2 * w]), 0x07060302u);
+    for (int w = 0; w < 4; ++w) {
+      const uint32_t b0 = __builtin_bit_cast(uint32_t, pj[2 * w]), b1 = __builtin_bit_cast(uint32_t, pj[2 * w + 1]);
+      ph[w] = __builtin_amdgcn_perm(b1, b0, 0x07060302u);
+      pl[w] = __builtin_amdgcn_perm(__builtin_bit_cast(uint32_t, pj[2 * w + 1] - __builtin_bit_cast(float, b1 & 0xFFFF0000u)),
+                                    __builtin_bit_cast(uint32_t, pj[2 * w] - __builtin_bit_cast(float, b0 & 0xFFFF0000u)),
+                                    0x07060302u);
+    }
+    pl = tokens_by_eight(pl);
+  } else {
+#pragma unroll
+    for (int w = 0; w < 4; ++w) ph[w] = pack_f16(pj[2 * w], pj[2 * w + 1]);
   }
   ph = tokens_by_eight(ph);
-  pl = tokens_by_eight(pl);
   // ---- V tail mask: k-slot j of lane group kg is token 8kg + j
   u32x4 vmask = u32x4{~0u, ~0u, ~0u, ~0u};
   if (tail) {
@@ -254,15 +254,16 @@ __device__ __forceinline__ void process_chunk(const Chunk<D, BS, KVT>& ch, const
   // ---- O += P V
 #pragma unroll
   for (int t = 0; t < D / 16; ++t) {
-    u32x4 vop;
     if constexpr (KVT == PKV_BF16) {
-      vop = ch.v[t];
+      u32x4 vop = ch.v[t];
+      if (tail) vop &= vmask;
+      acc[t] = mfma16x16x32(ph, vop, acc[t]);
+      acc[t] = mfma16x16x32(pl, vop, acc[t]);
     } else {
-      vop = e4m3x8_to_bf16x8(ch.v[t][0], ch.v[t][1]);
+      u32x4 vop = e4m3x8_to_f16x8(ch.v[t][0], ch.v[t][1]);
+      if (tail) vop &= vmask;
+      acc[t] = mfma16x16x32_f16(ph, vop, acc[t]);
     }
-    if (tail) vop &= vmask;
-    acc[t] = mfma16x16x32(ph, vop, acc[t]);
-    acc[t] = mfma16x16x32(pl, vop, acc[t]);
   }
 }
 

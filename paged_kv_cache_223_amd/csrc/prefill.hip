@@ -47,9 +47,7 @@ namespace pkv {
 namespace {
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
-typedef float f32x2 __attribute__((ext_vector_type(2)));
-typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
-typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+
 
 __device__ __forceinline__ f32x16 mfma32(u32x4 a, u32x4 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c,
@@ -91,15 +89,6 @@ __device__ __forceinline__ uint32_t bf16_pair_to_f16(uint32_t w) {
 // whether a bf16 pair holds a value outside [-65280, 65280], an infinity or a NaN
 __device__ __forceinline__ bool bf16_pair_beyond_f16(uint32_t w) {
   return (w & 0x7FFFu) > 0x477Fu || ((w >> 16) & 0x7FFFu) > 0x477Fu;
-}
-
-// eight E4M3 codes (w0: codes 0-3, w1: codes 4-7) -> four fp16 pairs in order (exact: every E4M3
-// value is an fp16 value)
-__device__ __forceinline__ u32x4 e4m3x8_to_f16x8(uint32_t w0, uint32_t w1) {
-  return u32x4{__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w0, 1.0f, false)),
-               __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w0, 1.0f, true)),
-               __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w1, 1.0f, false)),
-               __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w1, 1.0f, true))};
 }
 
 // ids[idx] for a lane-dependent idx < N, as selects between scalars (an indexed read of the local
@@ -318,7 +307,7 @@ __device__ __forceinline__ void chunk_pack16(const float (&p)[16], float& l, u32
   uint32_t wh[8];
 #pragma unroll
   for (int k = 0; k < 8; ++k)
-    wh[k] = __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2{p[2 * k], p[2 * k + 1]}), f16x2));
+    wh[k] = pack_f16(p[2 * k], p[2 * k + 1]);
   regroup_p(wh, ph);
 }
 

@@ -1,7 +1,7 @@
 // Matrix-core tile operations shared by the paged decode and prefill kernels
-// (gfx950): operand types, the bf16 MFMA, E4M3 -> bf16 conversion, the P
-// regroup across lane groups, the maximum over lane groups, and the clamped
-// block-table lookup.
+// (gfx950): operand types, the bf16 and fp16 MFMAs, E4M3 -> bf16 and fp16
+// conversions, the P regroup across lane groups, the maximum over lane groups,
+// and the clamped block-table lookup.
 //
 // MFMA v_mfma_f32_16x16x32_bf16 lane layouts (checked on the device):
 //   A[16][32]: lane l holds A[l % 16][8 * (l / 16) + j], j = 0..7
@@ -21,8 +21,11 @@ namespace {
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 
 constexpr float kRescaleLog2 = 8.0f;
 
@@ -67,9 +70,28 @@ __device__ __forceinline__ u32x4 e4m3x8_to_bf16x8(uint32_t w0, uint32_t w1) {
                e4m3x2_to_bf16x2(w1, true)};
 }
 
+// eight E4M3 codes (w0: codes 0-3, w1: codes 4-7) -> four fp16 pairs in order (exact: every E4M3
+// value is an fp16 value)
+__device__ __forceinline__ u32x4 e4m3x8_to_f16x8(uint32_t w0, uint32_t w1) {
+  return u32x4{__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w0, 1.0f, false)),
+               __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w0, 1.0f, true)),
+               __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w1, 1.0f, false)),
+               __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w1, 1.0f, true))};
+}
+
+// two fp32 -> packed fp16 pair, round to nearest even; x in the low half
+__device__ __forceinline__ uint32_t pack_f16(float x, float y) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2{x, y}), f16x2));
+}
+
 __device__ __forceinline__ f32x4 mfma16x16x32(u32x4 a, u32x4 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c,
                                                  0, 0, 0);
+}
+
+__device__ __forceinline__ f32x4 mfma16x16x32_f16(u32x4 a, u32x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c,
+                                                0, 0, 0);
 }
 
 // Regroup the P operand across lane groups.  In: lane group r (lanes 16r ..
