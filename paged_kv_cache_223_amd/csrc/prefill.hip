@@ -15,11 +15,14 @@
 // With keys as the rows of S^T and columns in lanes, a lane holds 16 scores of
 // one column: the chunk maximum is 15 maxima in the lane and one exchange with
 // lane l ^ 32, and the accumulator rows a lane holds in O^T belong to the same
-// column, so the online-softmax rescale is lane-local.  P keeps about 16 bits
-// as bf16 hi + lo parts (two MFMAs each); a single bf16 P exceeds a 2e-3
-// relative row error on short contexts.  Each P part is regrouped with four
-// v_permlane32_swap so that lane group h holds keys 8h .. 8h+7 of each 16-key
-// half, which V^T's operand (8 consecutive keys of one head-dim row) matches.
+// column, so the online-softmax rescale is lane-local.  PV runs in fp16 on
+// v_mfma_f32_32x32x16_f16: P rounded to fp16 (a single bf16 P would exceed a
+// 2e-3 relative row error on short contexts) and V staged as fp16, exact for
+// E4M3 and for bf16 up to 65280 in magnitude; a workgroup whose bf16 V holds a
+// larger value runs again with the pool's bf16 V and P as bf16 hi + lo parts
+// (two MFMAs each).  P is regrouped with four v_permlane32_swap so that lane
+// group h holds keys 8h .. 8h+7 of each 16-key half, which V^T's operand (8
+// consecutive keys of one head-dim row) matches.
 //
 // Workgroups.  NW = 12 waves (three per SIMD at about 165 VGPRs) cover
 // NW * 32 / G consecutive query tokens of one (sequence, KV head); measured on
@@ -29,9 +32,9 @@
 // workgroup copies the chunk's pool tiles into one of two LDS buffers while
 // the waves compute the previous chunk from the other, with the chunk after
 // that already loading into registers.  The LDS copy is laid out for the
-// operand reads, without bank conflicts: K as [D/8][32 keys][8 elements]
-// (E4M3: [D/8][32 keys][8 bytes]), V as [D][32 keys] rows padded to 80 bytes
-// (E4M3: 40).  Work items are dealt to the 8 XCDs so that the workgroups of
+// operand reads, without bank conflicts: K as bf16 [D/8][32 keys][8 elements]
+// (E4M3 codes decoded once, while staging, rather than by each of the 12 waves
+// that read them), V as [D][32 keys] two-byte rows padded to 80 bytes.  Work items are dealt to the 8 XCDs so that the workgroups of
 // one (sequence, KV head) share one XCD's L2, latest (longest) tiles first.
 
 #include <hip/hip_runtime.h>
@@ -72,23 +75,28 @@ struct Stage {
   static constexpr int S = KvTraits<KVT>::kBytes;
   static constexpr int NBCH = BS >= 32 ? 1 : 32 / BS;  // blocks of one chunk
   static constexpr int kTile = D * BS * S;             // one block's tile of one head (K or V) in the pool
-  static constexpr int kKBytes = 32 * D * S;           // K: [D/8][32][8 elements]
+  static constexpr int kKBytes = 32 * D * 2;           // K as bf16: [D/8][32][8 elements]
   static constexpr int kVRow = 32 * 2 + 16;            // V row of 32 two-byte elements, padded (bank spread)
   static constexpr int kBytes = kKBytes + D * kVRow;
   static constexpr int kUnits = 2 * NBCH * kTile / 16;  // 16-byte pool units of the chunk (K then V)
 };
 
-// bf16 pair -> fp16 pair, exact while both magnitudes are at most 65280 (the largest bf16 value
-// below fp16's maximum; bf16_pair_beyond_f16 tells)
-__device__ __forceinline__ uint32_t bf16_pair_to_f16(uint32_t w) {
-  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2{__builtin_bit_cast(float, w << 16),
-                                                                      __builtin_bit_cast(float, w & 0xFFFF0000u)}),
-                                                              f16x2));
-}
-
-// whether a bf16 pair holds a value outside [-65280, 65280], an infinity or a NaN
-__device__ __forceinline__ bool bf16_pair_beyond_f16(uint32_t w) {
-  return (w & 0x7FFFu) > 0x477Fu || ((w >> 16) & 0x7FFFu) > 0x477Fu;
+// Eight bf16 (a 16-byte unit) -> eight fp16, exact for every finite magnitude up to 65280 (the
+// largest bf16 value below fp16's maximum; larger ones would become infinities).  Returns the
+// largest magnitude in the unit (NaNs ignored: they stay NaNs in fp16) for the range check.
+__device__ __forceinline__ float bf16x8_to_f16x8(const u32x4& v, u32x4& h) {
+  float lo[4], hi[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t w = v[i];
+    lo[i] = __builtin_bit_cast(float, w << 16);
+    hi[i] = __builtin_bit_cast(float, w & 0xFFFF0000u);
+    h[i] = __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2{lo[i], hi[i]}), f16x2));
+  }
+  const float m0 = fmaxf(fmaxf(fabsf(lo[0]), fabsf(hi[0])), fabsf(lo[1]));
+  const float m1 = fmaxf(fmaxf(m0, fabsf(hi[1])), fabsf(lo[2]));
+  const float m2 = fmaxf(fmaxf(m1, fabsf(hi[2])), fabsf(lo[3]));
+  return fmaxf(m2, fabsf(hi[3]));
 }
 
 // ids[idx] for a lane-dependent idx < N, as selects between scalars (an indexed read of the local
@@ -159,9 +167,9 @@ struct Stager {
         const int dg = e0 / (BS * E), t = (e0 / E) % BS, key = blk * BS + t;
         if constexpr (S == 2) {
           *(u32x4*)(lds + ((size_t)dg * 32 + key) * 16) = v;
-        } else {  // 16 dims -> planes 2 dg (low 8) and 2 dg + 1 (high 8) of [D/8][32][8 bytes]
-          *(u32x2*)(lds + ((size_t)(2 * dg) * 32 + key) * 8) = u32x2{v.x, v.y};
-          *(u32x2*)(lds + ((size_t)(2 * dg + 1) * 32 + key) * 8) = u32x2{v.z, v.w};
+        } else {  // 16 dims, decoded to bf16 (exact) -> planes 2 dg (dims 0-7) and 2 dg + 1 (8-15)
+          *(u32x4*)(lds + ((size_t)(2 * dg) * 32 + key) * 16) = e4m3x8_to_bf16x8(v.x, v.y);
+          *(u32x4*)(lds + ((size_t)(2 * dg + 1) * 32 + key) * 16) = e4m3x8_to_bf16x8(v.z, v.w);
         }
       } else {
         // pool V tile [D][BS]: unit holds E consecutive elements starting at (d, t0)
@@ -178,13 +186,7 @@ struct Stager {
             const int d = e0 / BS, t0 = e0 % BS;
             u32x4 h = v;
             if constexpr (!RAW) {
-              bool out = false;
-#pragma unroll
-              for (int i = 0; i < 4; ++i) {
-                out = out || bf16_pair_beyond_f16(v[i]);
-                h[i] = bf16_pair_to_f16(v[i]);
-              }
-              if (out) *beyond = 1;
+              if (bf16x8_to_f16x8(v, h) > 65280.f) *beyond = 1;
             }
             *(u32x4*)(vb + (size_t)d * St::kVRow + (size_t)(blk * BS + t0) * 2) = h;
           }
@@ -223,22 +225,14 @@ __device__ __forceinline__ void regroup_p(const uint32_t (&w)[8], u32x4 (&op)[2]
 
 // S^T[32 keys][32 cols] = K Q^T over one staged chunk: MFMA u covers dims 16 u + 8 h + j in lane
 // group h; lane (key, h) holds rows 8 (i / 4) + 4 h + i % 4 of its column.
-template <int D, int BS, int KVT>
+template <int D>
 __device__ __forceinline__ f32x16 chunk_scores(const char* lds, const u32x4 (&qop)[D / 16], int lane) {
   const int key = lane & 31, h = lane >> 5;
   f32x16 s = {};
-  if constexpr (KVT == PKV_BF16) {
 #pragma unroll
-    for (int u = 0; u < D / 16; ++u) {
-      const u32x4 kop = *(const u32x4*)(lds + ((size_t)(2 * u + h) * 32 + key) * 16);
-      s = mfma32(kop, qop[u], s);
-    }
-  } else {
-#pragma unroll
-    for (int u = 0; u < D / 16; ++u) {
-      const u32x2 w = *(const u32x2*)(lds + ((size_t)(2 * u + h) * 32 + key) * 8);
-      s = mfma32(e4m3x8_to_bf16x8(w.x, w.y), qop[u], s);
-    }
+  for (int u = 0; u < D / 16; ++u) {
+    const u32x4 kop = *(const u32x4*)(lds + ((size_t)(2 * u + h) * 32 + key) * 16);
+    s = mfma32(kop, qop[u], s);
   }
   return s;
 }
@@ -432,7 +426,7 @@ __global__ __launch_bounds__(64 * NW, 2) void prefill_kernel(PrefillArgs a) {
         }
       }
       if (32 * c <= p_wmax) {
-        const f32x16 s = chunk_scores<D, BS, KVT>(sh_stage[c % kStages], qop, lane);
+        const f32x16 s = chunk_scores<D>(sh_stage[c % kStages], qop, lane);
         const bool moved = 32 * c + 31 > p_min ? chunk_exp<true>(s, m, l, alpha, p, 32 * c, p_lane, sl, lane)
                                                : chunk_exp<false>(s, m, l, alpha, p, 32 * c, p_lane, sl, lane);
         if (moved) {
