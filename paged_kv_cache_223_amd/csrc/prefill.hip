@@ -292,16 +292,21 @@ __device__ __forceinline__ void chunk_pack(const float (&p)[16], float& l, u32x4
 }
 
 // P as fp16 pairs (round to nearest even: relative error 2^-11, against 2^-8 for one bf16 part),
-// summed into l from the fp32 values, regrouped into the PV B operands.
+// regrouped into the PV B operands.  l takes the same fp16 values that PV multiplies, summed in
+// fp32 by dot products with (1, 1): eight instructions for the lane's 16 keys instead of 15 adds.
 __device__ __forceinline__ void chunk_pack16(const float (&p)[16], float& l, u32x4 (&ph)[2]) {
-  float ps[4];
-#pragma unroll
-  for (int j = 0; j < 4; ++j) ps[j] = (p[4 * j] + p[4 * j + 1]) + (p[4 * j + 2] + p[4 * j + 3]);
-  l += (ps[0] + ps[1]) + (ps[2] + ps[3]);
   uint32_t wh[8];
 #pragma unroll
   for (int k = 0; k < 8; ++k)
     wh[k] = pack_f16(p[2 * k], p[2 * k + 1]);
+  const f16x2 one = {(_Float16)1.0f, (_Float16)1.0f};
+  float s0 = 0.f, s1 = 0.f;
+#pragma unroll
+  for (int k = 0; k < 8; k += 2) {
+    s0 = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, wh[k]), one, s0, false);
+    s1 = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, wh[k + 1]), one, s1, false);
+  }
+  l += s0 + s1;
   regroup_p(wh, ph);
 }
 
