@@ -67,6 +67,8 @@ __device__ __forceinline__ uint32_t pack_bf16_rne(float x, float y) {
 }
 
 constexpr int kStages = 2;  // the chunk being computed and the next one, written at the iteration's start
+constexpr float kRescaleMax = 256.0f;  // 2^kRescaleLog2: the largest P term a running maximum allows
+static_assert(kRescaleLog2 == 8.0f, "kRescaleMax is 2^kRescaleLog2");
 
 // One 32-key chunk in LDS.  V holds two-byte elements: fp16 on the fast pass, the raw bf16 on the
 // rerun of a workgroup whose V does not fit fp16.
@@ -432,17 +434,34 @@ __global__ __launch_bounds__(64 * NW, 2) void prefill_kernel(PrefillArgs a) {
       }
       if (32 * c <= p_wmax) {
         const f32x16 s = chunk_scores<D>(sh_stage[c % kStages], qop, lane);
-        const bool moved = 32 * c + 31 > p_min ? chunk_exp<true>(s, m, l, alpha, p, 32 * c, p_lane, sl, lane)
-                                               : chunk_exp<false>(s, m, l, alpha, p, 32 * c, p_lane, sl, lane);
-        if (moved) {
-#pragma unroll
-          for (int t = 0; t < D / 32; ++t) acc[t] *= alpha;
-        }
         u32x4 ph[2], pl[2];
-        if constexpr (RAW)
-          chunk_pack(p, l, ph, pl);
-        else
-          chunk_pack16(p, l, ph);
+        bool done = false;
+        // bf16 pools at D = 128 skip the optimistic pass: holding S through it costs spills there.
+        if constexpr (!RAW && (KVT != PKV_BF16 || D < 128)) {
+          if (32 * c + 31 <= p_min) {
+            // Optimistic pass against the running maximum: if no lane's 16 terms sum past 2^8, no
+            // term exceeds it, so the maximum would not move and these are the same P and l
+            // that the full step computes.  Otherwise (first chunk: m = -inf) the full step runs.
+#pragma unroll
+            for (int i = 0; i < 16; ++i) p[i] = exp2_fast(fmaf(s[i], sl, -m));
+            float ls = 0.f;
+            chunk_pack16(p, ls, ph);
+            done = __ballot(ls > kRescaleMax) == 0ull;
+            if (done) l += ls;
+          }
+        }
+        if (!done) {
+          const bool moved = 32 * c + 31 > p_min ? chunk_exp<true>(s, m, l, alpha, p, 32 * c, p_lane, sl, lane)
+                                                 : chunk_exp<false>(s, m, l, alpha, p, 32 * c, p_lane, sl, lane);
+          if (moved) {
+#pragma unroll
+            for (int t = 0; t < D / 32; ++t) acc[t] *= alpha;
+          }
+          if constexpr (RAW)
+            chunk_pack(p, l, ph, pl);
+          else
+            chunk_pack16(p, l, ph);
+        }
         chunk_pv<D, BS, KVT, RAW>(sh_stage[c % kStages], ph, pl, acc, lane);
       }
       __syncthreads();

@@ -206,3 +206,28 @@ def test_prefill_v_beyond_fp16_range(bs):
     assert np.isfinite(got).all()
     assert row_rel_err(got, ref) <= 2e-3
     assert np.abs(got[:60]).max() > 1e4  # the scaled sequence's rows carry its large values
+
+
+@pytest.mark.parametrize("kv_dtype", ["bf16", "e4m3"])
+@pytest.mark.parametrize("d", [64, 128])
+def test_prefill_late_rescales(d, kv_dtype):
+    """Keys whose scores grow along the sequence (K scaled up fourfold from the first position to
+    the last): the running maximum keeps moving on chunks far before the diagonal, where the kernel
+    first weighs the chunk against the maximum it holds and takes the full step when that would
+    move."""
+    print(f"prefill late rescales d={d} {kv_dtype}", flush=True)
+    c = Case(priors=[700, 300], chunks=[24, 50], H_q=16, H_kv=2, d=d, bs=16, kv_dtype=kv_dtype, seed=41)
+    as_f32 = lambda bits: (bits.astype(np.uint32) << 16).view(np.float32)  # noqa: E731
+    for b, n in enumerate(c.lens):
+        grow = (1.0 + 3.0 * np.arange(n) / n).astype(np.float32)[:, None, None]
+        c.k_rows[b] = workloads.round_bf16(as_f32(c.k_rows[b]) * grow)
+    if kv_dtype == "e4m3":
+        c.k_scale = np.full(c.H_kv, 20.0 / 448, np.float32)
+    c.scale = float(np.float32(0.5))
+    c.device()
+    got = c.prefill()
+    kp, vp = c.oracle_pools()
+    ref = oracle.ref_prefill(c.q, "bf16", kp, vp, kv_dtype, c.tables, np.array(c.lens, np.int32), c.query_start,
+                             c.scale, c.bs, c.k_scale, c.v_scale)
+    assert np.isfinite(got).all()
+    assert row_rel_err(got, ref) <= (2e-2 if kv_dtype == "e4m3" else 2e-3)
