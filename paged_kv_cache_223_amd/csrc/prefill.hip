@@ -28,13 +28,16 @@
 // NW * 32 / G consecutive query tokens of one (sequence, KV head); measured on
 // the 70B layer shape, 12 waves beat 8 and 4, and a software-pipelined loop
 // (the next chunk's QK^T under this chunk's softmax) lost for want of
-// registers.  They share every 32-key K/V chunk through LDS: the
-// workgroup copies the chunk's pool tiles into one of two LDS buffers while
-// the waves compute the previous chunk from the other, with the chunk after
-// that already loading into registers.  The LDS copy is laid out for the
-// operand reads, without bank conflicts: K as bf16 [D/8][32 keys][8 elements]
-// (E4M3 codes decoded once, while staging, rather than by each of the 12 waves
-// that read them), V as [D][32 keys] two-byte rows padded to 80 bytes.  Work items are dealt to the 8 XCDs so that the workgroups of
+// registers.  They share every 32-key K/V chunk through LDS.  E4M3 pools: the
+// workgroup copies a chunk's pool tiles through registers into one of two LDS
+// buffers while the waves compute the previous chunk from the other, with the
+// chunk after that already loading into registers.  bf16 pools: K tiles go
+// straight from the pool into LDS (global_load_lds_dwordx4) two chunks ahead,
+// into the third of three buffers, and only V passes through registers.  The
+// LDS copy is laid out for the operand reads, without bank conflicts: K as bf16
+// [D/8][32 keys][8 elements] (E4M3 codes decoded once, while staging, rather
+// than by each of the 12 waves that read them), V as [D][32 keys] two-byte rows
+// padded to 80 bytes.  Work items are dealt to the 8 XCDs so that the workgroups of
 // one (sequence, KV head) share one XCD's L2, latest (longest) tiles first.
 
 #include <hip/hip_runtime.h>
@@ -66,7 +69,6 @@ __device__ __forceinline__ uint32_t pack_bf16_rne(float x, float y) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2{x, y}), bf16x2));
 }
 
-constexpr int kStages = 2;  // the chunk being computed and the next one, written at the iteration's start
 constexpr float kRescaleMax = 256.0f;  // 2^kRescaleLog2: the largest P term a running maximum allows
 static_assert(kRescaleLog2 == 8.0f, "kRescaleMax is 2^kRescaleLog2");
 
@@ -122,28 +124,39 @@ struct Stager {
   u32x4 r[kPer];
 
   // Table entries of one chunk's blocks (wave-uniform, scalar loads), clamped to the sequence's
-  // last block.  Taken one iteration ahead of the chunk's loads, so the table's latency is off the
-  // loop's critical path.
+  // last block and to the pool.  Taken one iteration ahead of the chunk's loads, so the table's
+  // latency is off the loop's critical path.  The table is read through the constant address
+  // space (the kernel never writes it), which keeps these loads scalar next to the direct-to-LDS
+  // copies (whose memory writes would otherwise make the compiler load them per lane and wait
+  // for every copy in flight).
   __device__ __forceinline__ static void chunk_ids(int (&ids)[St::NBCH], const int32_t* __restrict__ tab, int chunk,
                                                    int last_blk, int NB) {
+    const __attribute__((address_space(4))) int32_t* ct = (const __attribute__((address_space(4))) int32_t*)tab;
 #pragma unroll
-    for (int j = 0; j < St::NBCH; ++j) ids[j] = block_id(tab, chunk * 32 / BS + j, last_blk, NB);
+    for (int j = 0; j < St::NBCH; ++j) {
+      const int jj = min(chunk * 32 / BS + j, last_blk);
+      const int id = ct[jj];
+      ids[j] = (unsigned)id < (unsigned)NB ? id : 0;
+    }
+  }
+
+  // Pool address of unit u (K units first, then V) of the chunk whose block ids are ids.
+  __device__ __forceinline__ static const char* unit_src(const char* __restrict__ kpool,
+                                                         const char* __restrict__ vpool, const int (&ids)[St::NBCH],
+                                                         int H_kv, int g, int u) {
+    const int part = u / (St::NBCH * tileU);  // 0 = K, 1 = V
+    const int w = u % (St::NBCH * tileU);
+    const int id = pick_id<St::NBCH>(ids, w / tileU);
+    return (part == 0 ? kpool : vpool) + (size_t)id * ((size_t)H_kv * St::kTile) + (size_t)g * St::kTile +
+           (size_t)(w % tileU) * 16;
   }
 
   __device__ __forceinline__ void load(const char* __restrict__ kpool, const char* __restrict__ vpool,
                                        const int (&ids)[St::NBCH], int H_kv, int g, int tid) {
-    const size_t bstride = (size_t)H_kv * St::kTile;
 #pragma unroll
     for (int k = 0; k < kPer; ++k) {
       const int u = tid + k * NT;
-      if (St::kUnits % NT == 0 || u < St::kUnits) {
-        const int part = u / (St::NBCH * tileU);  // 0 = K, 1 = V
-        const int w = u % (St::NBCH * tileU);
-        const int id = pick_id<St::NBCH>(ids, w / tileU);
-        const char* src = (part == 0 ? kpool : vpool) + (size_t)id * bstride + (size_t)g * St::kTile +
-                          (size_t)(w % tileU) * 16;
-        r[k] = *(const u32x4*)src;
-      }
+      if (St::kUnits % NT == 0 || u < St::kUnits) r[k] = *(const u32x4*)unit_src(kpool, vpool, ids, H_kv, g, u);
     }
   }
 
@@ -154,61 +167,138 @@ struct Stager {
   // hold sets *beyond.
   template <bool RAW>
   __device__ __forceinline__ void store(char* lds, int tid, int nvalid, int* beyond) const {
-    constexpr int S = St::S;
-    constexpr int E = 16 / S;  // elements per 16-byte unit
 #pragma unroll
     for (int k = 0; k < kPer; ++k) {
       const int u = tid + k * NT;
-      if (!(St::kUnits % NT == 0 || u < St::kUnits)) continue;
-      u32x4 v = r[k];
-      const int part = u / (St::NBCH * tileU);
-      const int w = u % (St::NBCH * tileU);
-      const int blk = w / tileU, e0 = (w % tileU) * E;  // first element of the unit inside the block's tile
-      if (part == 0) {
-        // pool K tile [D/E][BS][E]: unit (dg, t) holds E dims of key blk * BS + t
-        const int dg = e0 / (BS * E), t = (e0 / E) % BS, key = blk * BS + t;
-        if constexpr (S == 2) {
-          *(u32x4*)(lds + ((size_t)dg * 32 + key) * 16) = v;
-        } else {  // 16 dims, decoded to bf16 (exact) -> planes 2 dg (dims 0-7) and 2 dg + 1 (8-15)
-          *(u32x4*)(lds + ((size_t)(2 * dg) * 32 + key) * 16) = e4m3x8_to_bf16x8(v.x, v.y);
-          *(u32x4*)(lds + ((size_t)(2 * dg + 1) * 32 + key) * 16) = e4m3x8_to_bf16x8(v.z, v.w);
+      if (St::kUnits % NT == 0 || u < St::kUnits) {
+        if (nvalid < 32)
+          put<RAW, true>(lds, u, r[k], nvalid, beyond);
+        else
+          put<RAW, false>(lds, u, r[k], nvalid, beyond);
+      }
+    }
+  }
+
+  // MASK: the chunk holds the sequence's end (nvalid < 32), a separate copy of the code so that
+  // the other chunks carry none of the masking.
+  template <bool RAW, bool MASK>
+  __device__ __forceinline__ static void put(char* lds, int u, u32x4 v, int nvalid, int* beyond) {
+    constexpr int S = St::S;
+    constexpr int E = 16 / S;  // elements per 16-byte unit
+    const int part = u / (St::NBCH * tileU);
+    const int w = u % (St::NBCH * tileU);
+    const int blk = w / tileU, e0 = (w % tileU) * E;  // first element of the unit inside the block's tile
+    if (part == 0) {
+      // pool K tile [D/E][BS][E]: unit (dg, t) holds E dims of key blk * BS + t
+      const int dg = e0 / (BS * E), t = (e0 / E) % BS, key = blk * BS + t;
+      if constexpr (S == 2) {
+        *(u32x4*)(lds + ((size_t)dg * 32 + key) * 16) = v;
+      } else {  // 16 dims, decoded to bf16 (exact) -> planes 2 dg (dims 0-7) and 2 dg + 1 (8-15)
+        *(u32x4*)(lds + ((size_t)(2 * dg) * 32 + key) * 16) = e4m3x8_to_bf16x8(v.x, v.y);
+        *(u32x4*)(lds + ((size_t)(2 * dg + 1) * 32 + key) * 16) = e4m3x8_to_bf16x8(v.z, v.w);
+      }
+    } else {
+      // pool V tile [D][BS]: unit holds E consecutive elements starting at (d, t0)
+      char* vb = lds + St::kKBytes;
+      if constexpr (MASK) {
+#pragma unroll
+        for (int j = 0; j < E; ++j) {
+          const int key = blk * BS + (e0 + j) % BS;
+          if (key >= nvalid) v[j * S / 4] &= ~(((1u << (8 * S)) - 1u) << (8 * ((j * S) % 4)));
+        }
+      }
+      if constexpr (S == 2) {
+        if constexpr (BS >= 8) {  // a unit is 8 keys of one row
+          const int d = e0 / BS, t0 = e0 % BS;
+          u32x4 h = v;
+          if constexpr (!RAW) {
+            if (bf16x8_to_f16x8(v, h) > 65280.f) *beyond = 1;
+          }
+          *(u32x4*)(vb + (size_t)d * St::kVRow + (size_t)(blk * BS + t0) * 2) = h;
         }
       } else {
-        // pool V tile [D][BS]: unit holds E consecutive elements starting at (d, t0)
-        char* vb = lds + St::kKBytes;
-        if (nvalid < 32) {
-#pragma unroll
-          for (int j = 0; j < E; ++j) {
-            const int key = blk * BS + (e0 + j) % BS;
-            if (key >= nvalid) v[j * S / 4] &= ~(((1u << (8 * S)) - 1u) << (8 * ((j * S) % 4)));
-          }
-        }
-        if constexpr (S == 2) {
-          if constexpr (BS >= 8) {  // a unit is 8 keys of one row
-            const int d = e0 / BS, t0 = e0 % BS;
-            u32x4 h = v;
-            if constexpr (!RAW) {
-              if (bf16x8_to_f16x8(v, h) > 65280.f) *beyond = 1;
-            }
-            *(u32x4*)(vb + (size_t)d * St::kVRow + (size_t)(blk * BS + t0) * 2) = h;
-          }
-        } else {
-          const u32x4 h0 = e4m3x8_to_f16x8(v.x, v.y), h1 = e4m3x8_to_f16x8(v.z, v.w);  // codes 0-7, 8-15
-          if constexpr (BS == 8) {  // a unit is two rows of 8 keys
-            const int d = e0 / 8;
-            *(u32x4*)(vb + (size_t)d * St::kVRow + (size_t)blk * 16) = h0;
-            *(u32x4*)(vb + (size_t)(d + 1) * St::kVRow + (size_t)blk * 16) = h1;
-          } else {  // 16 keys of one row
-            const int d = e0 / BS, t0 = e0 % BS;
-            char* p = vb + (size_t)d * St::kVRow + (size_t)(blk * BS + t0) * 2;
-            *(u32x4*)p = h0;
-            *(u32x4*)(p + 16) = h1;
-          }
+        const u32x4 h0 = e4m3x8_to_f16x8(v.x, v.y), h1 = e4m3x8_to_f16x8(v.z, v.w);  // codes 0-7, 8-15
+        if constexpr (BS == 8) {  // a unit is two rows of 8 keys
+          const int d = e0 / 8;
+          *(u32x4*)(vb + (size_t)d * St::kVRow + (size_t)blk * 16) = h0;
+          *(u32x4*)(vb + (size_t)(d + 1) * St::kVRow + (size_t)blk * 16) = h1;
+        } else {  // 16 keys of one row
+          const int d = e0 / BS, t0 = e0 % BS;
+          char* p = vb + (size_t)d * St::kVRow + (size_t)(blk * BS + t0) * 2;
+          *(u32x4*)p = h0;
+          *(u32x4*)(p + 16) = h1;
         }
       }
     }
   }
 };
+
+typedef __attribute__((address_space(3))) void* lds_void_ptr;
+typedef __attribute__((address_space(1))) void* global_void_ptr;
+
+// bf16 pools: a chunk's K tiles go from the pool straight into LDS (global_load_lds_dwordx4: 16
+// bytes per lane, 1 KiB of LDS per wave and instruction, neither registers nor LDS stores; the
+// bf16 K layout [D/8][32 keys][8 elements] is that instruction's lane order), and its V units,
+// which are converted to fp16 on the way, through one register unit in each of the last 4 D
+// threads.  The K copy lands asynchronously: a wave waits for its own copies (s_waitcnt vmcnt)
+// before the barrier that publishes the chunk.
+template <int D, int BS, int NT>
+struct SplitStager {
+  using Sg = Stager<D, BS, PKV_BF16, NT>;
+  using St = Stage<D, BS, PKV_BF16>;
+  static constexpr int kKWaves = St::kKBytes / 1024;  // waves that copy K, one instruction each
+  static constexpr int kVUnits = St::kUnits / 2;      // 16-byte V units of a chunk (4 D)
+  static constexpr int kV0 = NT - kVUnits;            // first thread that carries a V unit
+  static_assert(kKWaves * 64 <= NT && kVUnits <= NT && kV0 % 64 == 0, "chunk copy does not fit the workgroup");
+  u32x4 r;
+
+  __device__ __forceinline__ static void copy_k(char* lds, const char* __restrict__ kpool, const int (&ids)[St::NBCH],
+                                                int H_kv, int g, int w, int lane) {
+    if (w < kKWaves) {  // units 64 w + lane: (dg, key) = ((64 w + lane) / 32, lane % 32)
+      const char* src = Sg::unit_src(kpool, kpool, ids, H_kv, g, k_unit(64 * w + lane));
+      __builtin_amdgcn_global_load_lds((global_void_ptr)src, (lds_void_ptr)(lds + 1024 * w), 16, 0, 0);
+    }
+  }
+
+  // pool unit of LDS K slot L = dg * 32 + key: unit (blk, dg, t) = blk * tileU + dg * BS + t
+  __device__ __forceinline__ static int k_unit(int L) {
+    const int dg = L >> 5, key = L & 31;
+    return (key / BS) * Sg::tileU + dg * BS + key % BS;
+  }
+
+  __device__ __forceinline__ void load_v(const char* __restrict__ kpool, const char* __restrict__ vpool,
+                                         const int (&ids)[St::NBCH], int H_kv, int g, int tid) {
+    if (tid >= kV0) r = *(const u32x4*)Sg::unit_src(kpool, vpool, ids, H_kv, g, kVUnits + tid - kV0);
+  }
+
+  template <bool RAW>
+  __device__ __forceinline__ void store_v(char* lds, int tid, int nvalid, int* beyond) const {
+    if (tid >= kV0) {
+      if (nvalid < 32)
+        Sg::template put<RAW, true>(lds, kVUnits + tid - kV0, r, nvalid, beyond);
+      else
+        Sg::template put<RAW, false>(lds, kVUnits + tid - kV0, r, nvalid, beyond);
+    }
+  }
+
+  // vector-memory loads this wave issues per chunk (K copy, V unit)
+  __device__ __forceinline__ static int loads_per_chunk(int w) { return (w < kKWaves) + (64 * w >= kV0); }
+};
+
+// Workgroup barrier after this wave's LDS stores: s_waitcnt lgkmcnt(0), s_barrier, and no
+// reordering of memory accesses across it.  __syncthreads() would also wait for every
+// direct-to-LDS copy in flight, including those of chunks read two iterations later.
+__device__ __forceinline__ void barrier_lds() { __asm__ volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+// s_waitcnt vmcnt(n) for a wave-uniform n <= 2 (expcnt and lgkmcnt left alone)
+__device__ __forceinline__ void wait_vmcnt(int n) {
+  if (n <= 0)
+    __builtin_amdgcn_s_waitcnt(0xF70);
+  else if (n == 1)
+    __builtin_amdgcn_s_waitcnt(0xF71);
+  else
+    __builtin_amdgcn_s_waitcnt(0xF72);
+}
 
 // Regroup one P part for the PV MFMAs.  In: lane (col, h) holds packed bf16 pairs w[k] of keys
 // 8 (k / 2) + 4 h + 2 (k % 2) + {0, 1} (the S^T accumulator rows).  Out: op[a] holds keys
@@ -340,7 +430,13 @@ template <int D, int BS, int KVT, int NW>
 __global__ __launch_bounds__(64 * NW, 2) void prefill_kernel(PrefillArgs a) {
   using St = Stage<D, BS, KVT>;
   constexpr int NT = 64 * NW;
-  __shared__ __align__(16) char sh_stage[kStages][St::kBytes];
+  // Chunk buffers: two for E4M3 pools (register copy), three for bf16 pools, whose K copy lands
+  // asynchronously two iterations ahead.  Distinct arrays, so that the compiler can tell the
+  // buffer being copied into from the one being read and need not wait for the copy before
+  // every LDS read.
+  __shared__ __align__(16) char sh_b0[St::kBytes];
+  __shared__ __align__(16) char sh_b1[St::kBytes];
+  __shared__ __align__(16) char sh_b2[KVT == PKV_BF16 ? St::kBytes : 16];
   const int tid = threadIdx.x, lane = tid & 63, w = uniform(tid >> 6);
   const int G = a.G;
   const int tok_per_wave = 32 / G;
@@ -408,63 +504,106 @@ __global__ __launch_bounds__(64 * NW, 2) void prefill_kernel(PrefillArgs a) {
   __shared__ int sh_beyond;
   if (tid == 0) sh_beyond = 0;
   using Sg = Stager<D, BS, KVT, NT>;
+  // One 32-key chunk of the wave's columns from a staged buffer: S = K Q^T, the online-softmax
+  // step, P, O += V^T P^T.
+  float p[16], alpha;
+  auto compute = [&](auto raw_tag, int c, const char* buf) {
+    constexpr bool RAW = decltype(raw_tag)::value;
+    if (32 * c > p_wmax) return;
+    const f32x16 s = chunk_scores<D>(buf, qop, lane);
+    u32x4 ph[2], pl[2];
+    bool done = false;
+    // (bf16 pools at D = 128 keep the full step: holding S through the pass spills there)
+    if constexpr (!RAW && (KVT != PKV_BF16 || D < 128)) {
+      if (32 * c + 31 <= p_min) {
+        // Optimistic pass against the running maximum: if no lane's 16 terms sum past 2^8, no
+        // term exceeds it, so the maximum would not move and these are the same P and l that
+        // the full step computes.  Otherwise (first chunk: m = -inf) the full step runs.
+#pragma unroll
+        for (int i = 0; i < 16; ++i) p[i] = exp2_fast(fmaf(s[i], sl, -m));
+        float ls = 0.f;
+        chunk_pack16(p, ls, ph);
+        done = __ballot(ls > kRescaleMax) == 0ull;
+        if (done) l += ls;
+      }
+    }
+    if (!done) {
+      const bool moved = 32 * c + 31 > p_min ? chunk_exp<true>(s, m, l, alpha, p, 32 * c, p_lane, sl, lane)
+                                             : chunk_exp<false>(s, m, l, alpha, p, 32 * c, p_lane, sl, lane);
+      if (moved) {
+#pragma unroll
+        for (int t = 0; t < D / 32; ++t) acc[t] *= alpha;
+      }
+      if constexpr (RAW)
+        chunk_pack(p, l, ph, pl);
+      else
+        chunk_pack16(p, l, ph);
+    }
+    chunk_pv<D, BS, KVT, RAW>(buf, ph, pl, acc, lane);
+  };
   auto run = [&](auto raw_tag) {
     constexpr bool RAW = decltype(raw_tag)::value;
 #pragma unroll
     for (int t = 0; t < D / 32; ++t) acc[t] = f32x16{};
     m = -INFINITY;
     l = 0.f;
-    Sg A;
     int ids[St::NBCH];
-    Sg::chunk_ids(ids, tab, 0, last_blk, a.NB);
-    A.load(kpool, vpool, ids, a.H_kv, g, tid);
-    A.template store<RAW>(sh_stage[0], tid, n, &sh_beyond);
-    Sg::chunk_ids(ids, tab, 1, last_blk, a.NB);
-    if (nch > 1) A.load(kpool, vpool, ids, a.H_kv, g, tid);
-    Sg::chunk_ids(ids, tab, 2, last_blk, a.NB);  // clamped: always inside the table row
-    __syncthreads();
-    float p[16], alpha;
-    for (int c = 0; c < nch; ++c) {
-      if (c + 1 < nch) {
-        A.template store<RAW>(sh_stage[(c + 1) % kStages], tid, n - 32 * (c + 1), &sh_beyond);
-        if (c + 2 < nch) {
-          A.load(kpool, vpool, ids, a.H_kv, g, tid);
+    if constexpr (KVT == PKV_BF16) {
+      // Iteration c: V of chunk c + 1 into its buffer; K of chunk c + 2 copied into the buffer of
+      // chunk c - 1 (read up to the previous barrier) and its V loaded; chunk c computed; then
+      // this wave's copies older than those of this iteration waited for, and the barrier.
+      using Sp = SplitStager<D, BS, NT>;
+      Sp A;
+      const int per_chunk = Sp::loads_per_chunk(w);
+      Sg::chunk_ids(ids, tab, 0, last_blk, a.NB);
+      Sp::copy_k(sh_b0, kpool, ids, a.H_kv, g, w, lane);
+      A.load_v(kpool, vpool, ids, a.H_kv, g, tid);
+      A.template store_v<RAW>(sh_b0, tid, n, &sh_beyond);
+      Sg::chunk_ids(ids, tab, 1, last_blk, a.NB);
+      if (nch > 1) {
+        Sp::copy_k(sh_b1, kpool, ids, a.H_kv, g, w, lane);
+        A.load_v(kpool, vpool, ids, a.H_kv, g, tid);
+      }
+      Sg::chunk_ids(ids, tab, 2, last_blk, a.NB);  // clamped: always inside the table row
+      wait_vmcnt(nch > 1 ? per_chunk : 0);
+      __syncthreads();
+      auto step = [&](int c, const char* cur, char* nx1, char* nx2) {
+        if (c + 1 < nch) A.template store_v<RAW>(nx1, tid, n - 32 * (c + 1), &sh_beyond);
+        const bool more = c + 2 < nch;
+        if (more) {
+          Sp::copy_k(nx2, kpool, ids, a.H_kv, g, w, lane);
+          A.load_v(kpool, vpool, ids, a.H_kv, g, tid);
           Sg::chunk_ids(ids, tab, c + 3, last_blk, a.NB);
         }
+        compute(raw_tag, c, cur);
+        wait_vmcnt(more ? per_chunk : 0);
+        barrier_lds();
+      };
+      for (int c = 0; c < nch; c += 3) {
+        step(c, sh_b0, sh_b1, sh_b2);
+        if (c + 1 < nch) step(c + 1, sh_b1, sh_b2, sh_b0);
+        if (c + 2 < nch) step(c + 2, sh_b2, sh_b0, sh_b1);
       }
-      if (32 * c <= p_wmax) {
-        const f32x16 s = chunk_scores<D>(sh_stage[c % kStages], qop, lane);
-        u32x4 ph[2], pl[2];
-        bool done = false;
-        // bf16 pools at D = 128 skip the optimistic pass: holding S through it costs spills there.
-        if constexpr (!RAW && (KVT != PKV_BF16 || D < 128)) {
-          if (32 * c + 31 <= p_min) {
-            // Optimistic pass against the running maximum: if no lane's 16 terms sum past 2^8, no
-            // term exceeds it, so the maximum would not move and these are the same P and l
-            // that the full step computes.  Otherwise (first chunk: m = -inf) the full step runs.
-#pragma unroll
-            for (int i = 0; i < 16; ++i) p[i] = exp2_fast(fmaf(s[i], sl, -m));
-            float ls = 0.f;
-            chunk_pack16(p, ls, ph);
-            done = __ballot(ls > kRescaleMax) == 0ull;
-            if (done) l += ls;
-          }
-        }
-        if (!done) {
-          const bool moved = 32 * c + 31 > p_min ? chunk_exp<true>(s, m, l, alpha, p, 32 * c, p_lane, sl, lane)
-                                                 : chunk_exp<false>(s, m, l, alpha, p, 32 * c, p_lane, sl, lane);
-          if (moved) {
-#pragma unroll
-            for (int t = 0; t < D / 32; ++t) acc[t] *= alpha;
-          }
-          if constexpr (RAW)
-            chunk_pack(p, l, ph, pl);
-          else
-            chunk_pack16(p, l, ph);
-        }
-        chunk_pv<D, BS, KVT, RAW>(sh_stage[c % kStages], ph, pl, acc, lane);
-      }
+    } else {
+      Sg A;
+      Sg::chunk_ids(ids, tab, 0, last_blk, a.NB);
+      A.load(kpool, vpool, ids, a.H_kv, g, tid);
+      A.template store<RAW>(sh_b0, tid, n, &sh_beyond);
+      Sg::chunk_ids(ids, tab, 1, last_blk, a.NB);
+      if (nch > 1) A.load(kpool, vpool, ids, a.H_kv, g, tid);
+      Sg::chunk_ids(ids, tab, 2, last_blk, a.NB);  // clamped: always inside the table row
       __syncthreads();
+      for (int c = 0; c < nch; ++c) {
+        if (c + 1 < nch) {
+          A.template store<RAW>((c & 1) ? sh_b0 : sh_b1, tid, n - 32 * (c + 1), &sh_beyond);
+          if (c + 2 < nch) {
+            A.load(kpool, vpool, ids, a.H_kv, g, tid);
+            Sg::chunk_ids(ids, tab, c + 3, last_blk, a.NB);
+          }
+        }
+        compute(raw_tag, c, (c & 1) ? sh_b1 : sh_b0);
+        __syncthreads();
+      }
     }
   };
   run(std::false_type{});
