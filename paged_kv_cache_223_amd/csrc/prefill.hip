@@ -72,6 +72,8 @@ __device__ __forceinline__ uint32_t pack_bf16_rne(float x, float y) {
 constexpr float kRescaleMax = 256.0f;  // 2^kRescaleLog2: the largest P term a running maximum allows
 static_assert(kRescaleLog2 == 8.0f, "kRescaleMax is 2^kRescaleLog2");
 
+constexpr int kOutStride = 36;  // floats per row of the epilogue tile (16-byte rows, 4-bank shift)
+
 // One 32-key chunk in LDS.  V holds two-byte elements: fp16 on the fast pass, the raw bf16 on the
 // rerun of a workgroup whose V does not fit fp16.
 template <int D, int BS, int KVT>
@@ -437,6 +439,7 @@ __global__ __launch_bounds__(64 * NW, 2) void prefill_kernel(PrefillArgs a) {
   __shared__ __align__(16) char sh_b0[St::kBytes];
   __shared__ __align__(16) char sh_b1[St::kBytes];
   __shared__ __align__(16) char sh_b2[KVT == PKV_BF16 ? St::kBytes : 16];
+  __shared__ __align__(16) float sh_out[NW * 32 * kOutStride];  // the epilogue's per-wave tiles
   const int tid = threadIdx.x, lane = tid & 63, w = uniform(tid >> 6);
   const int G = a.G;
   const int tok_per_wave = 32 / G;
@@ -501,8 +504,10 @@ __global__ __launch_bounds__(64 * NW, 2) void prefill_kernel(PrefillArgs a) {
   // Fast pass with V and P in fp16.  A bf16 V value that fp16 cannot hold (beyond +-65280, or not
   // finite) raises sh_beyond while the chunks are staged; the workgroup then runs again with the
   // pool's bf16 V and P as bf16 hi + lo parts, which holds any input (E4M3 values always fit).
+  // (cleared before a barrier that every staging store follows)
   __shared__ int sh_beyond;
   if (tid == 0) sh_beyond = 0;
+  __syncthreads();
   using Sg = Stager<D, BS, KVT, NT>;
   // One 32-key chunk of the wave's columns from a staged buffer: S = K Q^T, the online-softmax
   // step, P, O += V^T P^T.
@@ -609,23 +614,37 @@ __global__ __launch_bounds__(64 * NW, 2) void prefill_kernel(PrefillArgs a) {
   run(std::false_type{});
   if constexpr (KVT == PKV_BF16)
     if (uniform(sh_beyond)) run(std::true_type{});  // every store to sh_beyond was before the last barrier
-  // ---- normalise and write the column's row: acc[t] register i is head-dim row
-  // 32 t + 8 (i / 4) + 4 h + i % 4 of O^T
-  if (!qvalid) return;
+  // ---- normalise and write the wave's 32 output rows (row c = column c: token wtok0 + c / G,
+  // head g G + c % G), through a per-wave LDS tile one 32-dim segment at a time: acc[t] register i
+  // of lane (c, h) is dim 32 t + 8 (i / 4) + 4 h + i % 4 of row c; read back, eight lanes cover a
+  // row's 128-byte segment, so each store instruction writes 8 whole cache lines instead of 32-byte
+  // pieces of 32 rows.
   {
     const uint32_t u = __builtin_bit_cast(uint32_t, l);
     const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
     const uint32_t r0 = r[0], r1 = r[1];
     l = __builtin_bit_cast(float, r0) + __builtin_bit_cast(float, r1);
   }
-  const float f = (KVT == PKV_FP8_E4M3 ? a.v_scale[g] : 1.f) / l;
-  float* orow = a.out + ((size_t)(q0 + qtok) * a.H_q + g * G + col % G) * D;
+  const float f = (KVT == PKV_FP8_E4M3 ? a.v_scale[g] : 1.f) / l;  // lanes of invalid columns: never stored
+  const int rows = uniform(min(32, max(0, (C - wtok0) * G)));
+  float* tw = sh_out + w * (32 * kOutStride);
+  const size_t row0 = (size_t)(q0 + wtok0) * a.H_q + (size_t)g * G;
 #pragma unroll
-  for (int t = 0; t < D / 32; ++t)
+  for (int t = 0; t < D / 32; ++t) {
 #pragma unroll
     for (int k = 0; k < 4; ++k)
-      *(f32x4*)(orow + 32 * t + 8 * k + 4 * h) =
+      *(f32x4*)(tw + col * kOutStride + 8 * k + 4 * h) =
           f32x4{acc[t][4 * k] * f, acc[t][4 * k + 1] * f, acc[t][4 * k + 2] * f, acc[t][4 * k + 3] * f};
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+#pragma unroll
+    for (int qq = 0; qq < 4; ++qq) {
+      const int row = 8 * qq + (lane >> 3), ch = lane & 7;
+      const f32x4 v = *(const f32x4*)(tw + row * kOutStride + 4 * ch);
+      if (row < rows)
+        *(f32x4*)(a.out + (row0 + (size_t)(row / G) * a.H_q + row % G) * D + 32 * t + 4 * ch) = v;
+    }
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+  }
 }
 
 constexpr int kPrefillWaves = 12;
