@@ -618,7 +618,8 @@ __global__ __launch_bounds__(64 * NW, 2) void prefill_kernel(PrefillArgs a) {
   // head g G + c % G), through a per-wave LDS tile one 32-dim segment at a time: acc[t] register i
   // of lane (c, h) is dim 32 t + 8 (i / 4) + 4 h + i % 4 of row c; read back, eight lanes cover a
   // row's 128-byte segment, so each store instruction writes 8 whole cache lines instead of 32-byte
-  // pieces of 32 rows.
+  // pieces of 32 rows.  The stores are non-temporal: the output streams past the L2, which then
+  // keeps more of the segment's K/V for the other workgroups reading it.
   {
     const uint32_t u = __builtin_bit_cast(uint32_t, l);
     const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
@@ -641,7 +642,7 @@ __global__ __launch_bounds__(64 * NW, 2) void prefill_kernel(PrefillArgs a) {
       const int row = 8 * qq + (lane >> 3), ch = lane & 7;
       const f32x4 v = *(const f32x4*)(tw + row * kOutStride + 4 * ch);
       if (row < rows)
-        *(f32x4*)(a.out + (row0 + (size_t)(row / G) * a.H_q + row % G) * D + 32 * t + 4 * ch) = v;
+        __builtin_nontemporal_store(v, (f32x4*)(a.out + (row0 + (size_t)(row / G) * a.H_q + row % G) * D + 32 * t + 4 * ch));
     }
     __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
   }
