@@ -299,11 +299,14 @@ int pkv_paged_attn_decode_hinted(float* out, const void* q, int q_dtype, const v
  * the sequence appends nothing this step).
  *   k_new, v_new   device [B][H_kv][D] of src_dtype; new_slots device int64 [B]
  *   others         as pkv_paged_attn_decode / pkv_kv_append
- * With bf16 q, bf16 source and bf16 pools on the matrix-core path, the append
- * runs inside the decode launch: the piece that reads position n - 1 takes the
- * new token from k_new/v_new (the bits the append stores) and stores it into
- * the pool after its reads, saving the append launch.  Other combinations
- * issue the two calls.  In the fused form, a new_slots[b] that is not the slot
+ * With bf16 q and bf16 source rows into bf16 or E4M3 pools on the
+ * matrix-core path, the append runs inside the decode launch: the piece that
+ * reads position n - 1 takes the new token from k_new/v_new (as the append
+ * stores it: the bits of a bf16 pool, the codes of x / scale of an E4M3 pool,
+ * encoded as pkv_kv_append encodes them) and stores it into the pool after its
+ * reads, saving the append launch.  Other combinations issue the two calls.
+ * ("Paged Attention and KV Cache Fragmentation", section "Quantization as a
+ * way to stretch paged memory further", for the one-byte codes.)  In the fused form, a new_slots[b] that is not the slot
  * of position n - 1 (or a sequence with n = 0) is a caller error: the token is
  * then stored (when its position's piece exists) but not attended.
  *   sum_context_lens  host hint: the sum of context_lens[b] over the batch, as

@@ -489,8 +489,8 @@ int pkv_decode_step(float* out, const void* q, int q_dtype, const void* k_new, c
                     int32_t bs, float scale, const float* k_scale, const float* v_scale, void* workspace,
                     size_t workspace_bytes, void* stream) {
   g_err[0] = 0;
-  const bool fused = B > 0 && H_kv > 0 && H_q % H_kv == 0 && kv_dtype == PKV_BF16 && src_dtype == PKV_BF16 &&
-                     use_matrix_path(q_dtype, kv_dtype, H_q / H_kv, D, bs);
+  const bool fused = B > 0 && H_kv > 0 && H_q % H_kv == 0 && (kv_dtype == PKV_BF16 || kv_dtype == PKV_FP8_E4M3) &&
+                     src_dtype == PKV_BF16 && use_matrix_path(q_dtype, kv_dtype, H_q / H_kv, D, bs);
   if (!fused) {  // the two calls, in order, on the stream; the decode's arguments are checked first
     int st = decode_impl(out, q, q_dtype, k_pool, v_pool, kv_dtype, block_tables, max_blocks_per_seq, context_lens,
                          max_context_len, nullptr, nullptr, B, H_q, H_kv, D, NB, bs, scale, k_scale, v_scale,

@@ -8,9 +8,10 @@
 namespace pkv {
 
 // A sequence's length as the decode uses it: negative lengths count as 0 and lengths above the
-// launch's cap are cut to it.
+// launch's cap are cut to it.  Read through the constant address space (no kernel writes the
+// lengths), which keeps wave-uniform reads scalar.
 __device__ __forceinline__ int seq_len(const int32_t* __restrict__ lens, int b, int cap) {
-  int n = lens[b];
+  int n = ((const __attribute__((address_space(4))) int32_t*)lens)[b];
   return n < 0 ? 0 : (n > cap ? cap : n);
 }
 

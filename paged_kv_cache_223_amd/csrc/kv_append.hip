@@ -14,32 +14,11 @@
 
 #include <hip/hip_runtime.h>
 
+#include "e4m3_encode.h"
 #include "internal.h"
 
 namespace pkv {
 namespace {
-
-// fp32 -> OCP E4M3FN, round to nearest even; |y| >= 448 or inf saturates to
-// +-448 (code 0x7E), NaN -> 0x7F with the input's sign.  Integer bit work for
-// the normal range, an exact power-of-two scaling plus rint for subnormals.
-__device__ __forceinline__ uint32_t f32_to_e4m3(float y) {
-  const uint32_t u = __builtin_bit_cast(uint32_t, y);
-  const uint32_t sign = (u >> 24) & 0x80u;
-  const uint32_t a = u & 0x7FFFFFFFu;
-  if (a > 0x7F800000u) return sign | 0x7Fu;   // NaN
-  if (a >= 0x43E00000u) return sign | 0x7Eu;  // >= 448 (and inf)
-  const int e = (int)(a >> 23) - 127;
-  if (e >= -6) {  // normal E4M3: keep 3 of the 23 mantissa bits, ties to even
-    const uint32_t mant = a & 0x7FFFFFu;
-    const uint32_t q = mant >> 20, rem = mant & 0xFFFFFu;
-    uint32_t code = ((uint32_t)(e + 7) << 3) | q;
-    if (rem > 0x80000u || (rem == 0x80000u && (q & 1u))) code += 1u;  // carry into the exponent is correct
-    return sign | code;
-  }
-  // subnormal E4M3: value = k * 2^-9, k = rint(|y| * 2^9) in 0..8 (8 is the smallest normal)
-  const float k = __builtin_rintf(__builtin_bit_cast(float, a) * 512.0f);
-  return sign | (uint32_t)k;
-}
 
 template <int SRC, int DST>
 __global__ __launch_bounds__(256) void kv_append_kernel(AppendArgs p) {
@@ -94,10 +73,7 @@ __global__ __launch_bounds__(256) void kv_append_kernel(AppendArgs p) {
         const uint32_t w[4] = {x.x, x.y, x.z, x.w};
         const float sc = (which ? p.v_scale : p.k_scale)[g];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const float xv = __builtin_bit_cast(float, (w[j / 2] >> (16 * (j % 2))) << 16);
-          c[j] = f32_to_e4m3(xv / sc);
-        }
+        for (int j = 0; j < 8; ++j) c[j] = bf16_to_e4m3((w[j / 2] >> (16 * (j % 2))) & 0xFFFFu, sc);
       }
       uint8_t* pp = (uint8_t*)pool + tile;
       if (!which) {  // K: X = 16, this thread's 8 codes are half of a 16-byte group

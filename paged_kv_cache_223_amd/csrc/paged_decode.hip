@@ -72,6 +72,7 @@
 #include <mutex>
 
 #include "decode_common.h"
+#include "e4m3_encode.h"
 #include "internal.h"
 #include "tile_ops.h"
 #include "wave_scan.h"
@@ -267,17 +268,21 @@ __device__ __forceinline__ void process_chunk(const Chunk<D, BS, KVT>& ch, const
   }
 }
 
+// The fused step's new token of one (sequence, KV head) as E4M3 codes, K then V (D <= 128), in LDS.
+__shared__ __align__(16) uint8_t sh_newtok[2 * 128];
+
 // ---------------------------------------------------------------------------
 // fused step (append + decode): the step's new token of (b, g) at position n - 1
 // ---------------------------------------------------------------------------
 // Put the new token straight into the loaded operands of the chunk holding
-// position n - 1 (tk = its offset in the chunk, wave-uniform): in a bf16 pool
-// the append stores the row's bits as they are, so the decode sees the
+// position n - 1 (tk = its offset in the chunk, wave-uniform), as the pool will
+// hold it: a bf16 pool stores the row's bits as they are, an E4M3 pool the codes
+// of x / scale (the append's encoding, taken once per piece into LDS before the
+// chunk loop: codes[0, D) for K, codes[D, 2 D) for V), so the decode sees the
 // appended token while the pool store waits until after the chunk loop.
 template <int D, int BS, int KVT>
 __device__ __forceinline__ void inject_new_token(Chunk<D, BS, KVT>& ch, const DecodeArgs& a, int b, int g, int tk,
-                                                 int lane) {
-  static_assert(KVT == PKV_BF16, "the fused step serves bf16 pools");
+                                                 const uint8_t* codes, int lane) {
   const uint16_t* nk = (const uint16_t*)a.new_k + ((size_t)b * a.H_kv + g) * D;
   const uint16_t* nv = (const uint16_t*)a.new_v + ((size_t)b * a.H_kv + g) * D;
   const int m = lane & 15, kg = lane >> 4;
@@ -286,34 +291,59 @@ __device__ __forceinline__ void inject_new_token(Chunk<D, BS, KVT>& ch, const De
     for (int half = 0; half < 2; ++half) {
       if (half != (tk >> 4)) continue;
 #pragma unroll
-      for (int c = 0; c < Chunk<D, BS, KVT>::kKLoads; ++c) ch.k[half][c] = *(const u32x4*)(nk + (kg + 4 * c) * 8);
+      for (int c = 0; c < Chunk<D, BS, KVT>::kKLoads; ++c) {
+        if constexpr (KVT == PKV_BF16) {
+          ch.k[half][c] = *(const u32x4*)(nk + (kg + 4 * c) * 8);
+        } else {  // codes of dims 16 (kg + 4 c) .. + 15
+          ch.k[half][c] = *(const u32x4*)(codes + 16 * (kg + 4 * c));
+        }
+      }
     }
   }
   if (kg == (tk >> 3)) {  // V: element tk % 8 of lane (m, kg)'s 8 tokens of column 16 t + m
-    const int j = tk & 7, sh = 16 * (j & 1);
+    const int j = tk & 7;
 #pragma unroll
     for (int t = 0; t < D / 16; ++t) {
-      const uint32_t x = nv[16 * t + m];
+      if constexpr (KVT == PKV_BF16) {
+        const uint32_t x = nv[16 * t + m];
+        const int sh = 16 * (j & 1);
 #pragma unroll
-      for (int wd = 0; wd < 4; ++wd)
-        if (wd == j / 2) ch.v[t][wd] = (ch.v[t][wd] & ~(0xFFFFu << sh)) | (x << sh);
+        for (int wd = 0; wd < 4; ++wd)
+          if (wd == j / 2) ch.v[t][wd] = (ch.v[t][wd] & ~(0xFFFFu << sh)) | (x << sh);
+      } else {
+        const int sh = 8 * (j & 3);
+        const uint32_t code = codes[D + 16 * t + m];
+#pragma unroll
+        for (int wd = 0; wd < 2; ++wd)
+          if (wd == j / 4) ch.v[t][wd] = (ch.v[t][wd] & ~(0xFFu << sh)) | (code << sh);
+      }
     }
   }
 }
 
 // The pool store of the new token's K and V rows of head g (one wave, after
-// the chunk loop), the same bytes pkv_kv_append writes into a bf16 pool.
-template <int D, int BS>
-__device__ __forceinline__ void write_new_token(const DecodeArgs& a, int b, int g, long long slot, int lane) {
+// the chunk loop), the same bytes pkv_kv_append writes into the pool.
+template <int D, int BS, int KVT>
+__device__ __forceinline__ void write_new_token(const DecodeArgs& a, int b, int g, long long slot,
+                                                const uint8_t* codes, int lane) {
   const uint16_t* nk = (const uint16_t*)a.new_k + ((size_t)b * a.H_kv + g) * D;
   const uint16_t* nv = (const uint16_t*)a.new_v + ((size_t)b * a.H_kv + g) * D;
-  const size_t tile = ((size_t)(slot / BS) * a.H_kv + g) * (size_t)D * BS;  // bf16 elements
   const int off = (int)(slot % BS);
-  uint16_t* kp = (uint16_t*)a.k_pool + tile;
-  uint16_t* vp = (uint16_t*)a.v_pool + tile;
-  if (lane < D / 8)  // K [D/8][BS][8]: one 16-byte dim group per lane
-    *(u32x4*)(kp + ((size_t)lane * BS + off) * 8) = *(const u32x4*)(nk + lane * 8);
-  for (int d = lane; d < D; d += 64) vp[(size_t)d * BS + off] = nv[d];  // V [D][BS]
+  if constexpr (KVT == PKV_BF16) {
+    const size_t tile = ((size_t)(slot / BS) * a.H_kv + g) * (size_t)D * BS;  // bf16 elements
+    uint16_t* kp = (uint16_t*)a.k_pool + tile;
+    uint16_t* vp = (uint16_t*)a.v_pool + tile;
+    if (lane < D / 8)  // K [D/8][BS][8]: one 16-byte dim group per lane
+      *(u32x4*)(kp + ((size_t)lane * BS + off) * 8) = *(const u32x4*)(nk + lane * 8);
+    for (int d = lane; d < D; d += 64) vp[(size_t)d * BS + off] = nv[d];  // V [D][BS]
+  } else {
+    const size_t tile = ((size_t)(slot / BS) * a.H_kv + g) * (size_t)D * BS;  // bytes
+    uint8_t* kp = (uint8_t*)a.k_pool + tile;
+    uint8_t* vp = (uint8_t*)a.v_pool + tile;
+    if (lane < D / 16)  // K [D/16][BS][16]: one 16-code dim group per lane
+      *(u32x4*)(kp + ((size_t)lane * BS + off) * 16) = *(const u32x4*)(codes + 16 * lane);
+    for (int d = lane; d < D; d += 64) vp[(size_t)d * BS + off] = codes[D + d];  // V [D][BS]
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -503,7 +533,7 @@ __device__ __forceinline__ void proc_chunk(Chunk<D, BS, KVT>& X, const DecodeArg
                                            f32x4 (&acc)[D / 16], WaveState& st, int c, int n, int hlo, int hhi,
                                            float sl, int inject_chunk, int b, int g, int lane) {
   if constexpr (APPEND)
-    if (c == inject_chunk) inject_new_token(X, a, b, g, n - 1 - 32 * c, lane);
+    if (c == inject_chunk) inject_new_token(X, a, b, g, n - 1 - 32 * c, sh_newtok, lane);
   process_chunk(X, qop, acc, st, c, n, hlo, hhi, sl, lane);
 }
 
@@ -696,6 +726,16 @@ __global__ __launch_bounds__(64 * NW, KVT == PKV_FP8_E4M3 ? 3 : 2) void decode_p
       if (expect == new_slot) inject_chunk = uc;
     }
     inject_chunk = uniform(inject_chunk);
+    if constexpr (KVT == PKV_FP8_E4M3) {
+      if (writer) {  // the new token's codes, once, before any wave's chunk loop takes them
+        const uint16_t* nk = (const uint16_t*)a.new_k + ((size_t)b * a.H_kv + g) * D;
+        const uint16_t* nv = (const uint16_t*)a.new_v + ((size_t)b * a.H_kv + g) * D;
+        const float ks = a.k_scale[g], vsc = a.v_scale[g];
+        for (int e = tid; e < 2 * D; e += NT)
+          sh_newtok[e] = (uint8_t)(e < D ? bf16_to_e4m3(nk[e], ks) : bf16_to_e4m3(nv[e - D], vsc));
+        __syncthreads();
+      }
+    }
   }
   f32x4 acc[D / 16];
   WaveState st;
@@ -743,7 +783,7 @@ __global__ __launch_bounds__(64 * NW, KVT == PKV_FP8_E4M3 ? 3 : 2) void decode_p
   }
   if (np > 1) merge_if_last<NT>(a, b, g, np, first_pid, orow, tid);
   if constexpr (APPEND)
-    if (writer && w == 0) write_new_token<D, BS>(a, b, g, new_slot, lane);
+    if (writer && w == 0) write_new_token<D, BS, KVT>(a, b, g, new_slot, sh_newtok, lane);
 }
 
 // workgroups of decode_piece_kernel<D, BS, KVT, NW, APPEND> one CU holds at once
@@ -807,8 +847,7 @@ hipError_t launch_mfma_a(const DecodeArgs& a, hipStream_t s) {
 
 template <int D, int BS, int KVT>
 hipError_t launch_mfma_t(const DecodeArgs& a, hipStream_t s) {
-  if constexpr (KVT == PKV_BF16)  // the fused step exists for bf16 pools (the host routes the others)
-    if (a.new_k) return launch_mfma_a<D, BS, KVT, true>(a, s);
+  if (a.new_k) return launch_mfma_a<D, BS, KVT, true>(a, s);
   return launch_mfma_a<D, BS, KVT, false>(a, s);
 }
 

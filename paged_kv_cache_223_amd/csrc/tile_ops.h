@@ -34,10 +34,12 @@ __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_ex
 __device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
 
 // physical block of logical block j (clamped to the sequence's last block; an
-// id outside the pool is read as block 0 so that no access leaves the pool)
+// id outside the pool is read as block 0 so that no access leaves the pool).
+// The table is read through the constant address space: no kernel writes it, and
+// so its wave-uniform reads stay scalar loads whatever else a kernel stores.
 __device__ __forceinline__ int block_id(const int32_t* __restrict__ tab, int j, int last, int NB) {
   j = j > last ? last : j;
-  const int id = tab[j];
+  const int id = ((const __attribute__((address_space(4))) int32_t*)tab)[j];
   return (unsigned)id < (unsigned)NB ? id : 0;
 }
 
