@@ -31,7 +31,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "paged decode attention KV GB/s (% of HBM peak) and sequences/s per layer"
 HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E
-KERNEL_SOURCE = [os.path.join(ROOT, "paged_kv_cache_223_amd", "csrc", f) for f in ("paged_decode.hip", "decode_common.h", "tile_ops.h", "wave_scan.h")]
+KERNEL_SOURCE = [os.path.join(ROOT, "paged_kv_cache_223_amd", "csrc", f) for f in ("paged_decode.hip", "decode_common.h", "tile_ops.h", "wave_scan.h", "e4m3_encode.h")]
 COUNTERS = os.path.join(ROOT, "profiles", "decode_counters.json")
 PREFILL_SOURCE = [os.path.join(ROOT, "paged_kv_cache_223_amd", "csrc", f) for f in ("prefill.hip", "tile_ops.h")]
 PREFILL_COUNTERS = os.path.join(ROOT, "profiles", "prefill_counters.json")
