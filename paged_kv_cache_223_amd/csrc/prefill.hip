@@ -501,10 +501,11 @@ __global__ __launch_bounds__(64 * NW, 2) void prefill_kernel(PrefillArgs a) {
   float m = -INFINITY, l = 0.f;
   const char* kpool = (const char*)a.k_pool;
   const char* vpool = (const char*)a.v_pool;
-  // Fast pass with V and P in fp16.  A bf16 V value that fp16 cannot hold (beyond +-65280, or not
-  // finite) raises sh_beyond while the chunks are staged; the workgroup then runs again with the
-  // pool's bf16 V and P as bf16 hi + lo parts, which holds any input (E4M3 values always fit).
-  // (cleared before a barrier that every staging store follows)
+  // Fast pass with V and P in fp16.  A bf16 V value that fp16 cannot hold (a magnitude beyond 65280,
+  // infinities included; NaNs stay NaNs in fp16) raises sh_beyond while the chunks are staged; the
+  // workgroup then runs again with the pool's bf16 V and P as bf16 hi + lo parts, which holds any
+  // input (E4M3 values always fit).  The flag is cleared before a barrier that every staging store
+  // follows.
   __shared__ int sh_beyond;
   if (tid == 0) sh_beyond = 0;
   __syncthreads();
