@@ -69,8 +69,6 @@ __device__ __forceinline__ uint32_t pack_bf16_rne(float x, float y) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2{x, y}), bf16x2));
 }
 
-constexpr float kRescaleMax = 256.0f;  // 2^kRescaleLog2: the largest P term a running maximum allows
-static_assert(kRescaleLog2 == 8.0f, "kRescaleMax is 2^kRescaleLog2");
 
 constexpr int kOutStride = 36;  // floats per row of the epilogue tile (16-byte rows, 4-bank shift)
 
@@ -331,11 +329,11 @@ __device__ __forceinline__ f32x16 chunk_scores(const char* lds, const u32x4 (&qo
   return s;
 }
 
-// Online-softmax step of the lane's column over one chunk (branch-free): the chunk maximum (keys
-// past the column's position left out on a diagonal chunk), the running maximum m moved only when
-// the chunk exceeds it by more than 2^8 (then alpha = 2^(m_old - m_new) rescales l here, and the
-// accumulator at the caller before this chunk's PV), and P = 2^(s sl - m), 0 for masked keys.
-// sl >= 0.  Returns whether any lane moved its maximum.
+// Online-softmax step of the lane's column over one chunk: the chunk maximum (keys past the
+// column's position left out on a diagonal chunk), the running maximum m moved only when the
+// chunk exceeds it by more than 8 in log2 units (then alpha = 2^(m_old - m_new) rescales l here,
+// and the accumulator at the caller before this chunk's PV), and P = 2^(s sl - m), 0 for masked
+// keys.  sl >= 0.  Returns whether any lane moved its maximum.
 template <bool DIAG>
 __device__ __forceinline__ bool chunk_exp(const f32x16& s, float& m, float& l, float& alpha, float (&p)[16], int cs,
                                           int p_lane, float sl, int lane) {
@@ -346,24 +344,30 @@ __device__ __forceinline__ bool chunk_exp(const f32x16& s, float& m, float& l, f
     const bool keep = !DIAG || cs + 8 * (i / 4) + 4 * h + (i % 4) <= p_lane;
     cm = fmaxf(cm, keep ? s[i] : -INFINITY);
   }
-  {  // with lane l ^ 32 (the column's other 16 keys)
-    const uint32_t u = __builtin_bit_cast(uint32_t, cm);
-    const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
-    const uint32_t r0 = r[0], r1 = r[1];
-    cm = fmaxf(__builtin_bit_cast(float, r0), __builtin_bit_cast(float, r1));
+  // Off the diagonal, when no lane's own maximum passes m + 8 neither does any column's, so m,
+  // l and the accumulator stay as they are and the exchange and the rescale factor are skipped.
+  bool moved = false;
+  if (DIAG || __ballot(cm * sl > m + kRescaleLog2) != 0ull) {
+    {  // with lane l ^ 32 (the column's other 16 keys)
+      const uint32_t u = __builtin_bit_cast(uint32_t, cm);
+      const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+      const uint32_t r0 = r[0], r1 = r[1];
+      cm = fmaxf(__builtin_bit_cast(float, r0), __builtin_bit_cast(float, r1));
+    }
+    cm *= sl;
+    const bool need = cm > m + kRescaleLog2;
+    const float mu = need ? cm : m;
+    alpha = exp2_fast(m - mu);  // 1 where the maximum stays (0 on the first chunk: m = -inf)
+    l *= alpha;
+    m = mu;
+    moved = __ballot(need) != 0ull;
   }
-  cm *= sl;
-  const bool need = cm > m + kRescaleLog2;
-  const float mu = need ? cm : m;
-  alpha = exp2_fast(m - mu);  // 1 where the maximum stays (0 on the first chunk: m = -inf)
-  l *= alpha;
-  m = mu;
 #pragma unroll
   for (int i = 0; i < 16; ++i) {  // key 0 is in every column's range: m is finite
     const float e = exp2_fast(fmaf(s[i], sl, -m));
     p[i] = (!DIAG || cs + 8 * (i / 4) + 4 * h + (i % 4) <= p_lane) ? e : 0.f;
   }
-  return __ballot(need) != 0ull;
+  return moved;
 }
 
 // P = hi + lo in bf16 (hi truncates p, lo = p - hi rounds to nearest), summed into l, regrouped
@@ -518,33 +522,16 @@ __global__ __launch_bounds__(64 * NW, 2) void prefill_kernel(PrefillArgs a) {
     if (32 * c > p_wmax) return;
     const f32x16 s = chunk_scores<D>(buf, qop, lane);
     u32x4 ph[2], pl[2];
-    bool done = false;
-    // (bf16 pools at D = 128 keep the full step: holding S through the pass spills there)
-    if constexpr (!RAW && (KVT != PKV_BF16 || D < 128)) {
-      if (32 * c + 31 <= p_min) {
-        // Optimistic pass against the running maximum: if no lane's 16 terms sum past 2^8, no
-        // term exceeds it, so the maximum would not move and these are the same P and l that
-        // the full step computes.  Otherwise (first chunk: m = -inf) the full step runs.
+    const bool moved = 32 * c + 31 > p_min ? chunk_exp<true>(s, m, l, alpha, p, 32 * c, p_lane, sl, lane)
+                                           : chunk_exp<false>(s, m, l, alpha, p, 32 * c, p_lane, sl, lane);
+    if (moved) {
 #pragma unroll
-        for (int i = 0; i < 16; ++i) p[i] = exp2_fast(fmaf(s[i], sl, -m));
-        float ls = 0.f;
-        chunk_pack16(p, ls, ph);
-        done = __ballot(ls > kRescaleMax) == 0ull;
-        if (done) l += ls;
-      }
+      for (int t = 0; t < D / 32; ++t) acc[t] *= alpha;
     }
-    if (!done) {
-      const bool moved = 32 * c + 31 > p_min ? chunk_exp<true>(s, m, l, alpha, p, 32 * c, p_lane, sl, lane)
-                                             : chunk_exp<false>(s, m, l, alpha, p, 32 * c, p_lane, sl, lane);
-      if (moved) {
-#pragma unroll
-        for (int t = 0; t < D / 32; ++t) acc[t] *= alpha;
-      }
-      if constexpr (RAW)
-        chunk_pack(p, l, ph, pl);
-      else
-        chunk_pack16(p, l, ph);
-    }
+    if constexpr (RAW)
+      chunk_pack(p, l, ph, pl);
+    else
+      chunk_pack16(p, l, ph);
     chunk_pv<D, BS, KVT, RAW>(buf, ph, pl, acc, lane);
   };
   auto run = [&](auto raw_tag) {
