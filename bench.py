@@ -89,6 +89,9 @@ def parse():
     p.add_argument("--sets", type=int, default=0,
                    help="independent copies of the inputs the steps rotate through (0 = enough for 1 GB of "
                         "KV, so the 256 MB last-level cache cannot hold the working set)")
+    p.add_argument("--graph-steps", type=int, default=20,
+                   help="consecutive steps captured in one HIP graph for the timed replays (rounded up to a "
+                        "multiple of the input sets; 1 = one graph per step)")
     return p.parse_args()
 
 
@@ -296,7 +299,9 @@ def bench_decode(wkey, args, torch, pkv, dev, steps, warmup, cpu_seconds, headli
     decode_ms = np.array([e[1].elapsed_time(e[2]) for e in ev])
     eager_step_ms = ev[0][0].elapsed_time(ev[-1][2]) / K
     # the timed region: K whole steps (kv_append + decode), replayed from captured HIP graphs
-    graphs = None
+    graphs = multi = None
+    # steps per multi-step graph (a multiple of the input sets, so the rotation carries on across replays)
+    R = n_sets * math.ceil(args.graph_steps / n_sets) if args.graph_steps > 1 else 1
     if not args.eager:  # one captured step per input set, replayed in rotation
         graphs = []
         for i in range(n_sets):
@@ -304,24 +309,55 @@ def bench_decode(wkey, args, torch, pkv, dev, steps, warmup, cpu_seconds, headli
             with torch.cuda.graph(g):
                 step(i)
             graphs.append(g)
+        if R > 1 and K >= R:
+            multi = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(multi):
+                for i in range(R):
+                    step(i)
         for i in range(warmup):
             graphs[i % n_sets].replay()
+        if multi is not None:
+            multi.replay()
     torch.cuda.synchronize()
-    g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    t0 = time.perf_counter()
-    g0.record()
-    for i in range(K):
-        graphs[i % n_sets].replay() if graphs is not None else step(i)
-    g1.record()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    step_ms = g0.elapsed_time(g1) / K
-    print(f"# {wkey}: timed {K} steps in {wall:.3f}s wall ({'eager' if graphs is None else 'graph'}); "
-          f"step {step_ms * 1e3:.1f} us; eager decode p10/p50/p90 {np.percentile(decode_ms, 10) * 1e3:.1f}/"
+
+    def timed(multi_graph):
+        """K steps bracketed by device syncs; returns (ms per step, wall s)."""
+        g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0 = time.perf_counter()
+        g0.record()
+        if graphs is None:
+            for i in range(K):
+                step(i)
+        else:
+            done = 0
+            if multi_graph:
+                for _ in range(K // R):
+                    multi.replay()
+                done = K // R * R
+            for i in range(done, K):
+                graphs[i % n_sets].replay()
+        g1.record()
+        torch.cuda.synchronize()
+        return g0.elapsed_time(g1) / K, time.perf_counter() - t0
+
+    # one graph launch per step first (each launch then pays the gap before its kernel starts), then
+    # the timed region proper: R consecutive steps per graph launch, as a decode loop over a model's
+    # layers is captured, so the kernels of consecutive steps follow each other without that gap
+    single_ms = timed(False)[0] if multi is not None else None
+    step_ms, wall = timed(multi is not None)
+    print(f"# {wkey}: timed {K} steps in {wall:.3f}s wall ({'eager' if graphs is None else 'graph'}, "
+          f"{R if multi is not None else 1} per launch); step {step_ms * 1e3:.1f} us"
+          + ("" if single_ms is None else f" (one step per graph launch: {single_ms * 1e3:.1f} us)")
+          + f"; eager decode p10/p50/p90 {np.percentile(decode_ms, 10) * 1e3:.1f}/"
           f"{np.median(decode_ms) * 1e3:.1f}/{np.percentile(decode_ms, 90) * 1e3:.1f} us", file=sys.stderr, flush=True)
 
-    dec_avg_s = decode_ms.mean() / 1e3
     call_bytes = by["decode"] + (by["append"] if fused else 0)  # bytes of the timed call
+    # the call's average duration: where a step is that one launch, replayed from multi-step graphs,
+    # the events around the timed region give it without per-call event overhead (consecutive
+    # launches run back to back there); otherwise the events around each eager call
+    one_launch = fused or not len(mat.step_slots)
+    from_region = one_launch and multi is not None
+    dec_avg_s = step_ms / 1e3 if from_region else decode_ms.mean() / 1e3
     dec_gbps = call_bytes / dec_avg_s / 1e9
     step_gbps = (by["decode"] + by["append"]) / (step_ms / 1e3) / 1e9
     traffic = measured_traffic(wkey)
@@ -333,6 +369,9 @@ def bench_decode(wkey, args, torch, pkv, dev, steps, warmup, cpu_seconds, headli
         "frac": round(dec_gbps / HBM_PEAK_GBPS, 4),
         "algorithmic_bytes_per_launch": call_bytes,
         "avg_launch_us": round(dec_avg_s * 1e6, 2),
+        "launch_timing": ("HIP events around the timed region (one launch per step, back to back)" if from_region
+                          else "HIP events around each eager call"),
+        "eager_call_us_avg": round(float(decode_ms.mean()) * 1e3, 2),
         "traffic": traffic,
     }
     common = {
@@ -347,6 +386,8 @@ def bench_decode(wkey, args, torch, pkv, dev, steps, warmup, cpu_seconds, headli
                      ("" if sum_lens < 0 else " (with the host's length sum)"),
         "eager_ms_per_step": round(eager_step_ms, 5),
         "step_launch": "eager" if graphs is None else "hip_graph",
+        "steps_per_graph": None if graphs is None else (R if multi is not None else 1),
+        "ms_per_step_one_graph_per_step": None if single_ms is None else round(single_ms, 5),
         "decode_GBps_unique": round(dec_gbps, 1),
         "decode_GBps_logical": round(by["decode_logical"] / dec_avg_s / 1e9, 1),
         "kv_bytes_unique": by["kv_unique"],

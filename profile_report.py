@@ -3,7 +3,7 @@
 
 Reads the rocpd SQLite databases of five runs of one workload (all from the repository root):
 
-    rocprofv3 --kernel-trace --stats -T -d T -o trace -- python3 bench.py --workload W --only --steps 20 --warmup 5 --no-cpu-baseline
+    rocprofv3 --kernel-trace --stats -T -d T -o trace -- python3 bench.py --workload W --only --steps 100 --warmup 10 --no-cpu-baseline
     rocprofv3 --pmc FETCH_SIZE -T -d F -o fetch -- python3 bench.py --workload W --only --steps 3 --warmup 1 --no-cpu-baseline --eager
     rocprofv3 --pmc WRITE_SIZE -T -d R -o write -- python3 bench.py --workload W --only --steps 3 --warmup 1 --no-cpu-baseline --eager
     rocprofv3 --pmc FETCH_SIZE -T -d CF -o cf -- python3 bench.py --copy-calibration 1024
@@ -35,8 +35,9 @@ from bench import COUNTERS, KERNEL_SOURCE, PREFILL_COUNTERS, PREFILL_SOURCE, ROO
 DECODE_KERNELS = ("decode_piece_kernel",)  # cut segments are merged inside it
 COPY_BYTES = 1 << 30
 
+TRACE_STEPS = 100  # timed steps of the traced decode run: its last TRACE_STEPS dispatches
 TRACE_CMD = ("rocprofv3 --kernel-trace --stats -T -d <out> -o trace -- python3 bench.py --workload {w} --only "
-             "--steps 20 --warmup 5 --no-cpu-baseline")
+             f"--steps {TRACE_STEPS} --warmup 10 --no-cpu-baseline")
 PMC_CMD = ("timeout -s KILL 150 rocprofv3 --pmc {c} -T -d <out> -o {o} -- python3 bench.py --workload {w} --only "
            "--steps 3 --warmup 1 --no-cpu-baseline --eager")
 COPY_CMD = "timeout -s KILL 90 rocprofv3 --pmc {c} -T -d <out> -o {o} -- python3 bench.py --copy-calibration 1024"
@@ -102,6 +103,29 @@ def dispatch_durations(d, kernel):
     con = _db(d)
     return [dur / 1e3 for name, dur in con.execute("select name, duration from kernels order by start")
             if _short(name) == kernel]
+
+
+def dispatch_spans(d, kernel):
+    """(start, end) in ns of every dispatch of `kernel`, in launch order."""
+    con = _db(d)
+    return [(st, en) for name, st, en in con.execute("select name, start, end from kernels order by start")
+            if _short(name) == kernel]
+
+
+def timed_region_lines(d, kernel, k):
+    """Statistics of the last k dispatches of `kernel` (a bench run's timed steps, replayed back to back
+    from multi-step graphs): durations, the gaps between consecutive ones, and the span per dispatch."""
+    sp = dispatch_spans(d, kernel)[-k:]
+    if len(sp) < 2:
+        return [], None
+    dur = sorted((en - st) / 1e3 for st, en in sp)
+    gaps = sorted((sp[i + 1][0] - sp[i][1]) / 1e3 for i in range(len(sp) - 1))
+    avg = sum(dur) / len(dur)
+    per = (sp[-1][1] - sp[0][0]) / 1e3 / len(sp)
+    return [f"Timed region ({kernel}, the last {len(sp)} dispatches: the bench's timed steps, replayed from "
+            f"multi-step graphs): duration average {avg:.2f} us, median {dur[len(dur) // 2]:.2f}, min {dur[0]:.2f}, "
+            f"max {dur[-1]:.2f}; gap from one dispatch's end to the next one's start median {gaps[len(gaps) // 2]:.2f} "
+            f"us, min {gaps[0]:.2f}, max {gaps[-1]:.2f}; span of the region per dispatch {per:.2f} us."], per
 
 
 def _calibration(cf_dir, cw_dir):
@@ -205,8 +229,15 @@ def report_decode(w, t_dir, f_dir, r_dir, cf_dir, cw_dir, kernels=DECODE_KERNELS
         json.dump(rec, f, indent=1, sort_keys=True)
         f.write("\n")
 
+    region, per = timed_region_lines(t_dir, DECODE_KERNELS[0], TRACE_STEPS)
+    if per is not None and DECODE_KERNELS[0] in entry:
+        entry[DECODE_KERNELS[0]]["us_per_timed_step_trace"] = round(per, 3)
+    with open(COUNTERS, "w") as f:
+        json.dump(rec, f, indent=1, sort_keys=True)
+        f.write("\n")
     L = [f"# paged decode on MI355X: workload `{w}`", "",
-         "Kernel trace (rocprofv3 --kernel-trace --stats), one GPU: 20 timed + 5 warm-up steps, the eager",
+         f"Kernel trace (rocprofv3 --kernel-trace --stats), one GPU: {TRACE_STEPS} timed steps twice (one graph",
+         "launch per step, then the timed region proper: multi-step graph launches), 10 warm-up steps, the eager",
          "per-call timing pass, and the bench's setup (prefill appends, a 4 GiB read-ceiling probe).", "",
          "Command (from the repository root):", "", "    " + TRACE_CMD.format(w=w), "",
          "| kernel | calls | total us | average us | % |", "|---|---|---|---|---|"]
@@ -218,6 +249,7 @@ def report_decode(w, t_dir, f_dir, r_dir, cf_dir, cw_dir, kernels=DECODE_KERNELS
             g, wg, v, ag, sg, lds, scr = launch[k]
             L.append(f"{k} launch: grid {g} threads in workgroups of {wg}; VGPR field {v}, AGPR {ag}, "
                      f"SGPR {sg}, LDS {lds} B, scratch {scr} B.")
+    L += [""] + region
     L += ["", "With bf16 pools the step's append runs inside decode_piece_kernel (pkv_decode_step), so every",
           "kv_append call is the setup's prefill; with E4M3 pools the step's kv_append calls are the short ones.", "",
           "## HBM traffic (rocprofv3 --pmc, one counter per run)", "", "Commands:", "",
