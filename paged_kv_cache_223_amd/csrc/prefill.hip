@@ -599,6 +599,16 @@ __global__ __launch_bounds__(64 * NW, 2) void prefill_kernel(PrefillArgs a) {
       }
     }
   };
+  // E4M3 pools: fixed wave priorities (waves 8-11 highest, then 4-7; the first 512 threads stage a
+  // chunk at D = 128), so that after each barrier the waves of a SIMD do not all issue their
+  // QK^T, softmax and PV in step: the first reaches its softmax while the others still use the
+  // matrix core (+1.3 % on the 70B shape; with bf16 pools every order measured was slower).
+  if constexpr (KVT == PKV_FP8_E4M3) {
+    if (w >= 8)
+      __builtin_amdgcn_s_setprio(2);
+    else if (w >= 4)
+      __builtin_amdgcn_s_setprio(1);
+  }
   run(std::false_type{});
   if constexpr (KVT == PKV_BF16)
     if (uniform(sh_beyond)) run(std::true_type{});  // every store to sh_beyond was before the last barrier
