@@ -300,8 +300,7 @@ def bench_decode(wkey, args, torch, pkv, dev, steps, warmup, cpu_seconds, headli
     eager_step_ms = ev[0][0].elapsed_time(ev[-1][2]) / K
     # the timed region: K whole steps (kv_append + decode), replayed from captured HIP graphs
     graphs = multi = None
-    # steps per multi-step graph (a multiple of the input sets, so the rotation carries on across replays)
-    R = n_sets * math.ceil(args.graph_steps / n_sets) if args.graph_steps > 1 else 1
+    R = steps_per_graph(args.graph_steps, n_sets)
     if not args.eager:  # one captured step per input set, replayed in rotation
         graphs = []
         for i in range(n_sets):
@@ -630,6 +629,12 @@ def bench_paths(args, torch, pkv, dev):
                                              "scattered tables", "B": B, "context": n, "H_kv": H_kv, "head_dim": D,
                                  "block_size": bs},
                       "rows": rows}), flush=True)
+
+
+def steps_per_graph(graph_steps, n_sets):
+    """Steps captured in one multi-step graph: `graph_steps` rounded up to a multiple of the input
+    sets, so that the rotation through them carries on across replays; 1 = one graph per step."""
+    return n_sets * math.ceil(graph_steps / n_sets) if graph_steps > 1 else 1
 
 
 def block_waste(tables, lens, bs):

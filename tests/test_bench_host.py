@@ -74,3 +74,13 @@ def test_bench_refuses_more_than_one_gpu():
                        text=True, timeout=120)
     assert r.returncode == 2
     assert "one GPU" in r.stderr
+
+
+def test_steps_per_graph_keeps_the_input_rotation():
+    assert bench.steps_per_graph(1, 1) == 1 and bench.steps_per_graph(1, 2) == 1
+    assert bench.steps_per_graph(20, 1) == 20 and bench.steps_per_graph(20, 2) == 20
+    assert bench.steps_per_graph(7, 2) == 8 and bench.steps_per_graph(2, 3) == 3
+    for gs in range(2, 30):
+        for n in range(1, 5):
+            r = bench.steps_per_graph(gs, n)
+            assert r % n == 0 and gs <= r < gs + n
