@@ -256,6 +256,53 @@ def test_captured_step_replays_match_eager():
 
 
 @pytest.mark.parametrize("kv", ["bf16", "e4m3"])
+def test_consecutive_calls_in_one_graph_share_the_workspace(kv):
+    """Four decode calls captured back to back in one HIP graph (as a decode loop over a model's
+    layers is captured, and as the bench replays its timed steps), each with its own q and output
+    but one shared workspace, on a batch whose long segments are cut and merged inside the launch:
+    on every replay each call's output equals the same call made eagerly."""
+    import paged_kv_cache_223_amd as pkv
+    rng = np.random.default_rng(61)
+    lens = np.unique(np.geomspace(1, 6000, 40).astype(int)).tolist()
+    lens = [int(n) for n in rng.permutation(lens)]
+    case = workloads.custom(f"graph_{kv}", len(lens), 32, 8, 128, 16, kv, "bf16", lens, seed=6100 + len(kv))
+    mat = materialize_with_model(case)
+    kp, vp = oracle_pools(case, mat)
+    dev = device_inputs(case, mat, kp, vp)
+    R = 4
+    qs = [dev["q"]] + [(dev["q"] * (1.0 + 0.25 * r)).contiguous() for r in range(1, R)]
+    outs = [torch.empty((case.B, 32, 128), dtype=torch.float32, device=DEV) for _ in range(R)]
+    ws = pkv.decode_workspace(case.B, 32, 128, case.max_context_len, case.bs, H_kv=8)
+
+    def call(r):
+        pkv.paged_attn_decode(qs[r], dev["k_pool"], dev["v_pool"], dev["block_tables"], dev["context_lens"],
+                              float(case.scale), dev["k_scale"], dev["v_scale"],
+                              max_context_len=case.max_context_len, out=outs[r], workspace=ws)
+
+    for r in range(R):
+        call(r)
+    torch.cuda.synchronize()
+    eager = [o.clone() for o in outs]
+    ref = oracle_decode(case, mat, kp, vp)
+    err = row_rel_err(eager[0].cpu().numpy().astype(np.float64), ref)
+    print(f"graph_{kv}: eager call 0 max row rel err {err:.3e}", flush=True)
+    assert err <= tol(case)
+    assert not torch.equal(eager[0], eager[1])  # the calls are told apart
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for r in range(R):
+            call(r)
+    for i in range(3):
+        for o in outs:
+            o.fill_(float("nan"))  # eager work between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for r in range(R):
+            assert torch.equal(outs[r], eager[r]), f"replay {i}: call {r} differs from the eager call"
+
+
+@pytest.mark.parametrize("kv", ["bf16", "e4m3"])
 def test_decode_many_segments_mixed_lengths(kv):
     """More (sequence, KV head) segments than one round of wide workgroups holds: the
     narrow-workgroup plan, with long sequences cut into pieces and short ones whole."""
