@@ -72,6 +72,11 @@ def parse():
     p.add_argument("--chunk", type=int, default=2048, help="new tokens per sequence (--op prefill)")
     p.add_argument("--seqs", type=int, default=4, help="sequences (--op prefill)")
     p.add_argument("--prefill-kv", default="bf16", choices=["bf16", "e4m3"], help="KV pool type (--op prefill)")
+    p.add_argument("--prefill-hq", type=int, default=64, choices=[8, 16, 32, 64, 128],
+                   help="query heads over 8 KV heads (--op prefill; 64 = the 70B layer, G = 8)")
+    p.add_argument("--prefill-d", type=int, default=128, choices=[64, 128], help="head dim (--op prefill)")
+    p.add_argument("--prefill-waves", type=int, default=0, choices=[0, 8, 12],
+                   help="prefill workgroup size (--op prefill; 0 = the library's automatic choice)")
     p.add_argument("--blocks", type=int, default=4096, help="blocks moved per swap call (--op swap)")
     p.add_argument("--pairs", type=int, default=4096, help="block pairs per copy_blocks call (--op copy_blocks)")
     p.add_argument("--unfused", action="store_true",
@@ -762,11 +767,12 @@ def bench_swap(args, torch, pkv, dev):
 
 
 def bench_prefill(args, torch, pkv, dev):
-    """Causal chunked prefill on the 70B layer shape (H_q 64, H_kv 8, D 128, bf16, bs 16): `seqs`
+    """Causal chunked prefill on the 70B layer shape (H_q 64, H_kv 8, D 128, bf16, bs 16; other query
+    head counts and head dims by option): `seqs`
     sequences, each with `prior` earlier tokens and a `chunk` of new ones (appended before the
     timed region).  FLOPs count the two products over the causal range only:
     4 * H_q * D * sum over queries of (position + 1)."""
-    H_q, H_kv, D, bs = 64, 8, 128, 16
+    H_q, H_kv, D, bs = args.prefill_hq, 8, args.prefill_d, 16
     B, prior, C = args.seqs, args.prior, args.chunk
     n = prior + C
     nb = -(-n // bs)
@@ -799,6 +805,8 @@ def bench_prefill(args, torch, pkv, dev):
     def call():
         pkv.paged_prefill(q, k_pool, v_pool, tab_d, lens_d, qs, scale, C, k_scale, v_scale, out=out)
 
+    pkv.set_prefill_waves(args.prefill_waves)
+
     for _ in range(args.warmup):
         call()
     torch.cuda.synchronize()
@@ -815,14 +823,15 @@ def bench_prefill(args, torch, pkv, dev):
     avg_s = ms.mean() / 1e3
     tf = flops / avg_s / 1e12
     print(f"# prefill: {K} timed calls, average {avg_s * 1e6:.1f} us, {tf:.1f} TFLOP/s", file=sys.stderr, flush=True)
-    wkey = f"prefill_{args.prefill_kv}_{B}x{prior}+{C}"
+    wkey = f"prefill_{args.prefill_kv}_{B}x{prior}+{C}" + ("" if (H_q, D) == (64, 128) else f"_hq{H_q}_d{D}")
     res = {
         "metric": "paged prefill TFLOP/s (causal, bf16 MFMA)", "value": round(tf, 1), "unit": "TFLOP/s",
         "n_gpus": 1, "steps": K, "warmup": args.warmup, "ms_per_step": round(float(ms.mean()), 4),
         "higher_is_better": True, "dtype": "bf16", "data": "synthetic (N(0,1) K/V/q, allocator-scattered tables)",
-        "config": {"workload": f"{B} sequences x ({prior} earlier + {C} new tokens), 70B layer shape "
-                               f"(H_q 64, H_kv 8, D 128, bs 16), {args.prefill_kv} KV", "seqs": B, "prior": prior,
-                   "chunk": C, "kv": args.prefill_kv},
+        "config": {"workload": f"{B} sequences x ({prior} earlier + {C} new tokens), "
+                               + ("70B layer shape " if (H_q, D) == (64, 128) else "")
+                               + f"(H_q {H_q}, H_kv 8, D {D}, bs 16), {args.prefill_kv} KV", "seqs": B, "prior": prior,
+                   "chunk": C, "kv": args.prefill_kv, "prefill_waves": args.prefill_waves or "auto"},
         "us_p50": round(float(np.median(ms)) * 1e3, 1), "flops_per_call": flops,
         "roofline": {"bound": "mfma", "kernel": "prefill_kernel", "achieved": round(tf, 1), "peak": 2500.0,
                      "unit": "TFLOP/s", "frac": round(tf / 2500.0, 4), "avg_launch_us": round(avg_s * 1e6, 2),

@@ -242,6 +242,21 @@ enum pkv_decode_path { PKV_DECODE_PATH_AUTO = 0, PKV_DECODE_PATH_VECTOR = 1 };
 int pkv_set_decode_path(int path);
 
 /*
+ * Design (not on the pages): the prefill's workgroup size.  pkv_paged_prefill
+ * runs 12-wave workgroups, or 8-wave ones (finer query tiles) when 12-wave
+ * ones would give the device fewer work items than it has compute units.
+ * pkv_set_prefill_waves(8 or 12) forces one size for every later call in the
+ * process, to test and compare the two; 0 restores the automatic choice.
+ * Each wave computes the same 32 columns either way, so the results are the
+ * same bits, except for bf16 V beyond fp16's range: the workgroups that hold
+ * such keys run again with bf16 V, and the two sizes cut the queries into
+ * different workgroups.  Returns the previous setting, or
+ * PKV_ERR_INVALID_ARG for another value.  A prefill already enqueued is not
+ * affected.
+ */
+int pkv_set_prefill_waves(int nw);
+
+/*
  * pkv_paged_attn_decode_noalloc — pkv_paged_attn_decode without a workspace
  * argument.  Design, for the callers that cannot allocate device memory: code
  * under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.  The

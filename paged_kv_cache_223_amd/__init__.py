@@ -48,6 +48,7 @@ SIGNATURES = {
     "pkv_last_error": (ctypes.c_char_p, []),
     "pkv_abi_version": (ctypes.c_int, []),
     "pkv_set_decode_path": (ctypes.c_int, [ctypes.c_int]),
+    "pkv_set_prefill_waves": (ctypes.c_int, [ctypes.c_int]),
     "pkv_kv_append": (ctypes.c_int, [_P, _P, ctypes.c_int, _P, _I32, _P, _P, ctypes.c_int, _I32, _I32, _I32,
                                      _I32, _P, _P, _P]),
     "pkv_copy_blocks": (ctypes.c_int, [_P, _P, ctypes.c_int, _I32, _I32, _I32, _I32, _P, _P, _I32, _P]),
@@ -144,6 +145,14 @@ def _check(st: int):
 def set_decode_path(path: int) -> int:
     """Process-wide decode kernel choice (DECODE_PATH_AUTO or DECODE_PATH_VECTOR); returns the previous one."""
     st = lib.pkv_set_decode_path(int(path))
+    if st < 0:
+        raise PkvError(st, last_error())
+    return st
+
+
+def set_prefill_waves(nw: int) -> int:
+    """Process-wide prefill workgroup size (0 = automatic, 8 or 12 waves); returns the previous one."""
+    st = lib.pkv_set_prefill_waves(int(nw))
     if st < 0:
         raise PkvError(st, last_error())
     return st
@@ -583,5 +592,5 @@ __all__ = ["lib", "LIB_PATH", "PkvError", "last_error", "kv_append", "copy_block
            "decode_workspace_bytes",
            "decode_workspace",
            "pool_shapes", "dtype_code", "stream_read", "copy_", "Allocator", "SIGNATURES",
-           "set_decode_path", "DECODE_PATH_AUTO", "DECODE_PATH_VECTOR",
+           "set_decode_path", "DECODE_PATH_AUTO", "DECODE_PATH_VECTOR", "set_prefill_waves",
            "F32", "BF16", "FP8_E4M3"]

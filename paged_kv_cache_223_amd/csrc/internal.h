@@ -155,8 +155,9 @@ struct PrefillArgs {
   int kv_dtype;
   int items;           // B * H_kv * groups_per_seq work items
   int groups_per_seq;  // tile groups that cover the longest chunk
+  int nw;              // waves per workgroup: 12, or 8 where 12 would leave CUs without work
 };
-int prefill_wg_tokens(int G);  // query tokens one workgroup covers
+int prefill_wg_tokens(int G, int nw);  // query tokens one workgroup of nw waves covers
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t s);
 
 // whole-block moves of both pools: pool -> pool (copy-on-write pairs),

@@ -28,7 +28,9 @@
 // NW * 32 / G consecutive query tokens of one (sequence, KV head); measured on
 // the 70B layer shape, 12 waves beat 8 and 4, and a software-pipelined loop
 // (the next chunk's QK^T under this chunk's softmax) lost for want of
-// registers.  They share every 32-key K/V chunk through LDS.  E4M3 pools: the
+// registers.  Where 12-wave workgroups would leave compute units idle (few
+// work items: small batches, small G), the host launches 8-wave ones; each
+// wave's columns and chunks are the same either way.  They share every 32-key K/V chunk through LDS.  E4M3 pools: the
 // workgroup copies a chunk's pool tiles through registers into one of two LDS
 // buffers while the waves compute the previous chunk from the other, with the
 // chunk after that already loading into registers.  bf16 pools: K tiles go
@@ -646,12 +648,13 @@ __global__ __launch_bounds__(64 * NW, 2) void prefill_kernel(PrefillArgs a) {
   }
 }
 
-constexpr int kPrefillWaves = 12;
-
 template <int D, int BS, int KVT>
 hipError_t launch_prefill_t(const PrefillArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL((prefill_kernel<D, BS, KVT, kPrefillWaves>), dim3((unsigned)((a.items + 7) / 8 * 8)),
-                     dim3(64 * kPrefillWaves), 0, s, a);
+  const dim3 grid((unsigned)((a.items + 7) / 8 * 8));
+  if (a.nw == 8)
+    hipLaunchKernelGGL((prefill_kernel<D, BS, KVT, 8>), grid, dim3(64 * 8), 0, s, a);
+  else
+    hipLaunchKernelGGL((prefill_kernel<D, BS, KVT, 12>), grid, dim3(64 * 12), 0, s, a);
   return hipGetLastError();
 }
 
@@ -666,7 +669,7 @@ hipError_t launch_prefill_bs(const PrefillArgs& a, hipStream_t s) {
 
 }  // namespace
 
-int prefill_wg_tokens(int G) { return kPrefillWaves * (32 / G); }
+int prefill_wg_tokens(int G, int nw) { return nw * (32 / G); }
 
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t s) {
   if (a.kv_dtype == PKV_BF16)

@@ -152,6 +152,19 @@ def test_decode_path_setting_round_trips_and_rejects_unknown_values():
     assert pkv.set_decode_path(pkv.DECODE_PATH_AUTO) == pkv.DECODE_PATH_AUTO
 
 
+def test_prefill_waves_setting_round_trips_and_rejects_unknown_values():
+    assert pkv.set_prefill_waves(12) == 0
+    try:
+        assert pkv.set_prefill_waves(8) == 12
+        assert pkv.lib.pkv_set_prefill_waves(4) == pkv.ERR_INVALID_ARG
+        assert "unknown workgroup size" in pkv.last_error()
+        with pytest.raises(pkv.PkvError):
+            pkv.set_prefill_waves(-1)
+    finally:  # a refused value leaves the setting as it was
+        assert pkv.set_prefill_waves(0) == 8
+    assert pkv.set_prefill_waves(0) == 0
+
+
 # dummy non-null device pointers: every call below must fail validation before touching them
 P = ctypes.c_void_p(0x1000)
 

@@ -99,17 +99,47 @@ SMALL = {
 }
 
 
+class waves:
+    """Forces the prefill's workgroup size (0 = automatic) for the block, then restores it."""
+
+    def __init__(self, nw):
+        self.nw = nw
+
+    def __enter__(self):
+        self.prev = pkv.set_prefill_waves(self.nw)
+
+    def __exit__(self, *exc):
+        pkv.set_prefill_waves(self.prev)
+
+
+@pytest.mark.parametrize("nw", [0, 12])
 @pytest.mark.parametrize("kv_dtype", ["bf16", "e4m3"])
 @pytest.mark.parametrize("name", sorted(SMALL))
-def test_prefill_matches_oracle(name, kv_dtype):
-    print(f"prefill {name} {kv_dtype}", flush=True)
+def test_prefill_matches_oracle(name, kv_dtype, nw):
+    """Every small case with the automatic workgroup size (8 waves for these few work items) and
+    with 12-wave workgroups forced."""
+    print(f"prefill {name} {kv_dtype} waves {nw}", flush=True)
     c = Case(**SMALL[name], kv_dtype=kv_dtype, seed=sum(map(ord, name))).device()
-    got = c.prefill()
+    with waves(nw):
+        got = c.prefill()
     kp, vp = c.oracle_pools()
     ref = oracle.ref_prefill(c.q, "bf16", kp, vp, kv_dtype, c.tables, np.array(c.lens, np.int32), c.query_start,
                              c.scale, c.bs, c.k_scale, c.v_scale)
     assert np.isfinite(got).all()
     assert row_rel_err(got, ref) <= (2e-2 if kv_dtype == "e4m3" else 2e-3)
+
+
+@pytest.mark.parametrize("kv_dtype", ["bf16", "e4m3"])
+@pytest.mark.parametrize("name", sorted(SMALL))
+def test_prefill_workgroup_sizes_give_the_same_bits(name, kv_dtype):
+    """8- and 12-wave workgroups: each wave computes the same 32 columns over the same chunks, so
+    with V inside fp16's range the outputs are equal bit for bit."""
+    c = Case(**SMALL[name], kv_dtype=kv_dtype, seed=sum(map(ord, name))).device()
+    with waves(8):
+        a = c.prefill()
+    with waves(12):
+        b = c.prefill()
+    assert np.array_equal(a, b)
 
 
 @pytest.mark.parametrize("kv_dtype", ["bf16", "e4m3"])
